@@ -1,0 +1,269 @@
+/*
+ * libmoe -- forward pass of a sparse Mixture-of-Experts feed-forward layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it:
+ *   - a linear router gives one logit per expert ("Every parameter, every
+ *     token", section "The gating network"; "Zen MoDE: Mixture of Distilled
+ *     Experts Architecture", section "Router Architecture", standard router
+ *     equation);
+ *   - the k largest are kept and their softmax renormalised into gates that
+ *     sum to one (same sections);
+ *   - an optional per-expert bias moves the selection only ("Zen-Max: Maximum
+ *     Capability via Mixture-of-Experts Architecture", section
+ *     "Auxiliary-Loss-Free Load Balancing");
+ *   - an optional per-expert capacity drops pairs over the budget ("Every
+ *     parameter, every token", section "A budget"; Zen MoDE, section
+ *     "Adaptive Capacity Factors");
+ *   - each token runs its k SwiGLU experts (Zen-Max, section "Fine-Grained
+ *     Expert Architecture", expert equation) plus any always-on shared experts
+ *     (same section; "Every parameter, every token", section "A shared
+ *     expert"), and the output is the gate-weighted sum ("The gating network");
+ *   - the Switch balance statistics f, P and alpha*N*sum(f*P) are emitted
+ *     alongside (Zen MoDE, section "Auxiliary Load Balancing Loss";
+ *     "Every parameter, every token", section "A balance penalty").
+ *
+ * One layer call is five library calls on one stream:
+ *   moe_route -> moe_permute -> moe_expert_swiglu (routed experts; and once
+ *   more for the shared experts) -> moe_combine, plus moe_balance_stats.
+ *
+ * General contract
+ *   - Every pointer is a DEVICE pointer unless marked (host).  Buffers are
+ *     owned by the caller; the library never allocates or frees memory and
+ *     keeps no device state besides its code objects.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream) and never synchronises.  Device-resident sizes (expert
+ *     counts and offsets) stay on the device.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is enqueued and moe_last_error() describes it.
+ *     MOE_EINVAL: a required pointer is NULL or a size is out of range.
+ *     MOE_EUNSUPPORTED: a shape these kernels do not implement.
+ *     MOE_EWORKSPACE: ws_bytes is below the size the *_workspace query gave.
+ *     MOE_EHIP: a kernel launch failed (hipGetLastError after the launch).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into.  Inputs are read only.
+ *     Inputs, outputs and workspace must not overlap.
+ *   - Token count T = 0 is a valid no-op (moe_permute then writes zero counts
+ *     and offsets, moe_balance_stats zero statistics).
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs (no floating-point atomics, fixed reduction orders).
+ *   - Calls on different streams with different buffers may run concurrently.
+ *
+ * Layouts (row-major, contiguous)
+ *   x         [T, d]          activations, dtype dt
+ *   w_router  [E, d]          router rows, dtype dt
+ *   w_gate    [G, h, d]       per-expert gate projection (the transpose of the
+ *   w_up      [G, h, d]       page's right-multiplied x W form, so every GEMM
+ *   w_down    [G, d, h]       operand is contiguous along its reduction axis)
+ *   pair p = t*k + j is slot j of token t.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* moe_route flag: skip the router GEMM and read the logits the caller put in
+ * `logits` (used to test selection on identical logits). */
+#define MOE_ROUTE_LOGITS_IN 1u
+
+/* Limits of these kernels (MOE_EUNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 32
+
+/* Version of this interface (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static description of a status code (host string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Detail of the last failed call on this host thread (host string, never
+ * NULL; empty after a successful call). */
+const char* moe_last_error(void);
+
+/* Per-expert token budget C = ceil(cf * T * k / E).
+ * "Zen MoDE", section "Adaptive Capacity Factors": capacity = factor * tokens /
+ * experts; "Every parameter, every token", section "A budget": a factor above
+ * one leaves slack.  Reading: tokens are counted as routed pairs T*k, and the
+ * quotient is rounded up.  cf is read as the shortest decimal that
+ * round-trips to the double (1.1 means 11/10) and the product is rounded up
+ * exactly, in integer arithmetic.  Returns -1 (unlimited) for cf <= 0 or a
+ * non-finite cf, -2 for T < 0, k < 1 or E < 1; saturates at INT64_MAX. */
+int64_t moe_capacity(double cf, int64_t T, int k, int E);
+
+/* ------------------------------------------------------------------------ */
+/* moe_route: router logits, top-k selection and renormalised gates.
+ *
+ *   logits[t,e] = sum_i x[t,i] * w_router[e,i] + logit_bias[e]      (fp32)
+ *   key[t,e]    = logits[t,e] + select_bias[e]   (one fp32 add, RNE)
+ *   topk_idx[t] = the k experts with the largest keys, in descending key
+ *                 order; equal keys go to the lower expert index (for both
+ *                 membership and order)
+ *   topk_gate[t,j] = exp(l_j - m) / sum_{i in topk} exp(l_i - m), l the
+ *                 logits WITHOUT select_bias, m their maximum over the set.
+ * Sources: "Every parameter, every token", section "The gating network";
+ * Zen MoDE, section "Router Architecture"; Zen-Max, section
+ * "Auxiliary-Loss-Free Load Balancing" (bias moves the choice only).
+ *
+ * x [T,d], w_router [E,d] in dtype dt; products accumulate in fp32.
+ * logit_bias [E] fp32 or NULL: part of the logits (the gates and
+ *   moe_balance_stats see it).
+ * select_bias [E] fp32 or NULL: selection key only.
+ * flags: MOE_ROUTE_LOGITS_IN reads `logits` instead of computing them
+ *   (x and w_router may then be NULL; logit_bias is ignored).
+ * logits [T,E] fp32 out (in with LOGITS_IN); topk_idx [T,k] int32 out;
+ * topk_gate [T,k] fp32 out.
+ * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK; for bf16
+ * d % 32 == 0.  Needs no workspace.  Logits must be finite.
+ */
+moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
+                       int k, const float* logit_bias, const float* select_bias,
+                       unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_permute: group the routed pairs by expert, apply the capacity drop,
+ * and (optionally) gather the token rows into expert order.
+ *
+ *   count[e]    = #{p : topk_idx[p] == e}               (before any drop)
+ *   rank(p)     = #{p' < p : topk_idx[p'] == topk_idx[p]}  (token order)
+ *   kept(p)     = capacity < 0 || rank(p) < capacity
+ *   offset      = exclusive prefix sum of min(count[e], capacity), [E+1]
+ *   pair_row[p] = offset[e] + rank(p) if kept(p) else -1
+ *   row_pair[r] = the pair at row r for r < offset[E], -1 for r >= offset[E]
+ *   x_perm[r,:] = x[row_pair[r] / k, :] for r < offset[E] (rows past offset[E]
+ *                 are left untouched)
+ * Sources: "Every parameter, every token", sections "A budget" (pairs past
+ * the budget are dropped and continue through the residual) and "What you
+ * still pay for" (a token travels to its assigned expert).  Reading: an
+ * expert keeps its first `capacity` pairs in token order.
+ *
+ * topk_idx [T,k] int32 (values in [0,E)); capacity < 0 means unlimited.
+ * x [T,d] in dtype dt, or NULL to skip the gather (x_perm then unused).
+ * Outputs (int32): expert_count [E], expert_offset [E+1], pair_row [T*k],
+ * row_pair [T*k]; x_perm [T*k, d] dtype dt.
+ * Workspace: moe_permute_workspace(T, k, E) bytes.
+ */
+size_t moe_permute_workspace(int64_t T, int k, int E);
+moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
+                         const void* x, int dt, int d, int32_t* expert_count,
+                         int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
+                         void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_expert_swiglu: G SwiGLU experts over contiguous row groups.
+ *
+ * For each group g and each row r in [group_offset[g], group_offset[g+1]):
+ *   a_r     = a[r]                       if a_rows == NULL
+ *           = a[a_rows[r] / a_rows_div]  otherwise (gathers token rows
+ *             straight from x through moe_permute's row_pair, div = k)
+ *   u       = a_r . w_gate[g]^T,  v = a_r . w_up[g]^T             ([h])
+ *   hid     = SiLU(u) * v,  SiLU(z) = z / (1 + exp(-z))
+ *   y[r]    = hid . w_down[g]^T                                   ([d])
+ * Source: Zen-Max, section "Fine-Grained Expert Architecture", expert
+ * equation (SiLU(x W_gate) * x W_up) W_down.  Shared experts are one call
+ * with G = 1, group_offset = {0, T}, a = x, and the shared experts' weights
+ * concatenated along the hidden axis (sum_s SwiGLU_s = SwiGLU of the
+ * concatenation, exactly).
+ *
+ * a [*, d] in dtype dt; weights in dtype dt; products accumulate in fp32;
+ * the hidden activation is stored in dtype dt (bf16: rounded to nearest
+ * even).  group_offset [G+1] int32 on the device, non-decreasing, with
+ * group_offset[0] == 0 and group_offset[G] <= max_rows (host bound).
+ * a_rows [max_rows] int32 or NULL; a_rows_div >= 1.
+ * y [max_rows, d] in dtype y_dt (rows past group_offset[G] untouched).
+ * Limits: bf16 needs d % 64 == 0 and h % 64 == 0.
+ * Workspace: moe_expert_swiglu_workspace(max_rows, d, h, G, dt) bytes.
+ */
+size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt);
+moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
+                               const int32_t* group_offset, int64_t max_rows,
+                               const int32_t* a_rows, int a_rows_div,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               void* y, int y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of moe_expert_swiglu, for callers that keep the hidden
+ * activation or time the two expert GEMMs apart (same sources, limits and
+ * row-group semantics as moe_expert_swiglu).
+ *
+ * moe_expert_gate_up: hid[r, :] = SiLU(a_r . w_gate[g]^T) * (a_r . w_up[g]^T)
+ *   for r < group_offset[G]; hid [max_rows, h] in dtype dt (rows past
+ *   group_offset[G] untouched).
+ * moe_expert_down:    y[r, :] = hid[r, :] . w_down[g]^T; y [max_rows, d] in
+ *   y_dt.
+ * Workspace of each: moe_expert_group_workspace(G) bytes (a tile table). */
+size_t moe_expert_group_workspace(int G);
+moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
+                                const int32_t* group_offset, int64_t max_rows,
+                                const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                const void* w_up, void* hid, void* ws, size_t ws_bytes,
+                                void* stream);
+moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
+                             const int32_t* group_offset, int64_t max_rows, const void* w_down,
+                             void* y, int y_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_combine: gate-weighted sum of the kept expert rows plus the shared
+ * output.
+ *
+ *   out[t,:] = shared_y[t,:] + sum_{j : pair_row[t*k+j] >= 0}
+ *                                topk_gate[t,j] * y_perm[pair_row[t*k+j], :]
+ * summed in fp32 in slot order j = 0..k-1, then the shared term, then
+ * rounded once to out_dt.  A dropped pair contributes nothing and the other
+ * gates are not renormalised.  The residual is NOT added.
+ * Sources: "Every parameter, every token", sections "The gating network"
+ * (y = g1 Expert1(x) + g2 Expert2(x)), "A budget" and "A shared expert";
+ * Zen-Max, section "Fine-Grained Expert Architecture" (shared experts added).
+ *
+ * y_perm [*, d] in y_dt; pair_row [T*k] int32; topk_gate [T,k] fp32;
+ * shared_y [T,d] in y_dt or NULL; out [T,d] in out_dt.
+ */
+moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
+                         const float* topk_gate, int64_t T, int k, int d,
+                         const void* shared_y, void* out, int out_dt, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* moe_balance_stats: Switch balance statistics and the router z-loss.
+ *
+ *   f[e]  = expert_count[e] / (T * k)       (pre-drop counts; sum f = 1)
+ *   P[e]  = (1/T) sum_t softmax(logits[t,:])[e]
+ *   loss  = alpha * E * sum_e f[e] * P[e]
+ *   zloss = (1/T) sum_t (log sum_e exp logits[t,e])^2
+ * Sources: Zen MoDE, section "Auxiliary Load Balancing Loss" (f counts
+ * membership in TopK, P the average routing probability, alpha = 0.01);
+ * "Every parameter, every token", section "A balance penalty"; Zen-Max,
+ * section "MoE-Specific Training Stability" (router z-loss).  Readings:
+ * f is normalised by T*k so that uniform routing gives loss = alpha for any
+ * k; P uses the full softmax of the logits (logit_bias included, selection
+ * bias excluded); N = E.
+ *
+ * logits [T,E] fp32; expert_count [E] int32; outputs fp32: f [E], P [E],
+ * loss [1], zloss [1] (zloss may be NULL).  Sums are fixed-order.
+ * Workspace: moe_balance_stats_workspace(T, E) bytes.
+ */
+size_t moe_balance_stats_workspace(int64_t T, int E);
+moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
+                               int E, int k, float alpha, float* f, float* P, float* loss,
+                               float* zloss, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,272 @@
+"""ctypes binding of libmoe (include/libmoe.h): argument marshalling only.
+
+Each Python function has the name of the C entry point it calls, takes torch
+tensors (device tensors for every buffer), allocates the outputs it is not
+given, enqueues on the current HIP stream and returns the outputs.  All of the
+computation happens in the library's kernels; nothing here falls back to any
+other implementation: if the library is missing, importing this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LIBMOE_PATH", os.path.join(_HERE, "lib", "libmoe.so"))
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUTE_LOGITS_IN = 1
+MOE_MAX_EXPERTS = 256
+MOE_MAX_TOPK = 32
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libmoe status {status}: {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libmoe is not built ({LIB_PATH} missing); run "
+            "`python -m sparse_mixture_experts_moe_amd.build`")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_L = _load()
+
+_p, _i, _i64, _sz, _u, _f, _d = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                  ctypes.c_uint, ctypes.c_float, ctypes.c_double)
+_SIGS = {
+    "moe_abi_version": (_i, []),
+    "moe_status_string": (ctypes.c_char_p, [_i]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_capacity": (_i64, [_d, _i64, _i, _i]),
+    "moe_route": (_i, [_p, _p, _i, _i64, _i, _i, _i, _p, _p, _u, _p, _p, _p, _p]),
+    "moe_permute_workspace": (_sz, [_i64, _i, _i]),
+    "moe_permute": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_swiglu_workspace": (_sz, [_i64, _i, _i, _i, _i]),
+    "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
+                               _sz, _p]),
+    "moe_expert_group_workspace": (_sz, [_i]),
+    "moe_expert_gate_up": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_down": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _p, _i, _p, _sz, _p]),
+    "moe_combine": (_i, [_p, _i, _p, _p, _i64, _i, _i, _p, _p, _i, _p]),
+    "moe_balance_stats_workspace": (_sz, [_i64, _i]),
+    "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
+}
+EXPORTED = tuple(_SIGS)
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_L, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoEError(status, _L.moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+_TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libmoe needs contiguous tensors")
+
+
+# ---------------------------------------------------------------------------
+def moe_abi_version() -> int:
+    return _L.moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return _L.moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return _L.moe_last_error().decode()
+
+
+def moe_capacity(cf: float, T: int, k: int, E: int) -> int:
+    return _L.moe_capacity(float(cf), T, k, E)
+
+
+def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None, topk_idx=None,
+              topk_gate=None, logits_in=False, stream=None):
+    """Router logits, top-k experts and renormalised gates.  With
+    ``logits_in`` the given ``logits`` [T, E] are used instead of x W_r^T."""
+    if logits_in:
+        T, E = logits.shape
+        dt, d = MOE_F32, 0
+        dev = logits.device
+    else:
+        T, d = x.shape
+        E = w_router.shape[0]
+        dt = _dt(x)
+        dev = x.device
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _contig(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate)
+    _check(_L.moe_route(_ptr(x), _ptr(w_router), dt, T, d, E, k, _ptr(logit_bias),
+                        _ptr(select_bias), MOE_ROUTE_LOGITS_IN if logits_in else 0,
+                        _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+    return logits, topk_idx, topk_gate
+
+
+def moe_permute_workspace(T, k, E) -> int:
+    return _L.moe_permute_workspace(T, k, E)
+
+
+def moe_permute(topk_idx, E, capacity=-1, x=None, *, expert_count=None, expert_offset=None,
+                pair_row=None, row_pair=None, x_perm=None, ws=None, stream=None):
+    """Expert counts, kept offsets, the pair/row permutation and (if ``x`` is
+    given) the expert-ordered copy of the token rows."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    R = T * k
+    if expert_count is None:
+        expert_count = torch.empty(E, dtype=torch.int32, device=dev)
+    if expert_offset is None:
+        expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pair_row is None:
+        pair_row = torch.empty(R, dtype=torch.int32, device=dev)
+    if row_pair is None:
+        row_pair = torch.empty(R, dtype=torch.int32, device=dev)
+    dt, d = MOE_F32, 0
+    if x is not None:
+        dt, d = _dt(x), x.shape[1]
+        if x_perm is None:
+            x_perm = torch.empty((R, d), dtype=x.dtype, device=dev)
+    nws = moe_permute_workspace(T, k, E)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _contig(topk_idx, x, expert_count, expert_offset, pair_row, row_pair, x_perm, ws)
+    _check(_L.moe_permute(_ptr(topk_idx), T, k, E, int(capacity), _ptr(x), dt, d,
+                          _ptr(expert_count), _ptr(expert_offset), _ptr(pair_row),
+                          _ptr(row_pair), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
+    return expert_count, expert_offset, pair_row, row_pair, x_perm
+
+
+def moe_expert_swiglu_workspace(max_rows, d, h, G, dt) -> int:
+    return _L.moe_expert_swiglu_workspace(max_rows, d, h, G, dt)
+
+
+def moe_expert_swiglu(a, group_offset, max_rows, w_gate, w_up, w_down, *, a_rows=None,
+                      a_rows_div=1, y=None, y_dtype=None, ws=None, stream=None):
+    """G SwiGLU experts over contiguous row groups: y[r] = SwiGLU_g(a_r)."""
+    G, h, d = w_gate.shape
+    dt = _dt(a)
+    dev = a.device
+    if y is None:
+        y = torch.empty((max_rows, d), dtype=y_dtype or a.dtype, device=dev)
+    nws = moe_expert_swiglu_workspace(max_rows, d, h, G, dt)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _contig(a, group_offset, a_rows, w_gate, w_up, w_down, y, ws)
+    _check(_L.moe_expert_swiglu(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
+                                _ptr(a_rows), a_rows_div, _ptr(w_gate), _ptr(w_up),
+                                _ptr(w_down), _ptr(y), _dt(y), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+    return y
+
+
+def moe_expert_group_workspace(G) -> int:
+    return _L.moe_expert_group_workspace(G)
+
+
+def moe_expert_gate_up(a, group_offset, max_rows, w_gate, w_up, *, a_rows=None, a_rows_div=1,
+                       hid=None, ws=None, stream=None):
+    """hid[r] = SiLU(a_r W_gate[g]^T) * (a_r W_up[g]^T) for the rows of each group."""
+    G, h, d = w_gate.shape
+    dev = a.device
+    if hid is None:
+        hid = torch.empty((max_rows, h), dtype=a.dtype, device=dev)
+    if ws is None:
+        ws = torch.empty(moe_expert_group_workspace(G), dtype=torch.uint8, device=dev)
+    _contig(a, group_offset, a_rows, w_gate, w_up, hid, ws)
+    _check(_L.moe_expert_gate_up(_ptr(a), _dt(a), d, h, G, _ptr(group_offset), max_rows,
+                                 _ptr(a_rows), a_rows_div, _ptr(w_gate), _ptr(w_up), _ptr(hid),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return hid
+
+
+def moe_expert_down(hid, group_offset, max_rows, w_down, *, y=None, y_dtype=None, ws=None,
+                    stream=None):
+    """y[r] = hid[r] W_down[g]^T for the rows of each group."""
+    G, d, h = w_down.shape
+    dev = hid.device
+    if y is None:
+        y = torch.empty((max_rows, d), dtype=y_dtype or hid.dtype, device=dev)
+    if ws is None:
+        ws = torch.empty(moe_expert_group_workspace(G), dtype=torch.uint8, device=dev)
+    _contig(hid, group_offset, w_down, y, ws)
+    _check(_L.moe_expert_down(_ptr(hid), _dt(hid), d, h, G, _ptr(group_offset), max_rows,
+                              _ptr(w_down), _ptr(y), _dt(y), _ptr(ws), ws.numel(),
+                              _stream(stream)))
+    return y
+
+
+def moe_combine(y_perm, pair_row, topk_gate, shared_y=None, *, out=None, out_dtype=None,
+                stream=None):
+    """out[t] = shared_y[t] + sum of kept g[t, j] * y_perm[pair_row[t k + j]]."""
+    T, k = topk_gate.shape
+    d = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype or y_perm.dtype, device=y_perm.device)
+    _contig(y_perm, pair_row, topk_gate, shared_y, out)
+    if shared_y is not None and shared_y.dtype != y_perm.dtype:
+        raise TypeError("shared_y must have the dtype of y_perm")
+    _check(_L.moe_combine(_ptr(y_perm), _dt(y_perm), _ptr(pair_row), _ptr(topk_gate), T, k, d,
+                          _ptr(shared_y), _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def moe_balance_stats_workspace(T, E) -> int:
+    return _L.moe_balance_stats_workspace(T, E)
+
+
+def moe_balance_stats(logits, expert_count, k, alpha=0.01, *, f=None, P=None, loss=None,
+                      zloss=None, ws=None, stream=None):
+    """Switch balance statistics f, P, alpha*E*sum(f*P) and the router z-loss."""
+    T, E = logits.shape
+    dev = logits.device
+    f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+    P = torch.empty(E, dtype=torch.float32, device=dev) if P is None else P
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    zloss = torch.empty(1, dtype=torch.float32, device=dev) if zloss is None else zloss
+    nws = moe_balance_stats_workspace(T, E)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _contig(logits, expert_count, f, P, loss, zloss, ws)
+    _check(_L.moe_balance_stats(_ptr(logits), _ptr(expert_count), T, E, k, float(alpha),
+                                _ptr(f), _ptr(P), _ptr(loss), _ptr(zloss), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+    return f, P, loss, zloss

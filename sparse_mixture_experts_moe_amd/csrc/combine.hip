@@ -1,0 +1,126 @@
+// Combine: out[t] = shared_y[t] + sum over kept slots j of g[t,j] * y_perm[pair_row[t*k+j]],
+// accumulated in fp32 in slot order and rounded once.
+//
+// Sources: "Every parameter, every token", sections "The gating network"
+// (the output is the gate-weighted sum of the selected experts), "A budget"
+// (a dropped pair contributes nothing) and "A shared expert"; "Zen-Max:
+// Maximum Capability via Mixture-of-Experts Architecture", section
+// "Fine-Grained Expert Architecture" (shared experts are added).
+//
+// HBM-bound: one workgroup per token, each lane handles 8 consecutive
+// columns per step (16-byte bf16 loads and stores).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
+    uint4 q;
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
+    q.z = pack_bf16x2(v[4], v[5]);
+    q.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = q;
+  }
+  static __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+};
+
+template <typename YT, typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
+                                                      const int32_t* __restrict__ pair_row,
+                                                      const float* __restrict__ gate, int k,
+                                                      int d, const YT* __restrict__ shared,
+                                                      OT* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int32_t* pr = pair_row + t * k;
+  const float* g = gate + t * k;
+  if ((d & 7) == 0) {
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int j = 0; j < k; ++j) {
+        const int row = pr[j];
+        if (row < 0) continue;
+        const float gj = g[j];
+        float v[8];
+        Vec8<YT>::load(y + static_cast<int64_t>(row) * d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
+      }
+      if (shared) {
+        float v[8];
+        Vec8<YT>::load(shared + t * d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+      Vec8<OT>::store(out + t * d + c, acc);
+    }
+  } else {
+    for (int c = threadIdx.x; c < d; c += 256) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int row = pr[j];
+        if (row < 0) continue;
+        acc = fmaf(g[j], Vec8<YT>::load1(y + static_cast<int64_t>(row) * d + c), acc);
+      }
+      if (shared) acc += Vec8<YT>::load1(shared + t * d + c);
+      Vec8<OT>::store1(out + t * d + c, acc);
+    }
+  }
+}
+
+template <typename YT, typename OT>
+hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_t T, int k, int d,
+                        const void* shared, void* out, hipStream_t stream) {
+  combine_kernel<YT, OT><<<static_cast<unsigned>(T), 256, 0, stream>>>(
+      static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
+      static_cast<OT*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
+                          int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
+                          hipStream_t stream) {
+  if (y_bf16) {
+    return out_bf16 ? launch_typed<uint16_t, uint16_t>(y, pair_row, gate, T, k, d, shared, out, stream)
+                    : launch_typed<uint16_t, float>(y, pair_row, gate, T, k, d, shared, out, stream);
+  }
+  return out_bf16 ? launch_typed<float, uint16_t>(y, pair_row, gate, T, k, d, shared, out, stream)
+                  : launch_typed<float, float>(y, pair_row, gate, T, k, d, shared, out, stream);
+}
+
+}  // namespace moe

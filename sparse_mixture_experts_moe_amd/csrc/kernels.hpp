@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI layer (libmoe_api.hip) and the
+// kernel translation units.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+
+// route.hip
+size_t route_lds_bytes(int E, int k);
+hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
+                        const float* logit_bias, const float* select_bias, bool logits_in,
+                        float* logits, int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+// permute.hip
+int64_t permute_chunks(int64_t R);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int64_t cap,
+                          const void* x, int elem_bytes, int d, int32_t* count, int32_t* offset,
+                          int32_t* pair_row, int32_t* row_pair, void* x_perm,
+                          int32_t* local_rank, int32_t* hist, hipStream_t stream);
+
+// grouped_gemm.hip
+struct SwigluArgs {
+  const void* a;
+  bool bf16;
+  int d, h, G;
+  const int32_t* group_offset;
+  int64_t max_rows;
+  const int32_t* a_rows;
+  int a_div;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* y;
+  bool y_bf16;
+  void* hid;        // [max_rows, h] in the compute dtype
+  int32_t* mstart;  // workspace [G + 1]
+};
+hipError_t launch_gate_up(const SwigluArgs& args, hipStream_t stream);
+hipError_t launch_down(const SwigluArgs& args, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
+                          int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
+                          hipStream_t stream);
+
+// stats.hip
+int64_t stats_blocks(int64_t T);
+hipError_t launch_balance_stats(const float* logits, const int32_t* count, int64_t T, int E, int k,
+                                float alpha, float* f, float* P, float* loss, float* zloss,
+                                float* part, float* zpart, hipStream_t stream);
+
+}  // namespace moe

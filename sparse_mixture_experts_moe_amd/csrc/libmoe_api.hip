@@ -1,0 +1,328 @@
+// C-ABI of libmoe: argument checks, workspace layout and kernel launches.
+// The operations and their sources are documented in include/libmoe.h.
+#include "../../include/libmoe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <charconv>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+int elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or type";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_capacity(double cf, int64_t T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return -2;
+  if (!std::isfinite(cf) || cf <= 0.0) return -1;
+  if (T == 0) return 0;
+  // shortest round-trip decimal of cf: digits * 10^exp10
+  char buf[64];
+  const auto res = std::to_chars(buf, buf + sizeof(buf), cf);
+  *res.ptr = '\0';
+  unsigned __int128 digits = 0;
+  int exp10 = 0;
+  bool frac = false;
+  const char* p = buf;
+  for (; *p && *p != 'e' && *p != 'E'; ++p) {
+    if (*p == '.') {
+      frac = true;
+      continue;
+    }
+    digits = digits * 10 + static_cast<unsigned>(*p - '0');
+    if (frac) --exp10;
+  }
+  if (*p == 'e' || *p == 'E') exp10 += static_cast<int>(strtol(p + 1, nullptr, 10));
+  const unsigned __int128 pairs = static_cast<unsigned __int128>(T) * static_cast<unsigned>(k);
+  if (pairs > (static_cast<unsigned __int128>(1) << 64)) return INT64_MAX;
+  unsigned __int128 num = digits * pairs;  // < 2^57 * 2^64
+  unsigned __int128 den = static_cast<unsigned>(E);
+  const unsigned __int128 kCap = static_cast<unsigned __int128>(1) << 125;
+  if (exp10 >= 0) {
+    for (int i = 0; i < exp10; ++i) {
+      if (num > kCap / 10) return INT64_MAX;
+      num *= 10;
+    }
+  } else {
+    // the divisor E * 10^-exp10 exceeds num once 10^-exp10 > num: budget 1
+    for (int i = 0; i < -exp10; ++i) {
+      if (den > num) return 1;
+      den *= 10;
+    }
+  }
+  const unsigned __int128 c = (num + den - 1) / den;
+  if (c > static_cast<unsigned __int128>(INT64_MAX)) return INT64_MAX;
+  return static_cast<int64_t>(c);
+}
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
+                       int k, const float* logit_bias, const float* select_bias,
+                       unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
+                       void* stream) {
+  const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+  if (flags & ~MOE_ROUTE_LOGITS_IN) return fail(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
+  if (T < 0) return fail(MOE_EINVAL, "moe_route: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_route: need 1 <= k <= E");
+  if (!valid_dtype(dt)) return fail(MOE_EINVAL, "moe_route: bad dtype %d", dt);
+  if (!logits_in && d < 1) return fail(MOE_EINVAL, "moe_route: d < 1");
+  if (E > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "moe_route: E > %d", moe::kMaxExperts);
+  if (k > moe::kMaxTopK) return fail(MOE_EUNSUPPORTED, "moe_route: k > %d", moe::kMaxTopK);
+  if (!logits_in && dt == MOE_BF16 && d % 32 != 0)
+    return fail(MOE_EUNSUPPORTED, "moe_route: bf16 needs d %% 32 == 0");
+  if (T == 0) return ok();  // per-token buffers of zero size may be NULL
+  if (!logits || !topk_idx || !topk_gate)
+    return fail(MOE_EINVAL, "moe_route: NULL output pointer");
+  if (!logits_in && (!x || !w_router)) return fail(MOE_EINVAL, "moe_route: NULL x or w_router");
+  return hip_status(moe::launch_route(x, w_router, dt == MOE_BF16, T, d, E, k, logit_bias,
+                                      select_bias, logits_in, logits, topk_idx, topk_gate,
+                                      as_stream(stream)),
+                    "moe_route");
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_permute_workspace(int64_t T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const int64_t R = T * k;
+  return align256(sizeof(int32_t) * static_cast<size_t>(R)) +
+         align256(sizeof(int32_t) * static_cast<size_t>(moe::permute_chunks(R)) * E);
+}
+
+moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
+                         const void* x, int dt, int d, int32_t* expert_count,
+                         int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
+                         void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_permute: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_permute: need 1 <= k <= E");
+  if (!expert_count || !expert_offset) return fail(MOE_EINVAL, "moe_permute: NULL pointer");
+  if (T > 0 && (!topk_idx || !pair_row || !row_pair))
+    return fail(MOE_EINVAL, "moe_permute: NULL pointer");
+  if (x && (!x_perm || d < 1 || !valid_dtype(dt)))
+    return fail(MOE_EINVAL, "moe_permute: gather needs x_perm, d >= 1 and a valid dtype");
+  if (E > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "moe_permute: E > %d", moe::kMaxExperts);
+  if (T * k > INT32_MAX) return fail(MOE_EUNSUPPORTED, "moe_permute: T*k exceeds int32");
+  const size_t need = moe_permute_workspace(T, k, E);
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_EWORKSPACE, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
+  if (T == 0) {
+    // no pairs: counts and offsets are all zero
+    hipError_t e = moe::launch_fill_i32(expert_count, E, 0, as_stream(stream));
+    if (e == hipSuccess) e = moe::launch_fill_i32(expert_offset, E + 1, 0, as_stream(stream));
+    return hip_status(e, "moe_permute");
+  }
+  int32_t* local_rank = static_cast<int32_t*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                             align256(sizeof(int32_t) * static_cast<size_t>(T * k)));
+  return hip_status(moe::launch_permute(topk_idx, T, k, E, capacity, x, elem_bytes(dt), d,
+                                        expert_count, expert_offset, pair_row, row_pair, x_perm,
+                                        local_rank, hist, as_stream(stream)),
+                    "moe_permute");
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+moe_status_t check_experts(const char* fn, int dt, int d, int h, int G, int64_t max_rows,
+                           const int32_t* group_offset) {
+  if (d < 1 || h < 1 || G < 1 || max_rows < 0)
+    return fail(MOE_EINVAL, "%s: need d, h, G >= 1 and max_rows >= 0", fn);
+  if (!valid_dtype(dt)) return fail(MOE_EINVAL, "%s: dtype", fn);
+  if (!group_offset) return fail(MOE_EINVAL, "%s: NULL group_offset", fn);
+  if (dt == MOE_BF16 && (d % 64 != 0 || h % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "%s: bf16 needs d %% 64 == 0 and h %% 64 == 0", fn);
+  if (max_rows > INT32_MAX || static_cast<int64_t>(G) * (max_rows + 1) > INT32_MAX)
+    return fail(MOE_EUNSUPPORTED, "%s: too many rows", fn);
+  return MOE_OK;
+}
+
+size_t tile_table_bytes(int G) { return align256(sizeof(int32_t) * (static_cast<size_t>(G) + 1)); }
+
+}  // namespace
+
+size_t moe_expert_group_workspace(int G) { return G < 1 ? 0 : tile_table_bytes(G); }
+
+size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt) {
+  if (max_rows < 0 || d < 1 || h < 1 || G < 1 || !valid_dtype(dt)) return 0;
+  return align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt)) + tile_table_bytes(G);
+}
+
+moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
+                                const int32_t* group_offset, int64_t max_rows,
+                                const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                const void* w_up, void* hid, void* ws, size_t ws_bytes,
+                                void* stream) {
+  moe_status_t st = check_experts("moe_expert_gate_up", dt, d, h, G, max_rows, group_offset);
+  if (st != MOE_OK) return st;
+  if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
+  if (!a || !w_gate || !w_up || !hid) return fail(MOE_EINVAL, "moe_expert_gate_up: NULL pointer");
+  if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "moe_expert_gate_up: a_rows_div < 1");
+  if (ws_bytes < tile_table_bytes(G) || !ws)
+    return fail(MOE_EWORKSPACE, "moe_expert_gate_up: workspace %zu < %zu bytes", ws_bytes,
+                tile_table_bytes(G));
+  moe::SwigluArgs s{};
+  s.a = a;
+  s.bf16 = dt == MOE_BF16;
+  s.d = d;
+  s.h = h;
+  s.G = G;
+  s.group_offset = group_offset;
+  s.max_rows = max_rows;
+  s.a_rows = a_rows;
+  s.a_div = a_rows ? a_rows_div : 1;
+  s.w_gate = w_gate;
+  s.w_up = w_up;
+  s.hid = hid;
+  s.mstart = static_cast<int32_t*>(ws);
+  return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up");
+}
+
+moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
+                             const int32_t* group_offset, int64_t max_rows, const void* w_down,
+                             void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_experts("moe_expert_down", dt, d, h, G, max_rows, group_offset);
+  if (st != MOE_OK) return st;
+  if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
+  if (!valid_dtype(y_dt)) return fail(MOE_EINVAL, "moe_expert_down: dtype");
+  if (!hid || !w_down || !y) return fail(MOE_EINVAL, "moe_expert_down: NULL pointer");
+  if (ws_bytes < tile_table_bytes(G) || !ws)
+    return fail(MOE_EWORKSPACE, "moe_expert_down: workspace %zu < %zu bytes", ws_bytes,
+                tile_table_bytes(G));
+  moe::SwigluArgs s{};
+  s.bf16 = dt == MOE_BF16;
+  s.d = d;
+  s.h = h;
+  s.G = G;
+  s.group_offset = group_offset;
+  s.max_rows = max_rows;
+  s.w_down = w_down;
+  s.y = y;
+  s.y_bf16 = y_dt == MOE_BF16;
+  s.hid = const_cast<void*>(hid);
+  s.mstart = static_cast<int32_t*>(ws);
+  return hip_status(moe::launch_down(s, as_stream(stream)), "moe_expert_down");
+}
+
+moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
+                               const int32_t* group_offset, int64_t max_rows,
+                               const int32_t* a_rows, int a_rows_div,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_experts("moe_expert_swiglu", dt, d, h, G, max_rows, group_offset);
+  if (st != MOE_OK) return st;
+  if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
+  if (!valid_dtype(y_dt)) return fail(MOE_EINVAL, "moe_expert_swiglu: dtype");
+  if (!a || !w_gate || !w_up || !w_down || !y)
+    return fail(MOE_EINVAL, "moe_expert_swiglu: NULL pointer");
+  if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "moe_expert_swiglu: a_rows_div < 1");
+  const size_t need = moe_expert_swiglu_workspace(max_rows, d, h, G, dt);
+  if (ws_bytes < need || !ws)
+    return fail(MOE_EWORKSPACE, "moe_expert_swiglu: workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t hid_bytes = align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt));
+  void* hid = ws;
+  void* table = static_cast<char*>(ws) + hid_bytes;
+  st = moe_expert_gate_up(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate,
+                          w_up, hid, table, ws_bytes - hid_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down(hid, dt, d, h, G, group_offset, max_rows, w_down, y, y_dt, table,
+                         ws_bytes - hid_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
+                         const float* topk_gate, int64_t T, int k, int d,
+                         const void* shared_y, void* out, int out_dt, void* stream) {
+  if (T < 0 || k < 1 || d < 1) return fail(MOE_EINVAL, "moe_combine: need T >= 0, k >= 1, d >= 1");
+  if (!valid_dtype(y_dt) || !valid_dtype(out_dt)) return fail(MOE_EINVAL, "moe_combine: dtype");
+  if (T == 0) return ok();
+  if (!y_perm || !pair_row || !topk_gate || !out)
+    return fail(MOE_EINVAL, "moe_combine: NULL pointer");
+  return hip_status(moe::launch_combine(y_perm, y_dt == MOE_BF16, pair_row, topk_gate, T, k, d,
+                                        shared_y, out, out_dt == MOE_BF16, as_stream(stream)),
+                    "moe_combine");
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_balance_stats_workspace(int64_t T, int E) {
+  if (T < 0 || E < 1) return 0;
+  const size_t nb = static_cast<size_t>(moe::stats_blocks(T));
+  return align256(sizeof(float) * nb * E) + align256(sizeof(float) * nb);
+}
+
+moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
+                               int E, int k, float alpha, float* f, float* P, float* loss,
+                               float* zloss, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_balance_stats: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_balance_stats: need 1 <= k <= E");
+  if (!expert_count || !f || !P || !loss || (T > 0 && !logits))
+    return fail(MOE_EINVAL, "moe_balance_stats: NULL pointer");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_balance_stats: E > %d", moe::kMaxExperts);
+  if (T == 0) {
+    // no tokens: every statistic is written as zero
+    hipStream_t st = as_stream(stream);
+    hipError_t e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(f), E, 0, st);
+    if (e == hipSuccess) e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(P), E, 0, st);
+    if (e == hipSuccess) e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(loss), 1, 0, st);
+    if (e == hipSuccess && zloss) e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(zloss), 1, 0, st);
+    return hip_status(e, "moe_balance_stats");
+  }
+  const size_t need = moe_balance_stats_workspace(T, E);
+  if (ws_bytes < need || !ws)
+    return fail(MOE_EWORKSPACE, "moe_balance_stats: workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t nb = static_cast<size_t>(moe::stats_blocks(T));
+  float* part = static_cast<float*>(ws);
+  float* zpart = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(sizeof(float) * nb * E));
+  return hip_status(moe::launch_balance_stats(logits, expert_count, T, E, k, alpha, f, P, loss,
+                                              zloss, part, zpart, as_stream(stream)),
+                    "moe_balance_stats");
+}
+
+}  // extern "C"

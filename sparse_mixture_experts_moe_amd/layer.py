@@ -1,0 +1,129 @@
+"""MoELayer: one forward pass of the sparse MoE feed-forward layer as five
+libmoe calls on one stream (route, permute, routed experts [+ shared experts],
+combine, balance statistics).  Buffers are allocated on the first call for a
+token count and reused afterwards, so repeated calls allocate nothing.
+
+The layer output excludes the residual ("Every parameter, every token",
+section "The gating network": the weighted sum is added back to the residual
+stream outside the slot).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class MoELayer:
+    def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
+                 select_bias=None, capacity=-1, alpha=0.01, gather="fused"):
+        """Weights are device tensors: w_router [E, d]; w_gate, w_up [E, h, d];
+        w_down [E, d, h]; ``shared`` is None or (gate [Hs, d], up [Hs, d],
+        down [d, Hs]) with the shared experts concatenated along the hidden
+        axis.  ``capacity`` < 0 means unlimited.  ``gather`` is "fused" (the
+        first expert GEMM reads token rows through the permutation) or "copy"
+        (moe_permute writes an expert-ordered copy of x first)."""
+        if gather not in ("fused", "copy"):
+            raise ValueError("gather must be 'fused' or 'copy'")
+        self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
+        self.E, self.h, self.d = w_gate.shape
+        self.k = k
+        self.shared = None
+        if shared is not None:
+            sg, su, sd = shared
+            self.shared = (sg.reshape(1, *sg.shape), su.reshape(1, *su.shape),
+                           sd.reshape(1, *sd.shape))
+        self.logit_bias, self.select_bias = logit_bias, select_bias
+        self.capacity = int(capacity)
+        self.alpha = alpha
+        self.gather = gather
+        self._bufs = {}
+
+    def _buffers(self, x):
+        T = x.shape[0]
+        key = (T, x.dtype, x.device)
+        b = self._bufs.get(key)
+        if b is not None:
+            return b
+        dev, E, k, d, h = x.device, self.E, self.k, self.d, self.h
+        R = T * k
+        dt = _lib._dt(x)
+        b = dict(
+            logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+            topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+            topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+            expert_count=torch.empty(E, dtype=torch.int32, device=dev),
+            expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            pair_row=torch.empty(R, dtype=torch.int32, device=dev),
+            row_pair=torch.empty(R, dtype=torch.int32, device=dev),
+            x_perm=(torch.empty((R, d), dtype=x.dtype, device=dev)
+                    if self.gather == "copy" else None),
+            perm_ws=torch.empty(max(1, _lib.moe_permute_workspace(T, k, E)), dtype=torch.uint8,
+                                device=dev),
+            hid=torch.empty((R, h), dtype=x.dtype, device=dev),
+            y_perm=torch.empty((R, d), dtype=x.dtype, device=dev),
+            table_ws=torch.empty(_lib.moe_expert_group_workspace(E), dtype=torch.uint8,
+                                 device=dev),
+            out=torch.empty((T, d), dtype=x.dtype, device=dev),
+            f=torch.empty(E, dtype=torch.float32, device=dev),
+            P=torch.empty(E, dtype=torch.float32, device=dev),
+            loss=torch.empty(1, dtype=torch.float32, device=dev),
+            zloss=torch.empty(1, dtype=torch.float32, device=dev),
+            stats_ws=torch.empty(max(1, _lib.moe_balance_stats_workspace(T, E)),
+                                 dtype=torch.uint8, device=dev),
+        )
+        if self.shared is not None:
+            Hs = self.shared[0].shape[1]
+            b["shared_off"] = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            b["shared_y"] = torch.empty((T, d), dtype=x.dtype, device=dev)
+            b["shared_ws"] = torch.empty(
+                max(1, _lib.moe_expert_swiglu_workspace(T, d, Hs, 1, dt)), dtype=torch.uint8,
+                device=dev)
+        self._bufs[key] = b
+        return b
+
+    def forward(self, x, stream=None, mark=None):
+        """Returns a dict of the output and every intermediate the calls produce.
+        ``mark(name)``, if given, is called after each library call is enqueued
+        (the benchmark records a HIP event there)."""
+        b = self._buffers(x)
+        T = x.shape[0]
+        k, E = self.k, self.E
+        mark = mark or (lambda name: None)
+        _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
+                       logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
+                       stream=stream)
+        mark("route")
+        _lib.moe_permute(b["topk_idx"], E, self.capacity,
+                         x if self.gather == "copy" else None,
+                         expert_count=b["expert_count"], expert_offset=b["expert_offset"],
+                         pair_row=b["pair_row"], row_pair=b["row_pair"], x_perm=b["x_perm"],
+                         ws=b["perm_ws"], stream=stream)
+        mark("permute")
+        if self.gather == "copy":
+            a, a_rows = b["x_perm"], None
+        else:
+            a, a_rows = x, b["row_pair"]
+        _lib.moe_expert_gate_up(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
+                                a_rows=a_rows, a_rows_div=k, hid=b["hid"], ws=b["table_ws"],
+                                stream=stream)
+        mark("gate_up")
+        _lib.moe_expert_down(b["hid"], b["expert_offset"], T * k, self.w_down, y=b["y_perm"],
+                             ws=b["table_ws"], stream=stream)
+        mark("down")
+        shared_y = None
+        if self.shared is not None:
+            sg, su, sd = self.shared
+            shared_y = _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd,
+                                              y=b["shared_y"], ws=b["shared_ws"], stream=stream)
+            mark("shared")
+        _lib.moe_combine(b["y_perm"], b["pair_row"], b["topk_gate"], shared_y, out=b["out"],
+                         stream=stream)
+        mark("combine")
+        _lib.moe_balance_stats(b["logits"], b["expert_count"], k, self.alpha, f=b["f"], P=b["P"],
+                               loss=b["loss"], zloss=b["zloss"], ws=b["stats_ws"], stream=stream)
+        mark("stats")
+        return b
+
+    __call__ = forward

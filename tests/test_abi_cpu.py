@@ -1,0 +1,151 @@
+"""The C-ABI library on the host: it loads, exports every declared entry
+point, computes the capacity exactly, and rejects bad arguments before it
+touches the GPU (no call here launches a kernel)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+
+L = pytest.importorskip("sparse_mixture_experts_moe_amd._lib",
+                        reason="libmoe not built (python -m sparse_mixture_experts_moe_amd.build)")
+C = L._L
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(L.EXPORTED) == names  # the binding declares exactly these
+
+
+def test_version_and_strings():
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_string(L.MOE_OK) == "ok"
+    assert L.moe_status_string(L.MOE_EWORKSPACE) == "workspace too small"
+    assert L.moe_status_string(99) == "unknown status"
+
+
+def test_capacity_worked():
+    assert L.moe_capacity(1.25, 16384, 2, 64) == 640
+    assert L.moe_capacity(0.1, 10, 1, 1) == 1
+    assert L.moe_capacity(1.1, 100, 1, 10) == 11
+    assert L.moe_capacity(0.0, 10, 2, 3) == -1
+    assert L.moe_capacity(-1.0, 10, 2, 3) == -1
+    assert L.moe_capacity(float("nan"), 10, 2, 3) == -1
+    assert L.moe_capacity(1.0, -1, 2, 3) == -2
+    assert L.moe_capacity(1e-300, 10, 2, 3) == 1
+    assert L.moe_capacity(1e300, 10, 2, 3) == 2 ** 63 - 1
+
+
+@settings(max_examples=400, deadline=None)
+@given(st.floats(min_value=1e-6, max_value=1e6, allow_nan=False, allow_infinity=False),
+       st.integers(1, 10 ** 7), st.integers(1, 32), st.integers(1, 256))
+def test_capacity_matches_oracle(cf, T, k, E):
+    assert L.moe_capacity(cf, T, k, E) == oracle.capacity(cf, T, k, E)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 10 ** 6), st.integers(1, 32), st.integers(1, 256),
+       st.integers(1, 400).map(lambda n: n / 100))
+def test_capacity_two_decimal_factors(T, k, E, cf):
+    # factors written with two decimals, as configs write them
+    assert L.moe_capacity(cf, T, k, E) == oracle.capacity(cf, T, k, E)
+
+
+def _err():
+    return L.moe_last_error()
+
+
+def test_route_rejects():
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 8, 9, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EINVAL and "k <= E" in _err()
+    s = C.moe_route(None, FAKE, L.MOE_BF16, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EINVAL
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 300, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EUNSUPPORTED
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 100, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EUNSUPPORTED and "d % 32" in _err()
+    s = C.moe_route(FAKE, FAKE, 7, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EINVAL
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 64, 33, None, None, 0, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EUNSUPPORTED
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None, 4, FAKE, FAKE, FAKE, None)
+    assert s == L.MOE_EINVAL and "flags" in _err()
+    # T = 0 is a no-op that enqueues nothing
+    assert C.moe_route(FAKE, FAKE, L.MOE_F32, 0, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE,
+                       None) == L.MOE_OK
+    assert _err() == ""
+
+
+def test_permute_rejects():
+    ws = L.moe_permute_workspace(100, 2, 8)
+    assert ws > 0
+    s = C.moe_permute(FAKE, 100, 2, 8, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+                      None)
+    assert s == L.MOE_EWORKSPACE
+    s = C.moe_permute(None, 100, 2, 8, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert s == L.MOE_EINVAL
+    s = C.moe_permute(FAKE, 100, 2, 8, -1, FAKE, L.MOE_BF16, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                      ws, None)
+    assert s == L.MOE_EINVAL and "x_perm" in _err()
+    s = C.moe_permute(FAKE, 100, 3, 2, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert s == L.MOE_EINVAL
+
+
+def test_expert_swiglu_rejects():
+    ws = L.moe_expert_swiglu_workspace(1000, 128, 256, 8, L.MOE_BF16)
+    assert ws >= 1000 * 256 * 2
+    args = dict(a=FAKE, dt=L.MOE_BF16, d=128, h=256, G=8, off=FAKE, mr=1000, rows=None, div=1,
+                wg=FAKE, wu=FAKE, wd=FAKE, y=FAKE, ydt=L.MOE_BF16, ws=FAKE, nws=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return C.moe_expert_swiglu(a["a"], a["dt"], a["d"], a["h"], a["G"], a["off"], a["mr"],
+                                   a["rows"], a["div"], a["wg"], a["wu"], a["wd"], a["y"],
+                                   a["ydt"], a["ws"], a["nws"], None)
+
+    assert call(nws=ws - 1) == L.MOE_EWORKSPACE
+    assert call(d=100) == L.MOE_EUNSUPPORTED
+    assert call(h=96) == L.MOE_EUNSUPPORTED
+    assert call(wd=None) == L.MOE_EINVAL
+    assert call(rows=FAKE, div=0) == L.MOE_EINVAL
+    assert call(G=0) == L.MOE_EINVAL
+    assert call(ydt=5) == L.MOE_EINVAL
+    # no rows: nothing to do
+    assert call(mr=0, nws=L.moe_expert_swiglu_workspace(0, 128, 256, 8, L.MOE_BF16)) == L.MOE_OK
+
+
+def test_combine_and_stats_reject():
+    assert C.moe_combine(None, L.MOE_BF16, FAKE, FAKE, 10, 2, 64, None, FAKE, L.MOE_BF16,
+                         None) == L.MOE_EINVAL
+    assert C.moe_combine(FAKE, L.MOE_BF16, FAKE, FAKE, 10, 0, 64, None, FAKE, L.MOE_BF16,
+                         None) == L.MOE_EINVAL
+    assert C.moe_combine(FAKE, L.MOE_BF16, FAKE, FAKE, 0, 2, 64, None, FAKE, L.MOE_BF16,
+                         None) == L.MOE_OK
+    ws = L.moe_balance_stats_workspace(1000, 64)
+    assert C.moe_balance_stats(FAKE, FAKE, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+                               None) == L.MOE_EWORKSPACE
+    assert C.moe_balance_stats(FAKE, FAKE, 1000, 300, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
+                               None) == L.MOE_EUNSUPPORTED
+    assert C.moe_balance_stats(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
+                               None) == L.MOE_EINVAL

@@ -1,0 +1,252 @@
+"""GPU parity of libmoe against the CPU oracle (needs an MI355X).
+
+Small cases span several tiles with ragged tails and finish in seconds on the
+oracle; every output is compared.  Tolerances: routing, counts, offsets and
+the permutation bit-exact given identical logits; logits 1e-5 max-abs
+relative; gates 1e-6 absolute; layer output 1e-4 (fp32) / 2e-2 (bf16) max-abs
+relative; P, loss, z-loss 1e-5 relative; f exact.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import MoEConfig, WORKLOADS, as_f32, generate, small_case
+from tests.gpu_helpers import build_layer, check_layer, host, normwise, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = {
+    "tiny_f32": WORKLOADS["tiny_f32"],
+    "mixtral_small_128tile": small_case("mixtral_bf16", T=700, d=256, h=320),
+    "mixtral_small_256tile": small_case("mixtral_bf16", T=1600, d=256, h=320, cid_offset=200),
+    "finegrained_small": small_case("finegrained_shared_bf16", T=512, d=128, h=128, h_shared=64),
+    "capacity_small": small_case("capacity_balance_bf16", T=2048, d=192, h=256),
+    "decode_small": small_case("decode_bf16", T=64, d=256, h=128, h_shared=512),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from sparse_mixture_experts_moe_amd import _lib  # noqa: F401  (fails loudly if not built)
+
+
+@pytest.mark.parametrize("gather", ["fused", "copy"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_small(name, gather):
+    cfg = SMALL[name]
+    _say(f"[case] {name} gather={gather} {cfg}")
+    inp = generate(cfg)
+    layer = build_layer(inp, gather)
+    res = layer(to_device(inp["x"]))
+    torch.cuda.synchronize()
+    errs = check_layer(inp, res)
+    _say(f"[ok] {name}: {errs}")
+
+
+def test_layer_deterministic():
+    cfg = SMALL["capacity_small"]
+    inp = generate(cfg)
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    a = {k: v.clone() for k, v in layer(x).items() if torch.is_tensor(v)}
+    torch.cuda.synchronize()
+    b = layer(x)
+    torch.cuda.synchronize()
+    for k, v in a.items():
+        if k.endswith("ws"):
+            continue
+        assert torch.equal(v.view(torch.uint8) if v.dtype == torch.bfloat16 else v, (
+            b[k].view(torch.uint8) if b[k].dtype == torch.bfloat16 else b[k])), k
+
+
+# ---------------------------------------------------------------------------
+# moe_route in isolation on adversarial logits (ties, signed zeros, bias that
+# rounds away in float32)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 2), (8, 8), (64, 2), (128, 8), (256, 32), (200, 7)])
+def test_route_logits_in(E, k):
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] route logits_in E={E} k={k}")
+    rng = np.random.default_rng(E * 100 + k)
+    T = 333
+    lg = np.round(rng.standard_normal((T, E)) * 2).astype(np.float32)  # many ties
+    lg[0] = 0.0                      # all tie: experts 0..k-1
+    lg[1, ::2] = -0.0                # signed zeros tie with +0
+    lg[2] = np.linspace(1, 0, E)     # strictly decreasing
+    sb = np.zeros(E, dtype=np.float32)
+    sb[-1] = 2.0 ** -24              # 1 + 2^-24 rounds to 1 in float32
+    lg[3] = 1.0
+    for bias in (None, sb, (rng.standard_normal(E) * 0.7).astype(np.float32)):
+        logits = torch.from_numpy(lg).cuda()
+        b = None if bias is None else torch.from_numpy(bias).cuda()
+        _, idx, gate = _lib.moe_route(None, None, k, None, b, logits=logits, logits_in=True)
+        torch.cuda.synchronize()
+        ref_idx = oracle.top_k(oracle.selection_keys(lg, bias), k)
+        assert np.array_equal(host(idx), ref_idx)
+        assert np.max(np.abs(host(gate) - oracle.gates(lg, ref_idx))) <= 1e-6
+        assert np.array_equal(host(logits), lg)  # input untouched
+        if bias is None:
+            assert host(idx)[0].tolist() == list(range(k))  # all-tie row
+
+
+# ---------------------------------------------------------------------------
+# moe_permute in isolation on constructed selections
+# ---------------------------------------------------------------------------
+def _selections(T, E, k, kind, rng):
+    if kind == "random":
+        return np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    if kind == "same":      # every token picks experts 0..k-1: all others empty
+        return np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    if kind == "skewed":    # half the experts never chosen
+        half = max(k, E // 2)
+        return np.array([rng.permutation(half)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("T,E,k,kind,cap", [
+    (1, 1, 1, "random", -1), (5, 3, 3, "random", -1), (1000, 8, 2, "random", -1),
+    (1025, 8, 2, "same", -1), (4099, 64, 2, "skewed", 80), (3000, 64, 2, "random", 0),
+    (3000, 64, 2, "random", 1), (2000, 16, 4, "random", 2000), (20000, 128, 8, "skewed", -1),
+    (777, 256, 32, "random", 50), (513, 200, 7, "same", 300)])
+def test_permute(T, E, k, kind, cap):
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] permute T={T} E={E} k={k} {kind} cap={cap}")
+    rng = np.random.default_rng(T + E + k)
+    idx = _selections(T, E, k, kind, rng)
+    x = torch.randn(T, 71 if T < 10 else 72, device="cuda").to(torch.bfloat16)
+    cnt, off, pr, rp, xp = _lib.moe_permute(torch.from_numpy(idx).cuda(), E, cap, x)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(idx, E, None if cap < 0 else cap)
+    assert np.array_equal(host(cnt), d["count"])
+    assert np.array_equal(host(off), d["offset"])
+    assert np.array_equal(host(pr), d["pair_row"])
+    assert np.array_equal(host(rp), d["row_pair"])
+    nk = int(d["offset"][-1])
+    want = x[torch.from_numpy(d["row_pair"][:nk] // k).cuda().long()]
+    assert torch.equal(xp[:nk].view(torch.int16), want.view(torch.int16))
+
+
+def test_permute_empty():
+    from sparse_mixture_experts_moe_amd import _lib
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    cnt, off, _, _, _ = _lib.moe_permute(idx, 8, -1)
+    torch.cuda.synchronize()
+    assert host(cnt).tolist() == [0] * 8 and host(off).tolist() == [0] * 9
+
+
+# ---------------------------------------------------------------------------
+# moe_expert_swiglu in isolation: empty, tiny and multi-tile groups
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("sizes,d,h", [
+    ([0, 1, 0, 31, 300, 0, 129, 2], 128, 192),
+    ([1000, 0, 700], 256, 320),
+    ([5] * 40, 64, 128),
+    ([2000, 1500], 192, 256)])
+def test_expert_swiglu_groups(sizes, d, h, dt):
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] swiglu groups={sizes} d={d} h={h} {dt}")
+    rng = np.random.default_rng(len(sizes) * 7 + d + h)
+    G = len(sizes)
+    rows = int(sum(sizes))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+
+    def mk(shape, s):
+        return torch.from_numpy((rng.standard_normal(shape) * s).astype(np.float32)).to(tdt).cuda()
+    a = mk((rows + 3, d), 1.0)
+    wg, wu = mk((G, h, d), d ** -0.5), mk((G, h, d), d ** -0.5)
+    wd = mk((G, d, h), h ** -0.5)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    perm = rng.permutation(rows + 3).astype(np.int32)  # gather through a row index
+    an, wgn, wun, wdn = (host(t) for t in (a, wg, wu, wd))
+    for gather in (False, True):
+        a_rows = torch.from_numpy(perm[:rows] * 3).cuda() if gather else None
+        y = _lib.moe_expert_swiglu(a, torch.from_numpy(off).cuda(), rows + 3, wg, wu, wd,
+                                   a_rows=a_rows, a_rows_div=3, y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        yn = host(y)
+        for g in range(G):
+            r0, r1 = off[g], off[g + 1]
+            if r1 == r0:
+                continue
+            src = perm[r0:r1] if gather else np.arange(r0, r1)
+            ref = oracle.swiglu(an[src], wgn[g], wun[g], wdn[g])
+            tol = 2e-2 if dt == "bf16" else 1e-4
+            assert normwise(yn[r0:r1], ref) <= tol, (g, gather)
+
+
+# ---------------------------------------------------------------------------
+# moe_combine in isolation: oracle expert outputs in, oracle layer output out
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_combine_isolated(with_shared):
+    from sparse_mixture_experts_moe_amd import _lib
+    rng = np.random.default_rng(5)
+    T, d, E, h, k = 300, 64, 6, 32, 3
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    wg = rng.standard_normal((E, h, d)) / 8
+    wu = rng.standard_normal((E, h, d)) / 8
+    wd = rng.standard_normal((E, d, h)) / 6
+    shared = [(rng.standard_normal((h, d)) / 8, rng.standard_normal((h, d)) / 8,
+               rng.standard_normal((d, h)) / 6)] if with_shared else ()
+    r = oracle.forward(x, wr, wg, wu, wd, k, shared=shared, cap=40)
+    # expert outputs of every kept row, from the oracle
+    rp = r["row_pair"]
+    nk = int(r["offset"][-1])
+    y_perm = np.zeros((T * k, d))
+    for row in range(nk):
+        p = rp[row]
+        e = r["topk_idx"].reshape(-1)[p]
+        y_perm[row] = oracle.swiglu(x[p // k][None], wg[e], wu[e], wd[e])[0]
+    sy = None
+    if with_shared:
+        sy = torch.from_numpy(oracle.swiglu(x, *shared[0]).astype(np.float32)).cuda()
+    out = _lib.moe_combine(torch.from_numpy(y_perm.astype(np.float32)).cuda(),
+                           torch.from_numpy(r["pair_row"].astype(np.int32)).cuda(),
+                           torch.from_numpy(r["topk_gate"].astype(np.float32)).cuda(), sy)
+    torch.cuda.synchronize()
+    assert (r["pair_row"] < 0).any()
+    assert normwise(host(out), r["y"]) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# whole layer at the full workload sizes: every logit, every routing decision
+# and the permutation; outputs on sampled tokens
+# ---------------------------------------------------------------------------
+def _sample_tokens(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    if T <= n:
+        return np.arange(T)
+    fixed = list(range(8)) + list(range(T - 8, T))
+    rest = rng.choice(np.arange(8, T - 8), size=n - 16, replace=False)
+    return np.sort(np.concatenate([fixed, rest]))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mixtral_bf16", "finegrained_shared_bf16",
+                                  "capacity_balance_bf16", "decode_bf16"])
+def test_layer_full_size(name):
+    cfg = WORKLOADS[name]
+    _say(f"[case] full-size {name}: generating inputs")
+    inp = generate(cfg)
+    _say(f"[case] full-size {name}: uploading")
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    _say(f"[case] full-size {name}: running")
+    res = layer(x)
+    torch.cuda.synchronize()
+    _say(f"[case] full-size {name}: checking")
+    tokens = None if cfg.T <= 64 else _sample_tokens(cfg.T)
+    errs = check_layer(inp, res, tokens=tokens)
+    _say(f"[ok] full-size {name}: {errs}")
