@@ -36,18 +36,19 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(src_dir: str = CSRC):
+    return sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, src_dir: str = CSRC) -> str:
+    """Compile every .hip file of ``src_dir`` and link ``out``."""
     hipcc = _hipcc()
-    objdir = os.path.join(LIBDIR, "obj")
+    objdir = os.path.join(os.path.dirname(out), "obj")
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, "-I", CSRC, *extra_flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops' is not a recognized feature" not in l)
@@ -57,16 +58,16 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             print(out)
         return obj
 
-    srcs = sources()
+    srcs = sources(src_dir)
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -11,12 +11,11 @@
 //     the BN/2 up rows of the same hidden columns, so each wave owns matching
 //     gate and up accumulators and the epilogue writes hid directly (bf16).
 //   GEMM 2 (down): y = hid W_down^T.
-//   Block tile BM x BN x 64, 4 waves in a 2 x 2 grid, each wave a
-//   (BM/2) x (BN/2) grid of v_mfma_f32_32x32x16_bf16 tiles.  A and B tiles are
-//   staged through LDS, double-buffered, with the next K slice prefetched into
-//   registers while the current one feeds the matrix cores.  LDS rows are 128
-//   bytes (8 chunks of 16 bytes); chunk c of row r is stored at c ^ (r & 7), so
-//   both the 16-byte stores and the 16-byte fragment reads are conflict-free.
+//   Block tile BM x BN, 4 waves in a 2 x 2 grid, each wave a (BM/2) x (BN/2)
+//   grid of v_mfma_f32_32x32x16_bf16 tiles.  K advances in slices of 32 that
+//   the direct-to-LDS load streams through two rings of LDS stages (see the
+//   kernel); fragment reads are double-buffered in registers and interleaved
+//   one-for-one with the MFMAs.
 //   Tiles are ordered group-major, n-tile next, m-tile fastest, and spread in
 //   contiguous runs over the 8 XCDs so that tiles that share a weight panel
 //   or an activation panel run together on one XCD's L2.
@@ -28,7 +27,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
@@ -93,52 +91,87 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
   return true;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) {  // element offset in a 64-wide LDS row
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
-}
-
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel.  kFused: B rows [0, BN/2) are W_gate rows n0.., rows
 // [BN/2, BN) are W_up rows n0..; output columns n0 .. n0 + BN/2 of hid.
 // Otherwise B rows are W rows n0 .. n0 + BN and the output is A W^T.
+//
+// K advances in slices of 32.  The gfx950 direct-to-LDS load
+// (global_load_lds_dwordx4) streams the A slices through a ring of SA LDS
+// stages and the B slices through a ring of SB stages, so A slice kt+SA and B
+// slice kt+SB are requested while slice kt feeds the matrix cores; there is
+// one barrier per slice.  A DMA instruction writes 64 x 16 bytes = 16 tile
+// rows of 64 bytes (lane l lands in chunk l % 4 of row l / 4); LDS chunk c of
+// row r holds the logical chunk c ^ ((r >> 2) & 3), so that the 16 lanes
+// served per LDS cycle by a 16-byte fragment read (16 consecutive rows, one
+// logical chunk) touch 16 distinct bank groups.  Each lane therefore fetches
+// the global chunk (l % 4) ^ ((l / 16) % 4).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool kFused, typename OutT>
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+
+__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (lds_ptr_t)(l), 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained to <= n (n < 64)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ int swz32(int row, int chunk) {  // element offset, 32-wide rows
+  return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+template <int BM, int BN, int SA, int SB, bool kFused, typename OutT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
     OutT* __restrict__ C) {
+  constexpr int BKs = 32;                     // K per stage
   constexpr int NCOL = kFused ? BN / 2 : BN;  // output columns per tile
   constexpr int MT = BM / 64;                 // 32-row MFMA tiles per wave
   constexpr int NT = BN / 64;                 // 32-col MFMA tiles per wave
-  constexpr int AP = BM / 32;                 // A rows loaded per thread per K slice
-  constexpr int BP = BN / 32;
+  constexpr int AP = BM / 64;                 // DMA instructions per thread per stage (A)
+  constexpr int BP = BN / 64;                 // (B)
+  constexpr int P = AP + BP;
   static_assert(!kFused || NT % 2 == 0, "fused tile needs matching gate/up halves");
 
   Tile tile;
   if (!decode_tile(off, mstart, G, ntn, BM, NCOL, tile)) return;
 
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                     // [2][BM * 64]
-  uint16_t* Bs = smem + 2 * BM * kBK;      // [2][BN * 64]
+  uint16_t* As = smem;                     // [SA][BM * 32]
+  uint16_t* Bs = smem + SA * BM * BKs;     // [SB][BN * 32]
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave & 1, wn = wave >> 1;
-  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int drow = 16 * wave + (lane >> 2);              // tile row of DMA instruction 0
+  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);     // global chunk this lane fetches
 
-  // per-thread source rows of the A and B tiles
-  const uint16_t* ap[AP];
+  int src[AP];
 #pragma unroll
   for (int j = 0; j < AP; ++j) {
-    int r = tile.m0 + lrow + 32 * j;
-    r = r < tile.row_end ? r : tile.row_end - 1;  // rows past the group: valid row, result unused
-    const int64_t src = a_rows ? static_cast<int64_t>(a_rows[r] / a_div) : r;
-    ap[j] = A + src * K + lchunk * 8;
+    const int r = tile.m0 + drow + 64 * j;
+    src[j] = r < tile.row_end ? r : tile.row_end - 1;  // rows past the group: valid row, unused
   }
+  if (a_rows) {  // gather: all index loads first, then the divisions
+#pragma unroll
+    for (int j = 0; j < AP; ++j) src[j] = a_rows[src[j]];
+#pragma unroll
+    for (int j = 0; j < AP; ++j) src[j] /= a_div;
+  }
+  const uint16_t* ap[AP];
+#pragma unroll
+  for (int j = 0; j < AP; ++j) ap[j] = A + static_cast<int64_t>(src[j]) * K + gchunk * 8;
   const uint16_t* bp[BP];
 #pragma unroll
   for (int j = 0; j < BP; ++j) {
-    const int r = lrow + 32 * j;
+    const int r = drow + 64 * j;
     const uint16_t* base = B0;
     int n = tile.n0 + r;
     if (kFused && r >= BN / 2) {
@@ -146,25 +179,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       n = tile.n0 + r - BN / 2;
     }
     n = n < N ? n : N - 1;
-    bp[j] = base + tile.g * b_stride + static_cast<int64_t>(n) * K + lchunk * 8;
+    bp[j] = base + tile.g * b_stride + static_cast<int64_t>(n) * K + gchunk * 8;
   }
 
-  u32x4 ra[AP], rb[BP];
-#define MOE_LOAD_GLOBAL(k0)                                                          \
+  const int nk = K / BKs;
+  // copy K slice `ks` (clamped into range: surplus copies reload the last slice
+  // into a stage nobody reads again, which keeps the loop branch-free)
+#define MOE_ISSUE_A(stage, ks)                                                       \
   do {                                                                               \
+    const int k0_ = ((ks) < nk ? (ks) : nk - 1) * BKs;                               \
+    uint16_t* as_ = As + (stage) * BM * BKs + 16 * wave_u * BKs;                     \
     _Pragma("unroll") for (int j = 0; j < AP; ++j)                                   \
-        ra[j] = *reinterpret_cast<const u32x4*>(ap[j] + (k0));                       \
-    _Pragma("unroll") for (int j = 0; j < BP; ++j)                                   \
-        rb[j] = *reinterpret_cast<const u32x4*>(bp[j] + (k0));                       \
+        load_lds16(ap[j] + k0_, as_ + 64 * j * BKs);                                 \
   } while (0)
-#define MOE_STORE_LDS(buf)                                                           \
+#define MOE_ISSUE_B(stage, ks)                                                       \
   do {                                                                               \
-    uint16_t* as_ = As + (buf) * BM * kBK;                                           \
-    uint16_t* bs_ = Bs + (buf) * BN * kBK;                                           \
-    _Pragma("unroll") for (int j = 0; j < AP; ++j)                                   \
-        *reinterpret_cast<u32x4*>(as_ + swz(lrow + 32 * j, lchunk)) = ra[j];         \
+    const int k0_ = ((ks) < nk ? (ks) : nk - 1) * BKs;                               \
+    uint16_t* bs_ = Bs + (stage) * BN * BKs + 16 * wave_u * BKs;                     \
     _Pragma("unroll") for (int j = 0; j < BP; ++j)                                   \
-        *reinterpret_cast<u32x4*>(bs_ + swz(lrow + 32 * j, lchunk)) = rb[j];         \
+        load_lds16(bp[j] + k0_, bs_ + 64 * j * BKs);                                 \
   } while (0)
 
   f32x16 acc[MT][NT];
@@ -173,7 +206,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-  // rows of this wave's fragments inside the tiles
   int arow[MT], brow[NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
@@ -188,34 +220,77 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
   const int khalf = lane >> 5;
 
-  const int nk = K / kBK;
-  MOE_LOAD_GLOBAL(0);
-  MOE_STORE_LDS(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) MOE_LOAD_GLOBAL((kt + 1) * kBK);
-    const uint16_t* as = As + cur * BM * kBK;
-    const uint16_t* bs = Bs + cur * BN * kBK;
+#define MOE_READ(F, sa, sb, step)                                                    \
+  do {                                                                               \
+    const uint16_t* as_ = As + (sa) * BM * BKs;                                      \
+    const uint16_t* bs_ = Bs + (sb) * BN * BKs;                                      \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i)                                   \
+        F##a[i] = *reinterpret_cast<const bf16x8*>(as_ + swz32(arow[i], (step) * 2 + khalf)); \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j)                                   \
+        F##b[j] = *reinterpret_cast<const bf16x8*>(bs_ + swz32(brow[j], (step) * 2 + khalf)); \
+  } while (0)
+#define MOE_MFMA(F)                                                                  \
+  _Pragma("unroll") for (int i = 0; i < MT; ++i)                                     \
+  _Pragma("unroll") for (int j = 0; j < NT; ++j)                                     \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[i], F##b[j], acc[i][j], 0, 0, 0)
+
+  bf16x8 f0a[MT], f0b[NT], f1a[MT], f1b[NT];
+  constexpr int kPairs = MT + NT;                 // (MFMA, LDS read) pairs per half slice
+  constexpr int kRest = MT * NT - kPairs;         // MFMAs left after the pairs
+  constexpr int kPerG = kRest / P;                // MFMAs between DMA issues
+  static_assert(SB >= SA && SA >= 2, "B ring at least as deep as the A ring");
+  // Virtual iteration v issues A slice v+SA and B slice v+SB; the prologue runs
+  // v = -SB .. -1 (A only from v = -SA).  Loads complete in issue order, so
+  // "A slice kt+1 (and the older B slice kt+1) landed" means at most the loads
+  // of iterations kt+2-SA .. kt-1 are still outstanding.
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + khalf;
-      bf16x8 af[MT], bfr[NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + swz(arow[i], c));
-#pragma unroll
-      for (int j = 0; j < NT; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + swz(brow[j], c));
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_STORE_LDS(cur ^ 1);
-    __syncthreads();
+  for (int v = -SB; v < 0; ++v) {
+    if (v + SA >= 0) MOE_ISSUE_A(v + SA, v + SA);
+    MOE_ISSUE_B(v + SB, v + SB);
   }
-#undef MOE_LOAD_GLOBAL
-#undef MOE_STORE_LDS
+  wait_vm<(SA - 1) * P>();
+  __syncthreads();
+  int sa = 0, sb = 0;  // stages of slice kt
+  MOE_READ(f0, 0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_READ(f1, sa, sb, 1);
+    MOE_MFMA(f0);
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(SA - 2) * P>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_READ(f0, sa1, sb1, 0);
+    MOE_ISSUE_A(sa, kt + SA);
+    MOE_ISSUE_B(sb, kt + SB);
+    MOE_MFMA(f1);
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (kPerG > 0) __builtin_amdgcn_sched_group_barrier(0x008, kPerG, 0);
+    }
+    if (kRest - kPerG * P > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest - kPerG * P, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    sa = sa1;
+    sb = sb1;
+  }
+  wait_vm<0>();
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_B
+#undef MOE_READ
+#undef MOE_MFMA
 
   // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
   const int rbase = tile.m0 + wm * (BM / 2) + (lane >> 5) * 4;
@@ -252,6 +327,143 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
             } else {
               C[static_cast<int64_t>(row) * N + col] = v;
             }
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny bf16 kernel for groups of a few rows (decode-shaped batches): the
+// weights are streamed once from HBM and dominate the bytes, so one wave per
+// workgroup walks a 64-row slab of the weight matrix (fused: 32 gate rows and
+// the matching 32 up rows) along K, with the weight rows as the 16-row A
+// operand of v_mfma_f32_16x16x32_bf16 and up to TBN blocks of 16 token rows as
+// the B operand.  No LDS: each lane loads 32 contiguous bytes of a weight row
+// per 64-wide K chunk (a full 128-byte line per row across the 4 lanes that
+// share it) and the matching 32 bytes of its token row.  The K order inside a
+// chunk is permuted identically for both operands, which leaves the
+// contraction unchanged: MFMA step i of chunk c uses k = 64c + 16 (lane/16)
+// + 8i + 0..7.  Groups with more than 16*TBN rows loop over row blocks.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyCols = 64;   // weight rows per wave
+
+template <bool kFused, int TBN, typename OutT>
+__global__ __launch_bounds__(64) void skinny_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
+    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int64_t w_stride, int K,
+    int N, const int32_t* __restrict__ off, int nslices, OutT* __restrict__ C) {
+  constexpr int NBW = 4;                            // 16-row weight blocks per wave
+  constexpr int NOUT = kFused ? 32 : 64;            // output columns per wave
+  const int g = blockIdx.x / nslices;
+  const int slice = blockIdx.x - g * nslices;
+  const int r0 = off[g], r1 = off[g + 1];
+  if (r0 >= r1) return;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, kq = (lane >> 4) * 16;
+  const int n0 = slice * NOUT;
+
+  const uint16_t* wrow[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const uint16_t* base = W0;
+    int n = n0 + 16 * b + l16;
+    if (kFused && b >= NBW / 2) {
+      base = W1;
+      n = n0 + 16 * (b - NBW / 2) + l16;
+    }
+    n = n < N ? n : N - 1;
+    wrow[b] = base + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(n) * K + kq;
+  }
+
+  for (int rb = r0; rb < r1; rb += 16 * TBN) {
+    const uint16_t* xrow[TBN];
+#pragma unroll
+    for (int tb = 0; tb < TBN; ++tb) {
+      int r = rb + 16 * tb + l16;
+      r = r < r1 ? r : r1 - 1;  // rows past the group: valid row, result unused
+      const int64_t src = a_rows ? static_cast<int64_t>(a_rows[r] / a_div) : r;
+      xrow[tb] = A + src * K + kq;
+    }
+    f32x4 acc[NBW][TBN];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+      for (int tb = 0; tb < TBN; ++tb) acc[b][tb] = f32x4{};
+
+    const int nchunk = K / 64;
+    int c = 0;
+    // two chunks per step: all loads first, then the MFMAs
+    for (; c + 2 <= nchunk; c += 2) {
+      bf16x8 wf[2][NBW][2], xf[2][TBN][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const bf16x8* p = reinterpret_cast<const bf16x8*>(wrow[b] + (c + u) * 64);
+          wf[u][b][0] = p[0];
+          wf[u][b][1] = p[1];
+        }
+#pragma unroll
+        for (int tb = 0; tb < TBN; ++tb) {
+          const bf16x8* p = reinterpret_cast<const bf16x8*>(xrow[tb] + (c + u) * 64);
+          xf[u][tb][0] = p[0];
+          xf[u][tb][1] = p[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int tb = 0; tb < TBN; ++tb)
+              acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][b][i], xf[u][tb][i],
+                                                                  acc[b][tb], 0, 0, 0);
+    }
+    for (; c < nchunk; ++c) {
+      bf16x8 wf[NBW][2], xf[TBN][2];
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(wrow[b] + c * 64);
+        wf[b][0] = p[0];
+        wf[b][1] = p[1];
+      }
+#pragma unroll
+      for (int tb = 0; tb < TBN; ++tb) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(xrow[tb] + c * 64);
+        xf[tb][0] = p[0];
+        xf[tb][1] = p[1];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+          for (int tb = 0; tb < TBN; ++tb)
+            acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b][i], xf[tb][i], acc[b][tb],
+                                                                0, 0, 0);
+    }
+
+    // D[weight row][token]: lane holds token column l16 and weight rows 4*(lane/16)+j
+#pragma unroll
+    for (int tb = 0; tb < TBN; ++tb) {
+      const int row = rb + 16 * tb + l16;
+      if (row >= r1) continue;
+      OutT* crow = C + static_cast<int64_t>(row) * N;
+#pragma unroll
+      for (int b = 0; b < (kFused ? NBW / 2 : NBW); ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + 16 * b + (lane >> 4) * 4 + j;
+          if (n >= N) continue;
+          float v = acc[b][tb][j];
+          if constexpr (kFused) v = silu_f32(v) * acc[b + NBW / 2][tb][j];
+          if constexpr (sizeof(OutT) == 2) {
+            crow[n] = f32_to_bf16_bits(v);
+          } else {
+            crow[n] = v;
           }
         }
     }
@@ -332,13 +544,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// LDS ring depths: activations mostly hit in L2, weight slices are first
+// touches from HBM and get the deeper ring (3 x 16 KB + 6 x 16 KB for 256 x 256).
+constexpr int kRingA = 3;
+constexpr int kRingB = 6;
+
 template <int BM, int BN>
 hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + BM - 1) / BM + s.G;
   const int ntn = static_cast<int>((s.h + BN / 2 - 1) / (BN / 2));
-  const size_t lds = sizeof(uint16_t) * 2 * (BM + BN) * kBK;
+  const size_t lds = sizeof(uint16_t) * (kRingA * BM + kRingB * BN) * 32;
   tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, BM, s.mstart);
-  auto kern = gemm_bf16_kernel<BM, BN, true, uint16_t>;
+  auto kern = gemm_bf16_kernel<BM, BN, kRingA, kRingB, true, uint16_t>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   kern<<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, lds, stream>>>(
@@ -352,9 +569,9 @@ template <int BM, int BN, typename OutT>
 hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + BM - 1) / BM + s.G;
   const int ntn = static_cast<int>((s.d + BN - 1) / BN);
-  const size_t lds = sizeof(uint16_t) * 2 * (BM + BN) * kBK;
+  const size_t lds = sizeof(uint16_t) * (kRingA * BM + kRingB * BN) * 32;
   tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, BM, s.mstart);
-  auto kern = gemm_bf16_kernel<BM, BN, false, OutT>;
+  auto kern = gemm_bf16_kernel<BM, BN, kRingA, kRingB, false, OutT>;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   kern<<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, lds, stream>>>(
@@ -386,18 +603,50 @@ hipError_t down_f32(const SwigluArgs& s, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Large tiles once groups average at least 384 rows; otherwise 128 x 128.
+template <bool kFused, typename OutT>
+hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const int32_t* a_rows,
+                       int a_div, const void* w0, const void* w1, void* out, hipStream_t stream) {
+  const int per_wave = kFused ? 32 : 64;
+  const int nslices = (N + per_wave - 1) / per_wave;
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(s.G) * nslices);
+  const int64_t mean = (s.max_rows + s.G - 1) / s.G;
+  const int64_t wstride = static_cast<int64_t>(N) * K;
+#define MOE_SKINNY(TBN)                                                                    \
+  skinny_kernel<kFused, TBN, OutT><<<grid, 64, 0, stream>>>(                               \
+      static_cast<const uint16_t*>(a), a_rows, a_div, static_cast<const uint16_t*>(w0),    \
+      static_cast<const uint16_t*>(w1), wstride, K, N, s.group_offset, nslices,            \
+      static_cast<OutT*>(out))
+  if (mean <= 16) MOE_SKINNY(1);
+  else if (mean <= 32) MOE_SKINNY(2);
+  else MOE_SKINNY(4);
+#undef MOE_SKINNY
+  return hipGetLastError();
+}
+
+// Groups averaging at most 64 rows stream weights through the skinny kernel;
+// large tiles once groups average at least 384 rows; otherwise 128 x 128.
+bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
 bool big_tiles(const SwigluArgs& s) { return s.max_rows >= static_cast<int64_t>(s.G) * 384; }
 
 }  // namespace
 
 hipError_t launch_gate_up(const SwigluArgs& s, hipStream_t stream) {
   if (!s.bf16) return gate_up_f32(s, stream);
+  if (skinny(s))
+    return skinny_bf16<true, uint16_t>(s, s.d, s.h, s.a, s.a_rows, s.a_div, s.w_gate, s.w_up,
+                                       s.hid, stream);
   return big_tiles(s) ? gate_up_bf16<256, 256>(s, stream) : gate_up_bf16<128, 128>(s, stream);
 }
 
 hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
   if (!s.bf16) return down_f32(s, stream);
+  if (skinny(s)) {
+    if (s.y_bf16)
+      return skinny_bf16<false, uint16_t>(s, s.h, s.d, s.hid, nullptr, 1, s.w_down, nullptr, s.y,
+                                          stream);
+    return skinny_bf16<false, float>(s, s.h, s.d, s.hid, nullptr, 1, s.w_down, nullptr, s.y,
+                                     stream);
+  }
   if (s.y_bf16)
     return big_tiles(s) ? down_bf16<256, 256, uint16_t>(s, stream)
                         : down_bf16<128, 128, uint16_t>(s, stream);
