@@ -107,12 +107,14 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
+    t_host = time.perf_counter()
     for _ in range(args.steps):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         marks.append([("start", ev0)])
         res = layer(x, mark=mark)
     end.record(stream)
+    host_ms = (time.perf_counter() - t_host) * 1e3 / args.steps  # enqueue cost per step
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
@@ -176,6 +178,7 @@ def main():
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "layer_hbm_gbs": bytes_ / (ms * 1e-3) / 1e9,
         "phase_ms": phase_ms,
+        "host_enqueue_ms_per_step": host_ms,
         "routing": {"kept_pairs": R_kept, "dropped_pairs": T * k - R_kept,
                     "touched_experts": touched, "max_rows": int(kept.max()),
                     "min_rows": int(kept.min()), "max_demand": int(counts.max())},

@@ -130,12 +130,16 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E);
  * logits [T,E] fp32 out (in with LOGITS_IN); topk_idx [T,k] int32 out;
  * topk_gate [T,k] fp32 out.
  * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK; for bf16
- * d % 32 == 0.  Needs no workspace.  Logits must be finite.
+ * d % 32 == 0.  Logits must be finite.
+ * Workspace: moe_route_workspace(T, d, E, k, dt) bytes (partial sums when the
+ * reduction over d is split across waves for small batches; 0 when it is not
+ * and with MOE_ROUTE_LOGITS_IN).
  */
+size_t moe_route_workspace(int64_t T, int d, int E, int k, int dt);
 moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
                        int k, const float* logit_bias, const float* select_bias,
                        unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
-                       void* stream);
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* moe_permute: group the routed pairs by expert, apply the capacity drop,

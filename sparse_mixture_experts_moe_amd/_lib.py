@@ -47,7 +47,8 @@ _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_capacity": (_i64, [_d, _i64, _i, _i]),
-    "moe_route": (_i, [_p, _p, _i, _i64, _i, _i, _i, _p, _p, _u, _p, _p, _p, _p]),
+    "moe_route_workspace": (_sz, [_i64, _i, _i, _i, _i]),
+    "moe_route": (_i, [_p, _p, _i, _i64, _i, _i, _i, _p, _p, _u, _p, _p, _p, _p, _sz, _p]),
     "moe_permute_workspace": (_sz, [_i64, _i, _i]),
     "moe_permute": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_swiglu_workspace": (_sz, [_i64, _i, _i, _i, _i]),
@@ -115,8 +116,12 @@ def moe_capacity(cf: float, T: int, k: int, E: int) -> int:
     return _L.moe_capacity(float(cf), T, k, E)
 
 
+def moe_route_workspace(T, d, E, k, dt) -> int:
+    return _L.moe_route_workspace(T, d, E, k, dt)
+
+
 def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None, topk_idx=None,
-              topk_gate=None, logits_in=False, stream=None):
+              topk_gate=None, logits_in=False, ws=None, stream=None):
     """Router logits, top-k experts and renormalised gates.  With
     ``logits_in`` the given ``logits`` [T, E] are used instead of x W_r^T."""
     if logits_in:
@@ -134,10 +139,14 @@ def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None,
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     if topk_gate is None:
         topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
-    _contig(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate)
+    nws = 0 if logits_in else moe_route_workspace(T, d, E, k, dt)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _contig(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate, ws)
     _check(_L.moe_route(_ptr(x), _ptr(w_router), dt, T, d, E, k, _ptr(logit_bias),
                         _ptr(select_bias), MOE_ROUTE_LOGITS_IN if logits_in else 0,
-                        _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _stream(stream)))
+                        _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), ws.numel(),
+                        _stream(stream)))
     return logits, topk_idx, topk_gate
 
 

@@ -7,18 +7,21 @@
 // operand is contiguous along its reduction axis.
 //
 // bf16 path (gfx950 MFMA, fp32 accumulation):
-//   GEMM 1 (gate || up, fused SiLU*mul): one B tile holds BN/2 gate rows and
-//     the BN/2 up rows of the same hidden columns, so each wave owns matching
+//   GEMM 1 (gate || up, fused SiLU*mul): one B tile holds 128 gate rows and
+//     the 128 up rows of the same hidden columns, so each wave owns matching
 //     gate and up accumulators and the epilogue writes hid directly (bf16).
 //   GEMM 2 (down): y = hid W_down^T.
-//   Block tile BM x BN, 4 waves in a 2 x 2 grid, each wave a (BM/2) x (BN/2)
-//   grid of v_mfma_f32_32x32x16_bf16 tiles.  K advances in slices of 32 that
-//   the direct-to-LDS load streams through two rings of LDS stages (see the
-//   kernel); fragment reads are double-buffered in registers and interleaved
-//   one-for-one with the MFMAs.
-//   Tiles are ordered group-major, n-tile next, m-tile fastest, and spread in
-//   contiguous runs over the 8 XCDs so that tiles that share a weight panel
-//   or an activation panel run together on one XCD's L2.
+//   Output tiles are 256 columns wide and 256 rows high, except that the last
+//   m-tile of each group runs as a 64-, 128- or 256-row tile according to the
+//   rows left, so a short remainder costs a quarter or a half of a full tile.
+//   Four waves form a 2 x 2 (256 rows) or 1 x 4 (64 and 128 rows) grid of
+//   v_mfma_f32_32x32x16_bf16 tiles.  K advances in slices of 32 that the
+//   direct-to-LDS load streams through two rings of LDS stages (see
+//   gemm_tile); fragment reads are double-buffered in registers and
+//   interleaved one-for-one with the MFMAs.
+//   Tiles are ordered group-major, n-tile next, m-tile fastest, and laid out
+//   in contiguous runs per XCD so that tiles sharing a weight panel or an
+//   activation panel run together on one XCD's L2.
 // fp32 path: a plain LDS-tiled FMA kernel with the same tile order.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -107,6 +110,36 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
 // logical chunk) touch 16 distinct bank groups.  Each lane therefore fetches
 // the global chunk (l % 4) ^ ((l / 16) % 4).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// bf16 tiles are 256 rows high except the last m-tile of each group, which
+// runs as a 64-, 128- or 256-row tile according to the rows it holds (so a
+// short remainder costs a quarter or a half of a full tile).  It stays in the
+// group-major order, next to the tiles that share its weight panel.
+// ---------------------------------------------------------------------------
+constexpr int kTileM = 256;
+// LDS ring depths: activations mostly hit in L2, weight slices are first
+// touches from HBM and get the deeper ring (3 x 16 KB + 6 x 16 KB).
+constexpr int kRingA = 3;
+constexpr int kRingB = 6;
+
+struct Tile2 {
+  int g, m0, row_end, n0, cls;  // cls 0: 256 rows, 1: 128 rows, 2: 64 rows
+};
+
+__device__ __forceinline__ bool decode_tile2(const int32_t* __restrict__ off,
+                                             const int32_t* __restrict__ mstart, int G, int ntn,
+                                             int ncol, Tile2& tile) {
+  Tile t;
+  if (!decode_tile(off, mstart, G, ntn, kTileM, ncol, t)) return false;
+  tile.g = t.g;
+  tile.m0 = t.m0;
+  tile.row_end = t.row_end;
+  tile.n0 = t.n0;
+  const int rem = t.row_end - t.m0;
+  tile.cls = rem <= 64 ? 2 : (rem <= 128 ? 1 : 0);
+  return true;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 
@@ -125,31 +158,29 @@ __device__ __forceinline__ int swz32(int row, int chunk) {  // element offset, 3
   return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-template <int BM, int BN, int SA, int SB, bool kFused, typename OutT>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+// One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
+// waves form a WM x WN grid, each wave a (BM/WM) x (BN/WN) block of MFMA
+// tiles.  The LDS rings are laid out for kTileM rows of A whatever BM is.
+template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename OutT>
+__device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
-    int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
-    OutT* __restrict__ C) {
+    int N, const Tile2& tile, uint16_t* smem, OutT* __restrict__ C) {
+  static_assert(WM * WN == 4, "four waves");
   constexpr int BKs = 32;                     // K per stage
-  constexpr int NCOL = kFused ? BN / 2 : BN;  // output columns per tile
-  constexpr int MT = BM / 64;                 // 32-row MFMA tiles per wave
-  constexpr int NT = BN / 64;                 // 32-col MFMA tiles per wave
+  constexpr int MT = BM / WM / 32;            // 32-row MFMA tiles per wave
+  constexpr int NT = BN / WN / 32;            // 32-col MFMA tiles per wave
   constexpr int AP = BM / 64;                 // DMA instructions per thread per stage (A)
   constexpr int BP = BN / 64;                 // (B)
   constexpr int P = AP + BP;
   static_assert(!kFused || NT % 2 == 0, "fused tile needs matching gate/up halves");
 
-  Tile tile;
-  if (!decode_tile(off, mstart, G, ntn, BM, NCOL, tile)) return;
-
-  extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* As = smem;                     // [SA][BM * 32]
-  uint16_t* Bs = smem + SA * BM * BKs;     // [SB][BN * 32]
+  uint16_t* As = smem;                         // [SA][kTileM * 32]
+  uint16_t* Bs = smem + SA * kTileM * BKs;     // [SB][BN * 32]
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = WM == 1 ? 0 : (wave & 1), wn = WM == 1 ? wave : (wave >> 1);
   const int drow = 16 * wave + (lane >> 2);              // tile row of DMA instruction 0
   const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);     // global chunk this lane fetches
 
@@ -188,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #define MOE_ISSUE_A(stage, ks)                                                       \
   do {                                                                               \
     const int k0_ = ((ks) < nk ? (ks) : nk - 1) * BKs;                               \
-    uint16_t* as_ = As + (stage) * BM * BKs + 16 * wave_u * BKs;                     \
+    uint16_t* as_ = As + (stage) * kTileM * BKs + 16 * wave_u * BKs;                 \
     _Pragma("unroll") for (int j = 0; j < AP; ++j)                                   \
         load_lds16(ap[j] + k0_, as_ + 64 * j * BKs);                                 \
   } while (0)
@@ -208,13 +239,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
   int arow[MT], brow[NT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
+  for (int i = 0; i < MT; ++i) arow[i] = wm * (BM / WM) + i * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     if (kFused) {
-      brow[j] = (j < NT / 2) ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - NT / 2) * 32;
+      brow[j] = (j < NT / 2) ? wn * (BN / (2 * WN)) + j * 32
+                             : BN / 2 + wn * (BN / (2 * WN)) + (j - NT / 2) * 32;
     } else {
-      brow[j] = wn * (BN / 2) + j * 32;
+      brow[j] = wn * (BN / WN) + j * 32;
     }
     brow[j] += lane & 31;
   }
@@ -222,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
 #define MOE_READ(F, sa, sb, step)                                                    \
   do {                                                                               \
-    const uint16_t* as_ = As + (sa) * BM * BKs;                                      \
+    const uint16_t* as_ = As + (sa) * kTileM * BKs;                                  \
     const uint16_t* bs_ = Bs + (sb) * BN * BKs;                                      \
     _Pragma("unroll") for (int i = 0; i < MT; ++i)                                   \
         F##a[i] = *reinterpret_cast<const bf16x8*>(as_ + swz32(arow[i], (step) * 2 + khalf)); \
@@ -293,11 +325,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #undef MOE_MFMA
 
   // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
-  const int rbase = tile.m0 + wm * (BM / 2) + (lane >> 5) * 4;
+  const int rbase = tile.m0 + wm * (BM / WM) + (lane >> 5) * 4;
   if constexpr (kFused) {
 #pragma unroll
     for (int j = 0; j < NT / 2; ++j) {
-      const int col = tile.n0 + wn * (BN / 4) + j * 32 + (lane & 31);
+      const int col = tile.n0 + wn * (BN / (2 * WN)) + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -313,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   } else {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int col = tile.n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+      const int col = tile.n0 + wn * (BN / WN) + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -333,20 +365,44 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
 }
 
+template <bool kFused, typename OutT>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
+    int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
+    OutT* __restrict__ C) {
+  constexpr int BN = 256;
+  Tile2 tile;
+  if (!decode_tile2(off, mstart, G, ntn, kFused ? BN / 2 : BN, tile)) return;
+  extern __shared__ __align__(16) uint16_t smem[];
+  if (tile.cls == 0) {
+    gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
+                                                          N, tile, smem, C);
+  } else if (tile.cls == 1) {
+    gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
+                                                          N, tile, smem, C);
+  } else {
+    gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
+                                                         N, tile, smem, C);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Skinny bf16 kernel for groups of a few rows (decode-shaped batches): the
 // weights are streamed once from HBM and dominate the bytes, so one wave per
 // workgroup walks a 64-row slab of the weight matrix (fused: 32 gate rows and
 // the matching 32 up rows) along K, with the weight rows as the 16-row A
 // operand of v_mfma_f32_16x16x32_bf16 and up to TBN blocks of 16 token rows as
-// the B operand.  No LDS: each lane loads 32 contiguous bytes of a weight row
-// per 64-wide K chunk (a full 128-byte line per row across the 4 lanes that
-// share it) and the matching 32 bytes of its token row.  The K order inside a
-// chunk is permuted identically for both operands, which leaves the
-// contraction unchanged: MFMA step i of chunk c uses k = 64c + 16 (lane/16)
-// + 8i + 0..7.  Groups with more than 16*TBN rows loop over row blocks.
+// the B operand.  No LDS: per 64-wide K chunk each lane loads two 16-byte
+// pieces of a weight row, at k = 64c + 8 (lane/16) and 32 later, so that every
+// load instruction covers 64 contiguous bytes of each of its 16 rows (the two
+// instructions together the full 128-byte line), and the matching pieces of
+// its token row.  The K order inside a chunk is permuted identically for both
+// operands, which leaves the contraction unchanged: MFMA step i of chunk c
+// uses k = 64c + 32i + 8 (lane/16) + 0..7.  Groups with more than 16*TBN rows
+// loop over row blocks.
 // ---------------------------------------------------------------------------
-constexpr int kSkinnyCols = 64;   // weight rows per wave
+constexpr int kSkinnyBatch = 4;   // 64-wide K chunks loaded per step
 
 template <bool kFused, int TBN, typename OutT>
 __global__ __launch_bounds__(64) void skinny_kernel(
@@ -360,7 +416,7 @@ __global__ __launch_bounds__(64) void skinny_kernel(
   const int r0 = off[g], r1 = off[g + 1];
   if (r0 >= r1) return;
   const int lane = threadIdx.x;
-  const int l16 = lane & 15, kq = (lane >> 4) * 16;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
   const int n0 = slice * NOUT;
 
   const uint16_t* wrow[NBW];
@@ -393,26 +449,27 @@ __global__ __launch_bounds__(64) void skinny_kernel(
 
     const int nchunk = K / 64;
     int c = 0;
-    // two chunks per step: all loads first, then the MFMAs
-    for (; c + 2 <= nchunk; c += 2) {
-      bf16x8 wf[2][NBW][2], xf[2][TBN][2];
+    // kSkinnyBatch chunks per step: all loads first, then the MFMAs
+    for (; c + kSkinnyBatch <= nchunk; c += kSkinnyBatch) {
+      bf16x8 wf[kSkinnyBatch][NBW][2], xf[kSkinnyBatch][TBN][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kSkinnyBatch; ++u) {
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
           const bf16x8* p = reinterpret_cast<const bf16x8*>(wrow[b] + (c + u) * 64);
           wf[u][b][0] = p[0];
-          wf[u][b][1] = p[1];
+          wf[u][b][1] = p[4];
         }
 #pragma unroll
         for (int tb = 0; tb < TBN; ++tb) {
           const bf16x8* p = reinterpret_cast<const bf16x8*>(xrow[tb] + (c + u) * 64);
           xf[u][tb][0] = p[0];
-          xf[u][tb][1] = p[1];
+          xf[u][tb][1] = p[4];
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < kSkinnyBatch; ++u)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -421,6 +478,7 @@ __global__ __launch_bounds__(64) void skinny_kernel(
             for (int tb = 0; tb < TBN; ++tb)
               acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][b][i], xf[u][tb][i],
                                                                   acc[b][tb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     for (; c < nchunk; ++c) {
       bf16x8 wf[NBW][2], xf[TBN][2];
@@ -428,13 +486,13 @@ __global__ __launch_bounds__(64) void skinny_kernel(
       for (int b = 0; b < NBW; ++b) {
         const bf16x8* p = reinterpret_cast<const bf16x8*>(wrow[b] + c * 64);
         wf[b][0] = p[0];
-        wf[b][1] = p[1];
+        wf[b][1] = p[4];
       }
 #pragma unroll
       for (int tb = 0; tb < TBN; ++tb) {
         const bf16x8* p = reinterpret_cast<const bf16x8*>(xrow[tb] + c * 64);
         xf[tb][0] = p[0];
-        xf[tb][1] = p[1];
+        xf[tb][1] = p[4];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -544,37 +602,33 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// LDS ring depths: activations mostly hit in L2, weight slices are first
-// touches from HBM and get the deeper ring (3 x 16 KB + 6 x 16 KB for 256 x 256).
-constexpr int kRingA = 3;
-constexpr int kRingB = 6;
+constexpr size_t kGemmLds = sizeof(uint16_t) * (kRingA * kTileM + kRingB * 256) * 32;
 
-template <int BM, int BN>
+// grid: sum over groups of ceil(rows / 256) <= ceil(max_rows / 256) + G m-tiles
+unsigned gemm_grid(const SwigluArgs& s, int ntn) {
+  const int64_t mt = (s.max_rows + kTileM - 1) / kTileM + s.G;
+  return static_cast<unsigned>((mt * ntn + 7) & ~int64_t{7});
+}
+
 hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
-  const int64_t mt_ub = (s.max_rows + BM - 1) / BM + s.G;
-  const int ntn = static_cast<int>((s.h + BN / 2 - 1) / (BN / 2));
-  const size_t lds = sizeof(uint16_t) * (kRingA * BM + kRingB * BN) * 32;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, BM, s.mstart);
-  auto kern = gemm_bf16_kernel<BM, BN, kRingA, kRingB, true, uint16_t>;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  kern<<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, lds, stream>>>(
+  const int ntn = (s.h + 127) / 128;
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, s.mstart);
+  auto kern = gemm_bf16_kernel<true, uint16_t>;
+  ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
+  kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
       s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid));
   return hipGetLastError();
 }
 
-template <int BM, int BN, typename OutT>
+template <typename OutT>
 hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
-  const int64_t mt_ub = (s.max_rows + BM - 1) / BM + s.G;
-  const int ntn = static_cast<int>((s.d + BN - 1) / BN);
-  const size_t lds = sizeof(uint16_t) * (kRingA * BM + kRingB * BN) * 32;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, BM, s.mstart);
-  auto kern = gemm_bf16_kernel<BM, BN, kRingA, kRingB, false, OutT>;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  kern<<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, lds, stream>>>(
+  const int ntn = (s.d + 255) / 256;
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, s.mstart);
+  auto kern = gemm_bf16_kernel<false, OutT>;
+  ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
+  kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
       static_cast<OutT*>(s.y));
@@ -624,9 +678,8 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
 }
 
 // Groups averaging at most 64 rows stream weights through the skinny kernel;
-// large tiles once groups average at least 384 rows; otherwise 128 x 128.
+// the others run the tiled MFMA kernel.
 bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
-bool big_tiles(const SwigluArgs& s) { return s.max_rows >= static_cast<int64_t>(s.G) * 384; }
 
 }  // namespace
 
@@ -635,7 +688,7 @@ hipError_t launch_gate_up(const SwigluArgs& s, hipStream_t stream) {
   if (skinny(s))
     return skinny_bf16<true, uint16_t>(s, s.d, s.h, s.a, s.a_rows, s.a_div, s.w_gate, s.w_up,
                                        s.hid, stream);
-  return big_tiles(s) ? gate_up_bf16<256, 256>(s, stream) : gate_up_bf16<128, 128>(s, stream);
+  return gate_up_bf16(s, stream);
 }
 
 hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
@@ -647,11 +700,7 @@ hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
     return skinny_bf16<false, float>(s, s.h, s.d, s.hid, nullptr, 1, s.w_down, nullptr, s.y,
                                      stream);
   }
-  if (s.y_bf16)
-    return big_tiles(s) ? down_bf16<256, 256, uint16_t>(s, stream)
-                        : down_bf16<128, 128, uint16_t>(s, stream);
-  return big_tiles(s) ? down_bf16<256, 256, float>(s, stream)
-                      : down_bf16<128, 128, float>(s, stream);
+  return s.y_bf16 ? down_bf16<uint16_t>(s, stream) : down_bf16<float>(s, stream);
 }
 
 }  // namespace moe

@@ -8,14 +8,20 @@
 
 namespace moe {
 
+// Raises a kernel's dynamic-LDS limit to `bytes` once per (kernel, device);
+// later calls are a lock-free lookup (libmoe_api.hip).
+void ensure_dynamic_lds(const void* kernel, int bytes);
+
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 
 // route.hip
 size_t route_lds_bytes(int E, int k);
+size_t route_workspace_bytes(int64_t T, int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
                         const float* logit_bias, const float* select_bias, bool logits_in,
-                        float* logits, int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+                        float* logits, int32_t* topk_idx, float* topk_gate, void* ws,
+                        hipStream_t stream);
 
 // permute.hip
 int64_t permute_chunks(int64_t R);
@@ -40,7 +46,7 @@ struct SwigluArgs {
   void* y;
   bool y_bf16;
   void* hid;        // [max_rows, h] in the compute dtype
-  int32_t* mstart;  // workspace [G + 1]
+  int32_t* mstart;  // workspace: tile table, G + 1 entries
 };
 hipError_t launch_gate_up(const SwigluArgs& args, hipStream_t stream);
 hipError_t launch_down(const SwigluArgs& args, hipStream_t stream);

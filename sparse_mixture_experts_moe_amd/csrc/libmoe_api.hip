@@ -4,13 +4,52 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <charconv>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
 #include "kernels.hpp"
+
+namespace moe {
+
+void ensure_dynamic_lds(const void* kernel, int bytes) {
+  // (kernel, device, bytes) triples already applied; a short fixed table suffices
+  // (a handful of kernels times the visible devices)
+  struct Entry {
+    std::atomic<const void*> fn{nullptr};
+    std::atomic<int> dev{-1};
+    std::atomic<int> bytes{0};
+  };
+  static Entry table[256];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  for (auto& e : table) {
+    const void* f = e.fn.load(std::memory_order_acquire);
+    if (f == nullptr) break;
+    if (f == kernel && e.dev.load() == dev && e.bytes.load() >= bytes) return;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  for (auto& e : table) {
+    if (e.fn.load() == nullptr) {
+      e.dev.store(dev);
+      e.bytes.store(bytes);
+      e.fn.store(kernel, std::memory_order_release);
+      return;
+    }
+    if (e.fn.load() == kernel && e.dev.load() == dev) {
+      if (e.bytes.load() < bytes) e.bytes.store(bytes);
+      return;
+    }
+  }
+}
+
+}  // namespace moe
 
 namespace {
 
@@ -104,10 +143,16 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E) {
 }
 
 // ---------------------------------------------------------------------------
+size_t moe_route_workspace(int64_t T, int d, int E, int k, int dt) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || !valid_dtype(dt)) return 0;
+  if (E > moe::kMaxExperts || d % 32 != 0) return 0;
+  return moe::route_workspace_bytes(T, d, E, dt == MOE_BF16);
+}
+
 moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
                        int k, const float* logit_bias, const float* select_bias,
                        unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
-                       void* stream) {
+                       void* ws, size_t ws_bytes, void* stream) {
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   if (flags & ~MOE_ROUTE_LOGITS_IN) return fail(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
   if (T < 0) return fail(MOE_EINVAL, "moe_route: T < 0");
@@ -122,8 +167,11 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
   if (!logits || !topk_idx || !topk_gate)
     return fail(MOE_EINVAL, "moe_route: NULL output pointer");
   if (!logits_in && (!x || !w_router)) return fail(MOE_EINVAL, "moe_route: NULL x or w_router");
+  const size_t need = logits_in ? 0 : moe::route_workspace_bytes(T, d, E, dt == MOE_BF16);
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_EWORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(moe::launch_route(x, w_router, dt == MOE_BF16, T, d, E, k, logit_bias,
-                                      select_bias, logits_in, logits, topk_idx, topk_gate,
+                                      select_bias, logits_in, logits, topk_idx, topk_gate, ws,
                                       as_stream(stream)),
                     "moe_route");
 }

@@ -7,9 +7,13 @@
 // "A balance penalty"; "Zen-Max: Maximum Capability via Mixture-of-Experts
 // Architecture", section "MoE-Specific Training Stability" (z-loss).
 //
-// Deterministic: workgroup b sums a fixed 256-token block into partials[b][E]
-// (fp32, token order), then one workgroup adds the partials in block order in
-// fp64.
+// Deterministic: workgroup b owns a fixed block of 64 tokens, taken 32 at a
+// time with eight lanes per token (each lane covers an eighth of the experts;
+// max and sum-exp combine with lane shuffles); the probabilities of the 32
+// tokens are summed per expert in token order and accumulated over the two
+// rounds, giving partials[b][E].  One workgroup then adds the partials: 1024
+// threads sum fixed segments of blocks per expert in fp64, and the segments
+// are added in segment order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,61 +21,84 @@ namespace moe {
 
 namespace {
 
-constexpr int kTok = 256;
+constexpr int kTok = 64;        // tokens per partial block
+constexpr int kRound = 32;      // tokens per round
+constexpr int kLanes = 8;       // lanes per token
 
 __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits,
                                                             int64_t T, int E,
                                                             float* __restrict__ part,
                                                             float* __restrict__ zpart) {
-  __shared__ float sm[kTok], sinv[kTok], slse2[kTok];
+  extern __shared__ float sp[];  // [kRound][E] probabilities of the current round
+  __shared__ float zs[kRound];
   const int tid = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  const int ntok = static_cast<int>(T - t0 < kTok ? T - t0 : kTok);
-  if (tid < ntok) {
-    const float* row = logits + (t0 + tid) * E;
+  const int tt = tid / kLanes, q = tid % kLanes;
+  const int64_t tb0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  float acc = 0.0f;    // this thread's expert column sum (thread e < E)
+  float zacc = 0.0f;   // thread 0: sum of lse^2
+  for (int r = 0; r < kTok / kRound; ++r) {
+    const int64_t t = tb0 + r * kRound + tt;
+    const bool active = t < T;
+    const float* row = logits + (active ? t : 0) * E;
     float m = -__builtin_inff();
-    for (int e = 0; e < E; ++e) m = fmaxf(m, row[e]);
+    if (active)
+      for (int e = q; e < E; e += kLanes) m = fmaxf(m, row[e]);
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kLanes));
     float s = 0.0f;
-    for (int e = 0; e < E; ++e) s += expf(row[e] - m);
-    sm[tid] = m;
-    sinv[tid] = 1.0f / s;
-    const float lse = m + logf(s);
-    slse2[tid] = lse * lse;
+    if (active)
+      for (int e = q; e < E; e += kLanes) s += expf(row[e] - m);
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) s += __shfl_xor(s, o, kLanes);
+    const float inv = 1.0f / s;
+    for (int e = q; e < E; e += kLanes) sp[tt * E + e] = active ? expf(row[e] - m) * inv : 0.0f;
+    if (q == 0) {
+      const float lse = m + logf(s);
+      zs[tt] = active ? lse * lse : 0.0f;
+    }
+    __syncthreads();
+    if (tid < E)
+      for (int u = 0; u < kRound; ++u) acc += sp[u * E + tid];
+    if (tid == 0)
+      for (int u = 0; u < kRound; ++u) zacc += zs[u];
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    float acc = 0.0f;
-    for (int t = 0; t < ntok; ++t) acc += expf(logits[(t0 + t) * E + e] - sm[t]) * sinv[t];
-    part[static_cast<int64_t>(blockIdx.x) * E + e] = acc;
-  }
-  if (tid == 0) {
-    float z = 0.0f;
-    for (int t = 0; t < ntok; ++t) z += slse2[t];
-    zpart[blockIdx.x] = z;
-  }
+  if (tid < E) part[static_cast<int64_t>(blockIdx.x) * E + tid] = acc;
+  if (tid == 0) zpart[blockIdx.x] = zacc;
 }
 
-__global__ __launch_bounds__(256) void stats_final_kernel(const float* __restrict__ part,
-                                                          const float* __restrict__ zpart,
-                                                          int nblk, const int32_t* __restrict__ count,
-                                                          int64_t T, int E, int k, float alpha,
-                                                          float* __restrict__ f,
-                                                          float* __restrict__ P,
-                                                          float* __restrict__ loss,
-                                                          float* __restrict__ zloss) {
+__global__ __launch_bounds__(1024) void stats_final_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ zpart,
+                                                           int nblk, const int32_t* __restrict__ count,
+                                                           int64_t T, int E, int k, float alpha,
+                                                           float* __restrict__ f,
+                                                           float* __restrict__ P,
+                                                           float* __restrict__ loss,
+                                                           float* __restrict__ zloss) {
+  __shared__ double seg[1024];
   __shared__ double fp[256];
   const int tid = threadIdx.x;
+  const int nseg = 1024 / E;  // segments per expert (E <= 256 -> >= 4)
+  const int e = tid % E, sgi = tid / E;
+  double acc = 0.0;
+  if (sgi < nseg) {
+    const int b0 = static_cast<int>(static_cast<int64_t>(nblk) * sgi / nseg);
+    const int b1 = static_cast<int>(static_cast<int64_t>(nblk) * (sgi + 1) / nseg);
+    for (int b = b0; b < b1; ++b) acc += part[static_cast<int64_t>(b) * E + e];
+  }
+  seg[tid] = acc;
+  __syncthreads();
   double term = 0.0;
   if (tid < E) {
-    double acc = 0.0;
-    for (int b = 0; b < nblk; ++b) acc += part[static_cast<int64_t>(b) * E + tid];
-    const double pe = acc / static_cast<double>(T);
+    double tot = 0.0;
+    for (int u = 0; u < nseg; ++u) tot += seg[u * E + tid];
+    const double pe = tot / static_cast<double>(T);
     const double fe = static_cast<double>(count[tid]) / (static_cast<double>(T) * k);
     P[tid] = static_cast<float>(pe);
     f[tid] = static_cast<float>(fe);
     term = fe * pe;
   }
-  fp[tid] = term;
+  if (tid < 256) fp[tid] = term;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if (tid < s) fp[tid] += fp[tid + s];
@@ -95,9 +122,10 @@ hipError_t launch_balance_stats(const float* logits, const int32_t* count, int64
                                 float alpha, float* f, float* P, float* loss, float* zloss,
                                 float* part, float* zpart, hipStream_t stream) {
   const int64_t nblk = stats_blocks(T);
-  stats_partial_kernel<<<static_cast<unsigned>(nblk), 256, 0, stream>>>(logits, T, E, part, zpart);
-  stats_final_kernel<<<1, 256, 0, stream>>>(part, zpart, static_cast<int>(nblk), count, T, E, k,
-                                            alpha, f, P, loss, zloss);
+  const size_t lds = sizeof(float) * kRound * E;
+  stats_partial_kernel<<<static_cast<unsigned>(nblk), 256, lds, stream>>>(logits, T, E, part, zpart);
+  stats_final_kernel<<<1, 1024, 0, stream>>>(part, zpart, static_cast<int>(nblk), count, T, E, k,
+                                             alpha, f, P, loss, zloss);
   return hipGetLastError();
 }
 

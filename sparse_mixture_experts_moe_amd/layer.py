@@ -53,6 +53,8 @@ class MoELayer:
             logits=torch.empty((T, E), dtype=torch.float32, device=dev),
             topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
             topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+            route_ws=torch.empty(max(1, _lib.moe_route_workspace(T, d, E, k, dt)),
+                                 dtype=torch.uint8, device=dev),
             expert_count=torch.empty(E, dtype=torch.int32, device=dev),
             expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
             pair_row=torch.empty(R, dtype=torch.int32, device=dev),
@@ -93,7 +95,7 @@ class MoELayer:
         mark = mark or (lambda name: None)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
-                       stream=stream)
+                       ws=b["route_ws"], stream=stream)
         mark("route")
         _lib.moe_permute(b["topk_idx"], E, self.capacity,
                          x if self.gather == "copy" else None,

@@ -77,24 +77,31 @@ def _err():
 
 
 def test_route_rejects():
-    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 8, 9, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 8, 9, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EINVAL and "k <= E" in _err()
-    s = C.moe_route(None, FAKE, L.MOE_BF16, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(None, FAKE, L.MOE_BF16, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EINVAL
-    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 300, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 128, 300, 2, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EUNSUPPORTED
-    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 100, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 100, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EUNSUPPORTED and "d % 32" in _err()
-    s = C.moe_route(FAKE, FAKE, 7, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, 7, 64, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EINVAL
-    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 64, 33, None, None, 0, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 64, 33, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EUNSUPPORTED
-    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None, 4, FAKE, FAKE, FAKE, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None, 4, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EINVAL and "flags" in _err()
     # T = 0 is a no-op that enqueues nothing
     assert C.moe_route(FAKE, FAKE, L.MOE_F32, 0, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE,
-                       None) == L.MOE_OK
+                       None, 0, None) == L.MOE_OK
     assert _err() == ""
+    # a small bf16 batch splits the reduction over d and needs a workspace
+    need = L.moe_route_workspace(64, 6144, 128, 8, L.MOE_BF16)
+    assert need > 0
+    s = C.moe_route(FAKE, FAKE, L.MOE_BF16, 64, 6144, 128, 8, None, None, 0, FAKE, FAKE, FAKE,
+                    FAKE, need - 1, None)
+    assert s == L.MOE_EWORKSPACE
+    assert L.moe_route_workspace(64, 6144, 128, 8, L.MOE_F32) == 0
 
 
 def test_permute_rejects():
