@@ -192,7 +192,9 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
  * group_offset[0] == 0 and group_offset[G] <= max_rows (host bound).
  * a_rows [max_rows] int32 or NULL; a_rows_div >= 1.
  * y [max_rows, d] in dtype y_dt (rows past group_offset[G] untouched).
- * Limits: bf16 needs d % 64 == 0 and h % 64 == 0.
+ * Limits: bf16 needs d % 64 == 0, h % 64 == 0 and 2 d h < 2^32 (one
+ * expert's weight matrix addressed with 32-bit offsets), else
+ * MOE_EUNSUPPORTED.
  * Workspace: moe_expert_swiglu_workspace(max_rows, d, h, G, dt) bytes.
  */
 size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt);

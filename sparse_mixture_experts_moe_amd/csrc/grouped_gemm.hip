@@ -15,10 +15,12 @@
 //   m-tile of each group runs as a 64-, 128- or 256-row tile according to the
 //   rows left, so a short remainder costs a quarter or a half of a full tile.
 //   Four waves form a 2 x 2 (256 rows) or 1 x 4 (64 and 128 rows) grid of
-//   v_mfma_f32_32x32x16_bf16 tiles.  K advances in slices of 32 that the
-//   direct-to-LDS load streams through two rings of LDS stages (see
-//   gemm_tile); fragment reads are double-buffered in registers and
-//   interleaved one-for-one with the MFMAs.
+//   v_mfma_f32_32x32x16_bf16 tiles.  K advances in slices of 64 (one
+//   128-byte line per row) that direct-to-LDS copies stream through a
+//   two-stage A ring and a three-stage B ring (160 KB); the copies are spread
+//   over the whole slice, since a compute unit accepts one about every 16
+//   cycles.  Fragment reads are double-buffered in registers and interleaved
+//   one-for-one with the MFMAs (see gemm_tile).
 //   Tiles are ordered group-major, n-tile next, m-tile fastest, and laid out
 //   in contiguous runs per XCD so that tiles sharing a weight panel or an
 //   activation panel run together on one XCD's L2.
@@ -119,8 +121,8 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
 constexpr int kTileM = 256;
 // LDS ring depths: activations mostly hit in L2, weight slices are first
 // touches from HBM and get the deeper ring (3 x 16 KB + 6 x 16 KB).
-constexpr int kRingA = 3;
-constexpr int kRingB = 6;
+constexpr int kRingA = 2;
+constexpr int kRingB = 3;
 
 struct Tile2 {
   int g, m0, row_end, n0, cls;  // cls 0: 256 rows, 1: 128 rows, 2: 64 rows
@@ -140,12 +142,7 @@ __device__ __forceinline__ bool decode_tile2(const int32_t* __restrict__ off,
   return true;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-
-__device__ __forceinline__ void load_lds16(const uint16_t* g, uint16_t* l) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), (lds_ptr_t)(l), 16, 0, 0);
-}
 
 // s_waitcnt with only the vector-memory counter constrained to <= n (n < 64)
 template <int n>
@@ -154,8 +151,41 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00);
 }
 
-__device__ __forceinline__ int swz32(int row, int chunk) {  // element offset, 32-wide rows
-  return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+// The direct-to-LDS copy of 16 bytes per lane written as an instruction the
+// compiler does not model: it then adds no waits of its own around the copies
+// and does not keep LDS reads ordered after them, which leaves both to the
+// kernel (every wait on a copy is the explicit vmcnt wait before a barrier).
+// M0 holds the wave's LDS destination; one wait state separates its write
+// from the copy.
+__device__ __forceinline__ void dma_lds16(const uint16_t* g, const uint16_t* l) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint16_t*)l));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0)
+               : "m0");
+}
+
+// The same copy from a workgroup-uniform base `sbase` plus a 32-bit per-lane
+// byte offset.
+__device__ __forceinline__ void dma_lds16_s(const uint16_t* sbase, uint32_t voff,
+                                            const uint16_t* l) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<size_t>((const __attribute__((address_space(3))) uint16_t*)l));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(m0)
+               : "m0");
+}
+
+// K slice per stage: 64 bf16, one 128-byte line of every row.  A compute
+// unit's L2-to-LDS rate is bounded by its requests, one per row segment, so
+// full-line rows move twice the bytes of half-line rows per request.
+constexpr int kBK = 64;
+
+// Element offset of 16-byte chunk `chunk` (0..7) of row `row` in a stage of
+// 64-element rows.  The XOR with (row >> 1) & 7 puts the same chunk of 16
+// consecutive rows on 16 distinct 16-byte bank groups, so that the 16 lanes
+// served together by a 128-bit LDS read never collide.
+__device__ __forceinline__ int swz64(int row, int chunk) {
+  return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
@@ -167,27 +197,30 @@ __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const Tile2& tile, uint16_t* smem, OutT* __restrict__ C) {
   static_assert(WM * WN == 4, "four waves");
-  constexpr int BKs = 32;                     // K per stage
   constexpr int MT = BM / WM / 32;            // 32-row MFMA tiles per wave
   constexpr int NT = BN / WN / 32;            // 32-col MFMA tiles per wave
-  constexpr int AP = BM / 64;                 // DMA instructions per thread per stage (A)
-  constexpr int BP = BN / 64;                 // (B)
+  constexpr int AP = BM / 32;                 // copies per wave per stage (A): 8 rows each
+  constexpr int BP = BN / 32;                 // (B)
   constexpr int P = AP + BP;
   static_assert(!kFused || NT % 2 == 0, "fused tile needs matching gate/up halves");
 
-  uint16_t* As = smem;                         // [SA][kTileM * 32]
-  uint16_t* Bs = smem + SA * kTileM * BKs;     // [SB][BN * 32]
+  uint16_t* As = smem;                         // [SA][kTileM * kBK]
+  uint16_t* Bs = smem + SA * kTileM * kBK;     // [SB][BN * kBK]
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = WM == 1 ? 0 : (wave & 1), wn = WM == 1 ? wave : (wave >> 1);
-  const int drow = 16 * wave + (lane >> 2);              // tile row of DMA instruction 0
-  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);     // global chunk this lane fetches
+  // Copy j of a wave covers the 8 tile rows 8 (4 j + wave) + 0..7: lane l
+  // lands in row l / 8, chunk slot l % 8 of that 1 KB block and fetches the
+  // global chunk that the swizzle stores there.  ((row >> 1) & 7 of those
+  // rows depends only on the wave's parity and l / 16.)
+  const int lrow = lane >> 3;
+  const int gchunk = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
 
   int src[AP];
 #pragma unroll
   for (int j = 0; j < AP; ++j) {
-    const int r = tile.m0 + drow + 64 * j;
+    const int r = tile.m0 + 8 * (4 * j + wave) + lrow;
     src[j] = r < tile.row_end ? r : tile.row_end - 1;  // rows past the group: valid row, unused
   }
   if (a_rows) {  // gather: all index loads first, then the divisions
@@ -199,37 +232,28 @@ __device__ __forceinline__ void gemm_tile(
   const uint16_t* ap[AP];
 #pragma unroll
   for (int j = 0; j < AP; ++j) ap[j] = A + static_cast<int64_t>(src[j]) * K + gchunk * 8;
-  const uint16_t* bp[BP];
+  // B copies: the expert's weight slab (gate rows for j < BP/2 of a fused
+  // tile, up rows after) is uniform, the row offset within it per lane
+  uint32_t boff[BP];
 #pragma unroll
   for (int j = 0; j < BP; ++j) {
-    const int r = drow + 64 * j;
-    const uint16_t* base = B0;
-    int n = tile.n0 + r;
-    if (kFused && r >= BN / 2) {
-      base = B1;
-      n = tile.n0 + r - BN / 2;
-    }
+    const int r = 8 * (4 * j + wave) + lrow;
+    int n = tile.n0 + ((kFused && r >= BN / 2) ? r - BN / 2 : r);
     n = n < N ? n : N - 1;
-    bp[j] = base + tile.g * b_stride + static_cast<int64_t>(n) * K + gchunk * 8;
+    boff[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K * 2) + gchunk * 16;
   }
+  const uint16_t* bslab0 = B0 + tile.g * b_stride;
+  const uint16_t* bslab1 = (kFused ? B1 : B0) + tile.g * b_stride;
 
-  const int nk = K / BKs;
+  const int nk = K / kBK;
   // copy K slice `ks` (clamped into range: surplus copies reload the last slice
   // into a stage nobody reads again, which keeps the loop branch-free)
-#define MOE_ISSUE_A(stage, ks)                                                       \
-  do {                                                                               \
-    const int k0_ = ((ks) < nk ? (ks) : nk - 1) * BKs;                               \
-    uint16_t* as_ = As + (stage) * kTileM * BKs + 16 * wave_u * BKs;                 \
-    _Pragma("unroll") for (int j = 0; j < AP; ++j)                                   \
-        load_lds16(ap[j] + k0_, as_ + 64 * j * BKs);                                 \
-  } while (0)
-#define MOE_ISSUE_B(stage, ks)                                                       \
-  do {                                                                               \
-    const int k0_ = ((ks) < nk ? (ks) : nk - 1) * BKs;                               \
-    uint16_t* bs_ = Bs + (stage) * BN * BKs + 16 * wave_u * BKs;                     \
-    _Pragma("unroll") for (int j = 0; j < BP; ++j)                                   \
-        load_lds16(bp[j] + k0_, bs_ + 64 * j * BKs);                                 \
-  } while (0)
+#define MOE_COPY_A(j, stage, ks)                                                     \
+  dma_lds16(ap[(j)] + ((ks) < nk ? (ks) : nk - 1) * kBK,                             \
+            As + (stage) * kTileM * kBK + 8 * (4 * (j) + wave_u) * kBK)
+#define MOE_COPY_B(j, stage, ks)                                                     \
+  dma_lds16_s(((kFused && (j) >= BP / 2) ? bslab1 : bslab0) + ((ks) < nk ? (ks) : nk - 1) * kBK, \
+              boff[(j)], Bs + (stage) * BN * kBK + 8 * (4 * (j) + wave_u) * kBK)
 
   f32x16 acc[MT][NT];
 #pragma unroll
@@ -237,93 +261,106 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-  int arow[MT], brow[NT];
+  // LDS element offsets of this lane's fragments for k step 0; step s is the
+  // same offset XOR (s << 4), as the swizzle flips only chunk bits
+  int aoff[MT], boffl[NT];
+  const int khalf = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) arow[i] = wm * (BM / WM) + i * 32 + (lane & 31);
+  for (int i = 0; i < MT; ++i) aoff[i] = swz64(wm * (BM / WM) + i * 32 + (lane & 31), khalf);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
+    int row;
     if (kFused) {
-      brow[j] = (j < NT / 2) ? wn * (BN / (2 * WN)) + j * 32
-                             : BN / 2 + wn * (BN / (2 * WN)) + (j - NT / 2) * 32;
+      row = (j < NT / 2) ? wn * (BN / (2 * WN)) + j * 32
+                         : BN / 2 + wn * (BN / (2 * WN)) + (j - NT / 2) * 32;
     } else {
-      brow[j] = wn * (BN / WN) + j * 32;
+      row = wn * (BN / WN) + j * 32;
     }
-    brow[j] += lane & 31;
+    boffl[j] = swz64(row + (lane & 31), khalf);
   }
-  const int khalf = lane >> 5;
 
-#define MOE_READ(F, sa, sb, step)                                                    \
+  // read r < MT is A fragment r, else B fragment r - MT, of k step `step`
+#define MOE_READ1(F, sa, sb, step, r)                                                \
   do {                                                                               \
-    const uint16_t* as_ = As + (sa) * kTileM * BKs;                                  \
-    const uint16_t* bs_ = Bs + (sb) * BN * BKs;                                      \
-    _Pragma("unroll") for (int i = 0; i < MT; ++i)                                   \
-        F##a[i] = *reinterpret_cast<const bf16x8*>(as_ + swz32(arow[i], (step) * 2 + khalf)); \
-    _Pragma("unroll") for (int j = 0; j < NT; ++j)                                   \
-        F##b[j] = *reinterpret_cast<const bf16x8*>(bs_ + swz32(brow[j], (step) * 2 + khalf)); \
+    if ((r) < MT) {                                                                  \
+      const int i_ = (r) < MT ? (r) : 0;                                             \
+      F##a[i_] = *reinterpret_cast<const bf16x8*>(As + (sa) * kTileM * kBK +         \
+                                                  (aoff[i_] ^ ((step) << 4)));       \
+    } else {                                                                         \
+      const int j_ = (r) >= MT ? (r) - MT : 0;                                       \
+      F##b[j_] = *reinterpret_cast<const bf16x8*>(Bs + (sb) * BN * kBK +             \
+                                                  (boffl[j_] ^ ((step) << 4)));      \
+    }                                                                                \
   } while (0)
-#define MOE_MFMA(F)                                                                  \
-  _Pragma("unroll") for (int i = 0; i < MT; ++i)                                     \
-  _Pragma("unroll") for (int j = 0; j < NT; ++j)                                     \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F##a[i], F##b[j], acc[i][j], 0, 0, 0)
+#define MOE_MFMA1(F, t)                                                              \
+  acc[(t) / NT][(t) % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                 \
+      F##a[(t) / NT], F##b[(t) % NT], acc[(t) / NT][(t) % NT], 0, 0, 0)
 
   bf16x8 f0a[MT], f0b[NT], f1a[MT], f1b[NT];
-  constexpr int kPairs = MT + NT;                 // (MFMA, LDS read) pairs per half slice
-  constexpr int kRest = MT * NT - kPairs;         // MFMAs left after the pairs
-  constexpr int kPerG = kRest / P;                // MFMAs between DMA issues
-  static_assert(SB >= SA && SA >= 2, "B ring at least as deep as the A ring");
-  // Virtual iteration v issues A slice v+SA and B slice v+SB; the prologue runs
-  // v = -SB .. -1 (A only from v = -SA).  Loads complete in issue order, so
-  // "A slice kt+1 (and the older B slice kt+1) landed" means at most the loads
-  // of iterations kt+2-SA .. kt-1 are still outstanding.
-#pragma unroll
-  for (int v = -SB; v < 0; ++v) {
-    if (v + SA >= 0) MOE_ISSUE_A(v + SA, v + SA);
-    MOE_ISSUE_B(v + SB, v + SB);
+  constexpr int kSlots = MT * NT;                 // MFMAs per k step
+  constexpr int kReads = MT + NT;                 // LDS reads per k step
+  static_assert(kReads <= kSlots, "one read per MFMA slot at most");
+  static_assert(SA == 2 && SB == 3, "copy placement below assumes rings of 2 (A) and 3 (B)");
+  // A compute unit takes a copy instruction about every 16 cycles, so the
+  // copies are spread over the whole slice: B slice kt+2 during the three k
+  // steps before the barrier of iteration kt (into the stage of slice kt-1,
+  // retired by the previous barrier), A slice kt+2 during the step after it
+  // (into the stage of slice kt).  Slot t of a k step issues MFMA t, then
+  // read t (t < kReads) of the next step's fragments, then its copies.
+#define MOE_STEP(FU, FL, sa_, sb_, step_, MODE, PART, stage_, ks_)                     \
+  _Pragma("unroll") for (int t = 0; t < kSlots; ++t) {                               \
+    MOE_MFMA1(FU, t);                                                                \
+    if (t < kReads) MOE_READ1(FL, sa_, sb_, step_, t);                               \
+    if (MODE == 1) {                                                                 \
+      _Pragma("unroll") for (int c = 0; c < BP; ++c)                                 \
+        if (c * 3 * kSlots / BP == (PART) * kSlots + t) MOE_COPY_B(c, stage_, ks_);  \
+    } else if (MODE == 2) {                                                          \
+      _Pragma("unroll") for (int c = 0; c < AP; ++c)                                 \
+        if (c * kSlots / AP == t) MOE_COPY_A(c, stage_, ks_);                        \
+    }                                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                               \
   }
-  wait_vm<(SA - 1) * P>();
+
+  // Virtual iteration v issues B slice v+2 and then A slice v+2; the prologue
+  // runs v = -2, -1.  Loads of a wave complete in issue order: when A slice
+  // kt+1 (issued in iteration kt-1) has landed, only B slice kt+2 (issued
+  // before the barrier of iteration kt) may still be in flight, and B slice
+  // kt+1 (issued before A slice kt+1) has landed.
+#pragma unroll
+  for (int v = -2; v < 0; ++v) {
+#pragma unroll
+    for (int j = 0; j < BP; ++j) MOE_COPY_B(j, v + 2, v + 2);
+#pragma unroll
+    for (int j = 0; j < AP; ++j) MOE_COPY_A(j, v + 2, v + 2);
+  }
+  wait_vm<P>();
   __syncthreads();
   int sa = 0, sb = 0;  // stages of slice kt
-  MOE_READ(f0, 0, 0, 0);
+  int sbn = 2;         // B stage of slice kt+2
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) MOE_READ1(f0, 0, 0, 0, r);
   for (int kt = 0; kt < nk; ++kt) {
     const int sa1 = sa + 1 == SA ? 0 : sa + 1, sb1 = sb + 1 == SB ? 0 : sb + 1;
     __builtin_amdgcn_sched_barrier(0);
-    MOE_READ(f1, sa, sb, 1);
-    MOE_MFMA(f0);
-#pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(SA - 2) * P>();
+    MOE_STEP(f0, f1, sa, sb, 1, 1, 0, sbn, kt + 2)
+    MOE_STEP(f1, f0, sa, sb, 2, 1, 1, sbn, kt + 2)
+    MOE_STEP(f0, f1, sa, sb, 3, 1, 2, sbn, kt + 2)
+    // every wave has read slice kt (the compiler's LDS wait precedes the
+    // barrier); slice kt+1 has landed once this wave's A copies of it have
+    wait_vm<BP>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_READ(f0, sa1, sb1, 0);
-    MOE_ISSUE_A(sa, kt + SA);
-    MOE_ISSUE_B(sb, kt + SB);
-    MOE_MFMA(f1);
-#pragma unroll
-    for (int q = 0; q < kPairs; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (kPerG > 0) __builtin_amdgcn_sched_group_barrier(0x008, kPerG, 0);
-    }
-    if (kRest - kPerG * P > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest - kPerG * P, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    MOE_STEP(f1, f0, sa1, sb1, 0, 2, 0, sa, kt + 2)
+    sbn = sb;
     sa = sa1;
     sb = sb1;
   }
   wait_vm<0>();
-#undef MOE_ISSUE_A
-#undef MOE_ISSUE_B
-#undef MOE_READ
-#undef MOE_MFMA
-
+#undef MOE_COPY_A
+#undef MOE_COPY_B
+#undef MOE_READ1
+#undef MOE_MFMA1
+#undef MOE_STEP
   // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
   const int rbase = tile.m0 + wm * (BM / WM) + (lane >> 5) * 4;
   if constexpr (kFused) {
@@ -602,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-constexpr size_t kGemmLds = sizeof(uint16_t) * (kRingA * kTileM + kRingB * 256) * 32;
+constexpr size_t kGemmLds = sizeof(uint16_t) * (kRingA * kTileM + kRingB * 256) * kBK;
 
 // grid: sum over groups of ceil(rows / 256) <= ceil(max_rows / 256) + G m-tiles
 unsigned gemm_grid(const SwigluArgs& s, int ntn) {

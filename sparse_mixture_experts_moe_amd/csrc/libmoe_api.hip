@@ -226,6 +226,8 @@ moe_status_t check_experts(const char* fn, int dt, int d, int h, int G, int64_t 
   if (!group_offset) return fail(MOE_EINVAL, "%s: NULL group_offset", fn);
   if (dt == MOE_BF16 && (d % 64 != 0 || h % 64 != 0))
     return fail(MOE_EUNSUPPORTED, "%s: bf16 needs d %% 64 == 0 and h %% 64 == 0", fn);
+  if (dt == MOE_BF16 && static_cast<int64_t>(d) * h * 2 > static_cast<int64_t>(UINT32_MAX))
+    return fail(MOE_EUNSUPPORTED, "%s: bf16 expert weight matrix over 4 GiB", fn);
   if (max_rows > INT32_MAX || static_cast<int64_t>(G) * (max_rows + 1) > INT32_MAX)
     return fail(MOE_EUNSUPPORTED, "%s: too many rows", fn);
   return MOE_OK;

@@ -134,6 +134,10 @@ def test_expert_swiglu_rejects():
     assert call(nws=ws - 1) == L.MOE_EWORKSPACE
     assert call(d=100) == L.MOE_EUNSUPPORTED
     assert call(h=96) == L.MOE_EUNSUPPORTED
+    # one expert's bf16 weight matrix must fit 32-bit byte offsets
+    assert call(d=65536, h=32768, nws=L.moe_expert_swiglu_workspace(1000, 65536, 32768, 8,
+                                                                    L.MOE_BF16)) == L.MOE_EUNSUPPORTED
+    assert "4 GiB" in _err()
     assert call(wd=None) == L.MOE_EINVAL
     assert call(rows=FAKE, div=0) == L.MOE_EINVAL
     assert call(G=0) == L.MOE_EINVAL
