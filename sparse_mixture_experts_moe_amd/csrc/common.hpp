@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 8 raw bytes
 
 constexpr int kWave = 64;
 
@@ -24,16 +25,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two floats -> packed bfloat16 pair (low half = a), round to nearest even.
+// Two floats -> packed bfloat16 pair (low half = a), round to nearest even
+// (one v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(a)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
+// z * sigmoid(z) = z * rcp(1 + exp(-z)), with the hardware reciprocal (about
+// one ulp); for very negative z, exp(-z) overflows to inf and the result is
+// the correct limit -0.
 __device__ __forceinline__ float silu_f32(float z) {
-  // z * sigmoid(z); for very negative z, exp(-z) overflows to inf and the
-  // quotient is the correct limit -0.
-  return z / (1.0f + __expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

@@ -292,9 +292,12 @@ __device__ __forceinline__ void gemm_tile(
                                                   (boffl[j_] ^ ((step) << 4)));      \
     }                                                                                \
   } while (0)
+// acc[i][j] accumulates the transposed product of m-block i and n-block j
+// (the weight fragment is the MFMA's first operand), so that a lane ends up
+// holding one row of C and runs of four consecutive columns
 #define MOE_MFMA1(F, t)                                                              \
   acc[(t) / NT][(t) % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                 \
-      F##a[(t) / NT], F##b[(t) % NT], acc[(t) / NT][(t) % NT], 0, 0, 0)
+      F##b[(t) % NT], F##a[(t) / NT], acc[(t) / NT][(t) % NT], 0, 0, 0)
 
   bf16x8 f0a[MT], f0b[NT], f1a[MT], f1b[NT];
   constexpr int kSlots = MT * NT;                 // MFMAs per k step
@@ -361,43 +364,51 @@ __device__ __forceinline__ void gemm_tile(
 #undef MOE_READ1
 #undef MOE_MFMA1
 #undef MOE_STEP
-  // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
-  const int rbase = tile.m0 + wm * (BM / WM) + (lane >> 5) * 4;
-  if constexpr (kFused) {
+  // epilogue: acc[i][j] element 4q + e of lane l is C[row, col] with row =
+  // m-block i row (l & 31) and col = n-block j column 8q + 4 (l >> 5) + e, so
+  // every lane stores runs of four columns (N % 64 == 0 keeps a run whole)
+  const int row0 = tile.m0 + wm * (BM / WM) + (lane & 31);
+  const int cq = 4 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < NT / 2; ++j) {
-      const int col = tile.n0 + wn * (BN / (2 * WN)) + j * 32 + (lane & 31);
-      if (col >= N) continue;
+  for (int i = 0; i < MT; ++i) {
+    const int row = row0 + i * 32;
+    if (row >= tile.row_end) continue;
+    OutT* crow = C + static_cast<int64_t>(row) * N;
+    if constexpr (kFused) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int j = 0; j < NT / 2; ++j) {
+        const int cb = tile.n0 + wn * (BN / (2 * WN)) + j * 32 + cq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (row < tile.row_end) {
-            const float v = silu_f32(acc[i][j][r]) * acc[i][j + NT / 2][r];
-            C[static_cast<int64_t>(row) * N + col] = static_cast<OutT>(f32_to_bf16_bits(v));
+        for (int q = 0; q < 4; ++q) {
+          const int col = cb + 8 * q;
+          if (col >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = silu_f32(acc[i][j][4 * q + e]) * acc[i][j + NT / 2][4 * q + e];
+          u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(crow + col) = pk;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int cb = tile.n0 + wn * (BN / WN) + j * 32 + cq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = cb + 8 * q;
+          if (col >= N) continue;
+          if constexpr (sizeof(OutT) == 2) {
+            u32x2 pk = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            *reinterpret_cast<u32x2*>(crow + col) = pk;
+          } else {
+            f32x4 o = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                       acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(crow + col) = o;
           }
         }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int col = tile.n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-      if (col >= N) continue;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (row < tile.row_end) {
-            const float v = acc[i][j][r];
-            if constexpr (sizeof(OutT) == 2) {
-              C[static_cast<int64_t>(row) * N + col] = f32_to_bf16_bits(v);
-            } else {
-              C[static_cast<int64_t>(row) * N + col] = v;
-            }
-          }
-        }
+      }
     }
   }
 }
