@@ -213,8 +213,15 @@ moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
  *   group_offset[G] untouched).
  * moe_expert_down:    y[r, :] = hid[r, :] . w_down[g]^T; y [max_rows, d] in
  *   y_dt.
- * Workspace of each: moe_expert_group_workspace(G) bytes (a tile table). */
+ * Workspace: moe_expert_group_workspace(G) bytes for moe_expert_gate_up (a
+ * tile table); moe_expert_down_workspace(G) bytes for moe_expert_down (the
+ * tile table and 64 MiB of fp32 partial tiles: when the last round of output
+ * tiles would leave compute units idle, those tiles are split along K and
+ * their parts added in a fixed order afterwards, so results stay
+ * deterministic).  The workspace contents need no initialisation and are
+ * dead after the call. */
 size_t moe_expert_group_workspace(int G);
+size_t moe_expert_down_workspace(int G);
 moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
                                 const int32_t* group_offset, int64_t max_rows,
                                 const int32_t* a_rows, int a_rows_div, const void* w_gate,

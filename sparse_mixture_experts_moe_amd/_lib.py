@@ -55,6 +55,7 @@ _SIGS = {
     "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
                                _sz, _p]),
     "moe_expert_group_workspace": (_sz, [_i]),
+    "moe_expert_down_workspace": (_sz, [_i]),
     "moe_expert_gate_up": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_down": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _p, _i, _p, _sz, _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i64, _i, _i, _p, _p, _i, _p]),
@@ -211,6 +212,10 @@ def moe_expert_group_workspace(G) -> int:
     return _L.moe_expert_group_workspace(G)
 
 
+def moe_expert_down_workspace(G) -> int:
+    return _L.moe_expert_down_workspace(G)
+
+
 def moe_expert_gate_up(a, group_offset, max_rows, w_gate, w_up, *, a_rows=None, a_rows_div=1,
                        hid=None, ws=None, stream=None):
     """hid[r] = SiLU(a_r W_gate[g]^T) * (a_r W_up[g]^T) for the rows of each group."""
@@ -235,7 +240,7 @@ def moe_expert_down(hid, group_offset, max_rows, w_down, *, y=None, y_dtype=None
     if y is None:
         y = torch.empty((max_rows, d), dtype=y_dtype or hid.dtype, device=dev)
     if ws is None:
-        ws = torch.empty(moe_expert_group_workspace(G), dtype=torch.uint8, device=dev)
+        ws = torch.empty(moe_expert_down_workspace(G), dtype=torch.uint8, device=dev)
     _contig(hid, group_offset, w_down, y, ws)
     _check(_L.moe_expert_down(_ptr(hid), _dt(hid), d, h, G, _ptr(group_offset), max_rows,
                               _ptr(w_down), _ptr(y), _dt(y), _ptr(ws), ws.numel(),

@@ -70,16 +70,14 @@ struct Tile {
   int g, m0, row_end, n0;
 };
 
-// Logical tile of this workgroup, or false if it has none.
-__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
-                                            const int32_t* __restrict__ mstart, int G, int ntn,
-                                            int BM, int ncol, Tile& tile) {
-  const int total = mstart[G] * ntn;
-  const int nw8 = (total + 7) & ~7;
-  const int bid = blockIdx.x;
-  if (bid >= nw8) return false;
-  const int L = (bid & 7) * (nw8 >> 3) + (bid >> 3);  // contiguous runs per XCD
-  if (L >= total) return false;
+// Workgroup b of a run of n8 (a multiple of 8) runs on XCD b mod 8; this
+// gives each XCD a contiguous run of logical indices.
+__device__ __forceinline__ int xcd_run(int b, int n8) { return (b & 7) * (n8 >> 3) + (b >> 3); }
+
+// Logical tile L: group-major, n-tile next, m-tile fastest.
+__device__ __forceinline__ Tile tile_at(int L, const int32_t* __restrict__ off,
+                                        const int32_t* __restrict__ mstart, int G, int ntn,
+                                        int BM, int ncol) {
   int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -89,10 +87,25 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
   const int mtg = mstart[g + 1] - mstart[g];
   const int local = L - mstart[g] * ntn;
   const int nt = local / mtg, mt = local - nt * mtg;
+  Tile tile;
   tile.g = g;
   tile.m0 = off[g] + mt * BM;
   tile.row_end = off[g + 1];
   tile.n0 = nt * ncol;
+  return tile;
+}
+
+// Logical tile of this workgroup, or false if it has none.
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
+                                            const int32_t* __restrict__ mstart, int G, int ntn,
+                                            int BM, int ncol, Tile& tile) {
+  const int total = mstart[G] * ntn;
+  const int nw8 = (total + 7) & ~7;
+  const int bid = blockIdx.x;
+  if (bid >= nw8) return false;
+  const int L = xcd_run(bid, nw8);
+  if (L >= total) return false;
+  tile = tile_at(L, off, mstart, G, ntn, BM, ncol);
   return true;
 }
 
@@ -128,21 +141,46 @@ struct Tile2 {
   int g, m0, row_end, n0, cls;  // cls 0: 256 rows, 1: 128 rows, 2: 64 rows
 };
 
-__device__ __forceinline__ bool decode_tile2(const int32_t* __restrict__ off,
-                                             const int32_t* __restrict__ mstart, int G, int ntn,
-                                             int ncol, Tile2& tile) {
-  Tile t;
-  if (!decode_tile(off, mstart, G, ntn, kTileM, ncol, t)) return false;
+__device__ __forceinline__ Tile2 classify(const Tile& t) {
+  Tile2 tile;
   tile.g = t.g;
   tile.m0 = t.m0;
   tile.row_end = t.row_end;
   tile.n0 = t.n0;
   const int rem = t.row_end - t.m0;
   tile.cls = rem <= 64 ? 2 : (rem <= 128 ? 1 : 0);
-  return true;
+  return tile;
 }
 
+// ---------------------------------------------------------------------------
+// Split-K of the last tiles.  With a long K (the down projection) one tile
+// runs long enough that a final partial round of tiles leaves most compute
+// units idle.  The last n_sk = total mod ncu tiles (in tile order) are cut
+// along K into S parts (2 <= S <= kSkMaxSplit, n_sk S <= kSkUnits, at least
+// kSkMinSlices slices per part), which the grid runs after the whole tiles;
+// part p of split tile i writes the fp32 partial sums of its 256 x 256 tile
+// to workspace unit i S + p, and sk_reduce_kernel adds the parts in part
+// order (a fixed order: results are deterministic) and writes the output.
+// ---------------------------------------------------------------------------
+constexpr int kSkUnits = 256;        // partial tiles the workspace holds
+constexpr int kSkMaxSplit = 4;
+constexpr int kSkMinSlices = 16;     // 64-wide K slices per part, at least
 
+struct SkPlan {
+  int n_dp, n_sk, S;  // whole tiles, split tiles, parts per split tile
+};
+
+__device__ __forceinline__ SkPlan sk_plan(int total, int ncu, int nk, bool enabled) {
+  SkPlan p{total, 0, 1};
+  const int rem = ncu > 0 ? total % ncu : 0;
+  if (!enabled || rem == 0) return p;
+  const int S = min(kSkMaxSplit, min(kSkUnits / rem, nk / kSkMinSlices));
+  if (S < 2) return p;
+  p.n_dp = total - rem;
+  p.n_sk = rem;
+  p.S = S;
+  return p;
+}
 
 // s_waitcnt with only the vector-memory counter constrained to <= n (n < 64)
 template <int n>
@@ -195,7 +233,8 @@ template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename 
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
-    int N, const Tile2& tile, uint16_t* smem, OutT* __restrict__ C) {
+    int N, const Tile2& tile, int ks0, int nk, uint16_t* smem, OutT* __restrict__ C,
+    float* __restrict__ part_out) {
   static_assert(WM * WN == 4, "four waves");
   constexpr int MT = BM / WM / 32;            // 32-row MFMA tiles per wave
   constexpr int NT = BN / WN / 32;            // 32-col MFMA tiles per wave
@@ -244,8 +283,13 @@ __device__ __forceinline__ void gemm_tile(
   }
   const uint16_t* bslab0 = B0 + tile.g * b_stride;
   const uint16_t* bslab1 = (kFused ? B1 : B0) + tile.g * b_stride;
+  static_assert(!kFused || sizeof(OutT) == 2, "split-K partials are for the unfused GEMM");
 
-  const int nk = K / kBK;
+  // this tile covers K slices ks0 .. ks0 + nk - 1 (all of K unless split)
+#pragma unroll
+  for (int j = 0; j < AP; ++j) ap[j] += ks0 * kBK;
+  bslab0 += ks0 * kBK;
+  bslab1 += ks0 * kBK;
   // copy K slice `ks` (clamped into range: surplus copies reload the last slice
   // into a stage nobody reads again, which keeps the loop branch-free)
 #define MOE_COPY_A(j, stage, ks)                                                     \
@@ -390,6 +434,20 @@ __device__ __forceinline__ void gemm_tile(
           *reinterpret_cast<u32x2*>(crow + col) = pk;
         }
       }
+    } else if (part_out) {  // fp32 partial sums, [256][256] relative to (m0, n0)
+      float* prow = part_out + (row - tile.m0) * BN;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int cb = wn * (BN / WN) + j * 32 + cq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cb + 8 * q;
+          if (tile.n0 + c >= N) continue;
+          f32x4 o = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                     acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(prow + c) = o;
+        }
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -413,25 +471,86 @@ __device__ __forceinline__ void gemm_tile(
   }
 }
 
+// skw: split-K workspace (kSkUnits fp32 256 x 256 tiles) or NULL (no split);
+// ncu: compute units of the device.  Workgroups [0, round8(n_dp)) run the
+// whole tiles, the next round8(n_sk S) the parts of the split tiles, each
+// range in contiguous runs per XCD.
 template <bool kFused, typename OutT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
-    OutT* __restrict__ C) {
+    OutT* __restrict__ C, float* __restrict__ skw, int ncu) {
   constexpr int BN = 256;
-  Tile2 tile;
-  if (!decode_tile2(off, mstart, G, ntn, kFused ? BN / 2 : BN, tile)) return;
+  const int total = mstart[G] * ntn;
+  const int nk_all = K / kBK;
+  const SkPlan plan = sk_plan(total, ncu, nk_all, !kFused && skw != nullptr);
+  const int nw8 = (plan.n_dp + 7) & ~7;
+  const int bid = blockIdx.x;
+  int L, ks0 = 0, nk = nk_all;
+  float* part_out = nullptr;
+  if (bid < nw8) {
+    L = xcd_run(bid, nw8);
+    if (L >= plan.n_dp) return;
+  } else {
+    const int nu = plan.n_sk * plan.S;
+    const int nu8 = (nu + 7) & ~7;
+    if (bid - nw8 >= nu8) return;
+    const int u = xcd_run(bid - nw8, nu8);
+    if (u >= nu) return;
+    const int slot = u / plan.S, part = u - slot * plan.S;
+    L = plan.n_dp + slot;
+    ks0 = part * nk_all / plan.S;
+    nk = (part + 1) * nk_all / plan.S - ks0;
+    part_out = skw + static_cast<size_t>(u) * (kTileM * BN);
+  }
+  const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, kFused ? BN / 2 : BN));
   extern __shared__ __align__(16) uint16_t smem[];
   if (tile.cls == 0) {
     gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                          N, tile, smem, C);
+                                                          N, tile, ks0, nk, smem, C, part_out);
   } else if (tile.cls == 1) {
     gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                          N, tile, smem, C);
+                                                          N, tile, ks0, nk, smem, C, part_out);
   } else {
     gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                         N, tile, smem, C);
+                                                         N, tile, ks0, nk, smem, C, part_out);
+  }
+}
+
+// Adds the S parts of every split tile in part order and writes the rows and
+// columns of the tile that exist; 32 workgroups per split tile, each thread 8
+// columns of one row.
+template <typename OutT>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(const float* __restrict__ skw,
+                                                        const int32_t* __restrict__ off,
+                                                        const int32_t* __restrict__ mstart, int G,
+                                                        int ntn, int K, int N, int ncu,
+                                                        OutT* __restrict__ C) {
+  constexpr int BN = 256;
+  const int total = mstart[G] * ntn;
+  const SkPlan plan = sk_plan(total, ncu, K / kBK, true);
+  const int slot = blockIdx.x / 32;
+  if (slot >= plan.n_sk) return;
+  const Tile t = tile_at(plan.n_dp + slot, off, mstart, G, ntn, kTileM, BN);
+  const int lr = (blockIdx.x % 32) * 8 + threadIdx.x / 32;
+  const int lc = (threadIdx.x % 32) * 8;
+  const int row = t.m0 + lr, col = t.n0 + lc;
+  if (row >= t.row_end || col >= N) return;
+  f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, b = a;
+  for (int part = 0; part < plan.S; ++part) {
+    const float* src = skw + static_cast<size_t>(slot * plan.S + part) * (kTileM * BN) + lr * BN + lc;
+    a += *reinterpret_cast<const f32x4*>(src);
+    b += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  OutT* dst = C + static_cast<int64_t>(row) * N + col;
+  if constexpr (sizeof(OutT) == 2) {
+    u32x4 pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                pack_bf16x2(b[2], b[3])};
+    *reinterpret_cast<u32x4*>(dst) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = a;
+    *reinterpret_cast<f32x4*>(dst + 4) = b;
   }
 }
 
@@ -666,7 +785,7 @@ hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
-      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid));
+      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, 0);
   return hipGetLastError();
 }
 
@@ -676,10 +795,16 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, s.mstart);
   auto kern = gemm_bf16_kernel<false, OutT>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-  kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
+  // whole tiles, then at most kSkUnits parts of split tiles
+  const unsigned grid = gemm_grid(s, ntn) + (s.sk_ws ? kSkUnits : 0);
+  const int ncu = compute_units();
+  kern<<<grid, kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
-      static_cast<OutT*>(s.y));
+      static_cast<OutT*>(s.y), s.sk_ws, ncu);
+  if (s.sk_ws)
+    sk_reduce_kernel<OutT><<<kSkUnits * 32, 256, 0, stream>>>(
+        s.sk_ws, s.group_offset, s.mstart, s.G, ntn, s.h, s.d, ncu, static_cast<OutT*>(s.y));
   return hipGetLastError();
 }
 
@@ -730,6 +855,10 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
 bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
 
 }  // namespace
+
+size_t split_k_workspace_bytes() {
+  return sizeof(float) * static_cast<size_t>(kSkUnits) * kTileM * 256;
+}
 
 hipError_t launch_gate_up(const SwigluArgs& s, hipStream_t stream) {
   if (!s.bf16) return gate_up_f32(s, stream);

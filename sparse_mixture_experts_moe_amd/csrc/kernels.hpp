@@ -47,7 +47,12 @@ struct SwigluArgs {
   bool y_bf16;
   void* hid;        // [max_rows, h] in the compute dtype
   int32_t* mstart;  // workspace: tile table, G + 1 entries
+  float* sk_ws;     // workspace: split-K partial tiles (down projection), or NULL
 };
+// bytes of the split-K partial-tile workspace of the down projection
+size_t split_k_workspace_bytes();
+// compute units of the current device (cached per device), 0 if unknown
+int compute_units();
 hipError_t launch_gate_up(const SwigluArgs& args, hipStream_t stream);
 hipError_t launch_down(const SwigluArgs& args, hipStream_t stream);
 

@@ -16,6 +16,20 @@
 
 namespace moe {
 
+int compute_units() {
+  static std::atomic<int> cache[64];  // per device, 0 = not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev < 64 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 void ensure_dynamic_lds(const void* kernel, int bytes) {
   // (kernel, device, bytes) triples already applied; a short fixed table suffices
   // (a handful of kernels times the visible devices)
@@ -239,9 +253,14 @@ size_t tile_table_bytes(int G) { return align256(sizeof(int32_t) * (static_cast<
 
 size_t moe_expert_group_workspace(int G) { return G < 1 ? 0 : tile_table_bytes(G); }
 
+size_t moe_expert_down_workspace(int G) {
+  return G < 1 ? 0 : tile_table_bytes(G) + moe::split_k_workspace_bytes();
+}
+
 size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt) {
   if (max_rows < 0 || d < 1 || h < 1 || G < 1 || !valid_dtype(dt)) return 0;
-  return align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt)) + tile_table_bytes(G);
+  return align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt)) +
+         moe_expert_down_workspace(G);
 }
 
 moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
@@ -282,9 +301,9 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
   if (!valid_dtype(y_dt)) return fail(MOE_EINVAL, "moe_expert_down: dtype");
   if (!hid || !w_down || !y) return fail(MOE_EINVAL, "moe_expert_down: NULL pointer");
-  if (ws_bytes < tile_table_bytes(G) || !ws)
+  if (ws_bytes < moe_expert_down_workspace(G) || !ws)
     return fail(MOE_EWORKSPACE, "moe_expert_down: workspace %zu < %zu bytes", ws_bytes,
-                tile_table_bytes(G));
+                moe_expert_down_workspace(G));
   moe::SwigluArgs s{};
   s.bf16 = dt == MOE_BF16;
   s.d = d;
@@ -297,6 +316,7 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
   s.y_bf16 = y_dt == MOE_BF16;
   s.hid = const_cast<void*>(hid);
   s.mstart = static_cast<int32_t*>(ws);
+  s.sk_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + tile_table_bytes(G));
   return hip_status(moe::launch_down(s, as_stream(stream)), "moe_expert_down");
 }
 

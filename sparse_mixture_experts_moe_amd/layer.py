@@ -65,7 +65,7 @@ class MoELayer:
                                 device=dev),
             hid=torch.empty((R, h), dtype=x.dtype, device=dev),
             y_perm=torch.empty((R, d), dtype=x.dtype, device=dev),
-            table_ws=torch.empty(_lib.moe_expert_group_workspace(E), dtype=torch.uint8,
+            table_ws=torch.empty(_lib.moe_expert_down_workspace(E), dtype=torch.uint8,
                                  device=dev),
             out=torch.empty((T, d), dtype=x.dtype, device=dev),
             f=torch.empty(E, dtype=torch.float32, device=dev),

@@ -153,7 +153,10 @@ def test_permute_empty():
     ([0, 1, 0, 31, 300, 0, 129, 2], 128, 192),
     ([1000, 0, 700], 256, 320),
     ([5] * 40, 64, 128),
-    ([2000, 1500], 192, 256)])
+    ([2000, 1500], 192, 256),
+    # 12 output tiles, fewer than the compute units: the down projection
+    # splits them along K (two parts of 16 slices) and adds the parts
+    ([300, 40, 517], 512, 2048)])
 def test_expert_swiglu_groups(sizes, d, h, dt):
     from sparse_mixture_experts_moe_amd import _lib
     _say(f"[case] swiglu groups={sizes} d={d} h={h} {dt}")
