@@ -46,13 +46,19 @@ def parse():
 
 
 def gate_up_sources():
-    """The files the gate/up kernel is built from, hashed to tell whether a
-    recorded traffic measurement still describes the kernel that runs."""
+    """The files the gate/up kernel is built from, hashed (comments and blank
+    lines dropped) to tell whether a recorded traffic measurement still
+    describes the kernel that runs."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("grouped_gemm.hip", "common.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "sparse_mixture_experts_moe_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_moe_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()
 
 

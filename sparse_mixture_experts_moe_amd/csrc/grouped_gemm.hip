@@ -114,16 +114,10 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
 // [BN/2, BN) are W_up rows n0..; output columns n0 .. n0 + BN/2 of hid.
 // Otherwise B rows are W rows n0 .. n0 + BN and the output is A W^T.
 //
-// K advances in slices of 32.  The gfx950 direct-to-LDS load
-// (global_load_lds_dwordx4) streams the A slices through a ring of SA LDS
-// stages and the B slices through a ring of SB stages, so A slice kt+SA and B
-// slice kt+SB are requested while slice kt feeds the matrix cores; there is
-// one barrier per slice.  A DMA instruction writes 64 x 16 bytes = 16 tile
-// rows of 64 bytes (lane l lands in chunk l % 4 of row l / 4); LDS chunk c of
-// row r holds the logical chunk c ^ ((r >> 2) & 3), so that the 16 lanes
-// served per LDS cycle by a 16-byte fragment read (16 consecutive rows, one
-// logical chunk) touch 16 distinct bank groups.  Each lane therefore fetches
-// the global chunk (l % 4) ^ ((l / 16) % 4).
+// K advances in slices of 64 (one 128-byte line per row); direct-to-LDS
+// copies stream the A slices through a two-stage LDS ring and the B slices
+// through a three-stage ring, one barrier per slice (see gemm_tile for the
+// copy placement, the LDS swizzle and the wait counts).
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // bf16 tiles are 256 rows high except the last m-tile of each group, which
@@ -132,8 +126,9 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ off,
 // group-major order, next to the tiles that share its weight panel.
 // ---------------------------------------------------------------------------
 constexpr int kTileM = 256;
-// LDS ring depths: activations mostly hit in L2, weight slices are first
-// touches from HBM and get the deeper ring (3 x 16 KB + 6 x 16 KB).
+// LDS ring depths (stages of 32 KB: 64 bf16 of 256 rows): two for A, three
+// for B, 160 KB in all.  The third B stage lets the weight copies of a slice
+// go out before the barrier that retires the previous one.
 constexpr int kRingA = 2;
 constexpr int kRingB = 3;
 
