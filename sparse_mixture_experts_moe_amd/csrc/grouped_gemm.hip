@@ -33,12 +33,41 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTileMBundle = 256;  // m-tile height of the bundled order
 
 // ---------------------------------------------------------------------------
-// Tile table: mstart[g] = sum over g' < g of ceil(rows_g' / BM), g = 0..G.
+// Bundled order of the gate/up tiles.  A group of rows = 256 m + r rows has m
+// full 256-row m-tiles (a remainder r > 128 runs as one more) and, when
+// 0 < r <= 128, a short last m-tile of r rows.  Short tiles would finish in a
+// quarter (r <= 64) or half (r <= 128) of the time of a full one and throw the
+// tiles that share an activation panel out of step, so that the panel is
+// fetched again; instead the group's n-tiles go in blocks of B = 4 (or 2):
+// the m x B full tiles of a block (m fastest), then one unit that runs the
+// block's B short tiles one after the other, about one full tile's time.
+// ---------------------------------------------------------------------------
+struct GroupUnits {
+  int mfull, bsz, units;  // full m-tiles, short tiles per bundle (0: none), work units
+};
+
+__device__ __forceinline__ GroupUnits group_units(int rows, int ntn) {
+  int mfull = rows / kTileMBundle, r = rows % kTileMBundle;
+  if (r > kTileMBundle / 2) {
+    ++mfull;
+    r = 0;
+  }
+  // a group without full tiles has nothing to keep in step: one short tile
+  // per unit, all of them in parallel
+  const int bsz = r == 0 ? 0 : (mfull == 0 ? 1 : (r <= kTileMBundle / 4 ? 4 : 2));
+  return GroupUnits{mfull, bsz, mfull * ntn + (bsz ? (ntn + bsz - 1) / bsz : 0)};
+}
+
+// ---------------------------------------------------------------------------
+// Tile table: mstart[g] = sum over g' < g of ceil(rows_g' / BM), g = 0..G
+// (ntn > 0: of the work units of the bundled order instead).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ off, int G,
-                                                          int BM, int32_t* __restrict__ mstart) {
+                                                          int BM, int ntn,
+                                                          int32_t* __restrict__ mstart) {
   __shared__ int wsum[16];
   __shared__ int carry;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -47,7 +76,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   for (int base = 0; base < G; base += 1024) {
     const int g = base + tid;
     const int rows = g < G ? off[g + 1] - off[g] : 0;
-    const int v = (rows + BM - 1) / BM;
+    const int v = ntn > 0 ? group_units(rows, ntn).units : (rows + BM - 1) / BM;
     int incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -93,6 +122,48 @@ __device__ __forceinline__ Tile tile_at(int L, const int32_t* __restrict__ off,
   tile.row_end = off[g + 1];
   tile.n0 = nt * ncol;
   return tile;
+}
+
+// Work unit L of the bundled order: a full tile (count = 0) or a bundle of
+// `count` short tiles of n-tiles nt0 .. nt0 + count - 1.
+struct Unit {
+  int g, m0, row_end, nt0, count;
+};
+
+__device__ __forceinline__ Unit unit_at(int L, const int32_t* __restrict__ off,
+                                        const int32_t* __restrict__ ustart, int G, int ntn) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ustart[mid] <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int local = L - ustart[g];
+  const GroupUnits gu = group_units(off[g + 1] - off[g], ntn);
+  Unit u;
+  u.g = g;
+  u.row_end = off[g + 1];
+  if (gu.bsz == 0) {
+    const int nt = local / gu.mfull;
+    u.m0 = off[g] + (local - nt * gu.mfull) * kTileMBundle;
+    u.nt0 = nt;
+    u.count = 0;
+    return u;
+  }
+  const int per = gu.mfull * gu.bsz + 1;  // units of a whole block
+  const int blk = local / per, i = local - blk * per;
+  const int nb = min(gu.bsz, ntn - blk * gu.bsz);
+  if (i < gu.mfull * nb) {
+    const int nt = i / gu.mfull;
+    u.m0 = off[g] + (i - nt * gu.mfull) * kTileMBundle;
+    u.nt0 = blk * gu.bsz + nt;
+    u.count = 0;
+  } else {
+    u.m0 = off[g] + gu.mfull * kTileMBundle;
+    u.nt0 = blk * gu.bsz;
+    u.count = nb;
+  }
+  return u;
 }
 
 // Logical tile of this workgroup, or false if it has none.
@@ -477,6 +548,39 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
     OutT* __restrict__ C, float* __restrict__ skw, int ncu) {
   constexpr int BN = 256;
+  extern __shared__ __align__(16) uint16_t smem[];
+  if constexpr (kFused) {  // bundled order, no split
+    const int total = mstart[G];
+    const int nw8 = (total + 7) & ~7;
+    const int bid = blockIdx.x;
+    if (bid >= nw8) return;
+    const int L = xcd_run(bid, nw8);
+    if (L >= total) return;
+    const Unit u = unit_at(L, off, mstart, G, ntn);
+    Tile t{u.g, u.m0, u.row_end, 0};
+    if (u.count == 0) {
+      t.n0 = u.nt0 * (BN / 2);
+      const Tile2 tile = classify(t);
+      gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
+                                                            K, N, tile, 0, K / kBK, smem, C,
+                                                            nullptr);
+      return;
+    }
+    for (int s = 0; s < u.count; ++s) {
+      if (s > 0) __syncthreads();  // the previous tile's last LDS reads are done
+      t.n0 = (u.nt0 + s) * (BN / 2);
+      const Tile2 tile = classify(t);
+      if (tile.cls == 1)
+        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
+                                                              K, N, tile, 0, K / kBK, smem, C,
+                                                              nullptr);
+      else
+        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
+                                                             K, N, tile, 0, K / kBK, smem, C,
+                                                             nullptr);
+    }
+    return;
+  }
   const int total = mstart[G] * ntn;
   const int nk_all = K / kBK;
   const SkPlan plan = sk_plan(total, ncu, nk_all, !kFused && skw != nullptr);
@@ -500,7 +604,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     part_out = skw + static_cast<size_t>(u) * (kTileM * BN);
   }
   const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, kFused ? BN / 2 : BN));
-  extern __shared__ __align__(16) uint16_t smem[];
   if (tile.cls == 0) {
     gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
                                                           N, tile, ks0, nk, smem, C, part_out);
@@ -774,7 +877,7 @@ unsigned gemm_grid(const SwigluArgs& s, int ntn) {
 
 hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ntn = (s.h + 127) / 128;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, s.mstart);
   auto kern = gemm_bf16_kernel<true, uint16_t>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
@@ -787,7 +890,7 @@ hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
 template <typename OutT>
 hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ntn = (s.d + 255) / 256;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, 0, s.mstart);
   auto kern = gemm_bf16_kernel<false, OutT>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   // whole tiles, then at most kSkUnits parts of split tiles
@@ -806,7 +909,7 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
 hipError_t gate_up_f32(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + kF32Tile - 1) / kF32Tile + s.G;
   const int ntn = static_cast<int>((s.h + kF32Tile - 1) / kF32Tile);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, s.mstart);
   gemm_f32_kernel<true><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.a), s.a_rows, s.a_div, static_cast<const float*>(s.w_gate),
       static_cast<const float*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h, s.group_offset,
@@ -817,7 +920,7 @@ hipError_t gate_up_f32(const SwigluArgs& s, hipStream_t stream) {
 hipError_t down_f32(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + kF32Tile - 1) / kF32Tile + s.G;
   const int ntn = static_cast<int>((s.d + kF32Tile - 1) / kF32Tile);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, s.mstart);
   gemm_f32_kernel<false><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.hid), nullptr, 1, static_cast<const float*>(s.w_down), nullptr,
       static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn, s.y,
