@@ -33,102 +33,137 @@ namespace {
 constexpr int kTokPerBlock = 32;
 constexpr int kThreads = 256;
 constexpr int kLanesPerTok = kThreads / kTokPerBlock;  // 8
-constexpr int kExpPerTile = 64;                        // experts per logits tile
+constexpr int kMaxSplits = 8;  // d-splits of the router GEMM, at most
 
 // (v, i) ranks before (bv, bi): larger key first, lower index on equal keys.
 __device__ __forceinline__ bool key_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// grid: (token tiles) x (expert tiles) x KS, one wave each.  NEB expert
-// blocks of 16 per tile (NEB = min(4, ceil(E/16)); blocks past E read a valid
-// row and are not stored).  The d chunks are consumed in batches of kBatch:
-// all fragments of a batch are loaded before its MFMAs, so a wave waits for
-// memory once per batch rather than once per chunk.
-constexpr int kBatch = 8;
+// Router GEMM, bf16: a workgroup of four waves takes 128 tokens (32 per wave)
+// and every expert, padded to NB blocks of 32 rows (rows past E repeat row
+// E-1; their results are not stored).  K (= d) goes in chunks of 64, S =
+// 8 / NB chunks per stage: the stage of w (32 KB) is loaded once into LDS, in
+// full 128-byte lines, and read by all four waves; each wave loads its
+// tokens' fragments of x for the whole stage straight from global memory
+// (every x element is used once), issued together with the w loads.
+// v_mfma_f32_32x32x16_bf16 takes the w fragment as first operand, so lane l
+// accumulates token l & 31 of its wave against experts 8 (r / 4) +
+// 4 (l >> 5) + r % 4 of each block.  A 32-wide last chunk (d % 64 == 32)
+// runs its first two k steps only.  grid: (ceil(T / 128), KS); split s
+// covers chunks [nch s / KS, nch (s + 1) / KS) and writes partial sums to
+// out + s T E (the logits themselves, bias added, when KS = 1).
+constexpr int kRouterTok = 128;
 
-template <int NEB>
-__global__ __launch_bounds__(64) void router_logits_kernel(
+// Element offset of 16-byte chunk `chunk` (0..7) of row `row` in 64-element
+// rows; the XOR spreads the 16 rows read together over distinct bank groups.
+__device__ __forceinline__ int rswz(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int d, int E,
     int KS, const float* __restrict__ logit_bias, float* __restrict__ out) {
-  const int lane = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlock;
-  const int e0 = blockIdx.y * kExpPerTile;
-  const int ks = blockIdx.z;
-  const int nchunk = d / 32;
-  const int c0 = static_cast<int>(static_cast<int64_t>(nchunk) * ks / KS);
-  const int c1 = static_cast<int>(static_cast<int64_t>(nchunk) * (ks + 1) / KS);
-  const int r16 = lane % 16, kq = (lane / 16) * 8;
-  const bf16x8* xrow[2];
+  constexpr int S = 8 / NB;             // chunks per stage
+  constexpr int ROWS = NB * 32;
+  constexpr int CH = ROWS * 64;         // elements of one chunk of w in LDS
+  constexpr int WP = S * CH / (256 * 8);  // 16-byte pieces per thread per stage (8)
+  static_assert(WP == 8, "stage of 32 KB");
+  __shared__ __align__(16) uint16_t wl[S * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTok;
+  const int ks = blockIdx.y;
+  const int nch = (d + 63) / 64;
+  const int c0 = static_cast<int>(static_cast<int64_t>(nch) * ks / KS);
+  const int c1 = static_cast<int>(static_cast<int64_t>(nch) * (ks + 1) / KS);
+  int64_t t = t0 + wave * 32 + (lane & 31);
+  const bool tok_ok = t < T;
+  t = tok_ok ? t : T - 1;  // rows past T read a valid row; results not stored
+  const uint16_t* xr = x + t * d + 8 * (lane >> 5);
+  f32x16 acc[NB];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    int64_t t = t0 + tb * 16 + r16;
-    t = t < T ? t : T - 1;  // rows past T read a valid row; results discarded
-    xrow[tb] = reinterpret_cast<const bf16x8*>(x + t * d + kq);
-  }
-  const bf16x8* wrow[NEB];
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+
+  for (int cs0 = c0; cs0 < c1; cs0 += S) {
+    // w pieces of this stage: piece q = tid + 256 p is row (q / 8) % ROWS,
+    // slot q % 8 of chunk q / (8 ROWS); the slot holds the swizzled chunk
+    bf16x8 wv[WP];
 #pragma unroll
-  for (int eb = 0; eb < NEB; ++eb) {
-    int e = e0 + eb * 16 + r16;
-    e = e < E ? e : E - 1;
-    wrow[eb] = reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(e) * d + kq);
-  }
-  f32x4 acc[NEB][2];
-#pragma unroll
-  for (int eb = 0; eb < NEB; ++eb) acc[eb][0] = acc[eb][1] = f32x4{};
-  int c = c0;
-  for (; c + kBatch <= c1; c += kBatch) {
-    bf16x8 a[kBatch][2], b[kBatch][NEB];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int o = (c + u) * 4;  // 32 elements = 4 fragments of 8
-      a[u][0] = xrow[0][o];
-      a[u][1] = xrow[1][o];
-#pragma unroll
-      for (int eb = 0; eb < NEB; ++eb) b[u][eb] = wrow[eb][o];
+    for (int p = 0; p < WP; ++p) {
+      const int q = tid + 256 * p;
+      const int cs = q / (8 * ROWS), row = (q / 8) % ROWS, slot = q % 8;
+      int c = cs0 + cs;
+      c = c < c1 ? c : c1 - 1;
+      int g = slot ^ ((row >> 1) & 7);
+      if (64 * c + 64 > d) g &= 3;  // 32-wide last chunk: stay inside the row
+      const int e = row < E ? row : E - 1;
+      wv[p] = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(e) * d + 64 * c + 8 * g);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads in flight
+    bf16x8 xv[S][4];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+    for (int cs = 0; cs < S; ++cs) {
+      int c = cs0 + cs;
+      c = c < c1 ? c : c1 - 1;
+      const bool half = 64 * c + 64 > d;
 #pragma unroll
-      for (int eb = 0; eb < NEB; ++eb) {
-        acc[eb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], b[u][eb], acc[eb][0], 0, 0, 0);
-        acc[eb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], b[u][eb], acc[eb][1], 0, 0, 0);
+      for (int st = 0; st < 4; ++st)
+        xv[cs][st] = *reinterpret_cast<const bf16x8*>(xr + 64 * c + 16 * (half ? (st & 1) : st));
+    }
+    __syncthreads();  // the previous stage's LDS reads are done
+#pragma unroll
+    for (int p = 0; p < WP; ++p) {
+      const int q = tid + 256 * p;
+      *reinterpret_cast<bf16x8*>(wl + (q / (8 * ROWS)) * CH + ((q / 8) % ROWS) * 64 + (q % 8) * 8) =
+          wv[p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cs = 0; cs < S; ++cs) {
+      const int c = cs0 + cs;
+      if (c >= c1) break;
+      const int nst = 64 * c + 64 > d ? 2 : 4;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st >= nst) break;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              wl + cs * CH + rswz(32 * b + (lane & 31), 2 * st + (lane >> 5)));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xv[cs][st], acc[b], 0, 0, 0);
+        }
       }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (; c < c1; ++c) {
-    const int o = c * 4;
-    const bf16x8 a0 = xrow[0][o], a1 = xrow[1][o];
-    bf16x8 b[NEB];
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb) b[eb] = wrow[eb][o];
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb) {
-      acc[eb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b[eb], acc[eb][0], 0, 0, 0);
-      acc[eb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b[eb], acc[eb][1], 0, 0, 0);
     }
   }
-  // D[token][expert]: lane holds expert column lane%16, token rows 4*(lane/16)+j
-  float* o = out + static_cast<int64_t>(ks) * T * E;
+  if (!tok_ok) return;
+  // runs of four consecutive experts: one 16-byte store each where the run is
+  // whole and aligned (E % 4 == 0), else element by element
+  float* o = out + static_cast<int64_t>(ks) * T * E + t * E;
+  const bool add_bias = KS == 1 && logit_bias;
 #pragma unroll
-  for (int eb = 0; eb < NEB; ++eb) {
-    const int e = e0 + eb * 16 + r16;
-    if (e >= E) continue;
-    const float lb = (KS == 1 && logit_bias) ? logit_bias[e] : 0.0f;
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int q = 0; q < 4; ++q) {
+      const int e = 32 * b + 8 * q + 4 * (lane >> 5);
+      f32x4 v = {acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]};
+      if (add_bias) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + tb * 16 + (lane / 16) * 4 + j;
-        if (t < T) o[t * E + e] = acc[eb][tb][j] + lb;
+        for (int j = 0; j < 4; ++j) v[j] += e + j < E ? logit_bias[e + j] : 0.0f;
       }
-  }
+      if ((E & 3) == 0 && e + 3 < E) {
+        *reinterpret_cast<f32x4*>(o + e) = v;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e + j < E) o[e + j] = v[j];
+      }
+    }
 }
 
 // mode: 0 = logits are in `logits` (caller's or written by the logits kernel
 // with KS = 1); 1 = sum KS partial tiles from `part` and add logit_bias;
 // 2 = fp32 inputs, compute with FMA.
+template <int KK>  // keys per lane: experts q, q+8, ... below 8 KK >= E
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     int mode, const float* __restrict__ xf, const float* __restrict__ wf,
     const float* __restrict__ part, int KS, int64_t T, int d, int E, int k,
@@ -146,35 +181,32 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
 
   for (int e = tid; e < E; e += kThreads) sb[e] = select_bias ? select_bias[e] : 0.0f;
   if (mode == 1) {
-    // the tile's logits are contiguous in every partial: add the KS partials in
-    // split order, all loads of one split issued together
+    // the tile's logits are contiguous in every partial: all KS partials of a
+    // pass are loaded together, then added in split order
     const int n = ntok * E;
     const int64_t base = t0 * E;
-    constexpr int kPer = 8;  // logits per thread per pass (32 * 256 / 256 = 32 at most)
+    constexpr int kPer = 8;  // logits per thread per pass
     for (int i0 = tid; i0 < n; i0 += kThreads * kPer) {
-      float v[kPer];
+      float v[kMaxSplits][kPer];
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = i0 + u * kThreads;
-        v[u] = i < n ? part[base + i] : 0.0f;
-      }
-      for (int s = 1; s < KS; ++s) {
-        const float* ps = part + static_cast<int64_t>(s) * T * E + base;
+      for (int sp = 0; sp < kMaxSplits; ++sp)
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
           const int i = i0 + u * kThreads;
-          if (i < n) v[u] += ps[i];
+          v[sp][u] = (sp < KS && i < n) ? part[static_cast<int64_t>(sp) * T * E + base + i] : 0.0f;
         }
-      }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int i = i0 + u * kThreads;
-        if (i < n) {
-          const int t = i / E, e = i % E;
-          const float l = v[u] + (logit_bias ? logit_bias[e] : 0.0f);
-          logits[base + i] = l;
-          lg[t * ldl + e] = l;
-        }
+        if (i >= n) continue;
+        float acc = v[0][u];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplits; ++sp)
+          if (sp < KS) acc += v[sp][u];
+        const int t = i / E, e = i % E;
+        const float l = acc + (logit_bias ? logit_bias[e] : 0.0f);
+        logits[base + i] = l;
+        lg[t * ldl + e] = l;
       }
     }
   }
@@ -196,24 +228,33 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   }
   __syncthreads();
 
-  // ---- top-k: eight lanes per token, lane q scans experts q, q+8, ... ----
+  // ---- top-k: eight lanes per token, lane q holds the keys of experts q,
+  // q+8, ... in registers (E <= 256: at most 32) ----
   const int tt = tid / kLanesPerTok, q = tid % kLanesPerTok;
   const bool active = tt < ntok;
   const float* row = lg + tt * ldl;
+  constexpr int kKeys = KK;
+  float key[kKeys];
+#pragma unroll
+  for (int u = 0; u < kKeys; ++u) {
+    const int e = q + u * kLanesPerTok;
+    key[u] = (active && e < E) ? (select_bias ? __fadd_rn(row[e], sb[e]) : row[e])
+                               : -__builtin_inff();
+  }
   float pv = __builtin_inff();
   int pi = -1;
   for (int j = 0; j < k; ++j) {
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
-    if (active) {
-      for (int e = q; e < E; e += kLanesPerTok) {
-        const float v = select_bias ? __fadd_rn(row[e], sb[e]) : row[e];
-        // candidates rank strictly after the previous winner
-        const bool after_prev = v < pv || (v == pv && e > pi);
-        if (after_prev && key_before(v, e, bv, bi)) {
-          bv = v;
-          bi = e;
-        }
+#pragma unroll
+    for (int u = 0; u < kKeys; ++u) {
+      const int e = q + u * kLanesPerTok;
+      const float v = key[u];
+      // candidates rank strictly after the previous winner
+      const bool after_prev = v < pv || (v == pv && e > pi);
+      if (e < E && after_prev && key_before(v, e, bv, bi)) {
+        bv = v;
+        bi = e;
       }
     }
 #pragma unroll
@@ -246,14 +287,14 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   }
 }
 
-// d-splits for the logits kernel: enough waves to cover the chip (~1024),
-// at most kMaxSplits (the select kernel adds that many partials per logit)
-// and at most one split per 32-wide chunk.
-constexpr int kMaxSplits = 8;
+// d-splits for the logits kernel: enough workgroups for two per compute unit
+// (~512), at most kMaxSplits (the select kernel adds that many partials per
+// logit) and at most one split per 64-wide chunk.
 int route_splits(int64_t T, int d, int E) {
-  const int64_t tiles = ((T + kTokPerBlock - 1) / kTokPerBlock) * ((E + kExpPerTile - 1) / kExpPerTile);
-  int64_t ks = (1024 + tiles - 1) / tiles;
-  const int64_t nchunk = d / 32;
+  (void)E;
+  const int64_t tiles = (T + kRouterTok - 1) / kRouterTok;
+  int64_t ks = (512 + tiles - 1) / tiles;
+  const int64_t nchunk = (d + 63) / 64;
   if (ks > kMaxSplits) ks = kMaxSplits;
   if (ks > nchunk) ks = nchunk;
   return static_cast<int>(ks < 1 ? 1 : ks);
@@ -279,30 +320,36 @@ hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int 
   const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
   const size_t lds = route_lds_bytes(E, k);
   // the logits tile can exceed the default 64 KB dynamic LDS limit
-  ensure_dynamic_lds(reinterpret_cast<const void*>(route_select_kernel), static_cast<int>(lds));
+  const void* sel_fn = E <= 32 ? reinterpret_cast<const void*>(route_select_kernel<4>)
+                       : E <= 64 ? reinterpret_cast<const void*>(route_select_kernel<8>)
+                       : E <= 128 ? reinterpret_cast<const void*>(route_select_kernel<16>)
+                                  : reinterpret_cast<const void*>(route_select_kernel<32>);
+  ensure_dynamic_lds(sel_fn, static_cast<int>(lds));
   int mode = 0, ks = 1;
   if (!logits_in && bf16) {
     ks = route_splits(T, d, E);
-    dim3 grid(blocks, static_cast<unsigned>((E + kExpPerTile - 1) / kExpPerTile),
-              static_cast<unsigned>(ks));
-    const int neb = (E + 15) / 16 < 4 ? (E + 15) / 16 : 4;
+    dim3 grid(static_cast<unsigned>((T + kRouterTok - 1) / kRouterTok), static_cast<unsigned>(ks));
     float* dst = ks > 1 ? static_cast<float*>(ws) : logits;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* wb = static_cast<const uint16_t*>(w);
-    switch (neb) {
-      case 1: router_logits_kernel<1><<<grid, 64, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst); break;
-      case 2: router_logits_kernel<2><<<grid, 64, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst); break;
-      case 3: router_logits_kernel<3><<<grid, 64, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst); break;
-      default: router_logits_kernel<4><<<grid, 64, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst); break;
-    }
+    if (E <= 32) router_logits_kernel<1><<<grid, 256, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst);
+    else if (E <= 64) router_logits_kernel<2><<<grid, 256, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst);
+    else if (E <= 128) router_logits_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst);
+    else router_logits_kernel<8><<<grid, 256, 0, stream>>>(xb, wb, T, d, E, ks, logit_bias, dst);
     mode = ks > 1 ? 1 : 0;
   } else if (!logits_in) {
     mode = 2;
   }
-  route_select_kernel<<<blocks, kThreads, lds, stream>>>(
-      mode, static_cast<const float*>(x), static_cast<const float*>(w),
-      static_cast<const float*>(ws), ks, T, d, E, k, logit_bias, select_bias, logits, topk_idx,
-      topk_gate);
+#define MOE_SELECT(KK)                                                                    \
+  route_select_kernel<KK><<<blocks, kThreads, lds, stream>>>(                              \
+      mode, static_cast<const float*>(x), static_cast<const float*>(w),                     \
+      static_cast<const float*>(ws), ks, T, d, E, k, logit_bias, select_bias, logits,       \
+      topk_idx, topk_gate)
+  if (E <= 32) MOE_SELECT(4);
+  else if (E <= 64) MOE_SELECT(8);
+  else if (E <= 128) MOE_SELECT(16);
+  else MOE_SELECT(32);
+#undef MOE_SELECT
   return hipGetLastError();
 }
 

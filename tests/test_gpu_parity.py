@@ -101,6 +101,37 @@ def test_route_logits_in(E, k):
 
 
 # ---------------------------------------------------------------------------
+# moe_route's bf16 router GEMM: expert counts that are not multiples of the
+# 32-expert blocks, a d with a 32-wide last chunk, token counts that are not
+# multiples of the 128-token tile, one and several d-splits
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k", [(333, 160, 40, 3), (130, 256, 1, 1), (1000, 2048, 200, 7),
+                                     (64, 6144, 256, 8), (4100, 128, 8, 2), (17, 96, 33, 4)])
+def test_route_bf16_router(T, d, E, k):
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] route bf16 T={T} d={d} E={E} k={k}")
+    rng = np.random.default_rng(T + d + E)
+    xf = rng.standard_normal((T, d)).astype(np.float32)
+    wf = (rng.standard_normal((E, d)) * d ** -0.5).astype(np.float32)
+    x = torch.from_numpy(xf).to(torch.bfloat16)
+    w = torch.from_numpy(wf).to(torch.bfloat16)
+    xb, wb = x.float().numpy(), w.float().numpy()  # the bf16 values, exactly
+    lb = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    sbias = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    for logit_bias, select_bias in ((None, None), (lb, sbias)):
+        lbt = None if logit_bias is None else torch.from_numpy(logit_bias).cuda()
+        sbt = None if select_bias is None else torch.from_numpy(select_bias).cuda()
+        logits, idx, gate = _lib.moe_route(x.cuda(), w.cuda(), k, lbt, sbt)
+        torch.cuda.synchronize()
+        gl = host(logits)
+        ref = oracle.router_logits(xb, wb, logit_bias)
+        assert normwise(gl, ref) <= 1e-5
+        ref_idx = oracle.top_k(oracle.selection_keys(gl, select_bias), k)
+        assert np.array_equal(host(idx), ref_idx)
+        assert np.max(np.abs(host(gate) - oracle.gates(gl, ref_idx))) <= 1e-6
+
+
+# ---------------------------------------------------------------------------
 # moe_permute in isolation on constructed selections
 # ---------------------------------------------------------------------------
 def _selections(T, E, k, kind, rng):
