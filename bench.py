@@ -200,6 +200,18 @@ def main():
     roof["kernel"] = "moe_expert_gate_up (fused gate/up grouped GEMM + SiLU*mul)"
     roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": gu_ms}
 
+    # algorithmic HBM bytes of the memory-bound phases (per call) and the rate
+    # the phase achieved, against the 8 TB/s peak
+    rows_moved = R_kept if args.gather == "copy" else 0  # x_perm written and read back
+    phase_bytes = {
+        "route": T * d * esz + E * d * esz + T * E * 4 + T * k * 8,
+        "permute": T * k * 4 + (E + 1) * 4 + 2 * T * k * 4 + 2 * rows_moved * d * esz,
+        "combine": (R_kept + T + (T if cfg.n_shared else 0)) * d * esz + T * k * 8,
+        "stats": T * E * 4,
+    }
+    phase_gbs = {name: phase_bytes[name] / (phase_ms[name] * 1e-3) / 1e9
+                 for name in phase_bytes if phase_ms.get(name, 0) > 0}
+
     # whole-layer algorithmic work
     hs = cfg.n_shared * cfg.h_shared
     flops = 2.0 * T * d * E + 6.0 * d * h * R_kept + 6.0 * d * hs * T
@@ -229,6 +241,7 @@ def main():
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "layer_hbm_gbs": bytes_ / (ms * 1e-3) / 1e9,
         "phase_ms": phase_ms,
+        "phase_hbm_gbs": phase_gbs,
         "host_enqueue_ms_per_step": host_ms,
         "routing": {"kept_pairs": R_kept, "dropped_pairs": T * k - R_kept,
                     "touched_experts": touched, "max_rows": int(kept.max()),

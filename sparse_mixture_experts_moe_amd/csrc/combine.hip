@@ -8,7 +8,9 @@
 // "Fine-Grained Expert Architecture" (shared experts are added).
 //
 // HBM-bound: one workgroup per token, each lane handles 8 consecutive
-// columns per step (16-byte bf16 loads and stores).
+// columns per step (16-byte bf16 loads and stores); the rows of up to
+// kSlotBatch slots (and the shared row) are loaded together before they are
+// added in slot order, so a lane waits for memory once per batch.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -16,27 +18,31 @@ namespace moe {
 
 namespace {
 
+constexpr int kSlotBatch = 8;
+
 template <typename T>
 struct Vec8;
 
 template <>
 struct Vec8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
+  static __device__ __forceinline__ void unpack(const Raw& q, float (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
     }
   }
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
+    unpack(load_raw(p), v);
+  }
   static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
-    uint4 q;
-    q.x = pack_bf16x2(v[0], v[1]);
-    q.y = pack_bf16x2(v[2], v[3]);
-    q.z = pack_bf16x2(v[4], v[5]);
-    q.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = q;
+    const u32x4 q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+    *reinterpret_cast<u32x4*>(p) = q;
   }
   static __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
   static __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
@@ -44,6 +50,19 @@ struct Vec8<uint16_t> {
 
 template <>
 struct Vec8<float> {
+  struct Raw {
+    f32x4 a, b;
+  };
+  static __device__ __forceinline__ Raw load_raw(const float* p) {
+    return Raw{reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]};
+  }
+  static __device__ __forceinline__ void unpack(const Raw& q, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = q.a[i];
+      v[4 + i] = q.b[i];
+    }
+  }
   static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
@@ -70,18 +89,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   if ((d & 7) == 0) {
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int j = 0; j < k; ++j) {
-        const int row = pr[j];
-        if (row < 0) continue;
-        const float gj = g[j];
-        float v[8];
-        Vec8<YT>::load(y + static_cast<int64_t>(row) * d + c, v);
+      typename Vec8<YT>::Raw sh{};
+      if (shared) sh = Vec8<YT>::load_raw(shared + t * d + c);
+      for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+        int rows[kSlotBatch];
+        typename Vec8<YT>::Raw raw[kSlotBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
+        for (int u = 0; u < kSlotBatch; ++u) {
+          rows[u] = j0 + u < k ? pr[j0 + u] : -1;
+          if (rows[u] >= 0) raw[u] = Vec8<YT>::load_raw(y + static_cast<int64_t>(rows[u]) * d + c);
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          if (rows[u] < 0) continue;  // dropped (or past k): contributes nothing
+          const float gj = g[j0 + u];
+          float v[8];
+          Vec8<YT>::unpack(raw[u], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
+        }
       }
       if (shared) {
         float v[8];
-        Vec8<YT>::load(shared + t * d + c, v);
+        Vec8<YT>::unpack(sh, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }

@@ -8,12 +8,13 @@
 // Architecture", section "MoE-Specific Training Stability" (z-loss).
 //
 // Deterministic: workgroup b owns a fixed block of 64 tokens, taken 32 at a
-// time with eight lanes per token (each lane covers an eighth of the experts;
-// max and sum-exp combine with lane shuffles); the probabilities of the 32
-// tokens are summed per expert in token order and accumulated over the two
-// rounds, giving partials[b][E].  One workgroup then adds the partials: 1024
-// threads sum fixed segments of blocks per expert in fp64, and the segments
-// are added in segment order.
+// time with eight lanes per token (each lane holds an eighth of the token's
+// logits in registers; max and sum-exp combine with lane shuffles); the
+// probabilities of the 32 tokens are summed per expert in token order and
+// accumulated over the two rounds, giving partials[b][E].  One workgroup then
+// adds the partials: 1024 threads sum fixed segments of blocks per expert in
+// fp64, and the segments are added in segment order; the z-loss partials go
+// through a fixed fp64 tree.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +26,7 @@ constexpr int kTok = 64;        // tokens per partial block
 constexpr int kRound = 32;      // tokens per round
 constexpr int kLanes = 8;       // lanes per token
 
+template <int KK>  // logits per lane: experts q, q+8, ... below 8 KK >= E
 __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits,
                                                             int64_t T, int E,
                                                             float* __restrict__ part,
@@ -40,18 +42,33 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
     const int64_t t = tb0 + r * kRound + tt;
     const bool active = t < T;
     const float* row = logits + (active ? t : 0) * E;
+    float v[KK];
+#pragma unroll
+    for (int u = 0; u < KK; ++u) {
+      const int e = q + u * kLanes;
+      v[u] = (active && e < E) ? row[e] : -__builtin_inff();
+    }
     float m = -__builtin_inff();
-    if (active)
-      for (int e = q; e < E; e += kLanes) m = fmaxf(m, row[e]);
+#pragma unroll
+    for (int u = 0; u < KK; ++u) m = fmaxf(m, v[u]);
 #pragma unroll
     for (int o = 1; o < kLanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kLanes));
     float s = 0.0f;
-    if (active)
-      for (int e = q; e < E; e += kLanes) s += expf(row[e] - m);
+#pragma unroll
+    for (int u = 0; u < KK; ++u) {
+      if (q + u * kLanes < E) {
+        v[u] = active ? expf(v[u] - m) : 0.0f;
+        s += v[u];
+      }
+    }
 #pragma unroll
     for (int o = 1; o < kLanes; o <<= 1) s += __shfl_xor(s, o, kLanes);
     const float inv = 1.0f / s;
-    for (int e = q; e < E; e += kLanes) sp[tt * E + e] = active ? expf(row[e] - m) * inv : 0.0f;
+#pragma unroll
+    for (int u = 0; u < KK; ++u) {
+      const int e = q + u * kLanes;
+      if (e < E) sp[tt * E + e] = active ? v[u] * inv : 0.0f;  // (inactive: s = 0)
+    }
     if (q == 0) {
       const float lse = m + logf(s);
       zs[tt] = active ? lse * lse : 0.0f;
@@ -77,6 +94,7 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float* __restri
                                                            float* __restrict__ zloss) {
   __shared__ double seg[1024];
   __shared__ double fp[256];
+  __shared__ double zt[1024];
   const int tid = threadIdx.x;
   const int nseg = 1024 / E;  // segments per expert (E <= 256 -> >= 4)
   const int e = tid % E, sgi = tid / E;
@@ -99,18 +117,23 @@ __global__ __launch_bounds__(1024) void stats_final_kernel(const float* __restri
     term = fe * pe;
   }
   if (tid < 256) fp[tid] = term;
+  // z-loss partials: thread i sums blocks i, i + 1024, ... in order, then a
+  // fixed tree adds the 1024 sums
+  double z = 0.0;
+  if (zloss)
+    for (int b = tid; b < nblk; b += 1024) z += zpart[b];
+  zt[tid] = z;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) fp[tid] += fp[tid + s];
+  for (int s = 512; s > 0; s >>= 1) {
+    if (tid < s) {
+      zt[tid] += zt[tid + s];
+      if (tid < 128 && s <= 128) fp[tid] += fp[tid + s];
+    }
     __syncthreads();
   }
   if (tid == 0) {
     loss[0] = static_cast<float>(static_cast<double>(alpha) * E * fp[0]);
-    if (zloss) {
-      double z = 0.0;
-      for (int b = 0; b < nblk; ++b) z += zpart[b];
-      zloss[0] = static_cast<float>(z / static_cast<double>(T));
-    }
+    if (zloss) zloss[0] = static_cast<float>(zt[0] / static_cast<double>(T));
   }
 }
 
@@ -123,7 +146,11 @@ hipError_t launch_balance_stats(const float* logits, const int32_t* count, int64
                                 float* part, float* zpart, hipStream_t stream) {
   const int64_t nblk = stats_blocks(T);
   const size_t lds = sizeof(float) * kRound * E;
-  stats_partial_kernel<<<static_cast<unsigned>(nblk), 256, lds, stream>>>(logits, T, E, part, zpart);
+  const unsigned g = static_cast<unsigned>(nblk);
+  if (E <= 32) stats_partial_kernel<4><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
+  else if (E <= 64) stats_partial_kernel<8><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
+  else if (E <= 128) stats_partial_kernel<16><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
+  else stats_partial_kernel<32><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
   stats_final_kernel<<<1, 1024, 0, stream>>>(part, zpart, static_cast<int>(nblk), count, T, E, k,
                                              alpha, f, P, loss, zloss);
   return hipGetLastError();
