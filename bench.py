@@ -78,6 +78,60 @@ def recorded_traffic(workload):
     return float(val.group(1))
 
 
+def _median_ms(torch, fn, warmup=3, reps=7):
+    """Median duration of fn() over reps launches (HIP events on the current
+    stream, one pair per launch), after warmup launches."""
+    import statistics
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times)
+
+
+def measured_ceilings(torch, gemm_shape):
+    """What this device sustains, measured right after the timed steps:
+    bf16 MFMAs on register-resident random operands (no memory traffic), a
+    streaming read of a 4 GiB buffer, and the vendor library's dense bf16 GEMM
+    (hipBLASLt through torch.matmul) of the given shape [M, K, N]."""
+    from sparse_mixture_experts_moe_amd import _lib as L
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4096
+    src = torch.randn(ncu * 256 * 64, device="cuda").to(torch.bfloat16)
+    out = torch.empty(ncu * 256, dtype=torch.float32, device="cuda")
+    ms = _median_ms(torch, lambda: L.moe_probe_mfma_bf16(src, ncu, iters, out=out))
+    mfma = ncu * 4 * iters * 16 * 32768 / (ms * 1e-3) / 1e12
+    del src, out
+    nbytes = 4 << 30
+    buf = torch.full((nbytes // 4,), 0x01010101, dtype=torch.int32, device="cuda")
+    rout = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    ms = _median_ms(torch, lambda: L.moe_probe_read(buf, 8192, out=rout))
+    hbm = nbytes / (ms * 1e-3) / 1e9
+    del buf, rout
+    res = {"mfma_bf16_tflops": mfma, "hbm_read_gbs": hbm,
+           "how": f"MFMA: {ncu} workgroups x 4 waves x {iters} x 16 v_mfma_f32_32x32x16_bf16 on "
+                  "random-normal register operands; read: 4 GiB streamed once in 16-byte loads; "
+                  "median of 7 launches after 3"}
+    if gemm_shape is not None:
+        M, K, N = gemm_shape
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = (torch.randn(K, N, device="cuda") * K ** -0.5).to(torch.bfloat16)
+        c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ms = _median_ms(torch, lambda: torch.matmul(a, b, out=c))
+        res["library_gemm"] = {"shape_mkn": [M, K, N], "tflops": 2.0 * M * K * N / (ms * 1e-3) / 1e12,
+                               "ms": ms}
+        del a, b, c
+    torch.cuda.synchronize()
+    return res
+
+
 def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5):
     """The oracle as it stands, on the first n_tok tokens taken as a batch of
     their own (same shapes, weights, biases and capacity factor), repeated
@@ -167,6 +221,11 @@ def main():
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
 
+    # per-step durations: from one step's start event to the next (the last
+    # to the closing event)
+    starts = [step[0][1] for step in marks] + [end]
+    step_ms = np.array([a.elapsed_time(b) for a, b in zip(starts[:-1], starts[1:])])
+
     phases = {}
     for step in marks:
         for (_, a), (name, b) in zip(step[:-1], step[1:]):
@@ -197,6 +256,14 @@ def main():
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs
     # recorded in profiles/ (scaled by a plain copy of known size), or null
     roof["traffic"] = recorded_traffic(cfg.name)
+    ceil = measured_ceilings(torch, None if cfg.name.startswith("decode") or cfg.dtype != "bf16"
+                             else (R_kept, d, 2 * h))
+    if roof["bound"] == "hbm":
+        roof["measured_peak"] = ceil["hbm_read_gbs"]
+    elif cfg.dtype == "bf16":
+        roof["measured_peak"] = ceil["mfma_bf16_tflops"]
+    if "measured_peak" in roof:
+        roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
     roof["kernel"] = "moe_expert_gate_up (fused gate/up grouped GEMM + SiLU*mul)"
     roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": gu_ms}
 
@@ -228,6 +295,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
+                    "p90": float(np.percentile(step_ms, 90))},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -237,6 +306,7 @@ def main():
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
                    "gather": args.gather, "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "measured_ceilings": ceil,
         "expert_gemm_mfma_util": expert_flops / (expert_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "layer_hbm_gbs": bytes_ / (ms * 1e-3) / 1e9,

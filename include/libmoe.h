@@ -275,6 +275,30 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
                                int E, int k, float alpha, float* f, float* P, float* loss,
                                float* zloss, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement probes: what the device sustains, for roofline fractions
+ * against a measured ceiling beside the datasheet peaks.  They compute
+ * nothing of the layer.
+ *
+ * moe_probe_mfma_bf16: `blocks` workgroups of 256 threads (each holds more
+ * than half of a CU's LDS, so one runs per CU; pass the CU count to cover
+ * the chip).  Every lane loads 8 fragments of 8 bf16 from src[lane * 64 ..]
+ * (src holds blocks * 256 * 64 bf16, e.g. random normals: the operands'
+ * bit patterns set the power drawn and so the clock), then each wave issues
+ * iters * 16 v_mfma_f32_32x32x16_bf16 on them, 32768 FLOP each, with no
+ * memory traffic.  out [blocks * 256] fp32 receives each lane's accumulator
+ * sum.  FLOP per launch: blocks * 4 * iters * 16 * 32768.
+ *
+ * moe_probe_read: reads bytes (a positive multiple of 16) of buf once, in
+ * 16-byte loads spread over `blocks` workgroups of 256 threads (grid
+ * stride); out [blocks * 256] uint32 receives each lane's XOR of what it
+ * read.  Bytes per launch: bytes.
+ */
+moe_status_t moe_probe_mfma_bf16(const void* src, int blocks, int iters, float* out,
+                                 void* stream);
+moe_status_t moe_probe_read(const void* buf, size_t bytes, int blocks, uint32_t* out,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,8 @@ _SIGS = {
     "moe_combine": (_i, [_p, _i, _p, _p, _i64, _i, _i, _p, _p, _i, _p]),
     "moe_balance_stats_workspace": (_sz, [_i64, _i]),
     "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_probe_mfma_bf16": (_i, [_p, _i, _i, _p, _p]),
+    "moe_probe_read": (_i, [_p, _sz, _i, _p, _p]),
 }
 EXPORTED = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -284,3 +286,25 @@ def moe_balance_stats(logits, expert_count, k, alpha=0.01, *, f=None, P=None, lo
                                 _ptr(f), _ptr(P), _ptr(loss), _ptr(zloss), _ptr(ws), ws.numel(),
                                 _stream(stream)))
     return f, P, loss, zloss
+
+
+def moe_probe_mfma_bf16(src, blocks, iters, *, out=None, stream=None):
+    """MFMA-only loop on register-resident bf16 operands loaded from src
+    (blocks*256*64 bf16); returns out [blocks*256] fp32.  FLOP per call:
+    blocks*4*iters*16*32768."""
+    if src.dtype != torch.bfloat16 or src.numel() < blocks * 256 * 64:
+        raise ValueError("src must hold blocks*256*64 bf16")
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=src.device) if out is None else out
+    _contig(src, out)
+    _check(_L.moe_probe_mfma_bf16(_ptr(src), blocks, iters, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_probe_read(buf, blocks, *, out=None, stream=None):
+    """Streaming read of every byte of buf; returns out [blocks*256] int32
+    (each lane's XOR of its words)."""
+    nbytes = buf.numel() * buf.element_size()
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=buf.device) if out is None else out
+    _contig(buf, out)
+    _check(_L.moe_probe_read(_ptr(buf), nbytes, blocks, _ptr(out), _stream(stream)))
+    return out

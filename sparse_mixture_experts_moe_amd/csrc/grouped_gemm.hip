@@ -21,10 +21,13 @@
 //   over the whole slice, since a compute unit accepts one about every 16
 //   cycles.  Fragment reads are double-buffered in registers and interleaved
 //   one-for-one with the MFMAs (see gemm_tile).
-//   Tiles are ordered group-major, n-tile next, m-tile fastest, and laid out
-//   in contiguous runs per XCD so that tiles sharing a weight panel or an
-//   activation panel run together on one XCD's L2.
-// fp32 path: a plain LDS-tiled FMA kernel with the same tile order.
+//   Tiles are ordered group-major, then in bands of four m-tiles (band,
+//   n-tile, m-tile fastest).  Both GEMMs run persistent, one workgroup per
+//   compute unit: the order is cut into one contiguous run per XCD, of equal
+//   estimated cost, so that tiles sharing a weight or activation panel run
+//   together on one XCD's L2 and every XCD stays busy to the end.
+// fp32 path: a plain LDS-tiled FMA kernel, one workgroup per tile, in
+// contiguous runs per XCD.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,8 +48,15 @@ constexpr int kTileMBundle = 256;  // m-tile height of the bundled order
 // the m x B full tiles of a block (m fastest), then one unit that runs the
 // block's B short tiles one after the other, about one full tile's time.
 // ---------------------------------------------------------------------------
+// Estimated time of one tile of bm rows (any n-tile): 6 for 256 rows, 4 for
+// 128, 3 for 64.  A short tile still copies the whole weight panel, so its
+// time falls by less than its rows.  Only the balance of the XCD runs (see
+// tile_table_kernel) depends on these numbers.
+__host__ __device__ constexpr int tile_cost(int bm) { return bm / 64 + 2; }
+
 struct GroupUnits {
   int mfull, bsz, units;  // full m-tiles, short tiles per bundle (0: none), work units
+  int cost;               // estimated time of all of the group's units
 };
 
 __device__ __forceinline__ GroupUnits group_units(int rows, int ntn) {
@@ -58,41 +68,189 @@ __device__ __forceinline__ GroupUnits group_units(int rows, int ntn) {
   // a group without full tiles has nothing to keep in step: one short tile
   // per unit, all of them in parallel
   const int bsz = r == 0 ? 0 : (mfull == 0 ? 1 : (r <= kTileMBundle / 4 ? 4 : 2));
-  return GroupUnits{mfull, bsz, mfull * ntn + (bsz ? (ntn + bsz - 1) / bsz : 0)};
+  const int cost = mfull * ntn * tile_cost(kTileMBundle) +
+                   (bsz ? ntn * tile_cost(r <= kTileMBundle / 4 ? 64 : 128) : 0);
+  return GroupUnits{mfull, bsz, mfull * ntn + (bsz ? (ntn + bsz - 1) / bsz : 0), cost};
+}
+
+// Estimated time of a group's tiles in the plain order (every m-tile is 256
+// rows high but the last, which runs as 64, 128 or 256 rows).
+__device__ __forceinline__ int group_tile_cost(int rows, int ntn) {
+  if (rows <= 0) return 0;
+  const int mt = (rows + kTileMBundle - 1) / kTileMBundle;
+  const int last = rows - (mt - 1) * kTileMBundle;
+  const int bm = last <= 64 ? 64 : (last <= 128 ? 128 : 256);
+  return ((mt - 1) * tile_cost(kTileMBundle) + tile_cost(bm)) * ntn;
 }
 
 // ---------------------------------------------------------------------------
-// Tile table: mstart[g] = sum over g' < g of ceil(rows_g' / BM), g = 0..G
-// (ntn > 0: of the work units of the bundled order instead).
+// Split-K of the last tiles.  With a long K (the down projection) one tile
+// runs long enough that a final partial round of tiles leaves most compute
+// units idle.  The last n_sk = total mod ncu tiles (in tile order) are cut
+// along K into S parts (2 <= S <= kSkMaxSplit, n_sk S <= kSkUnits, at least
+// kSkMinSlices slices per part), which run after the whole tiles; part p of
+// split tile i writes the fp32 partial sums of its 256 x 256 tile to
+// workspace unit i S + p, and sk_reduce_kernel adds the parts in part order
+// (a fixed order: results are deterministic) and writes the output.
+// ---------------------------------------------------------------------------
+constexpr int kSkUnits = 256;        // partial tiles the workspace holds
+constexpr int kSkMaxSplit = 4;
+constexpr int kSkMinSlices = 16;     // 64-wide K slices per part, at least
+
+struct SkPlan {
+  int n_dp, n_sk, S;  // whole tiles, split tiles, parts per split tile
+};
+
+__device__ __forceinline__ SkPlan sk_plan(int total, int ncu, int nk, bool enabled) {
+  SkPlan p{total, 0, 1};
+  const int rem = ncu > 0 ? total % ncu : 0;
+  if (!enabled || rem == 0) return p;
+  const int S = min(kSkMaxSplit, min(kSkUnits / rem, nk / kSkMinSlices));
+  if (S < 2) return p;
+  p.n_dp = total - rem;
+  p.n_sk = rem;
+  p.S = S;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent launches.  The bf16 GEMMs run one workgroup per compute unit;
+// workgroup b runs on XCD b mod 8 (checked with the hardware id register).
+// The whole tiles (or work units) are cut into kXcds contiguous runs of about
+// equal estimated cost, and the workgroups of XCD x take the units of run x
+// in order from a counter: the units that an XCD runs together are
+// consecutive in the order, so they share activation and weight panels in its
+// L2, and hot and cold experts (costly full tiles, cheap short ones) no
+// longer leave some XCDs idle while others still work.  When split-K is on
+// (long tiles), the runs are equal counts of whole rounds instead; the split
+// parts follow from one counter shared by all XCDs.
+// Workspace (int32): mstart [G + 1] | cstart [G + 1] | runs [kXcds + 1] |
+// counters [kXcds + 1], each array from a 64-entry boundary.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+__host__ __device__ constexpr int tt_pad(int n) { return (n + 63) / 64 * 64; }
+__host__ __device__ constexpr int tt_cstart(int G) { return tt_pad(G + 1); }
+__host__ __device__ constexpr int tt_runs(int G) { return 2 * tt_pad(G + 1); }
+__host__ __device__ constexpr int tt_counters(int G) { return 2 * tt_pad(G + 1) + 64; }
+__host__ __device__ constexpr int tt_entries(int G) { return 2 * tt_pad(G + 1) + 128; }
+
+// ---------------------------------------------------------------------------
+// Tile table (one workgroup): mstart[g] = sum over g' < g of ceil(rows_g' /
+// BM), g = 0..G, or with `units` of the work units of the bundled order.
+// With `tt` (the workspace of the persistent launches, mstart at its start):
+// also the cost prefixes cstart, the XCD runs of the whole tiles (ntn n-tiles
+// per m-tile; the split plan of ncu compute units and nk K slices decides
+// which tiles are whole) and zeroed counters.  A cut falls inside the group
+// whose cost range holds it, placed by linear interpolation of its cost.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ off, int G,
-                                                          int BM, int ntn,
-                                                          int32_t* __restrict__ mstart) {
-  __shared__ int wsum[16];
-  __shared__ int carry;
+                                                          int BM, int ntn, bool units,
+                                                          int32_t* __restrict__ mstart,
+                                                          int32_t* __restrict__ tt, int ncu,
+                                                          int nk, bool split) {
+  __shared__ long long wsum[16];
+  __shared__ long long carry;
+  __shared__ int s_ndp, s_cdp;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int32_t* cstart = tt ? tt + tt_cstart(G) : nullptr;
   if (tid == 0) carry = 0;
   __syncthreads();
+  // prefix sums of the unit counts (low 32 bits) and costs (high 32 bits)
   for (int base = 0; base < G; base += 1024) {
     const int g = base + tid;
     const int rows = g < G ? off[g + 1] - off[g] : 0;
-    const int v = ntn > 0 ? group_units(rows, ntn).units : (rows + BM - 1) / BM;
-    int incl = v;
+    int v, c;
+    if (units) {
+      const GroupUnits gu = group_units(rows, ntn);
+      v = gu.units;
+      c = gu.cost;
+    } else {
+      v = (rows + BM - 1) / BM;
+      c = tt ? group_tile_cost(rows, ntn) : 0;
+    }
+    const long long vc = (static_cast<long long>(c) << 32) | static_cast<unsigned>(v);
+    long long incl = vc;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-      const int n = __shfl_up(incl, o);
+      const long long n = __shfl_up(incl, o);
       if (lane >= o) incl += n;
     }
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    int pre = carry;
+    long long pre = carry;
     for (int w = 0; w < wave; ++w) pre += wsum[w];
-    if (g < G) mstart[g] = pre + incl - v;
+    pre += incl - vc;  // this group's exclusive prefix
+    if (g < G) {
+      mstart[g] = static_cast<int>(pre & 0xffffffffLL);
+      if (cstart) cstart[g] = static_cast<int>(pre >> 32);
+    }
     __syncthreads();
-    if (tid == 1023) carry = pre + incl;
+    if (tid == 1023) carry = pre + vc;
     __syncthreads();
   }
-  if (tid == 0) mstart[G] = carry;
+  const int total_v = static_cast<int>(carry & 0xffffffffLL);
+  const int total_c = static_cast<int>(carry >> 32);
+  if (tid == 0) {
+    mstart[G] = total_v;
+    if (cstart) cstart[G] = total_c;
+  }
+  if (!tt) return;
+  __syncthreads();  // the prefixes above are visible to the whole workgroup
+  const int per = units ? 1 : ntn;  // work items per entry of mstart
+  // index of work item L -> its group, by binary search over mstart
+  auto group_of = [&](int L) {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (mstart[mid] * per <= L) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  if (tid == 0) {
+    const int n_all = total_v * per;
+    const int n_dp = units ? n_all : sk_plan(n_all, ncu, nk, split).n_dp;
+    int c_dp = total_c;
+    if (n_dp < n_all) {  // estimated cost of the whole tiles before item n_dp
+      const int g = group_of(n_dp);
+      const int u0 = mstart[g] * per, nu = (mstart[g + 1] - mstart[g]) * per;
+      const int cg = cstart[g + 1] - cstart[g];
+      c_dp = cstart[g] + static_cast<int>(static_cast<long long>(n_dp - u0) * cg / nu);
+    }
+    s_ndp = n_dp;
+    s_cdp = c_dp;
+  }
+  __syncthreads();
+  int32_t* runs = tt + tt_runs(G);
+  int32_t* counters = tt + tt_counters(G);
+  const int n_dp = s_ndp;
+  if (tid > 0 && tid < kXcds) {
+    const long long target = static_cast<long long>(s_cdp) * tid / kXcds;
+    int cut = n_dp;
+    if (n_dp < total_v * per) {
+      // split-K is on: tiles are long and n_dp is a multiple of the compute
+      // units, so equal counts give every XCD the same whole rounds (a cut
+      // by estimated cost could leave one XCD a round more)
+      cut = static_cast<int>(static_cast<long long>(n_dp) * tid / kXcds);
+    } else if (target < s_cdp) {
+      // the last group whose cost range starts at or before the target
+      int lo = 0, hi = G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cstart[mid] <= target) lo = mid; else hi = mid;
+      }
+      const int cg = cstart[lo + 1] - cstart[lo];
+      const int u0 = mstart[lo] * per, nu = (mstart[lo + 1] - mstart[lo]) * per;
+      cut = u0 + (cg > 0 ? static_cast<int>((target - cstart[lo]) * nu / cg) : 0);
+      cut = min(cut, n_dp);
+    }
+    runs[tid] = cut;
+  }
+  if (tid == 0) {
+    runs[0] = 0;
+    runs[kXcds] = n_dp;
+  }
+  if (tid <= kXcds) counters[tid] = 0;
 }
 
 struct Tile {
@@ -103,7 +261,20 @@ struct Tile {
 // gives each XCD a contiguous run of logical indices.
 __device__ __forceinline__ int xcd_run(int b, int n8) { return (b & 7) * (n8 >> 3) + (b >> 3); }
 
-// Logical tile L: group-major, n-tile next, m-tile fastest.
+// A group's m-tiles go in bands of kBand: band, then n-tile, then m-tile
+// fastest within the band.  The 32 tiles that one XCD runs together (a run of
+// consecutive indices) then cover kBand m-tiles by 32 / kBand n-tiles of a
+// tall group, so every activation and weight slice they copy has several
+// readers in that XCD's L2 (with the m-tiles of a tall group fastest, each
+// activation slice had one reader and came from memory every time).  The last
+// band takes 1 .. kBand m-tiles.
+constexpr int kBand = 4;
+
+__device__ __forceinline__ int band_lead(int mtiles) {
+  return mtiles > kBand ? ((mtiles - 1) / kBand) * kBand : 0;
+}
+
+// Logical tile L: group-major, then the banded order above.
 __device__ __forceinline__ Tile tile_at(int L, const int32_t* __restrict__ off,
                                         const int32_t* __restrict__ mstart, int G, int ntn,
                                         int BM, int ncol) {
@@ -114,8 +285,19 @@ __device__ __forceinline__ Tile tile_at(int L, const int32_t* __restrict__ off,
   }
   const int g = lo;
   const int mtg = mstart[g + 1] - mstart[g];
-  const int local = L - mstart[g] * ntn;
-  const int nt = local / mtg, mt = local - nt * mtg;
+  int local = L - mstart[g] * ntn;
+  const int lead = band_lead(mtg);
+  int nt, mt;
+  if (local < lead * ntn) {
+    const int band = local / (kBand * ntn), i = local - band * (kBand * ntn);
+    nt = i / kBand;
+    mt = band * kBand + (i - nt * kBand);
+  } else {
+    local -= lead * ntn;
+    const int mtail = mtg - lead;
+    nt = local / mtail;
+    mt = lead + (local - nt * mtail);
+  }
   Tile tile;
   tile.g = g;
   tile.m0 = off[g] + mt * BM;
@@ -138,28 +320,40 @@ __device__ __forceinline__ Unit unit_at(int L, const int32_t* __restrict__ off,
     if (ustart[mid] <= L) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int local = L - ustart[g];
+  int local = L - ustart[g];
   const GroupUnits gu = group_units(off[g + 1] - off[g], ntn);
   Unit u;
   u.g = g;
   u.row_end = off[g + 1];
-  if (gu.bsz == 0) {
-    const int nt = local / gu.mfull;
-    u.m0 = off[g] + (local - nt * gu.mfull) * kTileMBundle;
+  u.count = 0;
+  // leading bands of full m-tiles (banded order, as in tile_at)
+  const int lead = band_lead(gu.mfull);
+  if (local < lead * ntn) {
+    const int band = local / (kBand * ntn), i = local - band * (kBand * ntn);
+    const int nt = i / kBand;
+    u.m0 = off[g] + (band * kBand + (i - nt * kBand)) * kTileMBundle;
     u.nt0 = nt;
-    u.count = 0;
     return u;
   }
-  const int per = gu.mfull * gu.bsz + 1;  // units of a whole block
+  // last band: its full m-tiles and the short tile, n-tiles in blocks of bsz
+  local -= lead * ntn;
+  const int mfull = gu.mfull - lead;
+  const int m_base = off[g] + lead * kTileMBundle;
+  if (gu.bsz == 0) {
+    const int nt = local / mfull;
+    u.m0 = m_base + (local - nt * mfull) * kTileMBundle;
+    u.nt0 = nt;
+    return u;
+  }
+  const int per = mfull * gu.bsz + 1;  // units of a whole block
   const int blk = local / per, i = local - blk * per;
   const int nb = min(gu.bsz, ntn - blk * gu.bsz);
-  if (i < gu.mfull * nb) {
-    const int nt = i / gu.mfull;
-    u.m0 = off[g] + (i - nt * gu.mfull) * kTileMBundle;
+  if (i < mfull * nb) {
+    const int nt = i / mfull;
+    u.m0 = m_base + (i - nt * mfull) * kTileMBundle;
     u.nt0 = blk * gu.bsz + nt;
-    u.count = 0;
   } else {
-    u.m0 = off[g] + gu.mfull * kTileMBundle;
+    u.m0 = m_base + mfull * kTileMBundle;
     u.nt0 = blk * gu.bsz;
     u.count = nb;
   }
@@ -216,36 +410,6 @@ __device__ __forceinline__ Tile2 classify(const Tile& t) {
   const int rem = t.row_end - t.m0;
   tile.cls = rem <= 64 ? 2 : (rem <= 128 ? 1 : 0);
   return tile;
-}
-
-// ---------------------------------------------------------------------------
-// Split-K of the last tiles.  With a long K (the down projection) one tile
-// runs long enough that a final partial round of tiles leaves most compute
-// units idle.  The last n_sk = total mod ncu tiles (in tile order) are cut
-// along K into S parts (2 <= S <= kSkMaxSplit, n_sk S <= kSkUnits, at least
-// kSkMinSlices slices per part), which the grid runs after the whole tiles;
-// part p of split tile i writes the fp32 partial sums of its 256 x 256 tile
-// to workspace unit i S + p, and sk_reduce_kernel adds the parts in part
-// order (a fixed order: results are deterministic) and writes the output.
-// ---------------------------------------------------------------------------
-constexpr int kSkUnits = 256;        // partial tiles the workspace holds
-constexpr int kSkMaxSplit = 4;
-constexpr int kSkMinSlices = 16;     // 64-wide K slices per part, at least
-
-struct SkPlan {
-  int n_dp, n_sk, S;  // whole tiles, split tiles, parts per split tile
-};
-
-__device__ __forceinline__ SkPlan sk_plan(int total, int ncu, int nk, bool enabled) {
-  SkPlan p{total, 0, 1};
-  const int rem = ncu > 0 ? total % ncu : 0;
-  if (!enabled || rem == 0) return p;
-  const int S = min(kSkMaxSplit, min(kSkUnits / rem, nk / kSkMinSlices));
-  if (S < 2) return p;
-  p.n_dp = total - rem;
-  p.n_sk = rem;
-  p.S = S;
-  return p;
 }
 
 // s_waitcnt with only the vector-memory counter constrained to <= n (n < 64)
@@ -537,82 +701,110 @@ __device__ __forceinline__ void gemm_tile(
   }
 }
 
-// skw: split-K workspace (kSkUnits fp32 256 x 256 tiles) or NULL (no split);
-// ncu: compute units of the device.  Workgroups [0, round8(n_dp)) run the
-// whole tiles, the next round8(n_sk S) the parts of the split tiles, each
-// range in contiguous runs per XCD.
+// Next work item of a persistent workgroup on XCD x: a whole tile (or work
+// unit) of run x, else (n_parts > 0) a split-K part from the shared counter;
+// returns the item (>= 0), -2 - p for split part p, or -1 when none is left.
+// Thread 0 takes it from the counters and hands it to the four waves through
+// the first word of the third B stage: between two items no copy and no real
+// fragment read touches that word (it lies in row 0, which only wave 0's
+// copies write, and wave 0 waited for all of its copies at the end of the
+// previous item; the next item first writes the third stage after its
+// prologue barrier, which every wave reaches only after reading the word).
+__device__ __forceinline__ int next_work(const int32_t* __restrict__ runs, int32_t* counters, int x,
+                                         int n_parts, uint16_t* smem) {
+  volatile int32_t* word =
+      reinterpret_cast<volatile int32_t*>(smem + (kRingA * kTileM + 2 * 256) * kBK);
+  if (threadIdx.x == 0) {
+    int code = runs[x] + atomicAdd(&counters[x], 1);
+    if (code >= runs[x + 1]) {
+      code = -1;
+      if (n_parts > 0) {
+        const int p = atomicAdd(&counters[kXcds], 1);
+        if (p < n_parts) code = -2 - p;
+      }
+    }
+    *word = code;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*word);
+}
+
+// Persistent: one workgroup per compute unit (see tile_table_kernel for the
+// runs).  tt: the tile-table workspace (mstart first); skw: split-K
+// workspace (kSkUnits fp32 256 x 256 tiles) or NULL (no split); ncu: compute
+// units of the device, as given to tile_table_kernel.
 template <bool kFused, typename OutT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
-    int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
+    int N, const int32_t* __restrict__ off, int32_t* __restrict__ tt, int G, int ntn,
     OutT* __restrict__ C, float* __restrict__ skw, int ncu) {
   constexpr int BN = 256;
   extern __shared__ __align__(16) uint16_t smem[];
+  const int32_t* mstart = tt;
+  const int32_t* runs = tt + tt_runs(G);
+  int32_t* counters = tt + tt_counters(G);
+  const int x = blockIdx.x % kXcds;
   if constexpr (kFused) {  // bundled order, no split
-    const int total = mstart[G];
-    const int nw8 = (total + 7) & ~7;
-    const int bid = blockIdx.x;
-    if (bid >= nw8) return;
-    const int L = xcd_run(bid, nw8);
-    if (L >= total) return;
-    const Unit u = unit_at(L, off, mstart, G, ntn);
-    Tile t{u.g, u.m0, u.row_end, 0};
-    if (u.count == 0) {
-      t.n0 = u.nt0 * (BN / 2);
-      const Tile2 tile = classify(t);
-      gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
-                                                            K, N, tile, 0, K / kBK, smem, C,
-                                                            nullptr);
-      return;
+    for (;;) {
+      const int L = next_work(runs, counters, x, 0, smem);
+      if (L < 0) return;
+      const Unit u = unit_at(L, off, mstart, G, ntn);
+      Tile t{u.g, u.m0, u.row_end, 0};
+      if (u.count == 0) {
+        t.n0 = u.nt0 * (BN / 2);
+        const Tile2 tile = classify(t);
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                              b_stride, K, N, tile, 0, K / kBK,
+                                                              smem, C, nullptr);
+        continue;
+      }
+      for (int s = 0; s < u.count; ++s) {
+        if (s > 0) __syncthreads();  // the previous tile's last LDS reads are done
+        t.n0 = (u.nt0 + s) * (BN / 2);
+        const Tile2 tile = classify(t);
+        if (tile.cls == 1)
+          gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                                b_stride, K, N, tile, 0, K / kBK,
+                                                                smem, C, nullptr);
+        else
+          gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                               b_stride, K, N, tile, 0, K / kBK,
+                                                               smem, C, nullptr);
+      }
     }
-    for (int s = 0; s < u.count; ++s) {
-      if (s > 0) __syncthreads();  // the previous tile's last LDS reads are done
-      t.n0 = (u.nt0 + s) * (BN / 2);
-      const Tile2 tile = classify(t);
-      if (tile.cls == 1)
-        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
-                                                              K, N, tile, 0, K / kBK, smem, C,
-                                                              nullptr);
-      else
-        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride,
-                                                             K, N, tile, 0, K / kBK, smem, C,
-                                                             nullptr);
+  } else {
+    const int nk_all = K / kBK;
+    const SkPlan plan = sk_plan(mstart[G] * ntn, ncu, nk_all, skw != nullptr);
+    const int n_parts = plan.n_sk * plan.S;
+    for (;;) {
+      const int code = next_work(runs, counters, x, n_parts, smem);
+      if (code == -1) return;
+      int L = code, ks0 = 0, nk = nk_all;
+      float* part_out = nullptr;
+      if (code < 0) {
+        const int u = -2 - code;
+        const int slot = u / plan.S, part = u - slot * plan.S;
+        L = plan.n_dp + slot;
+        ks0 = part * nk_all / plan.S;
+        nk = (part + 1) * nk_all / plan.S - ks0;
+        part_out = skw + static_cast<size_t>(u) * (kTileM * BN);
+      }
+      const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, BN));
+      if (tile.cls == 0) {
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                              b_stride, K, N, tile, ks0, nk,
+                                                              smem, C, part_out);
+      } else if (tile.cls == 1) {
+        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                              b_stride, K, N, tile, ks0, nk,
+                                                              smem, C, part_out);
+      } else {
+        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+                                                             b_stride, K, N, tile, ks0, nk,
+                                                             smem, C, part_out);
+      }
     }
-    return;
-  }
-  const int total = mstart[G] * ntn;
-  const int nk_all = K / kBK;
-  const SkPlan plan = sk_plan(total, ncu, nk_all, !kFused && skw != nullptr);
-  const int nw8 = (plan.n_dp + 7) & ~7;
-  const int bid = blockIdx.x;
-  int L, ks0 = 0, nk = nk_all;
-  float* part_out = nullptr;
-  if (bid < nw8) {
-    L = xcd_run(bid, nw8);
-    if (L >= plan.n_dp) return;
-  } else {
-    const int nu = plan.n_sk * plan.S;
-    const int nu8 = (nu + 7) & ~7;
-    if (bid - nw8 >= nu8) return;
-    const int u = xcd_run(bid - nw8, nu8);
-    if (u >= nu) return;
-    const int slot = u / plan.S, part = u - slot * plan.S;
-    L = plan.n_dp + slot;
-    ks0 = part * nk_all / plan.S;
-    nk = (part + 1) * nk_all / plan.S - ks0;
-    part_out = skw + static_cast<size_t>(u) * (kTileM * BN);
-  }
-  const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, kFused ? BN / 2 : BN));
-  if (tile.cls == 0) {
-    gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                          N, tile, ks0, nk, smem, C, part_out);
-  } else if (tile.cls == 1) {
-    gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                          N, tile, ks0, nk, smem, C, part_out);
-  } else {
-    gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1, b_stride, K,
-                                                         N, tile, ks0, nk, smem, C, part_out);
   }
 }
 
@@ -869,34 +1061,34 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 constexpr size_t kGemmLds = sizeof(uint16_t) * (kRingA * kTileM + kRingB * 256) * kBK;
 
-// grid: sum over groups of ceil(rows / 256) <= ceil(max_rows / 256) + G m-tiles
-unsigned gemm_grid(const SwigluArgs& s, int ntn) {
-  const int64_t mt = (s.max_rows + kTileM - 1) / kTileM + s.G;
-  return static_cast<unsigned>((mt * ntn + 7) & ~int64_t{7});
+// one workgroup per compute unit, kXcds at least (every run needs one)
+unsigned persistent_grid(int ncu) {
+  return static_cast<unsigned>(ncu >= kXcds ? ncu / kXcds * kXcds : kXcds);
 }
 
 hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ntn = (s.h + 127) / 128;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, s.mstart);
+  const int ncu = compute_units();
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, true, s.mstart,
+                                            s.mstart, ncu, s.d / kBK, false);
   auto kern = gemm_bf16_kernel<true, uint16_t>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-  kern<<<gemm_grid(s, ntn), kThreads, kGemmLds, stream>>>(
+  kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
-      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, 0);
+      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu);
   return hipGetLastError();
 }
 
 template <typename OutT>
 hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ntn = (s.d + 255) / 256;
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, 0, s.mstart);
+  const int ncu = compute_units();
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, false, s.mstart,
+                                            s.mstart, ncu, s.h / kBK, s.sk_ws != nullptr);
   auto kern = gemm_bf16_kernel<false, OutT>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-  // whole tiles, then at most kSkUnits parts of split tiles
-  const unsigned grid = gemm_grid(s, ntn) + (s.sk_ws ? kSkUnits : 0);
-  const int ncu = compute_units();
-  kern<<<grid, kThreads, kGemmLds, stream>>>(
+  kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
       static_cast<OutT*>(s.y), s.sk_ws, ncu);
@@ -909,7 +1101,8 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
 hipError_t gate_up_f32(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + kF32Tile - 1) / kF32Tile + s.G;
   const int ntn = static_cast<int>((s.h + kF32Tile - 1) / kF32Tile);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, false, s.mstart,
+                                            nullptr, 0, 0, false);
   gemm_f32_kernel<true><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.a), s.a_rows, s.a_div, static_cast<const float*>(s.w_gate),
       static_cast<const float*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h, s.group_offset,
@@ -920,7 +1113,8 @@ hipError_t gate_up_f32(const SwigluArgs& s, hipStream_t stream) {
 hipError_t down_f32(const SwigluArgs& s, hipStream_t stream) {
   const int64_t mt_ub = (s.max_rows + kF32Tile - 1) / kF32Tile + s.G;
   const int ntn = static_cast<int>((s.d + kF32Tile - 1) / kF32Tile);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, s.mstart);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kF32Tile, 0, false, s.mstart,
+                                            nullptr, 0, 0, false);
   gemm_f32_kernel<false><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.hid), nullptr, 1, static_cast<const float*>(s.w_down), nullptr,
       static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn, s.y,
@@ -953,6 +1147,8 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
 bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
 
 }  // namespace
+
+size_t tile_table_bytes(int G) { return sizeof(int32_t) * static_cast<size_t>(tt_entries(G)); }
 
 size_t split_k_workspace_bytes() {
   return sizeof(float) * static_cast<size_t>(kSkUnits) * kTileM * 256;

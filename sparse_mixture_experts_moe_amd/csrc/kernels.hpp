@@ -46,11 +46,12 @@ struct SwigluArgs {
   void* y;
   bool y_bf16;
   void* hid;        // [max_rows, h] in the compute dtype
-  int32_t* mstart;  // workspace: tile table, G + 1 entries
+  int32_t* mstart;  // workspace: tile table (tile_table_bytes(G))
   float* sk_ws;     // workspace: split-K partial tiles (down projection), or NULL
 };
 // bytes of the split-K partial-tile workspace of the down projection
 size_t split_k_workspace_bytes();
+size_t tile_table_bytes(int G);  // tile table, XCD runs and work counters of the grouped GEMMs
 // compute units of the current device (cached per device), 0 if unknown
 int compute_units();
 hipError_t launch_gate_up(const SwigluArgs& args, hipStream_t stream);
@@ -66,5 +67,11 @@ int64_t stats_blocks(int64_t T);
 hipError_t launch_balance_stats(const float* logits, const int32_t* count, int64_t T, int E, int k,
                                 float alpha, float* f, float* P, float* loss, float* zloss,
                                 float* part, float* zpart, hipStream_t stream);
+
+// measured device ceilings (not part of the layer)
+hipError_t launch_mfma_ceiling(const void* src, int blocks, int iters, float* out,
+                               hipStream_t stream);
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, int blocks, uint32_t* out,
+                               hipStream_t stream);
 
 }  // namespace moe

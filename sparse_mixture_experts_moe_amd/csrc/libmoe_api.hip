@@ -247,7 +247,7 @@ moe_status_t check_experts(const char* fn, int dt, int d, int h, int G, int64_t 
   return MOE_OK;
 }
 
-size_t tile_table_bytes(int G) { return align256(sizeof(int32_t) * (static_cast<size_t>(G) + 1)); }
+size_t tile_table_bytes(int G) { return align256(moe::tile_table_bytes(G)); }
 
 }  // namespace
 
@@ -393,6 +393,24 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
   return hip_status(moe::launch_balance_stats(logits, expert_count, T, E, k, alpha, f, P, loss,
                                               zloss, part, zpart, as_stream(stream)),
                     "moe_balance_stats");
+}
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_probe_mfma_bf16(const void* src, int blocks, int iters, float* out,
+                                 void* stream) {
+  if (blocks < 1 || iters < 1) return fail(MOE_EINVAL, "moe_probe_mfma_bf16: blocks, iters >= 1");
+  if (!src || !out) return fail(MOE_EINVAL, "moe_probe_mfma_bf16: NULL pointer");
+  return hip_status(moe::launch_mfma_ceiling(src, blocks, iters, out, as_stream(stream)),
+                    "moe_probe_mfma_bf16");
+}
+
+moe_status_t moe_probe_read(const void* buf, size_t bytes, int blocks, uint32_t* out,
+                            void* stream) {
+  if (blocks < 1 || bytes < 16 || bytes % 16 != 0)
+    return fail(MOE_EINVAL, "moe_probe_read: need blocks >= 1 and bytes a positive multiple of 16");
+  if (!buf || !out) return fail(MOE_EINVAL, "moe_probe_read: NULL pointer");
+  return hip_status(moe::launch_read_ceiling(buf, bytes, blocks, out, as_stream(stream)),
+                    "moe_probe_read");
 }
 
 }  // extern "C"

@@ -160,3 +160,13 @@ def test_combine_and_stats_reject():
                                None) == L.MOE_EUNSUPPORTED
     assert C.moe_balance_stats(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
                                None) == L.MOE_EINVAL
+
+
+def test_probes_reject():
+    assert C.moe_probe_mfma_bf16(FAKE, 0, 10, FAKE, None) == L.MOE_EINVAL
+    assert C.moe_probe_mfma_bf16(FAKE, 4, 0, FAKE, None) == L.MOE_EINVAL
+    assert C.moe_probe_mfma_bf16(None, 4, 10, FAKE, None) == L.MOE_EINVAL
+    assert C.moe_probe_read(FAKE, 24, 4, FAKE, None) == L.MOE_EINVAL and "multiple of 16" in _err()
+    assert C.moe_probe_read(FAKE, 0, 4, FAKE, None) == L.MOE_EINVAL
+    assert C.moe_probe_read(FAKE, 1024, 0, FAKE, None) == L.MOE_EINVAL
+    assert C.moe_probe_read(FAKE, 1024, 4, None, None) == L.MOE_EINVAL
