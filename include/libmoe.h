@@ -213,13 +213,14 @@ moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
  *   group_offset[G] untouched).
  * moe_expert_down:    y[r, :] = hid[r, :] . w_down[g]^T; y [max_rows, d] in
  *   y_dt.
- * Workspace: moe_expert_group_workspace(G) bytes for moe_expert_gate_up (a
- * tile table); moe_expert_down_workspace(G) bytes for moe_expert_down (the
- * tile table and 64 MiB of fp32 partial tiles: when the last round of output
- * tiles would leave compute units idle, those tiles are split along K and
- * their parts added in a fixed order afterwards, so results stay
- * deterministic).  The workspace contents need no initialisation and are
- * dead after the call. */
+ * Workspace: moe_expert_group_workspace(G) bytes for moe_expert_gate_up,
+ * moe_expert_down_workspace(G) bytes for moe_expert_down (today the same
+ * size): a tile table and 64 MiB of fp32 partial sums.  Work that would leave
+ * compute units idle is split along K (the last round of output tiles of a
+ * long-K GEMM; a few-row group whose weight slabs alone are too few waves,
+ * such as a shared expert at decode) and the parts are added in a fixed order
+ * afterwards, so results stay deterministic.  The workspace contents need no
+ * initialisation and are dead after the call. */
 size_t moe_expert_group_workspace(int G);
 size_t moe_expert_down_workspace(int G);
 moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,

@@ -28,6 +28,8 @@
 //   together on one XCD's L2 and every XCD stays busy to the end.
 // fp32 path: a plain LDS-tiled FMA kernel, one workgroup per tile, in
 // contiguous runs per XCD.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -476,7 +478,12 @@ __device__ __forceinline__ void gemm_tile(
   uint16_t* As = smem;                         // [SA][kTileM * kBK]
   uint16_t* Bs = smem + SA * kTileM * kBK;     // [SB][BN * kBK]
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // the thread index is made opaque here so that nothing derived from it is
+  // hoisted out of the persistent loop around this tile (such values would
+  // stay live through the epilogue and push accumulators out to scratch)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid % kWave, wave = tid / kWave;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = WM == 1 ? 0 : (wave & 1), wn = WM == 1 ? wave : (wave >> 1);
   // Copy j of a wave covers the 8 tile rows 8 (4 j + wave) + 0..7: lane l
@@ -858,14 +865,22 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(const float* __restrict_
 // operands, which leaves the contraction unchanged: MFMA step i of chunk c
 // uses k = 64c + 32i + 8 (lane/16) + 0..7.  Groups with more than 16*TBN rows
 // loop over row blocks.
+// When the slabs alone are too few waves to keep the memory system busy (a
+// shared expert: one group), K is split into nsplit parts (blockIdx.y): part
+// p covers chunks [p nchunk / nsplit, (p + 1) nchunk / nsplit) and writes its
+// fp32 sums (fused: gate columns [0, N), up columns [N, 2N)) to
+// part[(p * part_rows + row) * cols + col]; skinny_reduce_kernel adds the
+// parts in part order (and applies SiLU * up) afterwards.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyBatch = 4;   // 64-wide K chunks loaded per step
+constexpr int kSkinnyWaves = 768;  // fewer waves cost latency, more cost partial-sum traffic (measured)
 
 template <bool kFused, int TBN, typename OutT>
 __global__ __launch_bounds__(64) void skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int64_t w_stride, int K,
-    int N, const int32_t* __restrict__ off, int nslices, OutT* __restrict__ C) {
+    int N, const int32_t* __restrict__ off, int nslices, OutT* __restrict__ C,
+    float* __restrict__ part, int part_rows) {
   constexpr int NBW = 4;                            // 16-row weight blocks per wave
   constexpr int NOUT = kFused ? 32 : 64;            // output columns per wave
   const int g = blockIdx.x / nslices;
@@ -904,8 +919,10 @@ __global__ __launch_bounds__(64) void skinny_kernel(
 #pragma unroll
       for (int tb = 0; tb < TBN; ++tb) acc[b][tb] = f32x4{};
 
-    const int nchunk = K / 64;
-    int c = 0;
+    const int nchunk_all = K / 64;
+    const int c_begin = static_cast<int>(blockIdx.y) * nchunk_all / static_cast<int>(gridDim.y);
+    const int nchunk = (static_cast<int>(blockIdx.y) + 1) * nchunk_all / static_cast<int>(gridDim.y);
+    int c = c_begin;
     // kSkinnyBatch chunks per step: all loads first, then the MFMAs
     for (; c + kSkinnyBatch <= nchunk; c += kSkinnyBatch) {
       bf16x8 wf[kSkinnyBatch][NBW][2], xf[kSkinnyBatch][TBN][2];
@@ -962,6 +979,22 @@ __global__ __launch_bounds__(64) void skinny_kernel(
     }
 
     // D[weight row][token]: lane holds token column l16 and weight rows 4*(lane/16)+j
+    if (part) {  // fp32 partial sums of this K part, four consecutive columns per store
+      const int cols = kFused ? 2 * N : N;
+#pragma unroll
+      for (int tb = 0; tb < TBN; ++tb) {
+        const int row = rb + 16 * tb + l16;
+        if (row >= r1) continue;
+        float* prow = part + (static_cast<int64_t>(blockIdx.y) * part_rows + row) * cols;
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const int n = n0 + 16 * (kFused && b >= NBW / 2 ? b - NBW / 2 : b) + (lane >> 4) * 4;
+          if (n >= N) continue;  // N % 4 == 0: a run of four is whole
+          *reinterpret_cast<f32x4*>(prow + (kFused && b >= NBW / 2 ? N : 0) + n) = acc[b][tb];
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int tb = 0; tb < TBN; ++tb) {
       const int row = rb + 16 * tb + l16;
@@ -982,6 +1015,40 @@ __global__ __launch_bounds__(64) void skinny_kernel(
           }
         }
     }
+  }
+}
+
+// Adds the nsplit K parts of the skinny kernel in part order for rows below
+// off[G]; each thread four consecutive columns of one row.  Fused: SiLU of the
+// gate sum times the up sum.
+template <bool kFused, typename OutT>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part,
+                                                            int nsplit, int part_rows,
+                                                            const int32_t* __restrict__ off,
+                                                            int G, int N,
+                                                            OutT* __restrict__ C) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int q = N / 4;
+  const int64_t row = i / q;
+  const int col = static_cast<int>(i - row * q) * 4;
+  if (row >= off[G]) return;
+  const int cols = kFused ? 2 * N : N;
+  f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, u = a;
+  for (int p = 0; p < nsplit; ++p) {
+    const float* src = part + (static_cast<int64_t>(p) * part_rows + row) * cols + col;
+    a += *reinterpret_cast<const f32x4*>(src);
+    if constexpr (kFused) u += *reinterpret_cast<const f32x4*>(src + N);
+  }
+  f32x4 v = a;
+  if constexpr (kFused) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = silu_f32(a[e]) * u[e];
+  }
+  OutT* dst = C + row * N + col;
+  if constexpr (sizeof(OutT) == 2) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = v;
   }
 }
 
@@ -1127,18 +1194,39 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
                        int a_div, const void* w0, const void* w1, void* out, hipStream_t stream) {
   const int per_wave = kFused ? 32 : 64;
   const int nslices = (N + per_wave - 1) / per_wave;
-  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(s.G) * nslices);
+  const int64_t waves = static_cast<int64_t>(s.G) * nslices;
   const int64_t mean = (s.max_rows + s.G - 1) / s.G;
   const int64_t wstride = static_cast<int64_t>(N) * K;
+  // split K when the slabs are too few waves (at least kSkinnyBatch chunks
+  // per part, partial sums within the split-K workspace)
+  int nsplit = 1;
+  if (s.sk_ws && waves < kSkinnyWaves) {
+    const int64_t cols = kFused ? 2 * N : N;
+    const int64_t cap = static_cast<int64_t>(split_k_workspace_bytes() / sizeof(float)) /
+                        (s.max_rows * cols);
+    int64_t want = (kSkinnyWaves + waves - 1) / waves;
+    want = std::min<int64_t>(want, (K / 64) / kSkinnyBatch);
+    want = std::min<int64_t>(want, cap);
+    nsplit = static_cast<int>(std::max<int64_t>(want, 1));
+  }
+  float* part = nsplit > 1 ? s.sk_ws : nullptr;
+  const dim3 grid(static_cast<unsigned>(waves), static_cast<unsigned>(nsplit));
+  const int part_rows = static_cast<int>(s.max_rows);
 #define MOE_SKINNY(TBN)                                                                    \
   skinny_kernel<kFused, TBN, OutT><<<grid, 64, 0, stream>>>(                               \
       static_cast<const uint16_t*>(a), a_rows, a_div, static_cast<const uint16_t*>(w0),    \
       static_cast<const uint16_t*>(w1), wstride, K, N, s.group_offset, nslices,            \
-      static_cast<OutT*>(out))
+      static_cast<OutT*>(out), part, part_rows)
   if (mean <= 16) MOE_SKINNY(1);
   else if (mean <= 32) MOE_SKINNY(2);
   else MOE_SKINNY(4);
 #undef MOE_SKINNY
+  if (part) {
+    const int64_t threads = s.max_rows * (N / 4);
+    skinny_reduce_kernel<kFused, OutT><<<static_cast<unsigned>((threads + 255) / 256), 256, 0,
+                                         stream>>>(part, nsplit, part_rows, s.group_offset, s.G,
+                                                   N, static_cast<OutT*>(out));
+  }
   return hipGetLastError();
 }
 

@@ -251,7 +251,9 @@ size_t tile_table_bytes(int G) { return align256(moe::tile_table_bytes(G)); }
 
 }  // namespace
 
-size_t moe_expert_group_workspace(int G) { return G < 1 ? 0 : tile_table_bytes(G); }
+size_t moe_expert_group_workspace(int G) {
+  return G < 1 ? 0 : tile_table_bytes(G) + moe::split_k_workspace_bytes();
+}
 
 size_t moe_expert_down_workspace(int G) {
   return G < 1 ? 0 : tile_table_bytes(G) + moe::split_k_workspace_bytes();
@@ -273,9 +275,9 @@ moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
   if (!a || !w_gate || !w_up || !hid) return fail(MOE_EINVAL, "moe_expert_gate_up: NULL pointer");
   if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "moe_expert_gate_up: a_rows_div < 1");
-  if (ws_bytes < tile_table_bytes(G) || !ws)
+  if (ws_bytes < moe_expert_group_workspace(G) || !ws)
     return fail(MOE_EWORKSPACE, "moe_expert_gate_up: workspace %zu < %zu bytes", ws_bytes,
-                tile_table_bytes(G));
+                moe_expert_group_workspace(G));
   moe::SwigluArgs s{};
   s.a = a;
   s.bf16 = dt == MOE_BF16;
@@ -290,6 +292,7 @@ moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
   s.w_up = w_up;
   s.hid = hid;
   s.mstart = static_cast<int32_t*>(ws);
+  s.sk_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + tile_table_bytes(G));
   return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up");
 }
 

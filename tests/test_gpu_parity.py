@@ -187,7 +187,12 @@ def test_permute_empty():
     ([2000, 1500], 192, 256),
     # 12 output tiles, fewer than the compute units: the down projection
     # splits them along K (two parts of 16 slices) and adds the parts
-    ([300, 40, 517], 512, 2048)])
+    ([300, 40, 517], 512, 2048),
+    # few-row groups whose weight slabs are too few waves: the skinny kernel
+    # splits K (one group: 8 parts for gate/up, 2 for down; three groups with
+    # an empty one and 16 < rows: 4 parts for gate/up) and adds the parts
+    ([60], 2048, 512),
+    ([17, 0, 29], 1024, 256)])
 def test_expert_swiglu_groups(sizes, d, h, dt):
     from sparse_mixture_experts_moe_amd import _lib
     _say(f"[case] swiglu groups={sizes} d={d} h={h} {dt}")
