@@ -38,20 +38,19 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk + wave * 256;
   int my_e[4], my_r[4];
   const uint64_t lt = lanemask_lt();
+  const int ebits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t p = base + s * 64 + lane;
     const bool valid = p < R;
     const int e = valid ? idx[p] : -1;
-    // lanes holding the same expert: peel off one distinct value per pass
-    uint64_t todo = __ballot(valid);
-    uint64_t mine = 0;
-    while (todo) {
-      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t m = __ballot(valid && e == el);
-      if (e == el) mine = m;
-      todo &= ~m;
+    // lanes holding the same expert: the lanes that agree with this one on
+    // every bit of the expert id (one ballot per bit, constant time)
+    uint64_t mine = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      mine &= bit ? m : ~m;
     }
     int r = 0;
     if (valid) {

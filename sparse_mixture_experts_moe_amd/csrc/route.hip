@@ -35,9 +35,38 @@ constexpr int kThreads = 256;
 constexpr int kLanesPerTok = kThreads / kTokPerBlock;  // 8
 constexpr int kMaxSplits = 8;  // d-splits of the router GEMM, at most
 
-// (v, i) ranks before (bv, bi): larger key first, lower index on equal keys.
-__device__ __forceinline__ bool key_before(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// The selection order of (key v, expert i) as one unsigned 64-bit number:
+// larger keys first, equal keys (-0 and +0 included) to the lower index.  The
+// high word maps the float's bits to an order-preserving unsigned integer
+// (after -0 -> +0), the low word is ~i, so the larger number ranks first.
+// Every finite or infinite key gives a number above 0, which stands for "no
+// candidate".
+__device__ __forceinline__ uint64_t rank_code(float v, int i) {
+  const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~i);
+}
+
+// v from the lane that DPP control kCtrl selects within the lane's row.
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v)), kCtrl, 0xF,
+                                          0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v >> 32)), kCtrl,
+                                          0xF, 0xF, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Maximum over each group of eight consecutive lanes: swap neighbours, then
+// pairs (quad permutations), then mirror each half-row, which pairs every lane
+// of one quad with one of the other.
+__device__ __forceinline__ uint64_t max8_u64(uint64_t v) {
+  uint64_t o = dpp_u64<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);           // quad_perm [2, 3, 0, 1]
+  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v);          // row_half_mirror
+  return o > v ? o : v;
 }
 
 // Router GEMM, bf16: a workgroup of four waves takes 128 tokens (32 per wave)
@@ -173,19 +202,24 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   const int ldl = E + 1;                        // padded row of the logits tile
   float* lg = lds;                              // [32][E+1]
   float* sb = lds + kTokPerBlock * ldl;         // [E] selection bias
-  int* sel = reinterpret_cast<int*>(sb + E);    // [32][k] chosen experts
+  float* lb = sb + E;                           // [E] logit bias
+  int* sel = reinterpret_cast<int*>(lb + E);    // [32][k] chosen experts
 
   const int tid = threadIdx.x;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlock;
   const int ntok = static_cast<int>(T - t0 < kTokPerBlock ? T - t0 : kTokPerBlock);
 
-  for (int e = tid; e < E; e += kThreads) sb[e] = select_bias ? select_bias[e] : 0.0f;
+  for (int e = tid; e < E; e += kThreads) {
+    sb[e] = select_bias ? select_bias[e] : 0.0f;
+    lb[e] = logit_bias ? logit_bias[e] : 0.0f;
+  }
+  __syncthreads();
   if (mode == 1) {
     // the tile's logits are contiguous in every partial: all KS partials of a
     // pass are loaded together, then added in split order
     const int n = ntok * E;
     const int64_t base = t0 * E;
-    constexpr int kPer = 8;  // logits per thread per pass
+    constexpr int kPer = 16;  // logits per thread per pass (one pass for E <= 128)
     for (int i0 = tid; i0 < n; i0 += kThreads * kPer) {
       float v[kMaxSplits][kPer];
 #pragma unroll
@@ -204,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
         for (int sp = 1; sp < kMaxSplits; ++sp)
           if (sp < KS) acc += v[sp][u];
         const int t = i / E, e = i % E;
-        const float l = acc + (logit_bias ? logit_bias[e] : 0.0f);
+        const float l = acc + lb[e];
         logits[base + i] = l;
         lg[t * ldl + e] = l;
       }
@@ -221,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
       const float* wr = wf + static_cast<int64_t>(e) * d;
       float acc = 0.0f;
       for (int c = 0; c < d; ++c) acc = fmaf(xr[c], wr[c], acc);
-      v = acc + (logit_bias ? logit_bias[e] : 0.0f);
+      v = acc + lb[e];
       logits[g] = v;
     }
     lg[t * ldl + e] = v;
@@ -234,41 +268,26 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   const bool active = tt < ntok;
   const float* row = lg + tt * ldl;
   constexpr int kKeys = KK;
-  float key[kKeys];
+  uint64_t code[kKeys];  // 0: no candidate
 #pragma unroll
   for (int u = 0; u < kKeys; ++u) {
     const int e = q + u * kLanesPerTok;
-    key[u] = (active && e < E) ? (select_bias ? __fadd_rn(row[e], sb[e]) : row[e])
-                               : -__builtin_inff();
+    code[u] = (active && e < E)
+                  ? rank_code(select_bias ? __fadd_rn(row[e], sb[e]) : row[e], e)
+                  : uint64_t{0};
   }
-  float pv = __builtin_inff();
-  int pi = -1;
+  // pass j: the first candidate ranking after pass j-1's winner (branch-free)
+  uint64_t prev = ~uint64_t{0};
   for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
     for (int u = 0; u < kKeys; ++u) {
-      const int e = q + u * kLanesPerTok;
-      const float v = key[u];
-      // candidates rank strictly after the previous winner
-      const bool after_prev = v < pv || (v == pv && e > pi);
-      if (e < E && after_prev && key_before(v, e, bv, bi)) {
-        bv = v;
-        bi = e;
-      }
+      const uint64_t c = code[u] < prev ? code[u] : uint64_t{0};
+      best = c > best ? c : best;
     }
-#pragma unroll
-    for (int m = 1; m < kLanesPerTok; m <<= 1) {
-      const float ov = __shfl_xor(bv, m, kLanesPerTok);
-      const int oi = __shfl_xor(bi, m, kLanesPerTok);
-      if (key_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    pv = bv;
-    pi = bi;
-    if (active && q == 0) sel[tt * k + j] = bi;
+    best = max8_u64(best);
+    prev = best;
+    if (active && q == 0) sel[tt * k + j] = static_cast<int>(~static_cast<uint32_t>(best));
   }
   __syncthreads();
 
@@ -303,7 +322,7 @@ int route_splits(int64_t T, int d, int E) {
 }  // namespace
 
 size_t route_lds_bytes(int E, int k) {
-  return sizeof(float) * (static_cast<size_t>(kTokPerBlock) * (E + 1) + E) +
+  return sizeof(float) * (static_cast<size_t>(kTokPerBlock) * (E + 1) + 2 * E) +
          sizeof(int) * static_cast<size_t>(kTokPerBlock) * k;
 }
 
