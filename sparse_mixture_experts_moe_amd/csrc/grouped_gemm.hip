@@ -854,8 +854,8 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // Skinny bf16 kernel for groups of a few rows (decode-shaped batches): the
 // weights are streamed once from HBM and dominate the bytes, so one wave per
-// workgroup walks a 64-row slab of the weight matrix (fused: 32 gate rows and
-// the matching 32 up rows) along K, with the weight rows as the 16-row A
+// workgroup walks one or a few consecutive 64-row slabs of one group's weight
+// matrix (fused: 32 gate rows and the matching 32 up rows) along K, with the weight rows as the 16-row A
 // operand of v_mfma_f32_16x16x32_bf16 and up to TBN blocks of 16 token rows as
 // the B operand.  No LDS: per 64-wide K chunk each lane loads two 16-byte
 // pieces of a weight row, at k = 64c + 8 (lane/16) and 32 later, so that every
@@ -874,21 +874,29 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyBatch = 4;   // 64-wide K chunks loaded per step
 constexpr int kSkinnyWaves = 768;  // fewer waves cost latency, more cost partial-sum traffic (measured)
+// Past about 12 waves per compute unit more waves gain nothing, and a longer
+// wave amortizes its start and the last partial round of waves: a launch of
+// more slabs gives each wave slabs / kSkinnyWavesMax consecutive slabs
+// (measured on the decode shapes: 4 per wave for the down projection's 12288
+// slabs, 2 for gate/up's 8192, 10% and 3% faster than one).
+constexpr int kSkinnyWavesMax = 3072;
 
 template <bool kFused, int TBN, typename OutT>
 __global__ __launch_bounds__(64) void skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int64_t w_stride, int K,
     int N, const int32_t* __restrict__ off, int nslices, OutT* __restrict__ C,
-    float* __restrict__ part, int part_rows) {
+    float* __restrict__ part, int part_rows, int spw) {
   constexpr int NBW = 4;                            // 16-row weight blocks per wave
   constexpr int NOUT = kFused ? 32 : 64;            // output columns per wave
-  const int g = blockIdx.x / nslices;
-  const int slice = blockIdx.x - g * nslices;
+  const int nsg = (nslices + spw - 1) / spw;  // wave = spw consecutive slabs of one group
+  const int g = blockIdx.x / nsg;
+  const int sg = blockIdx.x - g * nsg;
   const int r0 = off[g], r1 = off[g + 1];
   if (r0 >= r1) return;
   const int lane = threadIdx.x;
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
+  for (int slice = sg * spw; slice < nslices && slice < (sg + 1) * spw; ++slice) {
   const int n0 = slice * NOUT;
 
   const uint16_t* wrow[NBW];
@@ -1016,6 +1024,7 @@ __global__ __launch_bounds__(64) void skinny_kernel(
         }
     }
   }
+}  // slabs of this wave
 }
 
 // Adds the nsplit K parts of the skinny kernel in part order for rows below
@@ -1210,13 +1219,15 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
     nsplit = static_cast<int>(std::max<int64_t>(want, 1));
   }
   float* part = nsplit > 1 ? s.sk_ws : nullptr;
-  const dim3 grid(static_cast<unsigned>(waves), static_cast<unsigned>(nsplit));
+  const int spw = nsplit > 1 ? 1 : static_cast<int>(std::max<int64_t>(1, waves / kSkinnyWavesMax));
+  const dim3 grid(static_cast<unsigned>(s.G * ((nslices + spw - 1) / spw)),
+                  static_cast<unsigned>(nsplit));
   const int part_rows = static_cast<int>(s.max_rows);
 #define MOE_SKINNY(TBN)                                                                    \
   skinny_kernel<kFused, TBN, OutT><<<grid, 64, 0, stream>>>(                               \
       static_cast<const uint16_t*>(a), a_rows, a_div, static_cast<const uint16_t*>(w0),    \
       static_cast<const uint16_t*>(w1), wstride, K, N, s.group_offset, nslices,            \
-      static_cast<OutT*>(out), part, part_rows)
+      static_cast<OutT*>(out), part, part_rows, spw)
   if (mean <= 16) MOE_SKINNY(1);
   else if (mean <= 32) MOE_SKINNY(2);
   else MOE_SKINNY(4);

@@ -192,7 +192,10 @@ def test_permute_empty():
     # splits K (one group: 8 parts for gate/up, 2 for down; three groups with
     # an empty one and 16 < rows: 4 parts for gate/up) and adds the parts
     ([60], 2048, 512),
-    ([17, 0, 29], 1024, 256)])
+    ([17, 0, 29], 1024, 256),
+    # many few-row groups: the down projection's 95 x 65 slabs go two to a
+    # wave, the last wave of each group with one
+    ([3] * 47 + [0] + [3] * 48, 4160, 512)])
 def test_expert_swiglu_groups(sizes, d, h, dt):
     from sparse_mixture_experts_moe_amd import _lib
     _say(f"[case] swiglu groups={sizes} d={d} h={h} {dt}")
