@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: chosen per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial-shared", action="store_true",
+                    help="run the shared experts in line on the layer's stream instead of "
+                         "overlapping them on a second stream")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the warmup, copy a buffer of this many MiB three times with a "
                          "plain device-to-device copy, so that a counter run can scale its byte "
@@ -182,6 +185,7 @@ def main():
     inp = generate(cfg)
     print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     layer = layer_from_inputs(inp, args.gather)
+    layer.overlap_shared = not args.serial_shared
     x = to_device(inp["x"])
     torch.cuda.synchronize()
 
@@ -230,6 +234,8 @@ def main():
     # Phase breakdown: a separate pass of the same K steps with an event after
     # every library call (outside the timed region; each phase includes the
     # few microseconds its opening event costs)
+    # (the shared experts, which the timed steps overlap with the routed path
+    # on a second stream, run in line here so that they get a phase of their own)
     marks = []
 
     def mark(name):
@@ -237,12 +243,15 @@ def main():
         ev.record(stream)
         marks[-1].append((name, ev))
 
+    overlap = layer.overlap_shared
+    layer.overlap_shared = False
     for _ in range(args.steps):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         marks.append([("start", ev0)])
         layer(x, mark=mark)
     torch.cuda.synchronize()
+    layer.overlap_shared = overlap
     phases = {}
     for step in marks:
         for (_, a), (name, b) in zip(step[:-1], step[1:]):
@@ -322,7 +331,8 @@ def main():
         "data": "synthetic (seeded normal inputs and random-init weights of the workload's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
-                   "gather": args.gather, "parallelism": "none (1 GPU)"},
+                   "gather": args.gather, "parallelism": "none (1 GPU)",
+                   "shared_overlap": bool(cfg.n_shared and layer.overlap_shared)},
         "roofline": roof,
         "measured_ceilings": ceil,
         "expert_gemm_mfma_util": expert_flops / (expert_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

@@ -1,7 +1,11 @@
 """MoELayer: one forward pass of the sparse MoE feed-forward layer as five
-libmoe calls on one stream (route, permute, routed experts [+ shared experts],
-combine, balance statistics).  Buffers are allocated on the first call for a
-token count and reused afterwards, so repeated calls allocate nothing.
+libmoe calls (route, permute, routed experts [+ shared experts], combine,
+balance statistics).  Buffers are allocated on the first call for a token
+count and reused afterwards, so repeated calls allocate nothing.
+
+The shared experts depend on x alone, so by default they run on a second
+stream (default priority) from the start of the call, overlapping the routing
+and the routed experts; the combine waits for them.
 
 The layer output excludes the residual ("Every parameter, every token",
 section "The gating network": the weighted sum is added back to the residual
@@ -17,13 +21,15 @@ from . import _lib
 
 class MoELayer:
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
-                 select_bias=None, capacity=-1, alpha=0.01, gather="fused"):
+                 select_bias=None, capacity=-1, alpha=0.01, gather="fused",
+                 overlap_shared=True):
         """Weights are device tensors: w_router [E, d]; w_gate, w_up [E, h, d];
         w_down [E, d, h]; ``shared`` is None or (gate [Hs, d], up [Hs, d],
         down [d, Hs]) with the shared experts concatenated along the hidden
         axis.  ``capacity`` < 0 means unlimited.  ``gather`` is "fused" (the
         first expert GEMM reads token rows through the permutation) or "copy"
-        (moe_permute writes an expert-ordered copy of x first)."""
+        (moe_permute writes an expert-ordered copy of x first).  ``overlap_shared``
+        runs the shared experts on a second stream."""
         if gather not in ("fused", "copy"):
             raise ValueError("gather must be 'fused' or 'copy'")
         self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
@@ -38,7 +44,9 @@ class MoELayer:
         self.capacity = int(capacity)
         self.alpha = alpha
         self.gather = gather
+        self.overlap_shared = overlap_shared
         self._bufs = {}
+        self._side = {}
 
     def _buffers(self, x):
         T = x.shape[0]
@@ -93,6 +101,23 @@ class MoELayer:
         T = x.shape[0]
         k, E = self.k, self.E
         mark = mark or (lambda name: None)
+        main = stream if stream is not None else torch.cuda.current_stream(x.device)
+        shared_y = shared_done = None
+        if self.shared is not None and self.overlap_shared:
+            # the side stream starts once everything enqueued so far on the
+            # main stream (x, and the previous call's combine, which reads
+            # shared_y) is done
+            side = self._side.get(x.device)
+            if side is None:
+                side = self._side[x.device] = torch.cuda.Stream(x.device)
+            x_ready = torch.cuda.Event()
+            x_ready.record(main)
+            side.wait_event(x_ready)
+            sg, su, sd = self.shared
+            shared_y = _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd,
+                                              y=b["shared_y"], ws=b["shared_ws"], stream=side)
+            shared_done = torch.cuda.Event()
+            shared_done.record(side)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
                        ws=b["route_ws"], stream=stream)
@@ -114,12 +139,13 @@ class MoELayer:
         _lib.moe_expert_down(b["hid"], b["expert_offset"], T * k, self.w_down, y=b["y_perm"],
                              ws=b["table_ws"], stream=stream)
         mark("down")
-        shared_y = None
-        if self.shared is not None:
+        if self.shared is not None and not self.overlap_shared:
             sg, su, sd = self.shared
             shared_y = _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd,
                                               y=b["shared_y"], ws=b["shared_ws"], stream=stream)
             mark("shared")
+        if shared_done is not None:
+            main.wait_event(shared_done)
         _lib.moe_combine(b["y_perm"], b["pair_row"], b["topk_gate"], shared_y, out=b["out"],
                          stream=stream)
         mark("combine")

@@ -292,3 +292,19 @@ def test_layer_full_size(name):
     tokens = None if cfg.T <= 64 else _sample_tokens(cfg.T)
     errs = check_layer(inp, res, tokens=tokens)
     _say(f"[ok] full-size {name}: {errs}")
+
+
+def test_shared_overlap_matches_serial():
+    """The shared experts on a second stream give the same bits as in line."""
+    inp = generate(SMALL["finegrained_small"])
+    _say("[case] shared experts overlapped vs in line")
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    outs = []
+    for overlap in (True, False, True):
+        layer.overlap_shared = overlap
+        for _ in range(3):  # back-to-back calls reuse the buffers
+            res = layer(x)
+        torch.cuda.synchronize()
+        outs.append(host(res["out"]).copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
