@@ -47,28 +47,6 @@ __device__ __forceinline__ uint64_t rank_code(float v, int i) {
   return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~i);
 }
 
-// v from the lane that DPP control kCtrl selects within the lane's row.
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v)), kCtrl, 0xF,
-                                          0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v >> 32)), kCtrl,
-                                          0xF, 0xF, false);
-  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-}
-
-// Maximum over each group of eight consecutive lanes: swap neighbours, then
-// pairs (quad permutations), then mirror each half-row, which pairs every lane
-// of one quad with one of the other.
-__device__ __forceinline__ uint64_t max8_u64(uint64_t v) {
-  uint64_t o = dpp_u64<0xB1>(v);  // quad_perm [1, 0, 3, 2]
-  v = o > v ? o : v;
-  o = dpp_u64<0x4E>(v);           // quad_perm [2, 3, 0, 1]
-  v = o > v ? o : v;
-  o = dpp_u64<0x141>(v);          // row_half_mirror
-  return o > v ? o : v;
-}
-
 // Router GEMM, bf16: a workgroup of four waves takes 128 tokens (32 per wave)
 // and every expert, padded to NB blocks of 32 rows (rows past E repeat row
 // E-1; their results are not stored).  K (= d) goes in chunks of 64, S =
@@ -220,7 +198,43 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const int n = ntok * E;
     const int64_t base = t0 * E;
     constexpr int kPer = 16;  // logits per thread per pass (one pass for E <= 128)
-    for (int i0 = tid; i0 < n; i0 += kThreads * kPer) {
+    // 16-byte accesses need E % 4 == 0 (four logits then share a row and
+    // every partial stays 16-byte aligned) and 16-byte aligned buffers
+    const bool vec = (E & 3) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+    if (vec) {
+      // thread j of a pass takes logits 4j .. 4j+3
+      constexpr int kPer4 = kPer / 4;
+      const int n4 = n / 4;
+      for (int j0 = tid; j0 < n4; j0 += kThreads * kPer4) {
+        f32x4 v[kMaxSplits][kPer4];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+#pragma unroll
+          for (int u = 0; u < kPer4; ++u) {
+            const int j = j0 + u * kThreads;
+            v[sp][u] = (sp < KS && j < n4)
+                           ? *reinterpret_cast<const f32x4*>(part + static_cast<int64_t>(sp) * T * E +
+                                                             base + 4 * j)
+                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+#pragma unroll
+        for (int u = 0; u < kPer4; ++u) {
+          const int j = j0 + u * kThreads;
+          if (j >= n4) continue;
+          f32x4 acc = v[0][u];
+#pragma unroll
+          for (int sp = 1; sp < kMaxSplits; ++sp)
+            if (sp < KS) acc += v[sp][u];
+          const int t = (4 * j) / E, e = (4 * j) % E;
+          const f32x4 l = acc + f32x4{lb[e], lb[e + 1], lb[e + 2], lb[e + 3]};
+          *reinterpret_cast<f32x4*>(logits + base + 4 * j) = l;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) lg[t * ldl + e + c] = l[c];
+        }
+      }
+    }
+    for (int i0 = tid; !vec && i0 < n; i0 += kThreads * kPer) {
       float v[kMaxSplits][kPer];
 #pragma unroll
       for (int sp = 0; sp < kMaxSplits; ++sp)

@@ -14,7 +14,9 @@
 // accumulated over the two rounds, giving partials[b][E].  One workgroup then
 // adds the partials: 1024 threads sum fixed segments of blocks per expert in
 // fp64, and the segments are added in segment order; the z-loss partials go
-// through a fixed fp64 tree.
+// through a fixed fp64 tree.  With a single block (T <= 64) that block
+// finishes the statistics itself, with the same operations.  The eight lanes
+// of a token combine through DPP moves.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,11 +28,15 @@ constexpr int kTok = 64;        // tokens per partial block
 constexpr int kRound = 32;      // tokens per round
 constexpr int kLanes = 8;       // lanes per token
 
-template <int KK>  // logits per lane: experts q, q+8, ... below 8 KK >= E
-__global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits,
-                                                            int64_t T, int E,
-                                                            float* __restrict__ part,
-                                                            float* __restrict__ zpart) {
+// kFinal (one block of tokens, T <= kTok): the block also finishes the
+// statistics, with exactly the operations stats_final_kernel would apply to
+// its single partial (the sums over empty segments add only zeros).
+template <int KK, bool kFinal>  // logits per lane: experts q, q+8, ... below 8 KK >= E
+__global__ __launch_bounds__(256) void stats_partial_kernel(
+    const float* __restrict__ logits, int64_t T, int E, float* __restrict__ part,
+    float* __restrict__ zpart, const int32_t* __restrict__ count, int k, float alpha,
+    float* __restrict__ f, float* __restrict__ P, float* __restrict__ loss,
+    float* __restrict__ zloss) {
   extern __shared__ float sp[];  // [kRound][E] probabilities of the current round
   __shared__ float zs[kRound];
   const int tid = threadIdx.x;
@@ -51,8 +57,7 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
     float m = -__builtin_inff();
 #pragma unroll
     for (int u = 0; u < KK; ++u) m = fmaxf(m, v[u]);
-#pragma unroll
-    for (int o = 1; o < kLanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kLanes));
+    m = max8_f32(m);
     float s = 0.0f;
 #pragma unroll
     for (int u = 0; u < KK; ++u) {
@@ -61,8 +66,7 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
         s += v[u];
       }
     }
-#pragma unroll
-    for (int o = 1; o < kLanes; o <<= 1) s += __shfl_xor(s, o, kLanes);
+    s = sum8_f32(s);
     const float inv = 1.0f / s;
 #pragma unroll
     for (int u = 0; u < KK; ++u) {
@@ -80,8 +84,30 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
       for (int u = 0; u < kRound; ++u) zacc += zs[u];
     __syncthreads();
   }
-  if (tid < E) part[static_cast<int64_t>(blockIdx.x) * E + tid] = acc;
-  if (tid == 0) zpart[blockIdx.x] = zacc;
+  if constexpr (!kFinal) {
+    if (tid < E) part[static_cast<int64_t>(blockIdx.x) * E + tid] = acc;
+    if (tid == 0) zpart[blockIdx.x] = zacc;
+  } else {
+    __shared__ double fp[256];
+    double term = 0.0;
+    if (tid < E) {
+      const double pe = static_cast<double>(acc) / static_cast<double>(T);
+      const double fe = static_cast<double>(count[tid]) / (static_cast<double>(T) * k);
+      P[tid] = static_cast<float>(pe);
+      f[tid] = static_cast<float>(fe);
+      term = fe * pe;
+    }
+    fp[tid] = term;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (tid < st) fp[tid] += fp[tid + st];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      loss[0] = static_cast<float>(static_cast<double>(alpha) * E * fp[0]);
+      if (zloss) zloss[0] = static_cast<float>(static_cast<double>(zacc) / static_cast<double>(T));
+    }
+  }
 }
 
 __global__ __launch_bounds__(1024) void stats_final_kernel(const float* __restrict__ part,
@@ -147,10 +173,21 @@ hipError_t launch_balance_stats(const float* logits, const int32_t* count, int64
   const int64_t nblk = stats_blocks(T);
   const size_t lds = sizeof(float) * kRound * E;
   const unsigned g = static_cast<unsigned>(nblk);
-  if (E <= 32) stats_partial_kernel<4><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
-  else if (E <= 64) stats_partial_kernel<8><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
-  else if (E <= 128) stats_partial_kernel<16><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
-  else stats_partial_kernel<32><<<g, 256, lds, stream>>>(logits, T, E, part, zpart);
+#define MOE_STATS(KK, FIN)                                                                 \
+  stats_partial_kernel<KK, FIN><<<g, 256, lds, stream>>>(logits, T, E, part, zpart, count, k, \
+                                                         alpha, f, P, loss, zloss)
+#define MOE_STATS_E(FIN)                    \
+  if (E <= 32) MOE_STATS(4, FIN);           \
+  else if (E <= 64) MOE_STATS(8, FIN);      \
+  else if (E <= 128) MOE_STATS(16, FIN);    \
+  else MOE_STATS(32, FIN)
+  if (nblk == 1) {  // one block: it finishes the statistics itself
+    MOE_STATS_E(true);
+    return hipGetLastError();
+  }
+  MOE_STATS_E(false);
+#undef MOE_STATS_E
+#undef MOE_STATS
   stats_final_kernel<<<1, 1024, 0, stream>>>(part, zpart, static_cast<int>(nblk), count, T, E, k,
                                              alpha, f, P, loss, zloss);
   return hipGetLastError();
