@@ -1,4 +1,5 @@
-"""CPU oracle for the sparse Mixture-of-Experts feed-forward layer (forward pass).
+"""CPU oracle for the sparse Mixture-of-Experts feed-forward layer (forward and
+backward passes).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -33,4 +34,15 @@ from .moe_oracle import (  # noqa: F401
     silu,
     swiglu,
     top_k,
+)
+from .moe_backward import (  # noqa: F401
+    backward,
+    balance_logit_grad,
+    gate_grad,
+    gate_logit_grad,
+    objective,
+    router_linear_backward,
+    silu_grad,
+    swiglu_backward,
+    z_loss_logit_grad,
 )
