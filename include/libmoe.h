@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -245,8 +245,9 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
  * (y = g1 Expert1(x) + g2 Expert2(x)), "A budget" and "A shared expert";
  * Zen-Max, section "Fine-Grained Expert Architecture" (shared experts added).
  *
- * y_perm [*, d] in y_dt; pair_row [T*k] int32; topk_gate [T,k] fp32;
- * shared_y [T,d] in y_dt or NULL; out [T,d] in out_dt.
+ * y_perm [*, d] in y_dt; pair_row [T*k] int32; topk_gate [T,k] fp32, or
+ * NULL for gates of 1 (the backward pass sums a token's input gradients
+ * this way); shared_y [T,d] in y_dt or NULL; out [T,d] in out_dt.
  */
 moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
                          const float* topk_gate, int64_t T, int k, int d,
@@ -275,6 +276,129 @@ size_t moe_balance_stats_workspace(int64_t T, int E);
 moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
                                int E, int k, float alpha, float* f, float* P, float* loss,
                                float* zloss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass.
+ *
+ * The objective differentiated is J = <dy, y> + coef_balance * loss +
+ * coef_z * zloss, with y the layer output, dy its upstream gradient and
+ * loss, zloss the outputs of moe_balance_stats.  Sources: "Every parameter,
+ * every token", section "The gating network" (the selected set is held fixed
+ * on the way forward; gradient reaches the router only through the gate
+ * weights of the experts that ran; an expert that was off for a token gets no
+ * gradient from it), sections "A balance penalty" (router trained on the
+ * task and the penalty together) and "A budget" (a dropped pair skips its
+ * expert update); Zen MoDE, section "Auxiliary Load Balancing Loss"; Zen-Max,
+ * sections "Fine-Grained Expert Architecture" and "MoE-Specific Training
+ * Stability".  Readings: no gradient flows through the selection, the
+ * capacity drop, the counts f or the selection bias; a dropped pair's gate
+ * gets no gradient from the output but stays in the renormalising softmax.
+ *
+ * A layer step: moe_expert_gate_up_train + moe_expert_down (forward, keeping
+ * the pre-activations uv and the expert rows y_perm) ... then
+ *   moe_combine_backward        dgate from dy and y_perm
+ *   moe_route_backward          dlogits
+ *   moe_expert_weights_t        transposed weight copies (once per weight update)
+ *   moe_expert_swiglu_backward  routed experts (a_rows = row_pair, row_gate =
+ *                               topk_gate) and shared experts (a_rows = NULL)
+ *   moe_router_backward         router weights, logit bias, dx (accumulate)
+ *   moe_combine(da_perm, NULL gates, shared_y = the accumulated dx) -> dx
+ * Every gradient output is fp32 and written (not accumulated) unless stated.
+ * The bf16 expert kernels keep u, v, [du | dv] and the gated hidden
+ * activation in bf16 (rounded to nearest even) between GEMMs.
+ */
+
+/* moe_expert_gate_up_train: moe_expert_gate_up that also keeps the
+ * pre-activations for the backward pass:
+ *   uv[r, 0:h] = a_r . w_gate[g]^T,  uv[r, h:2h] = a_r . w_up[g]^T
+ * uv [max_rows, 2h] bf16.  bf16 only (MOE_EUNSUPPORTED otherwise); runs the
+ * tiled kernel at every row count.  Workspace: moe_expert_group_workspace(G). */
+moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
+                                      const int32_t* group_offset, int64_t max_rows,
+                                      const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                      const void* w_up, void* hid, void* uv, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* moe_expert_weights_t: the transposed weight copies the input-gradient GEMMs
+ * read (the backward contracts over the weights' leading axis):
+ *   w_down_t[g] = w_down[g]^T                     [G, h, d]
+ *   w_gu_t[g]   = [w_gate[g]^T | w_up[g]^T]       [G, d, 2h]
+ * bf16 only, d % 64 == 0, h % 64 == 0.  They stay valid until the weights
+ * change, so a caller that runs several backward passes per weight update
+ * makes them once. */
+moe_status_t moe_expert_weights_t(const void* w_gate, const void* w_up, const void* w_down, int dt,
+                                  int d, int h, int G, void* w_down_t, void* w_gu_t,
+                                  void* stream);
+
+/* moe_expert_swiglu_backward: gradients of G SwiGLU experts over row groups
+ * (same group semantics, gather and limits as moe_expert_swiglu).  For row r
+ * of group g with s_r = row_gate[a_rows ? a_rows[r] : r] (1 if row_gate is
+ * NULL) and dy_r = dy[a_rows[r] / a_rows_div] (or dy[r]):
+ *   u, v    = uv[r, 0:h], uv[r, h:2h]      (from moe_expert_gate_up_train)
+ *   dhid    = s_r dy_r . w_down[g]                               ([h])
+ *   du      = dhid * v * SiLU'(u),  dv = dhid * SiLU(u)
+ *   da[r]   = du . w_gate[g] + dv . w_up[g]                      ([d], fp32)
+ *   dw_gate[g] = sum_r du_r^T a_r,  dw_up[g] = sum_r dv_r^T a_r  ([h, d], fp32)
+ *   dw_down[g] = sum_r s_r dy_r^T (SiLU(u_r) * v_r)              ([d, h], fp32)
+ * with SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z).  A group without rows
+ * gets zero weight gradients.  Routed experts: a = x, a_rows = row_pair,
+ * a_rows_div = k, row_gate = topk_gate.  Shared experts: a = x, a_rows =
+ * NULL, row_gate = NULL, G = 1 (concatenated hidden axis).
+ * dt must be bf16; additionally 4 d h < 2^32.  da [max_rows, d] fp32 (rows
+ * past group_offset[G] untouched).  w_down_t, w_gu_t from moe_expert_weights_t.
+ * Workspace: moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt)
+ * bytes (tile table, split-K partials, and the transposed bf16 operands of
+ * the weight gradients: about (2 d + 3 h) (max_rows + 64 G) + 4 h max_rows
+ * bytes); contents need no initialisation and are dead after the call. */
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt);
+moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
+                                        const int32_t* group_offset, int64_t max_rows,
+                                        const int32_t* a_rows, int a_rows_div, const void* dy,
+                                        const float* row_gate, const void* uv,
+                                        const void* w_down_t, const void* w_gu_t, float* da,
+                                        float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                                        size_t ws_bytes, void* stream);
+
+/* moe_combine_backward: the gate gradients of the combine,
+ *   dgate[t, j] = sum_i dy[t, i] * y_perm[pair_row[t*k+j], i]   (fp32)
+ * and 0 for a dropped pair (pair_row < 0).  Source: "The gating network"
+ * (y = sum_j g_j Expert_j(x)).  dy [T, d] in dy_dt; y_perm [*, d] in y_dt
+ * (the expert rows moe_expert_down wrote); dgate [T, k] fp32.
+ * (The input gradient of the expert rows, g * dy, is formed inside
+ * moe_expert_swiglu_backward through row_gate.) */
+moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+                                  const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
+                                  void* stream);
+
+/* moe_route_backward: dJ/dlogits [T, E] fp32,
+ *   dl[t,e] = g_tj (dgate_tj - sum_i g_ti dgate_ti)    for e = topk_idx[t,j]
+ *           + coef_balance * alpha * E / T * p_te (f_e - sum_e' f_e' p_te')
+ *           + coef_z * (2 / T) * lse_t * p_te
+ * with g = topk_gate (the forward's gates), p_t = softmax(logits[t,:]),
+ * lse_t = log sum_e exp logits[t,e], f_e = expert_count[e] / (T k) (the
+ * pre-drop counts of moe_permute).  Sources: "The gating network" (softmax
+ * over the selected set), Zen MoDE "Auxiliary Load Balancing Loss", Zen-Max
+ * "MoE-Specific Training Stability".  expert_count may be NULL when
+ * coef_balance == 0. */
+moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
+                                const float* topk_gate, const float* dgate,
+                                const int32_t* expert_count, int64_t T, int E, int k, float alpha,
+                                float coef_balance, float coef_z, float* dlogits, void* stream);
+
+/* moe_router_backward: gradients of logits = x w_router^T + logit_bias:
+ *   dw_router[e, i] = sum_t dlogits[t, e] x[t, i]       [E, d] fp32
+ *   dlogit_bias[e]  = sum_t dlogits[t, e]                [E]    fp32
+ *   dx[t, i]        = (accumulate_dx ? dx[t, i] : 0) + sum_e dlogits[t, e] w_router[e, i]
+ * x, w_router in dtype dt; dx [T, d] fp32.  Any of dw_router, dlogit_bias,
+ * dx may be NULL (not computed).  Sums over tokens go through fixed
+ * per-chunk partials (deterministic).  Source: "The gating network" (a
+ * linear gate).  Workspace: moe_router_backward_workspace(T, d, E) bytes
+ * (only when dw_router is requested). */
+size_t moe_router_backward_workspace(int64_t T, int d, int E);
+moe_status_t moe_router_backward(const void* x, const void* w_router, int dt,
+                                 const float* dlogits, int64_t T, int d, int E, float* dw_router,
+                                 float* dlogit_bias, float* dx, int accumulate_dx, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Measurement probes: what the device sustains, for roofline fractions

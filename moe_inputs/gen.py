@@ -17,6 +17,8 @@ Recipe (per workload ``cfg`` and seed):
     logit_bias "zipf"       -s * ln(e + 1), e = 0..E-1: the log of a Zipf(s)
                             prior over experts (expert 0 the most popular)
     select_bias "normal"    N(0, select_var), float32
+  backward pass (``generate_dy``): the upstream gradient dy [T, d] of the
+  layer output, N(0, 1), tensor id 4 + 3E + 3n_s, in the workload's dtype.
 Biases always stay float32.
 
 bfloat16 tensors are returned as ``Bf16`` objects holding the uint16 bit
@@ -150,3 +152,11 @@ def as_f32(a):
     if a is None:
         return None
     return a.f32() if isinstance(a, Bf16) else np.asarray(a, dtype=np.float32)
+
+
+def generate_dy(cfg: MoEConfig, seed: int = 0):
+    """Upstream gradient dy [T, d] of the layer output for the backward pass:
+    N(0, 1) in the workload's dtype (``Bf16`` for bf16 workloads)."""
+    tid = 4 + 3 * cfg.E + 3 * cfg.n_shared
+    z = _draw(seed, cfg.cid, tid, (cfg.T, cfg.d), 1.0, cfg.dtype)
+    return Bf16(z) if cfg.dtype == "bf16" else z

@@ -61,6 +61,16 @@ _SIGS = {
     "moe_combine": (_i, [_p, _i, _p, _p, _i64, _i, _i, _p, _p, _i, _p]),
     "moe_balance_stats_workspace": (_sz, [_i64, _i]),
     "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_expert_gate_up_train": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
+                                      _sz, _p]),
+    "moe_expert_weights_t": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]),
+    "moe_expert_swiglu_backward_workspace": (_sz, [_i64, _i, _i, _i, _i]),
+    "moe_expert_swiglu_backward": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
+                                        _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _i64, _i, _i, _p, _p]),
+    "moe_route_backward": (_i, [_p, _p, _p, _p, _p, _i64, _i, _i, _f, _f, _f, _p, _p]),
+    "moe_router_backward_workspace": (_sz, [_i64, _i, _i]),
+    "moe_router_backward": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
     "moe_probe_mfma_bf16": (_i, [_p, _i, _i, _p, _p]),
     "moe_probe_read": (_i, [_p, _sz, _i, _p, _p]),
 }
@@ -251,9 +261,13 @@ def moe_expert_down(hid, group_offset, max_rows, w_down, *, y=None, y_dtype=None
 
 
 def moe_combine(y_perm, pair_row, topk_gate, shared_y=None, *, out=None, out_dtype=None,
-                stream=None):
-    """out[t] = shared_y[t] + sum of kept g[t, j] * y_perm[pair_row[t k + j]]."""
-    T, k = topk_gate.shape
+                k=None, stream=None):
+    """out[t] = shared_y[t] + sum of kept g[t, j] * y_perm[pair_row[t k + j]];
+    with topk_gate None every gate is 1 (then ``k`` must be given)."""
+    if topk_gate is not None:
+        T, k = topk_gate.shape
+    else:
+        T = pair_row.numel() // k
     d = y_perm.shape[1]
     if out is None:
         out = torch.empty((T, d), dtype=out_dtype or y_perm.dtype, device=y_perm.device)
@@ -286,6 +300,125 @@ def moe_balance_stats(logits, expert_count, k, alpha=0.01, *, f=None, P=None, lo
                                 _ptr(f), _ptr(P), _ptr(loss), _ptr(zloss), _ptr(ws), ws.numel(),
                                 _stream(stream)))
     return f, P, loss, zloss
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+def moe_expert_gate_up_train(a, group_offset, max_rows, w_gate, w_up, *, a_rows=None,
+                             a_rows_div=1, hid=None, uv=None, ws=None, stream=None):
+    """moe_expert_gate_up that also keeps uv = [a W_gate^T | a W_up^T] (bf16)."""
+    G, h, d = w_gate.shape
+    dev = a.device
+    if hid is None:
+        hid = torch.empty((max_rows, h), dtype=a.dtype, device=dev)
+    if uv is None:
+        uv = torch.empty((max_rows, 2 * h), dtype=a.dtype, device=dev)
+    if ws is None:
+        ws = torch.empty(moe_expert_group_workspace(G), dtype=torch.uint8, device=dev)
+    _contig(a, group_offset, a_rows, w_gate, w_up, hid, uv, ws)
+    _check(_L.moe_expert_gate_up_train(_ptr(a), _dt(a), d, h, G, _ptr(group_offset), max_rows,
+                                       _ptr(a_rows), a_rows_div, _ptr(w_gate), _ptr(w_up),
+                                       _ptr(hid), _ptr(uv), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+    return hid, uv
+
+
+def moe_expert_weights_t(w_gate, w_up, w_down, *, w_down_t=None, w_gu_t=None, stream=None):
+    """Transposed weight copies w_down_t [G, h, d] and w_gu_t [G, d, 2h]."""
+    G, h, d = w_gate.shape
+    dev = w_gate.device
+    if w_down_t is None:
+        w_down_t = torch.empty((G, h, d), dtype=w_gate.dtype, device=dev)
+    if w_gu_t is None:
+        w_gu_t = torch.empty((G, d, 2 * h), dtype=w_gate.dtype, device=dev)
+    _contig(w_gate, w_up, w_down, w_down_t, w_gu_t)
+    _check(_L.moe_expert_weights_t(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _dt(w_gate), d, h, G,
+                                   _ptr(w_down_t), _ptr(w_gu_t), _stream(stream)))
+    return w_down_t, w_gu_t
+
+
+def moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt) -> int:
+    return _L.moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt)
+
+
+def moe_expert_swiglu_backward(a, group_offset, max_rows, dy, uv, w_down_t, w_gu_t, *,
+                               a_rows=None, a_rows_div=1, row_gate=None, da=None, dw_gate=None,
+                               dw_up=None, dw_down=None, ws=None, stream=None):
+    """Gradients of the grouped SwiGLU experts: da [max_rows, d] and dw_gate,
+    dw_up [G, h, d], dw_down [G, d, h] (all fp32)."""
+    G, h, d = w_down_t.shape
+    dev = a.device
+    f32 = torch.float32
+    da = torch.empty((max_rows, d), dtype=f32, device=dev) if da is None else da
+    dw_gate = torch.empty((G, h, d), dtype=f32, device=dev) if dw_gate is None else dw_gate
+    dw_up = torch.empty((G, h, d), dtype=f32, device=dev) if dw_up is None else dw_up
+    dw_down = torch.empty((G, d, h), dtype=f32, device=dev) if dw_down is None else dw_down
+    if ws is None:
+        ws = torch.empty(max(moe_expert_swiglu_backward_workspace(max_rows, d, h, G, _dt(a)), 1),
+                         dtype=torch.uint8, device=dev)
+    _contig(a, group_offset, dy, uv, w_down_t, w_gu_t, a_rows, row_gate, da, dw_gate, dw_up,
+            dw_down, ws)
+    _check(_L.moe_expert_swiglu_backward(_ptr(a), _dt(a), d, h, G, _ptr(group_offset), max_rows,
+                                         _ptr(a_rows), a_rows_div, _ptr(dy), _ptr(row_gate),
+                                         _ptr(uv), _ptr(w_down_t), _ptr(w_gu_t), _ptr(da),
+                                         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
+                                         ws.numel(), _stream(stream)))
+    return da, dw_gate, dw_up, dw_down
+
+
+def moe_combine_backward(dy, y_perm, pair_row, k, *, dgate=None, stream=None):
+    """dgate[t, j] = <dy[t], y_perm[pair_row[t k + j]]> (0 for dropped pairs)."""
+    T, d = dy.shape
+    if dgate is None:
+        dgate = torch.empty((T, k), dtype=torch.float32, device=dy.device)
+    _contig(dy, y_perm, pair_row, dgate)
+    _check(_L.moe_combine_backward(_ptr(dy), _dt(dy), _ptr(y_perm), _dt(y_perm), _ptr(pair_row),
+                                   T, k, d, _ptr(dgate), _stream(stream)))
+    return dgate
+
+
+def moe_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, alpha=0.01,
+                       coef_balance=0.0, coef_z=0.0, *, dlogits=None, stream=None):
+    """dJ/dlogits through the renormalised gates, the balance loss and the z-loss."""
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    _contig(logits, topk_idx, topk_gate, dgate, expert_count, dlogits)
+    _check(_L.moe_route_backward(_ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(dgate),
+                                 _ptr(expert_count), T, E, k, float(alpha), float(coef_balance),
+                                 float(coef_z), _ptr(dlogits), _stream(stream)))
+    return dlogits
+
+
+def moe_router_backward_workspace(T, d, E) -> int:
+    return _L.moe_router_backward_workspace(T, d, E)
+
+
+def moe_router_backward(x, w_router, dlogits, *, dw_router=None, dlogit_bias=None, dx=None,
+                        accumulate_dx=False, want=("dw", "db", "dx"), ws=None, stream=None):
+    """Gradients of the linear router: dw_router [E, d], dlogit_bias [E] and
+    dx [T, d] (added to the given dx with ``accumulate_dx``); fp32."""
+    T, E = dlogits.shape
+    d = w_router.shape[1]
+    dev = dlogits.device
+    f32 = torch.float32
+    if "dw" in want and dw_router is None:
+        dw_router = torch.empty((E, d), dtype=f32, device=dev)
+    if "db" in want and dlogit_bias is None:
+        dlogit_bias = torch.empty(E, dtype=f32, device=dev)
+    if "dx" in want and dx is None:
+        dx = torch.empty((T, d), dtype=f32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(moe_router_backward_workspace(T, d, E), 1), dtype=torch.uint8,
+                         device=dev)
+    _contig(x, w_router, dlogits, dw_router, dlogit_bias, dx, ws)
+    _check(_L.moe_router_backward(_ptr(x), _ptr(w_router), _dt(w_router), _ptr(dlogits), T, d, E,
+                                  _ptr(dw_router), _ptr(dlogit_bias), _ptr(dx),
+                                  1 if accumulate_dx else 0, _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return dw_router, dlogit_bias, dx
 
 
 def moe_probe_mfma_bf16(src, blocks, iters, *, out=None, stream=None):

@@ -1,0 +1,378 @@
+// Backward pass of the routing side of the layer: the gate gradients from the
+// combine, the logit gradients (renormalised gates, balance loss, z-loss) and
+// the gradients of the linear router.
+//
+// Sources: "Every parameter, every token", sections "The gating network"
+// (the selected set is held fixed; gradient reaches the router only through
+// the gates of the experts that ran, and experts that were off get none),
+// "A balance penalty" (the router is trained on the task and the penalty
+// together) and "A budget" (a dropped pair has no expert output); Zen MoDE,
+// section "Auxiliary Load Balancing Loss"; Zen-Max, section "MoE-Specific
+// Training Stability" (z-loss).
+//
+// All sums run in a fixed order (lane butterflies, per-chunk partials added
+// in chunk order): results are deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+__device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+// ---------------------------------------------------------------------------
+// dgate[t, j] = sum_i dy[t, i] * y[pair_row[t k + j], i], 0 for a dropped pair.
+// One wave per token (four per workgroup); each lane takes 8 consecutive
+// columns per step; slots go in batches of 8 and the lane partials of each
+// slot are added by a butterfly.
+// ---------------------------------------------------------------------------
+constexpr int kGradSlots = 8;
+
+template <typename DT, typename YT>
+__global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restrict__ dy,
+                                                               const YT* __restrict__ y,
+                                                               const int32_t* __restrict__ pair_row,
+                                                               int64_t T, int k, int d,
+                                                               float* __restrict__ dgate) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int32_t* pr = pair_row + t * k;
+  const DT* dyr = dy + t * d;
+  for (int j0 = 0; j0 < k; j0 += kGradSlots) {
+    int rows[kGradSlots];
+    float acc[kGradSlots];
+#pragma unroll
+    for (int u = 0; u < kGradSlots; ++u) {
+      rows[u] = j0 + u < k ? pr[j0 + u] : -1;
+      acc[u] = 0.0f;
+    }
+    if ((d & 7) == 0) {
+      for (int c = lane * 8; c < d; c += kWave * 8) {
+        float g[8];
+        load8(dyr + c, g);
+#pragma unroll
+        for (int u = 0; u < kGradSlots; ++u) {
+          if (rows[u] < 0) continue;
+          float v[8];
+          load8(y + static_cast<int64_t>(rows[u]) * d + c, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u] = fmaf(g[i], v[i], acc[u]);
+        }
+      }
+    } else {
+      for (int c = lane; c < d; c += kWave) {
+        const float g = load1(dyr + c);
+#pragma unroll
+        for (int u = 0; u < kGradSlots; ++u)
+          if (rows[u] >= 0) acc[u] = fmaf(g, load1(y + static_cast<int64_t>(rows[u]) * d + c), acc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGradSlots; ++u) {
+      const float s = wave_sum(acc[u]);
+      if (lane == 0 && j0 + u < k) dgate[t * k + j0 + u] = rows[u] >= 0 ? s : 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dlogits[t, e] = g_j (dg_j - sum_i g_i dg_i)               if e = idx[t, j]
+//              + c_bal alpha E / T  p_te (f_e - sum_e' f_e' p_te')
+//              + c_z (2 / T) lse_t p_te
+// with p_t = softmax(logits[t]), f_e = count[e] / (T k), g the forward's
+// gates.  One wave per token; lane l holds experts l, l + 64, ...
+// ---------------------------------------------------------------------------
+template <int KK>  // experts per lane: 64 KK >= E
+__global__ __launch_bounds__(256) void route_backward_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const float* __restrict__ dgate,
+    const int32_t* __restrict__ count, int64_t T, int E, int k, float alpha, float c_bal,
+    float c_z, float* __restrict__ dl) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float v[KK], f[KK];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < KK; ++u) {
+    const int e = lane + u * kWave;
+    v[u] = e < E ? row[e] : -__builtin_inff();
+    f[u] = (count && e < E)
+               ? static_cast<float>(count[e]) / (static_cast<float>(T) * static_cast<float>(k))
+               : 0.0f;
+    m = fmaxf(m, v[u]);
+  }
+  m = wave_max(m);
+  float s = 0.0f;
+#pragma unroll
+  for (int u = 0; u < KK; ++u) {
+    v[u] = lane + u * kWave < E ? __expf(v[u] - m) : 0.0f;
+    s += v[u];
+  }
+  s = wave_sum(s);
+  const float inv = 1.0f / s;
+  float fp = 0.0f;
+#pragma unroll
+  for (int u = 0; u < KK; ++u) {
+    v[u] *= inv;  // p
+    fp = fmaf(f[u], v[u], fp);
+  }
+  fp = wave_sum(fp);
+  const float lse = m + __logf(s);
+  const float cb = c_bal * alpha * static_cast<float>(E) / static_cast<float>(T);
+  const float cz = c_z * 2.0f * lse / static_cast<float>(T);
+  // gate term: every lane forms the same inner product in slot order
+  const int32_t* ir = idx + t * k;
+  const float* gr = gate + t * k;
+  const float* dgr = dgate + t * k;
+  float inner = 0.0f;
+  for (int j = 0; j < k; ++j) inner = fmaf(gr[j], dgr[j], inner);
+  float out[KK];
+#pragma unroll
+  for (int u = 0; u < KK; ++u) out[u] = cb * v[u] * (f[u] - fp) + cz * v[u];
+  for (int j = 0; j < k; ++j) {
+    const int e = ir[j];
+    const float gt = gr[j] * (dgr[j] - inner);
+#pragma unroll
+    for (int u = 0; u < KK; ++u)
+      if (e == lane + u * kWave) out[u] += gt;
+  }
+  float* o = dl + t * E;
+#pragma unroll
+  for (int u = 0; u < KK; ++u)
+    if (lane + u * kWave < E) o[lane + u * kWave] = out[u];
+}
+
+// ---------------------------------------------------------------------------
+// Linear router.  dx[t, i] (+)= sum_e dl[t, e] W[e, i]: a workgroup takes 32
+// tokens and 256 columns, one column per thread; the tokens' dl rows sit in
+// LDS expert-major so that each expert's 32 values are read as 8 broadcast
+// 16-byte words.
+// ---------------------------------------------------------------------------
+constexpr int kDxTok = 32;
+
+template <typename WT>
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dl,
+                                                        const WT* __restrict__ w, int64_t T, int d,
+                                                        int E, float* __restrict__ dx,
+                                                        bool accumulate) {
+  extern __shared__ __align__(16) float sdl[];  // [E][kDxTok]
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kDxTok;
+  for (int i = threadIdx.x; i < E * kDxTok; i += 256) {
+    const int e = i / kDxTok, tt = i % kDxTok;
+    sdl[i] = t0 + tt < T ? dl[(t0 + tt) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= d) return;
+  float acc[kDxTok];
+#pragma unroll
+  for (int tt = 0; tt < kDxTok; ++tt) acc[tt] = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    const float wv = load1(w + static_cast<int64_t>(e) * d + col);
+    const f32x4* p = reinterpret_cast<const f32x4*>(sdl + e * kDxTok);
+#pragma unroll
+    for (int q = 0; q < kDxTok / 4; ++q) {
+      const f32x4 a = p[q];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) acc[4 * q + z] = fmaf(a[z], wv, acc[4 * q + z]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kDxTok; ++tt) {
+    if (t0 + tt >= T) break;
+    float* o = dx + (t0 + tt) * d + col;
+    *o = accumulate ? *o + acc[tt] : acc[tt];
+  }
+}
+
+// dw[e, i] = sum_t dl[t, e] x[t, i]: workgroup (column tile of 256, expert
+// tile of 32, token chunk c) writes the chunk's partial sums to
+// part[c][e][i]; router_dw_reduce_kernel adds the chunks in order.
+constexpr int kDwExp = 32;
+constexpr int kDwSub = 64;  // tokens staged in LDS at a time
+
+template <typename XT>
+__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
+                                                        const XT* __restrict__ x, int64_t T, int d,
+                                                        int E, int64_t chunk,
+                                                        float* __restrict__ part) {
+  __shared__ __align__(16) float sdl[kDwSub][kDwExp];
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int e0 = blockIdx.y * kDwExp;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.z) * chunk;
+  const int64_t c1 = c0 + chunk < T ? c0 + chunk : T;
+  float acc[kDwExp];
+#pragma unroll
+  for (int u = 0; u < kDwExp; ++u) acc[u] = 0.0f;
+  for (int64_t s0 = c0; s0 < c1; s0 += kDwSub) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kDwSub * kDwExp; i += 256) {
+      const int tt = i / kDwExp, u = i % kDwExp;
+      const int64_t t = s0 + tt;
+      sdl[tt][u] = (t < c1 && e0 + u < E) ? dl[t * E + e0 + u] : 0.0f;
+    }
+    __syncthreads();
+    if (col < d) {
+      const int n = static_cast<int>(c1 - s0 < kDwSub ? c1 - s0 : kDwSub);
+      for (int tt = 0; tt < n; ++tt) {
+        const float xv = load1(x + (s0 + tt) * d + col);
+        const f32x4* p = reinterpret_cast<const f32x4*>(&sdl[tt][0]);
+#pragma unroll
+        for (int q = 0; q < kDwExp / 4; ++q) {
+          const f32x4 a = p[q];
+#pragma unroll
+          for (int z = 0; z < 4; ++z) acc[4 * q + z] = fmaf(a[z], xv, acc[4 * q + z]);
+        }
+      }
+    }
+  }
+  if (col >= d) return;
+#pragma unroll
+  for (int u = 0; u < kDwExp; ++u)
+    if (e0 + u < E) part[(static_cast<int64_t>(blockIdx.z) * E + e0 + u) * d + col] = acc[u];
+}
+
+__global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __restrict__ part,
+                                                               int nchunk, int64_t n,
+                                                               float* __restrict__ dw) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int c = 0; c < nchunk; ++c) s += part[c * n + i];
+  dw[i] = s;
+}
+
+// dlogit_bias[e] = sum_t dl[t, e]: one workgroup per expert, thread i sums
+// tokens i, i + 256, ... in order, then a fixed tree.
+__global__ __launch_bounds__(256) void router_db_kernel(const float* __restrict__ dl, int64_t T,
+                                                        int E, float* __restrict__ db) {
+  __shared__ float s[256];
+  const int e = blockIdx.x;
+  float acc = 0.0f;
+  for (int64_t t = threadIdx.x; t < T; t += 256) acc += dl[t * E + e];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s[threadIdx.x] += s[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) db[e] = s[0];
+}
+
+// token chunks of the dw partials: enough workgroups to cover the device
+int dw_chunks(int64_t T, int d, int E) {
+  const int64_t tiles = static_cast<int64_t>((d + 255) / 256) * ((E + kDwExp - 1) / kDwExp);
+  int64_t c = (1024 + tiles - 1) / tiles;
+  const int64_t cmax = (T + kDwSub - 1) / kDwSub;
+  if (c > cmax) c = cmax;
+  return static_cast<int>(c < 1 ? 1 : c);
+}
+
+template <typename T_>
+hipError_t router_backward_typed(const void* x, const void* w, const float* dl, int64_t T, int d,
+                                 int E, float* dw, float* db, float* dx, bool acc, float* part,
+                                 hipStream_t stream) {
+  const T_* xp = static_cast<const T_*>(x);
+  const T_* wp = static_cast<const T_*>(w);
+  if (dx) {
+    const dim3 grid((d + 255) / 256, static_cast<unsigned>((T + kDxTok - 1) / kDxTok));
+    router_dx_kernel<T_><<<grid, 256, sizeof(float) * E * kDxTok, stream>>>(dl, wp, T, d, E, dx,
+                                                                             acc);
+  }
+  if (dw) {
+    const int nchunk = dw_chunks(T, d, E);
+    const int64_t chunk = (T + nchunk - 1) / nchunk;
+    const dim3 grid((d + 255) / 256, (E + kDwExp - 1) / kDwExp, static_cast<unsigned>(nchunk));
+    router_dw_kernel<T_><<<grid, 256, 0, stream>>>(dl, xp, T, d, E, chunk, part);
+    const int64_t n = static_cast<int64_t>(E) * d;
+    router_dw_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
+        part, nchunk, n, dw);
+  }
+  if (db) router_db_kernel<<<E, 256, 0, stream>>>(dl, T, E, db);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,
+                                   const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
+                                   hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+#define MOE_CB(DT, YT)                                                                       \
+  combine_backward_kernel<DT, YT><<<grid, 256, 0, stream>>>(static_cast<const DT*>(dy),      \
+                                                            static_cast<const YT*>(y), pair_row, \
+                                                            T, k, d, dgate)
+  if (dy_bf16 && y_bf16) MOE_CB(uint16_t, uint16_t);
+  else if (dy_bf16) MOE_CB(uint16_t, float);
+  else if (y_bf16) MOE_CB(float, uint16_t);
+  else MOE_CB(float, float);
+#undef MOE_CB
+  return hipGetLastError();
+}
+
+hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
+                                 const float* dgate, const int32_t* count, int64_t T, int E, int k,
+                                 float alpha, float c_bal, float c_z, float* dlogits,
+                                 hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+#define MOE_RB(KK)                                                                          \
+  route_backward_kernel<KK><<<grid, 256, 0, stream>>>(logits, idx, gate, dgate, count, T, E, k, \
+                                                      alpha, c_bal, c_z, dlogits)
+  if (E <= 64) MOE_RB(1);
+  else if (E <= 128) MOE_RB(2);
+  else MOE_RB(4);
+#undef MOE_RB
+  return hipGetLastError();
+}
+
+size_t router_backward_workspace_bytes(int64_t T, int d, int E) {
+  return sizeof(float) * static_cast<size_t>(dw_chunks(T, d, E)) * E * d;
+}
+
+hipError_t launch_router_backward(const void* x, const void* w_router, bool bf16, const float* dl,
+                                  int64_t T, int d, int E, float* dw_router, float* dlogit_bias,
+                                  float* dx, bool dx_accumulate, void* ws, hipStream_t stream) {
+  float* part = static_cast<float*>(ws);
+  return bf16 ? router_backward_typed<uint16_t>(x, w_router, dl, T, d, E, dw_router, dlogit_bias,
+                                                dx, dx_accumulate, part, stream)
+              : router_backward_typed<float>(x, w_router, dl, T, d, E, dw_router, dlogit_bias, dx,
+                                             dx_accumulate, part, stream);
+}
+
+}  // namespace moe

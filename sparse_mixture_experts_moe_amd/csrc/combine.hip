@@ -1,5 +1,7 @@
 // Combine: out[t] = shared_y[t] + sum over kept slots j of g[t,j] * y_perm[pair_row[t*k+j]],
-// accumulated in fp32 in slot order and rounded once.
+// accumulated in fp32 in slot order and rounded once.  Without gates (g = 1)
+// the same kernel adds the input gradients of a token's kept pairs in the
+// backward pass.
 //
 // Sources: "Every parameter, every token", sections "The gating network"
 // (the output is the gate-weighted sum of the selected experts), "A budget"
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       OT* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int32_t* pr = pair_row + t * k;
-  const float* g = gate + t * k;
+  const float* g = gate ? gate + t * k : nullptr;  // NULL: every gate is 1
   if ((d & 7) == 0) {
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 #pragma unroll
         for (int u = 0; u < kSlotBatch; ++u) {
           if (rows[u] < 0) continue;  // dropped (or past k): contributes nothing
-          const float gj = g[j0 + u];
+          const float gj = g ? g[j0 + u] : 1.0f;
           float v[8];
           Vec8<YT>::unpack(raw[u], v);
 #pragma unroll
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
       for (int j = 0; j < k; ++j) {
         const int row = pr[j];
         if (row < 0) continue;
-        acc = fmaf(g[j], Vec8<YT>::load1(y + static_cast<int64_t>(row) * d + c), acc);
+        acc = fmaf(g ? g[j] : 1.0f, Vec8<YT>::load1(y + static_cast<int64_t>(row) * d + c), acc);
       }
       if (shared) acc += Vec8<YT>::load1(shared + t * d + c);
       Vec8<OT>::store1(out + t * d + c, acc);

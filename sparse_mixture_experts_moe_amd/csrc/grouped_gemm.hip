@@ -458,16 +458,48 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// Epilogue modes of the bf16 tiles.
+//   kEpiNone:    C = A B^T (fused: C = SiLU(gate) * up).
+//   kEpiSaveUV:  fused only; also keeps the two pre-activations of every
+//                output, uv[r, c] = gate sum and uv[r, N + c] = up sum (bf16),
+//                for the backward pass.
+//   kEpiSiluBwd: unfused, N = h, A rows = the upstream gradient rows of the
+//                tile's pairs; the accumulator is dhid / s_r with s_r the
+//                pair's gate (row_gate[a_rows[r]], or row_gate[r] without a
+//                gather, or 1 without row_gate).  With u, v read back from uv:
+//                  du = s dhid_acc v SiLU'(u),  dv = s dhid_acc SiLU(u)
+//                written to dab[r] = [du | dv] (row layout) and to the
+//                transposed buffers dabT[c][kc] (du), dabT[N + c][kc] (dv) and
+//                ghidT[c][kc] = s SiLU(u) v, where kc = kofs[g] + r - off[g]
+//                is the row's column in the K-grouped layout of the weight
+//                gradients.  C is not written.
+constexpr int kEpiNone = 0;
+constexpr int kEpiSaveUV = 1;
+constexpr int kEpiSiluBwd = 2;
+
+struct EpiArgs {
+  uint16_t* uv;                  // [rows, 2N]
+  const float* row_gate;         // per pair, or NULL
+  const int32_t* a_rows;         // the tile's row gather (pair of each row), or NULL
+  const int32_t* off;            // group offsets [G + 1]
+  const int32_t* kofs;           // first transposed column of each group [G + 1]
+  int64_t kt;                    // columns of the transposed buffers
+  uint16_t* dab;                 // [rows, 2N]
+  uint16_t* dabT;                // [2N, kt]
+  uint16_t* ghidT;               // [N, kt]
+};
+
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
 // waves form a WM x WN grid, each wave a (BM/WM) x (BN/WN) block of MFMA
 // tiles.  The LDS rings are laid out for kTileM rows of A whatever BM is.
-template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename OutT>
+template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename OutT, int kEpi>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const Tile2& tile, int ks0, int nk, uint16_t* smem, OutT* __restrict__ C,
-    float* __restrict__ part_out) {
+    float* __restrict__ part_out, const EpiArgs& ep) {
   static_assert(WM * WN == 4, "four waves");
+  static_assert(kEpi == kEpiNone || (kEpi == kEpiSaveUV) == kFused, "epilogue mode");
   constexpr int MT = BM / WM / 32;            // 32-row MFMA tiles per wave
   constexpr int NT = BN / WN / 32;            // 32-col MFMA tiles per wave
   constexpr int AP = BM / 32;                 // copies per wave per stage (A): 8 rows each
@@ -669,6 +701,56 @@ __device__ __forceinline__ void gemm_tile(
             v[e] = silu_f32(acc[i][j][4 * q + e]) * acc[i][j + NT / 2][4 * q + e];
           u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(crow + col) = pk;
+          if constexpr (kEpi == kEpiSaveUV) {
+            uint16_t* urow = ep.uv + static_cast<int64_t>(row) * (2 * N);
+            const f32x16& ga = acc[i][j];
+            const f32x16& ua = acc[i][j + NT / 2];
+            *reinterpret_cast<u32x2*>(urow + col) =
+                u32x2{pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3])};
+            *reinterpret_cast<u32x2*>(urow + N + col) =
+                u32x2{pack_bf16x2(ua[4 * q], ua[4 * q + 1]), pack_bf16x2(ua[4 * q + 2], ua[4 * q + 3])};
+          }
+        }
+      }
+    } else if constexpr (kEpi == kEpiSiluBwd) {
+      const int64_t pr = ep.a_rows ? ep.a_rows[row] : row;
+      const float sr = ep.row_gate ? ep.row_gate[pr] : 1.0f;
+      const int64_t kc = ep.kofs[tile.g] + (row - ep.off[tile.g]);
+      const uint16_t* urow = ep.uv + static_cast<int64_t>(row) * (2 * N);
+      uint16_t* drow = ep.dab + static_cast<int64_t>(row) * (2 * N);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int cb = tile.n0 + wn * (BN / WN) + j * 32 + cq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = cb + 8 * q;
+          if (col >= N) continue;
+          const u32x2 ur = *reinterpret_cast<const u32x2*>(urow + col);
+          const u32x2 vr = *reinterpret_cast<const u32x2*>(urow + N + col);
+          float du[4], dv[4], gh[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t uw = ur[e >> 1], vw = vr[e >> 1];
+            const float u = __uint_as_float((e & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
+            const float v = __uint_as_float((e & 1) ? (vw & 0xFFFF0000u) : (vw << 16));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-u));  // 0 once exp overflows
+            const float si = u * sg;
+            const float dh = sr * acc[i][j][4 * q + e];
+            du[e] = dh * v * (sg * (1.0f + u * (1.0f - sg)));
+            dv[e] = dh * si;
+            gh[e] = sr * (si * v);
+          }
+          *reinterpret_cast<u32x2*>(drow + col) =
+              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          *reinterpret_cast<u32x2*>(drow + N + col) =
+              u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t c = col + e;
+            ep.dabT[c * ep.kt + kc] = f32_to_bf16_bits(du[e]);
+            ep.dabT[(N + c) * ep.kt + kc] = f32_to_bf16_bits(dv[e]);
+            ep.ghidT[c * ep.kt + kc] = f32_to_bf16_bits(gh[e]);
+          }
         }
       }
     } else if (part_out) {  // fp32 partial sums, [256][256] relative to (m0, n0)
@@ -740,12 +822,12 @@ __device__ __forceinline__ int next_work(const int32_t* __restrict__ runs, int32
 // runs).  tt: the tile-table workspace (mstart first); skw: split-K
 // workspace (kSkUnits fp32 256 x 256 tiles) or NULL (no split); ncu: compute
 // units of the device, as given to tile_table_kernel.
-template <bool kFused, typename OutT>
+template <bool kFused, typename OutT, int kEpi>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const int32_t* __restrict__ off, int32_t* __restrict__ tt, int G, int ntn,
-    OutT* __restrict__ C, float* __restrict__ skw, int ncu) {
+    OutT* __restrict__ C, float* __restrict__ skw, int ncu, EpiArgs ep) {
   constexpr int BN = 256;
   extern __shared__ __align__(16) uint16_t smem[];
   const int32_t* mstart = tt;
@@ -761,9 +843,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       if (u.count == 0) {
         t.n0 = u.nt0 * (BN / 2);
         const Tile2 tile = classify(t);
-        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, 0, K / kBK,
-                                                              smem, C, nullptr);
+                                                              smem, C, nullptr, ep);
         continue;
       }
       for (int s = 0; s < u.count; ++s) {
@@ -771,13 +853,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
         t.n0 = (u.nt0 + s) * (BN / 2);
         const Tile2 tile = classify(t);
         if (tile.cls == 1)
-          gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+          gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                                 b_stride, K, N, tile, 0, K / kBK,
-                                                                smem, C, nullptr);
+                                                                smem, C, nullptr, ep);
         else
-          gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+          gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                                b_stride, K, N, tile, 0, K / kBK,
-                                                               smem, C, nullptr);
+                                                               smem, C, nullptr, ep);
       }
     }
   } else {
@@ -799,17 +881,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       }
       const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, BN));
       if (tile.cls == 0) {
-        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, ks0, nk,
-                                                              smem, C, part_out);
+                                                              smem, C, part_out, ep);
       } else if (tile.cls == 1) {
-        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, ks0, nk,
-                                                              smem, C, part_out);
+                                                              smem, C, part_out, ep);
       } else {
-        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT>(A, a_rows, a_div, B0, B1,
+        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
                                                              b_stride, K, N, tile, ks0, nk,
-                                                             smem, C, part_out);
+                                                             smem, C, part_out, ep);
       }
     }
   }
@@ -1147,12 +1229,15 @@ hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ncu = compute_units();
   tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, true, s.mstart,
                                             s.mstart, ncu, s.d / kBK, false);
-  auto kern = gemm_bf16_kernel<true, uint16_t>;
+  EpiArgs ep{};
+  ep.uv = static_cast<uint16_t*>(s.uv);
+  auto kern = s.uv ? gemm_bf16_kernel<true, uint16_t, kEpiSaveUV>
+                   : gemm_bf16_kernel<true, uint16_t, kEpiNone>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
-      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu);
+      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu, ep);
   return hipGetLastError();
 }
 
@@ -1162,12 +1247,12 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ncu = compute_units();
   tile_table_kernel<<<1, 1024, 0, stream>>>(s.group_offset, s.G, kTileM, ntn, false, s.mstart,
                                             s.mstart, ncu, s.h / kBK, s.sk_ws != nullptr);
-  auto kern = gemm_bf16_kernel<false, OutT>;
+  auto kern = gemm_bf16_kernel<false, OutT, kEpiNone>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
-      static_cast<OutT*>(s.y), s.sk_ws, ncu);
+      static_cast<OutT*>(s.y), s.sk_ws, ncu, EpiArgs{});
   if (s.sk_ws)
     sk_reduce_kernel<OutT><<<kSkUnits * 32, 256, 0, stream>>>(
         s.sk_ws, s.group_offset, s.mstart, s.G, ntn, s.h, s.d, ncu, static_cast<OutT*>(s.y));
@@ -1245,6 +1330,196 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
 // the others run the tiled MFMA kernel.
 bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
 
+// ---------------------------------------------------------------------------
+// Backward pass of the experts (bf16).  With dout_r = s_r dy_r (s_r the
+// pair's gate), per group g:
+//   dhid = dout W_down[g]                           (dgrad 1, K = d, N = h)
+//   du = dhid v SiLU'(u),  dv = dhid SiLU(u)        (its epilogue)
+//   da = du W_gate[g] + dv W_up[g]                  (dgrad 2, K = 2h, N = d)
+//   dW_down[g] = sum_r dy_r^T (s_r hid_r)           (weight gradients, K = rows)
+//   dW_gate[g] = sum_r du_r^T a_r,  dW_up[g] = sum_r dv_r^T a_r
+// The two input-gradient GEMMs contract over the weights' leading axis, so
+// they run on transposed weight copies (w_down_t [G, h, d], w_gu_t [G, d, 2h]
+// = [W_gate^T | W_up^T]) with the forward's grouped kernel.  The weight
+// gradients contract over the rows of a group: their operands are laid out
+// transposed, [features, kt], each group's rows in a run of columns that
+// starts at kofs[g] and is padded with zeros to a multiple of 64, so that
+// every group is a whole number of K slices of the same tiled kernel.
+// ---------------------------------------------------------------------------
+constexpr int kTr = 64;  // transpose tile
+
+__host__ __device__ constexpr int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// kofs[g] = sum over g' < g of pad64(rows of g'), g = 0..G (one thread: G is small)
+__global__ void kofs_kernel(const int32_t* __restrict__ off, int G, int32_t* __restrict__ kofs) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int32_t acc = 0;
+  for (int g = 0; g < G; ++g) {
+    kofs[g] = acc;
+    acc += static_cast<int32_t>(pad64(off[g + 1] - off[g]));
+  }
+  kofs[G] = acc;
+}
+
+// out[g][c][col_off + r] = in[g][r][c] for in [G][R][C] (R, C multiples of
+// 64); out rows hold ld elements.  A 64 x 64 tile goes through LDS with
+// 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             int R, int C,
+                                                             uint16_t* __restrict__ out, int ld,
+                                                             int col_off) {
+  __shared__ __align__(16) uint16_t t[kTr][kTr + 8];
+  const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr;
+  const uint16_t* src = in + static_cast<int64_t>(blockIdx.z) * R * C;
+  uint16_t* dst = out + static_cast<int64_t>(blockIdx.z) * C * ld;
+  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
+    const int r = i / 8, ch = i % 8;
+    *reinterpret_cast<u32x4*>(&t[r][ch * 8]) =
+        *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r0 + r) * C + c0 + ch * 8);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
+    const int c = i / 8, ch = i % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = static_cast<uint32_t>(t[ch * 8 + 2 * u][c]) |
+             (static_cast<uint32_t>(t[ch * 8 + 2 * u + 1][c]) << 16);
+    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c0 + c) * ld + col_off + r0 + ch * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Group of transposed column kc: the last g with kofs[g] <= kc (kc < kofs[G]).
+__device__ __forceinline__ int kgroup(const int32_t* __restrict__ kofs, int G, int kc) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (kofs[mid] <= kc) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// K-grouped transposed gather: out_z[i][kofs[g] + r - off[g]] = src_z[row(r)][i]
+// for r in group g, row(r) = a_rows[r] / a_div (or r), i < d; padding
+// columns are zero.  z = blockIdx.z selects (src0, out0) or (src1, out1).
+__global__ __launch_bounds__(256) void gather_transpose_kernel(
+    const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
+    const int32_t* __restrict__ a_rows, int a_div, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ kofs, int G, int d, uint16_t* __restrict__ out0,
+    uint16_t* __restrict__ out1, int64_t kt) {
+  __shared__ __align__(16) uint16_t t[kTr][kTr + 8];
+  const int kc0 = blockIdx.x * kTr;
+  if (kc0 >= kofs[G]) return;
+  const uint16_t* src = blockIdx.z ? src1 : src0;
+  uint16_t* out = blockIdx.z ? out1 : out0;
+  const int g = kgroup(kofs, G, kc0);
+  const int r_base = off[g] + (kc0 - kofs[g]), r_end = off[g + 1];
+  const int i0 = blockIdx.y * kTr;
+  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
+    const int rr = i / 8, ch = i % 8;
+    const int r = r_base + rr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < r_end) {
+      const int64_t sr = a_rows ? a_rows[r] / a_div : r;
+      v = *reinterpret_cast<const u32x4*>(src + sr * d + i0 + ch * 8);
+    }
+    *reinterpret_cast<u32x4*>(&t[rr][ch * 8]) = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
+    const int c = i / 8, ch = i % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = static_cast<uint32_t>(t[ch * 8 + 2 * u][c]) |
+             (static_cast<uint32_t>(t[ch * 8 + 2 * u + 1][c]) << 16);
+    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(i0 + c) * kt + kc0 + ch * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Zeroes the padding columns [kofs[g] + rows_g, kofs[g+1]) of rows0 rows of
+// p0 and rows1 rows of p1 (both [*, kt]); block (g, 64-row block).
+__global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ kofs,
+                                                       uint16_t* __restrict__ p0, int rows0,
+                                                       uint16_t* __restrict__ p1, int rows1,
+                                                       int64_t kt) {
+  const int g = blockIdx.x;
+  const int c0 = kofs[g] + (off[g + 1] - off[g]), c1 = kofs[g + 1];
+  if (c0 >= c1) return;
+  for (int i = threadIdx.x; i < kTr * kTr; i += 256) {
+    const int rr = i / kTr, c = i % kTr;
+    if (c0 + c >= c1) continue;
+    const int row = blockIdx.y * kTr + rr;
+    if (row < rows0) p0[row * kt + c0 + c] = 0;
+    else if (row - rows0 < rows1) p1[(row - rows0) * kt + c0 + c] = 0;
+  }
+}
+
+// Weight gradients: for every group g, C_g = A[:, cols_g] B[:, cols_g]^T with
+// A [M, kt], B [N, kt] and C_g [M, N] (fp32) at C + g M N; cols_g = the
+// group's (zero-padded) K slices.  One workgroup per output tile (tiles of a
+// group in the banded order, groups in order, contiguous runs per XCD); a
+// group without rows gets zeros.
+__global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int kt, int M, int N,
+    const int32_t* __restrict__ kofs, int G, int mtn, int ntn, float* __restrict__ C) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int per = mtn * ntn, total = G * per, nw8 = (total + 7) & ~7;
+  const int L = xcd_run(blockIdx.x, nw8);
+  if (L >= total) return;
+  const int g = L / per;
+  int local = L - g * per;
+  const int lead = band_lead(mtn);
+  int nt, mt;
+  if (local < lead * ntn) {
+    const int band = local / (kBand * ntn), i = local - band * (kBand * ntn);
+    nt = i / kBand;
+    mt = band * kBand + (i - nt * kBand);
+  } else {
+    local -= lead * ntn;
+    const int mtail = mtn - lead;
+    nt = local / mtail;
+    mt = lead + (local - nt * mtail);
+  }
+  const Tile2 tile = classify(Tile{0, mt * kTileM, M, nt * 256});
+  float* Cg = C + static_cast<int64_t>(g) * M * N;
+  const int ks0 = kofs[g] / kBK, nk = (kofs[g + 1] - kofs[g]) / kBK;
+  if (nk == 0) {
+    const int rows = min(kTileM, M - tile.m0);
+    for (int i = threadIdx.x; i < rows * 64; i += kThreads) {
+      const int r = i / 64, c = tile.n0 + (i % 64) * 4;
+      if (c < N)
+        *reinterpret_cast<f32x4*>(Cg + static_cast<int64_t>(tile.m0 + r) * N + c) =
+            f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    return;
+  }
+  const EpiArgs ep{};
+  if (tile.cls == 0)
+    gemm_tile<256, 2, 2, 256, kRingA, kRingB, false, float, kEpiNone>(
+        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+  else if (tile.cls == 1)
+    gemm_tile<128, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone>(
+        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+  else
+    gemm_tile<64, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone>(
+        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+}
+
+hipError_t wgrad_bf16(const uint16_t* A, const uint16_t* B, int64_t kt, int M, int N,
+                      const int32_t* kofs, int G, float* C, hipStream_t stream) {
+  const int mtn = (M + kTileM - 1) / kTileM, ntn = (N + 255) / 256;
+  const int64_t total = static_cast<int64_t>(G) * mtn * ntn;
+  auto kern = wgrad_bf16_kernel;
+  ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
+  kern<<<static_cast<unsigned>((total + 7) & ~7), kThreads, kGemmLds, stream>>>(
+      A, B, static_cast<int>(kt), M, N, kofs, G, mtn, ntn, C);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t tile_table_bytes(int G) { return sizeof(int32_t) * static_cast<size_t>(tt_entries(G)); }
@@ -1255,7 +1530,7 @@ size_t split_k_workspace_bytes() {
 
 hipError_t launch_gate_up(const SwigluArgs& s, hipStream_t stream) {
   if (!s.bf16) return gate_up_f32(s, stream);
-  if (skinny(s))
+  if (skinny(s) && !s.uv)
     return skinny_bf16<true, uint16_t>(s, s.d, s.h, s.a, s.a_rows, s.a_div, s.w_gate, s.w_up,
                                        s.hid, stream);
   return gate_up_bf16(s, stream);
@@ -1271,6 +1546,86 @@ hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
                                      stream);
   }
   return s.y_bf16 ? down_bf16<uint16_t>(s, stream) : down_bf16<float>(s, stream);
+}
+
+int64_t backward_kt(int64_t max_rows, int G) { return pad64(max_rows) + 64 * static_cast<int64_t>(G); }
+
+hipError_t launch_weights_t(const void* w_gate, const void* w_up, const void* w_down, int d, int h,
+                            int G, void* w_down_t, void* w_gu_t, hipStream_t stream) {
+  const auto* wg = static_cast<const uint16_t*>(w_gate);
+  const auto* wu = static_cast<const uint16_t*>(w_up);
+  const auto* wd = static_cast<const uint16_t*>(w_down);
+  auto* wdt = static_cast<uint16_t*>(w_down_t);
+  auto* wgut = static_cast<uint16_t*>(w_gu_t);
+  const unsigned G_ = static_cast<unsigned>(G);
+  // w_down [G, d, h] -> [G, h, d]; w_gate, w_up [G, h, d] -> halves of [G, d, 2h]
+  transpose_bf16_kernel<<<dim3(h / kTr, d / kTr, G_), 256, 0, stream>>>(wd, d, h, wdt, d, 0);
+  transpose_bf16_kernel<<<dim3(d / kTr, h / kTr, G_), 256, 0, stream>>>(wg, h, d, wgut, 2 * h, 0);
+  transpose_bf16_kernel<<<dim3(d / kTr, h / kTr, G_), 256, 0, stream>>>(wu, h, d, wgut, 2 * h, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
+  const int d = b.d, h = b.h, G = b.G;
+  const int64_t kt = b.kt;
+  kofs_kernel<<<1, 64, 0, stream>>>(b.group_offset, G, b.kofs);
+  // transposed activations for the weight gradients, and their zero padding
+  gather_transpose_kernel<<<dim3(static_cast<unsigned>(kt / kTr), d / kTr, 2), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(b.a), static_cast<const uint16_t*>(b.dy), b.a_rows, b.a_div,
+      b.group_offset, b.kofs, G, d, b.xs_t, b.dy_t, kt);
+  zero_pad_kernel<<<dim3(static_cast<unsigned>(G), (3 * h + kTr - 1) / kTr), 256, 0, stream>>>(
+      b.group_offset, b.kofs, b.dab_t, 2 * h, b.ghid_t, h, kt);
+  // dgrad 1 with the SiLU backward epilogue, then dgrad 2 (no rows: only the
+  // zero weight gradients below)
+  if (b.max_rows > 0) {
+    const int ntn = (h + 255) / 256;
+    const int ncu = compute_units();
+    tile_table_kernel<<<1, 1024, 0, stream>>>(b.group_offset, G, kTileM, ntn, false, b.mstart,
+                                              b.mstart, ncu, d / kBK, false);
+    EpiArgs ep{};
+    ep.uv = const_cast<uint16_t*>(static_cast<const uint16_t*>(b.uv));
+    ep.row_gate = b.row_gate;
+    ep.a_rows = b.a_rows;
+    ep.off = b.group_offset;
+    ep.kofs = b.kofs;
+    ep.kt = kt;
+    ep.dab = b.dab;
+    ep.dabT = b.dab_t;
+    ep.ghidT = b.ghid_t;
+    auto kern = gemm_bf16_kernel<false, uint16_t, kEpiSiluBwd>;
+    ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
+    kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
+        static_cast<const uint16_t*>(b.dy), b.a_rows, b.a_div,
+        static_cast<const uint16_t*>(b.w_down_t), nullptr, static_cast<int64_t>(h) * d, d, h,
+        b.group_offset, b.mstart, G, ntn, static_cast<uint16_t*>(nullptr), nullptr, ncu, ep);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dgrad 2: da = [du | dv] w_gu_t^T, the forward's down-projection path with K = 2h
+  if (b.max_rows > 0) {
+    SwigluArgs s2{};
+    s2.bf16 = true;
+    s2.d = d;
+    s2.h = 2 * h;
+    s2.G = G;
+    s2.group_offset = b.group_offset;
+    s2.max_rows = b.max_rows;
+    s2.w_down = b.w_gu_t;
+    s2.y = b.da;
+    s2.y_bf16 = false;
+    s2.hid = b.dab;
+    s2.mstart = b.mstart;
+    s2.sk_ws = b.sk_ws;
+    e = launch_down(s2, stream);
+    if (e != hipSuccess) return e;
+  }
+  // weight gradients
+  e = wgrad_bf16(b.dy_t, b.ghid_t, kt, d, h, b.kofs, G, b.dw_down, stream);
+  if (e == hipSuccess) e = wgrad_bf16(b.dab_t, b.xs_t, kt, h, d, b.kofs, G, b.dw_gate, stream);
+  if (e == hipSuccess)
+    e = wgrad_bf16(b.dab_t + static_cast<int64_t>(h) * kt, b.xs_t, kt, h, d, b.kofs, G, b.dw_up,
+                   stream);
+  return e;
 }
 
 }  // namespace moe

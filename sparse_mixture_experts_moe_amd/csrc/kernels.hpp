@@ -46,6 +46,7 @@ struct SwigluArgs {
   void* y;
   bool y_bf16;
   void* hid;        // [max_rows, h] in the compute dtype
+  void* uv;         // bf16 gate/up only: [max_rows, 2h] pre-activations kept, or NULL
   int32_t* mstart;  // workspace: tile table (tile_table_bytes(G))
   float* sk_ws;     // workspace: split-K partial tiles (down projection), or NULL
 };
@@ -57,10 +58,57 @@ int compute_units();
 hipError_t launch_gate_up(const SwigluArgs& args, hipStream_t stream);
 hipError_t launch_down(const SwigluArgs& args, hipStream_t stream);
 
+// backward pass of the experts (bf16)
+struct SwigluBwdArgs {
+  const void* a;
+  int d, h, G;
+  const int32_t* group_offset;
+  int64_t max_rows;
+  const int32_t* a_rows;
+  int a_div;
+  const void* dy;           // upstream gradient rows, gathered like a
+  const float* row_gate;    // per pair (a_rows[r]) or per row, or NULL (1)
+  const void* uv;           // [max_rows, 2h] pre-activations of the forward
+  const void* w_down_t;     // [G, h, d]
+  const void* w_gu_t;       // [G, d, 2h]
+  float* da;                // [max_rows, d]
+  float* dw_gate;           // [G, h, d]
+  float* dw_up;             // [G, h, d]
+  float* dw_down;           // [G, d, h]
+  // workspace
+  int32_t* mstart;          // tile table
+  float* sk_ws;             // split-K partial tiles
+  int32_t* kofs;            // [G + 1]
+  int64_t kt;               // backward_kt(max_rows, G)
+  uint16_t* xs_t;           // [d, kt]
+  uint16_t* dy_t;           // [d, kt]
+  uint16_t* dab;            // [max_rows, 2h]
+  uint16_t* dab_t;          // [2h, kt]
+  uint16_t* ghid_t;         // [h, kt]
+};
+// columns of the K-grouped transposed operands of the weight gradients
+int64_t backward_kt(int64_t max_rows, int G);
+hipError_t launch_weights_t(const void* w_gate, const void* w_up, const void* w_down, int d, int h,
+                            int G, void* w_down_t, void* w_gu_t, hipStream_t stream);
+hipError_t launch_expert_backward(const SwigluBwdArgs& args, hipStream_t stream);
+
 // combine.hip
 hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
                           int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
                           hipStream_t stream);
+
+// backward.hip: combine, gate/router and router-linear gradients
+hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,
+                                   const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
+                                   hipStream_t stream);
+hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
+                                 const float* dgate, const int32_t* count, int64_t T, int E, int k,
+                                 float alpha, float c_bal, float c_z, float* dlogits,
+                                 hipStream_t stream);
+size_t router_backward_workspace_bytes(int64_t T, int d, int E);
+hipError_t launch_router_backward(const void* x, const void* w_router, bool bf16, const float* dl,
+                                  int64_t T, int d, int E, float* dw_router, float* dlogit_bias,
+                                  float* dx, bool dx_accumulate, void* ws, hipStream_t stream);
 
 // stats.hip
 int64_t stats_blocks(int64_t T);

@@ -355,11 +355,221 @@ moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
   if (T < 0 || k < 1 || d < 1) return fail(MOE_EINVAL, "moe_combine: need T >= 0, k >= 1, d >= 1");
   if (!valid_dtype(y_dt) || !valid_dtype(out_dt)) return fail(MOE_EINVAL, "moe_combine: dtype");
   if (T == 0) return ok();
-  if (!y_perm || !pair_row || !topk_gate || !out)
-    return fail(MOE_EINVAL, "moe_combine: NULL pointer");
+  if (!y_perm || !pair_row || !out) return fail(MOE_EINVAL, "moe_combine: NULL pointer");
   return hip_status(moe::launch_combine(y_perm, y_dt == MOE_BF16, pair_row, topk_gate, T, k, d,
                                         shared_y, out, out_dt == MOE_BF16, as_stream(stream)),
                     "moe_combine");
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
+                                      const int32_t* group_offset, int64_t max_rows,
+                                      const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                      const void* w_up, void* hid, void* uv, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  moe_status_t st = check_experts("moe_expert_gate_up_train", dt, d, h, G, max_rows, group_offset);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_expert_gate_up_train: bf16 only");
+  if (max_rows == 0) return ok();
+  if (!a || !w_gate || !w_up || !hid || !uv)
+    return fail(MOE_EINVAL, "moe_expert_gate_up_train: NULL pointer");
+  if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "moe_expert_gate_up_train: a_rows_div < 1");
+  if (ws_bytes < moe_expert_group_workspace(G) || !ws)
+    return fail(MOE_EWORKSPACE, "moe_expert_gate_up_train: workspace %zu < %zu bytes", ws_bytes,
+                moe_expert_group_workspace(G));
+  moe::SwigluArgs s{};
+  s.a = a;
+  s.bf16 = true;
+  s.d = d;
+  s.h = h;
+  s.G = G;
+  s.group_offset = group_offset;
+  s.max_rows = max_rows;
+  s.a_rows = a_rows;
+  s.a_div = a_rows ? a_rows_div : 1;
+  s.w_gate = w_gate;
+  s.w_up = w_up;
+  s.hid = hid;
+  s.uv = uv;
+  s.mstart = static_cast<int32_t*>(ws);
+  s.sk_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + tile_table_bytes(G));
+  return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up_train");
+}
+
+moe_status_t moe_expert_weights_t(const void* w_gate, const void* w_up, const void* w_down, int dt,
+                                  int d, int h, int G, void* w_down_t, void* w_gu_t,
+                                  void* stream) {
+  if (d < 1 || h < 1 || G < 1) return fail(MOE_EINVAL, "moe_expert_weights_t: need d, h, G >= 1");
+  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: bf16 only");
+  if (d % 64 != 0 || h % 64 != 0)
+    return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: needs d %% 64 == 0 and h %% 64 == 0");
+  if (G > 65535) return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: G > 65535");
+  if (!w_gate || !w_up || !w_down || !w_down_t || !w_gu_t)
+    return fail(MOE_EINVAL, "moe_expert_weights_t: NULL pointer");
+  return hip_status(moe::launch_weights_t(w_gate, w_up, w_down, d, h, G, w_down_t, w_gu_t,
+                                          as_stream(stream)),
+                    "moe_expert_weights_t");
+}
+
+namespace {
+
+struct BwdLayout {
+  size_t table, sk, kofs, xs_t, dy_t, dab, dab_t, ghid_t, total;
+  int64_t kt;
+};
+
+BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G) {
+  BwdLayout L{};
+  L.kt = moe::backward_kt(max_rows, G);
+  const size_t kt = static_cast<size_t>(L.kt);
+  size_t o = 0;
+  L.table = o;
+  o += tile_table_bytes(G);
+  L.sk = o;
+  o += moe::split_k_workspace_bytes();
+  L.kofs = o;
+  o += align256(sizeof(int32_t) * (static_cast<size_t>(G) + 1));
+  L.xs_t = o;
+  o += align256(2 * static_cast<size_t>(d) * kt);
+  L.dy_t = o;
+  o += align256(2 * static_cast<size_t>(d) * kt);
+  L.dab = o;
+  o += align256(2 * static_cast<size_t>(max_rows) * 2 * h);
+  L.dab_t = o;
+  o += align256(2 * static_cast<size_t>(2 * h) * kt);
+  L.ghid_t = o;
+  o += align256(2 * static_cast<size_t>(h) * kt);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt) {
+  if (max_rows < 0 || d < 1 || h < 1 || G < 1 || dt != MOE_BF16) return 0;
+  return bwd_layout(max_rows, d, h, G).total;
+}
+
+moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
+                                        const int32_t* group_offset, int64_t max_rows,
+                                        const int32_t* a_rows, int a_rows_div, const void* dy,
+                                        const float* row_gate, const void* uv,
+                                        const void* w_down_t, const void* w_gu_t, float* da,
+                                        float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  const char* fn = "moe_expert_swiglu_backward";
+  moe_status_t st = check_experts(fn, dt, d, h, G, max_rows, group_offset);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: bf16 only", fn);
+  if (static_cast<int64_t>(d) * h * 4 > static_cast<int64_t>(UINT32_MAX))
+    return fail(MOE_EUNSUPPORTED, "%s: 4 d h over 2^32 (transposed gate/up weights)", fn);
+  const BwdLayout L = bwd_layout(max_rows, d, h, G);
+  if (static_cast<int64_t>(d > h ? d : h) * L.kt * 2 > static_cast<int64_t>(UINT32_MAX) ||
+      L.kt > INT32_MAX / 2)
+    return fail(MOE_EUNSUPPORTED, "%s: too many rows for 32-bit operand offsets", fn);
+  if (G > 65535) return fail(MOE_EUNSUPPORTED, "%s: G > 65535", fn);
+  if (!dw_gate || !dw_up || !dw_down || !w_down_t || !w_gu_t)
+    return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if (max_rows > 0 && (!a || !dy || !uv || !da)) return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "%s: a_rows_div < 1", fn);
+  if (ws_bytes < L.total || !ws)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  moe::SwigluBwdArgs b{};
+  b.a = a;
+  b.d = d;
+  b.h = h;
+  b.G = G;
+  b.group_offset = group_offset;
+  b.max_rows = max_rows;
+  b.a_rows = a_rows;
+  b.a_div = a_rows ? a_rows_div : 1;
+  b.dy = dy;
+  b.row_gate = row_gate;
+  b.uv = uv;
+  b.w_down_t = w_down_t;
+  b.w_gu_t = w_gu_t;
+  b.da = da;
+  b.dw_gate = dw_gate;
+  b.dw_up = dw_up;
+  b.dw_down = dw_down;
+  b.mstart = reinterpret_cast<int32_t*>(w + L.table);
+  b.sk_ws = reinterpret_cast<float*>(w + L.sk);
+  b.kofs = reinterpret_cast<int32_t*>(w + L.kofs);
+  b.kt = L.kt;
+  b.xs_t = reinterpret_cast<uint16_t*>(w + L.xs_t);
+  b.dy_t = reinterpret_cast<uint16_t*>(w + L.dy_t);
+  b.dab = reinterpret_cast<uint16_t*>(w + L.dab);
+  b.dab_t = reinterpret_cast<uint16_t*>(w + L.dab_t);
+  b.ghid_t = reinterpret_cast<uint16_t*>(w + L.ghid_t);
+  return hip_status(moe::launch_expert_backward(b, as_stream(stream)), fn);
+}
+
+moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+                                  const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
+                                  void* stream) {
+  if (T < 0 || k < 1 || d < 1)
+    return fail(MOE_EINVAL, "moe_combine_backward: need T >= 0, k >= 1, d >= 1");
+  if (!valid_dtype(dy_dt) || !valid_dtype(y_dt))
+    return fail(MOE_EINVAL, "moe_combine_backward: dtype");
+  if (T == 0) return ok();
+  if (!dy || !y_perm || !pair_row || !dgate)
+    return fail(MOE_EINVAL, "moe_combine_backward: NULL pointer");
+  return hip_status(moe::launch_combine_backward(dy, dy_dt == MOE_BF16, y_perm, y_dt == MOE_BF16,
+                                                 pair_row, T, k, d, dgate, as_stream(stream)),
+                    "moe_combine_backward");
+}
+
+moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
+                                const float* topk_gate, const float* dgate,
+                                const int32_t* expert_count, int64_t T, int E, int k, float alpha,
+                                float coef_balance, float coef_z, float* dlogits, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_route_backward: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_route_backward: need 1 <= k <= E");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_route_backward: E > %d", moe::kMaxExperts);
+  if (T == 0) return ok();
+  if (!logits || !topk_idx || !topk_gate || !dgate || !dlogits ||
+      (coef_balance != 0.0f && !expert_count))
+    return fail(MOE_EINVAL, "moe_route_backward: NULL pointer");
+  return hip_status(moe::launch_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, T,
+                                               E, k, alpha, coef_balance, coef_z, dlogits,
+                                               as_stream(stream)),
+                    "moe_route_backward");
+}
+
+size_t moe_router_backward_workspace(int64_t T, int d, int E) {
+  if (T < 0 || d < 1 || E < 1) return 0;
+  return align256(moe::router_backward_workspace_bytes(T, d, E));
+}
+
+moe_status_t moe_router_backward(const void* x, const void* w_router, int dt,
+                                 const float* dlogits, int64_t T, int d, int E, float* dw_router,
+                                 float* dlogit_bias, float* dx, int accumulate_dx, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (T < 0 || d < 1 || E < 1) return fail(MOE_EINVAL, "moe_router_backward: need T >= 0, d, E >= 1");
+  if (!valid_dtype(dt)) return fail(MOE_EINVAL, "moe_router_backward: dtype");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_router_backward: E > %d", moe::kMaxExperts);
+  if (T == 0) {
+    // no tokens: the weight and bias gradients are zero
+    hipStream_t s = as_stream(stream);
+    hipError_t e = hipSuccess;
+    if (dw_router) e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(dw_router), static_cast<int64_t>(E) * d, 0, s);
+    if (e == hipSuccess && dlogit_bias) e = moe::launch_fill_i32(reinterpret_cast<int32_t*>(dlogit_bias), E, 0, s);
+    return hip_status(e, "moe_router_backward");
+  }
+  if (!dlogits || (dw_router && !x) || (dx && !w_router))
+    return fail(MOE_EINVAL, "moe_router_backward: NULL pointer");
+  const size_t need = dw_router ? moe_router_backward_workspace(T, d, E) : 0;
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_EWORKSPACE, "moe_router_backward: workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(moe::launch_router_backward(x, w_router, dt == MOE_BF16, dlogits, T, d, E,
+                                                dw_router, dlogit_bias, dx, accumulate_dx != 0, ws,
+                                                as_stream(stream)),
+                    "moe_router_backward");
 }
 
 // ---------------------------------------------------------------------------

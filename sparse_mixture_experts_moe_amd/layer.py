@@ -10,6 +10,11 @@ and the routed experts; the combine waits for them.
 The layer output excludes the residual ("Every parameter, every token",
 section "The gating network": the weighted sum is added back to the residual
 stream outside the slot).
+
+``forward(x, train=True)`` also keeps what the backward pass reads (the
+experts' pre-activations); ``backward(dy)`` then returns the gradients of
+<dy, y> + coef_balance * loss + coef_z * zloss with respect to x and every
+weight, through seven more library calls.
 """
 
 from __future__ import annotations
@@ -93,11 +98,67 @@ class MoELayer:
         self._bufs[key] = b
         return b
 
-    def forward(self, x, stream=None, mark=None):
+    def _train_buffers(self, x, b):
+        """Buffers of the training forward (pre-activations) and the backward."""
+        if "uv" in b:
+            return b
+        T = x.shape[0]
+        dev, E, k, d, h = x.device, self.E, self.k, self.d, self.h
+        R = T * k
+        dt = _lib._dt(x)
+        f32 = torch.float32
+        b["uv"] = torch.empty((R, 2 * h), dtype=x.dtype, device=dev)
+        b["dgate"] = torch.empty((T, k), dtype=f32, device=dev)
+        b["dlogits"] = torch.empty((T, E), dtype=f32, device=dev)
+        b["w_down_t"] = torch.empty((E, h, d), dtype=x.dtype, device=dev)
+        b["w_gu_t"] = torch.empty((E, d, 2 * h), dtype=x.dtype, device=dev)
+        b["da"] = torch.empty((R, d), dtype=f32, device=dev)
+        b["dw_gate"] = torch.empty((E, h, d), dtype=f32, device=dev)
+        b["dw_up"] = torch.empty((E, h, d), dtype=f32, device=dev)
+        b["dw_down"] = torch.empty((E, d, h), dtype=f32, device=dev)
+        b["bwd_ws"] = torch.empty(max(1, _lib.moe_expert_swiglu_backward_workspace(R, d, h, E, dt)),
+                                  dtype=torch.uint8, device=dev)
+        b["dw_router"] = torch.empty((E, d), dtype=f32, device=dev)
+        b["dlogit_bias"] = torch.empty(E, dtype=f32, device=dev)
+        b["dx_acc"] = torch.empty((T, d), dtype=f32, device=dev)
+        b["dx"] = torch.empty((T, d), dtype=f32, device=dev)
+        b["router_ws"] = torch.empty(max(1, _lib.moe_router_backward_workspace(T, d, E)),
+                                     dtype=torch.uint8, device=dev)
+        if self.shared is not None:
+            Hs = self.shared[0].shape[1]
+            b["shared_hid"] = torch.empty((T, Hs), dtype=x.dtype, device=dev)
+            b["shared_uv"] = torch.empty((T, 2 * Hs), dtype=x.dtype, device=dev)
+            b["shared_w_down_t"] = torch.empty((1, Hs, d), dtype=x.dtype, device=dev)
+            b["shared_w_gu_t"] = torch.empty((1, d, 2 * Hs), dtype=x.dtype, device=dev)
+            b["shared_dw_gate"] = torch.empty((1, Hs, d), dtype=f32, device=dev)
+            b["shared_dw_up"] = torch.empty((1, Hs, d), dtype=f32, device=dev)
+            b["shared_dw_down"] = torch.empty((1, d, Hs), dtype=f32, device=dev)
+            b["shared_bwd_ws"] = torch.empty(
+                max(1, _lib.moe_expert_swiglu_backward_workspace(T, d, Hs, 1, dt)),
+                dtype=torch.uint8, device=dev)
+        return b
+
+    def _shared_forward(self, x, b, train, stream):
+        sg, su, sd = self.shared
+        T = x.shape[0]
+        if not train:
+            return _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd, y=b["shared_y"],
+                                          ws=b["shared_ws"], stream=stream)
+        table = b["shared_ws"][-_lib.moe_expert_group_workspace(1):]
+        _lib.moe_expert_gate_up_train(x, b["shared_off"], T, sg, su, hid=b["shared_hid"],
+                                      uv=b["shared_uv"], ws=table, stream=stream)
+        return _lib.moe_expert_down(b["shared_hid"], b["shared_off"], T, sd, y=b["shared_y"],
+                                    ws=table, stream=stream)
+
+    def forward(self, x, stream=None, mark=None, train=False):
         """Returns a dict of the output and every intermediate the calls produce.
         ``mark(name)``, if given, is called after each library call is enqueued
-        (the benchmark records a HIP event there)."""
+        (the benchmark records a HIP event there).  ``train`` keeps the experts'
+        pre-activations for ``backward`` (bf16 only)."""
         b = self._buffers(x)
+        if train:
+            self._train_buffers(x, b)
+            b["x"] = x
         T = x.shape[0]
         k, E = self.k, self.E
         mark = mark or (lambda name: None)
@@ -113,9 +174,7 @@ class MoELayer:
             x_ready = torch.cuda.Event()
             x_ready.record(main)
             side.wait_event(x_ready)
-            sg, su, sd = self.shared
-            shared_y = _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd,
-                                              y=b["shared_y"], ws=b["shared_ws"], stream=side)
+            shared_y = self._shared_forward(x, b, train, side)
             shared_done = torch.cuda.Event()
             shared_done.record(side)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
@@ -132,17 +191,20 @@ class MoELayer:
             a, a_rows = b["x_perm"], None
         else:
             a, a_rows = x, b["row_pair"]
-        _lib.moe_expert_gate_up(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
-                                a_rows=a_rows, a_rows_div=k, hid=b["hid"], ws=b["table_ws"],
-                                stream=stream)
+        if train:
+            _lib.moe_expert_gate_up_train(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
+                                          a_rows=a_rows, a_rows_div=k, hid=b["hid"], uv=b["uv"],
+                                          ws=b["table_ws"], stream=stream)
+        else:
+            _lib.moe_expert_gate_up(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
+                                    a_rows=a_rows, a_rows_div=k, hid=b["hid"], ws=b["table_ws"],
+                                    stream=stream)
         mark("gate_up")
         _lib.moe_expert_down(b["hid"], b["expert_offset"], T * k, self.w_down, y=b["y_perm"],
                              ws=b["table_ws"], stream=stream)
         mark("down")
         if self.shared is not None and not self.overlap_shared:
-            sg, su, sd = self.shared
-            shared_y = _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd,
-                                              y=b["shared_y"], ws=b["shared_ws"], stream=stream)
+            shared_y = self._shared_forward(x, b, train, stream)
             mark("shared")
         if shared_done is not None:
             main.wait_event(shared_done)
@@ -155,3 +217,56 @@ class MoELayer:
         return b
 
     __call__ = forward
+
+    def backward(self, dy, coef_balance=0.0, coef_z=0.0, stream=None, mark=None,
+                 weights_t=True):
+        """Gradients after ``forward(x, train=True)`` on the same x: fills and
+        returns the buffer dict with dx [T, d], dw_router, dlogit_bias (when the
+        layer has a logit bias), dw_gate, dw_up, dw_down, and shared_dw_* (fp32),
+        plus the intermediates dgate and dlogits.  ``weights_t`` False reuses the
+        transposed weight copies of the previous call (valid while the weights
+        are unchanged)."""
+        T = dy.shape[0]
+        b = self._bufs[(T, dy.dtype, dy.device)]
+        if "x" not in b:
+            raise RuntimeError("backward needs forward(x, train=True) first")
+        x = b["x"]
+        k, E = self.k, self.E
+        mark = mark or (lambda name: None)
+        _lib.moe_combine_backward(dy, b["y_perm"], b["pair_row"], k, dgate=b["dgate"],
+                                  stream=stream)
+        mark("combine_bwd")
+        _lib.moe_route_backward(b["logits"], b["topk_idx"], b["topk_gate"], b["dgate"],
+                                b["expert_count"], self.alpha, coef_balance, coef_z,
+                                dlogits=b["dlogits"], stream=stream)
+        mark("route_bwd")
+        if weights_t:
+            _lib.moe_expert_weights_t(self.w_gate, self.w_up, self.w_down,
+                                      w_down_t=b["w_down_t"], w_gu_t=b["w_gu_t"], stream=stream)
+            if self.shared is not None:
+                sg, su, sd = self.shared
+                _lib.moe_expert_weights_t(sg, su, sd, w_down_t=b["shared_w_down_t"],
+                                          w_gu_t=b["shared_w_gu_t"], stream=stream)
+            mark("weights_t")
+        _lib.moe_expert_swiglu_backward(
+            x, b["expert_offset"], T * k, dy, b["uv"], b["w_down_t"], b["w_gu_t"],
+            a_rows=b["row_pair"], a_rows_div=k, row_gate=b["topk_gate"], da=b["da"],
+            dw_gate=b["dw_gate"], dw_up=b["dw_up"], dw_down=b["dw_down"], ws=b["bwd_ws"],
+            stream=stream)
+        mark("experts_bwd")
+        if self.shared is not None:
+            _lib.moe_expert_swiglu_backward(
+                x, b["shared_off"], T, dy, b["shared_uv"], b["shared_w_down_t"],
+                b["shared_w_gu_t"], da=b["dx_acc"], dw_gate=b["shared_dw_gate"],
+                dw_up=b["shared_dw_up"], dw_down=b["shared_dw_down"], ws=b["shared_bwd_ws"],
+                stream=stream)
+            mark("shared_bwd")
+        _lib.moe_router_backward(x, self.w_router, b["dlogits"], dw_router=b["dw_router"],
+                                 dlogit_bias=b["dlogit_bias"] if self.logit_bias is not None else None,
+                                 dx=b["dx_acc"], accumulate_dx=self.shared is not None,
+                                 want=("dw", "dx"), ws=b["router_ws"], stream=stream)
+        mark("router_bwd")
+        _lib.moe_combine(b["da"], b["pair_row"], None, b["dx_acc"], out=b["dx"], k=k,
+                         stream=stream)
+        mark("dx")
+        return b

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert L.moe_status_string(L.MOE_OK) == "ok"
     assert L.moe_status_string(L.MOE_EWORKSPACE) == "workspace too small"
     assert L.moe_status_string(99) == "unknown status"

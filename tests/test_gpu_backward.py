@@ -1,0 +1,213 @@
+"""GPU parity of the backward pass against the CPU oracle (needs an MI355X).
+
+The objective is <dy, y> + c_bal * loss + c_z * zloss ("Every parameter,
+every token", sections "The gating network" and "A balance penalty"; Zen-Max,
+section "MoE-Specific Training Stability").  The oracle runs on the GPU's own
+float32 logits, so both sides route identically.
+
+Tolerances:
+  * routing-side kernels on identical inputs (the GPU's dgate and dlogits fed
+    to the oracle's formulas): 1e-5 max-abs relative (fp32 arithmetic);
+  * everything downstream of the bf16 expert GEMMs (dgate, dlogits, dx and
+    the expert weight gradients, per expert): 2e-2 max-abs relative, the bf16
+    output bar; u, v, [du | dv] and the gated hidden activation are rounded
+    to bf16 between the GEMMs (relative 2^-9 each);
+  * the kept pre-activations uv: 1e-2; transposed weights: bit-exact;
+  * experts without rows: exactly zero weight gradients.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import Bf16, as_f32, generate, generate_dy, small_case
+from tests.gpu_helpers import build_layer, check_layer, host, normwise, shared_list, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+CASES = {
+    "mixtral_small": (small_case("mixtral_bf16", T=1600, d=256, h=320, cid_offset=300), 1.0, 0.1),
+    "finegrained_small": (small_case("finegrained_shared_bf16", T=512, d=128, h=128, h_shared=64),
+                          1.0, 0.1),
+    "capacity_small": (small_case("capacity_balance_bf16", T=2048, d=192, h=256), 1.0, 0.0),
+    "decode_small": (small_case("decode_bf16", T=64, d=256, h=128, h_shared=512), 0.0, 0.1),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from sparse_mixture_experts_moe_amd import _lib  # noqa: F401  (fails loudly if not built)
+
+
+def _split_shared(g, inp):
+    """Concatenated shared-expert gradients -> per shared expert (gate, up, down)."""
+    ns, hs = inp["shared_gate"].shape[0], inp["shared_gate"].shape[1]
+    out = []
+    for s in range(ns):
+        sl = slice(s * hs, (s + 1) * hs)
+        out.append((g[0][0, sl], g[1][0, sl], g[2][0][:, sl]))
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_layer_backward(name):
+    cfg, c_bal, c_z = CASES[name]
+    _say(f"[case] {name} {cfg} c_bal={c_bal} c_z={c_z}")
+    inp = generate(cfg)
+    dy_h = generate_dy(cfg)
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    dy = to_device(dy_h)
+    res = layer.forward(x, train=True)
+    layer.backward(dy, c_bal, c_z)
+    torch.cuda.synchronize()
+    check_layer(inp, res)  # the training forward's output
+
+    T, E, k = cfg.T, cfg.E, cfg.k
+    xf, wr = as_f32(inp["x"]), as_f32(inp["w_router"])
+    wg, wu, wd = as_f32(inp["w_gate"]), as_f32(inp["w_up"]), as_f32(inp["w_down"])
+    dyf = as_f32(dy_h)
+    gl = host(res["logits"])
+    cap = oracle.capacity(cfg.cf, T, k, E)
+    ref = oracle.backward(xf, wr, wg, wu, wd, k, dyf, shared=shared_list(inp),
+                          logit_bias=inp["logit_bias"], select_bias=inp["select_bias"], cap=cap,
+                          alpha=cfg.alpha, c_bal=c_bal, c_z=c_z, logits=gl)
+    fw = ref["fwd"]
+    errs = {}
+
+    # kept pre-activations of the routed rows
+    R = int(fw["offset"][-1])
+    rp = fw["row_pair"][:R]
+    u_ref = np.concatenate([xf[rp[r] // k][None] @ wg[e].T for e in range(E)
+                            for r in range(fw["offset"][e], fw["offset"][e + 1])], axis=0) if R else None
+    if R:
+        v_ref = np.concatenate([xf[rp[r] // k][None] @ wu[e].T for e in range(E)
+                                for r in range(fw["offset"][e], fw["offset"][e + 1])], axis=0)
+        uv = host(res["uv"])[:R]
+        errs["uv"] = max(normwise(uv[:, :cfg.h], u_ref), normwise(uv[:, cfg.h:], v_ref))
+        assert errs["uv"] <= 1e-2, errs
+
+    # transposed weights: exact copies
+    assert torch.equal(res["w_down_t"], layer.w_down.transpose(1, 2).contiguous())
+    assert torch.equal(res["w_gu_t"][:, :, :cfg.h], layer.w_gate.transpose(1, 2).contiguous())
+    assert torch.equal(res["w_gu_t"][:, :, cfg.h:], layer.w_up.transpose(1, 2).contiguous())
+
+    # routing side on identical inputs (fp32 kernels)
+    gdg = host(res["dgate"])
+    gdl = host(res["dlogits"])
+    dl_same = oracle.gate_logit_grad(gl, fw["topk_idx"], gdg)
+    if c_bal:
+        dl_same = dl_same + c_bal * oracle.balance_logit_grad(gl, fw["count"], k, cfg.alpha)
+    if c_z:
+        dl_same = dl_same + c_z * oracle.z_loss_logit_grad(gl)
+    errs["dlogits_same_in"] = normwise(gdl, dl_same)
+    assert errs["dlogits_same_in"] <= 1e-5, errs
+    _, dwr_same, dlb_same = oracle.router_linear_backward(xf, wr, gdl)
+    errs["dw_router_same_in"] = normwise(host(res["dw_router"]), dwr_same)
+    assert errs["dw_router_same_in"] <= 1e-5, errs
+    if inp["logit_bias"] is not None:
+        errs["dlogit_bias_same_in"] = normwise(host(res["dlogit_bias"]), dlb_same)
+        assert errs["dlogit_bias_same_in"] <= 1e-5, errs
+    dropped = fw["pair_row"].reshape(T, k) < 0
+    assert np.all(gdg[dropped] == 0.0)
+
+    # end to end against the float64 oracle
+    for key in ("dgate", "dlogits", "dx", "dw_router"):
+        errs[key] = normwise(host(res[key]), ref[key])
+        assert errs[key] <= 2e-2, errs
+    kept = fw["kept"]
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        got = host(res[key])
+        worst = 0.0
+        for e in range(E):
+            if kept[e] == 0:
+                assert np.all(got[e] == 0.0), (key, e)
+                continue
+            worst = max(worst, normwise(got[e], ref[key][e]))
+        errs[key] = worst
+        assert worst <= 2e-2, errs
+    if inp["shared_gate"] is not None:
+        got = _split_shared((host(res["shared_dw_gate"]), host(res["shared_dw_up"]),
+                             host(res["shared_dw_down"])), inp)
+        worst = max(normwise(got[s][j], ref["dshared"][s][j])
+                    for s in range(len(got)) for j in range(3))
+        errs["shared"] = worst
+        assert worst <= 2e-2, errs
+    _say(f"[ok] {name}: " + ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+
+
+def test_backward_deterministic():
+    cfg, c_bal, c_z = CASES["finegrained_small"]
+    inp = generate(cfg)
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    dy = to_device(generate_dy(cfg))
+    outs = []
+    for _ in range(2):
+        layer.forward(x, train=True)
+        b = layer.backward(dy, c_bal, c_z)
+        torch.cuda.synchronize()
+        outs.append({k: b[k].clone() for k in ("dx", "dw_gate", "dw_up", "dw_down", "dw_router",
+                                                "dlogits", "shared_dw_gate")})
+    for key in outs[0]:
+        assert torch.equal(outs[0][key], outs[1][key]), key
+
+
+@pytest.mark.parametrize("sizes,d,h,gated", [
+    ([60], 128, 64, False),
+    ([17, 0, 29, 300], 192, 128, True),
+    ([3] * 47 + [0] + [3] * 48, 128, 192, True),
+    ([0, 0], 64, 64, False),
+    ([257, 1, 64, 128], 256, 320, True),
+])
+def test_expert_backward_groups(sizes, d, h, gated):
+    """moe_expert_swiglu_backward alone on ragged groups (empty ones included),
+    with and without a per-row gate, against the oracle's expert backward."""
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] groups {sizes[:6]}{'...' if len(sizes) > 6 else ''} d={d} h={h} gated={gated}")
+    rng = np.random.default_rng(len(sizes) * 1000 + d + h)
+    G = len(sizes)
+    R = int(sum(sizes))
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+    def bf(a):
+        from moe_inputs import bf16_bits_rne
+        return Bf16(bf16_bits_rne(a.astype(np.float32)))
+
+    a = bf(rng.standard_normal((max(R, 1), d)))
+    wg = bf(rng.standard_normal((G, h, d)) / np.sqrt(d))
+    wu = bf(rng.standard_normal((G, h, d)) / np.sqrt(d))
+    wd = bf(rng.standard_normal((G, d, h)) / np.sqrt(h))
+    dy = bf(rng.standard_normal((max(R, 1), d)))
+    gate = rng.uniform(0.1, 1.0, max(R, 1)).astype(np.float32)
+    A, WG, WU, WD, DY = (to_device(t) for t in (a, wg, wu, wd, dy))
+    goff = torch.from_numpy(off).cuda()
+    rg = torch.from_numpy(gate).cuda() if gated else None
+    _, uv = _lib.moe_expert_gate_up_train(A, goff, R, WG, WU)
+    wdt, wgut = _lib.moe_expert_weights_t(WG, WU, WD)
+    da, dwg, dwu, dwd = _lib.moe_expert_swiglu_backward(A, goff, R, DY, uv, wdt, wgut,
+                                                        row_gate=rg)
+    torch.cuda.synchronize()
+    af, dyf = as_f32(a), as_f32(dy)
+    wgf, wuf, wdf = as_f32(wg), as_f32(wu), as_f32(wd)
+    da_h, dwg_h, dwu_h, dwd_h = host(da), host(dwg), host(dwu), host(dwd)
+    for g in range(G):
+        r0, r1 = off[g], off[g + 1]
+        if r0 == r1:
+            assert np.all(dwg_h[g] == 0) and np.all(dwu_h[g] == 0) and np.all(dwd_h[g] == 0)
+            continue
+        s = gate[r0:r1, None] if gated else 1.0
+        ref = oracle.swiglu_backward(af[r0:r1], wgf[g], wuf[g], wdf[g], s * dyf[r0:r1])
+        for got, want in ((da_h[r0:r1], ref[0]), (dwg_h[g], ref[1]), (dwu_h[g], ref[2]),
+                          (dwd_h[g], ref[3])):
+            assert normwise(got, want) <= 2e-2, (g, normwise(got, want))
