@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared experts in line on the layer's stream instead of "
                          "overlapping them on a second stream")
+    ap.add_argument("--backward", action="store_true",
+                    help="time training steps instead: forward (keeping the pre-activations) "
+                         "plus the backward pass of <dy, y> + loss + 1e-3 zloss")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the warmup, copy a buffer of this many MiB three times with a "
                          "plain device-to-device copy, so that a counter run can scale its byte "
@@ -167,12 +170,168 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5):
                       f"{passes} passes (float64 NumPy, {dt:.1f} s)"}
 
 
+def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max_passes=5):
+    """The backward oracle as it stands (its forward included) on the first
+    n_tok tokens as a batch of their own, repeated until min_seconds."""
+    import oracle
+    from moe_inputs import as_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    x = as_f32(inp["x"])[:n_tok]
+    dyf = as_f32(dy)[:n_tok]
+    wr = as_f32(inp["w_router"])
+    shared = ()
+    if inp["shared_gate"] is not None:
+        shared = [(inp["shared_gate"][s], inp["shared_up"][s], inp["shared_down"][s])
+                  for s in range(cfg.n_shared)]
+    wg, wu, wd = as_f32(inp["w_gate"]), as_f32(inp["w_up"]), as_f32(inp["w_down"])
+    cap = oracle.capacity(cfg.cf, n_tok, cfg.k, cfg.E)
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.backward(x, wr, wg, wu, wd, cfg.k, dyf, shared=shared,
+                        logit_bias=inp["logit_bias"], select_bias=inp["select_bias"], cap=cap,
+                        alpha=cfg.alpha, c_bal=c_bal, c_z=c_z)
+        dt += time.perf_counter() - t0
+        passes += 1
+    return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name} as one batch, forward and "
+                      f"backward, {passes} passes (float64 NumPy, {dt:.1f} s)"}
+
+
+def main_backward(args):
+    """Training steps: forward(train=True) + backward, K timed steps."""
+    import numpy as np
+    import torch
+
+    from moe_inputs import WORKLOADS, generate, generate_dy
+    from sparse_mixture_experts_moe_amd.workload import layer_from_inputs, to_device
+
+    cfg = WORKLOADS[args.workload]
+    if cfg.dtype != "bf16":
+        print(json.dumps({"error": "the backward pass runs in bf16 only"}), flush=True)
+        sys.exit(2)
+    c_bal, c_z = 1.0, 1e-3
+    inp = generate(cfg)
+    dy_h = generate_dy(cfg)
+    layer = layer_from_inputs(inp, args.gather)
+    layer.overlap_shared = not args.serial_shared
+    x = to_device(inp["x"])
+    dy = to_device(dy_h)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        layer.forward(x, train=True)
+        layer.backward(dy, c_bal, c_z)
+    torch.cuda.synchronize()
+
+    # timed region: events only around the expert backward call (the roofline)
+    ex_marks = []
+
+    def mark_experts(name):
+        if name in ("weights_t", "experts_bwd"):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            ex_marks[-1].append(ev)
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        ex_marks.append([])
+        layer.forward(x, train=True)
+        res = layer.backward(dy, c_bal, c_z, mark=mark_experts)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    ex_ms = float(np.mean([a.elapsed_time(b) for a, b in ex_marks]))
+
+    # phase breakdown in a separate pass (shared experts in line)
+    marks = []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks[-1].append((name, ev))
+
+    overlap = layer.overlap_shared
+    layer.overlap_shared = False
+    for _ in range(args.steps):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        marks.append([("start", ev0)])
+        layer.forward(x, mark=mark, train=True)
+        layer.backward(dy, c_bal, c_z, mark=mark)
+    torch.cuda.synchronize()
+    layer.overlap_shared = overlap
+    phases = {}
+    for step in marks:
+        for (_, a), (name, b) in zip(step[:-1], step[1:]):
+            phases.setdefault(name, []).append(a.elapsed_time(b))
+    phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
+
+    offs = res["expert_offset"].cpu().numpy()
+    kept = offs[1:] - offs[:-1]
+    R_kept = int(offs[-1])
+    T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
+    hs = cfg.n_shared * cfg.h_shared
+    # the routed experts' backward call: five GEMMs, 12 d h flops per kept row
+    ex_flops = 12.0 * R_kept * d * h
+    achieved = ex_flops / (ex_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": "moe_expert_swiglu_backward (dgrad with SiLU-backward epilogue, dgrad of "
+                      "the gate/up input, three K-grouped weight-gradient GEMMs, operand "
+                      "transposes)",
+            "per_launch": {"flops": ex_flops, "avg_ms": ex_ms}}
+    ceil = measured_ceilings(torch, None)
+    roof["measured_peak"] = ceil["mfma_bf16_tflops"]
+    roof["frac_of_measured"] = achieved / ceil["mfma_bf16_tflops"]
+    step_flops = (2.0 * T * d * E) * 3 + 18.0 * d * h * R_kept + 18.0 * d * hs * T
+    out = {
+        "metric": "MoE-layer training tokens/sec (forward + backward, 1 GPU)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded normal inputs, upstream gradient and random-init weights of "
+                "the workload's shape)",
+        "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
+                   "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
+                   "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)",
+                   "weights_t_per_step": True},
+        "roofline": roof,
+        "measured_ceilings": ceil,
+        "step_tflops": step_flops / (ms * 1e-3) / 1e12,
+        "phase_ms": phase_ms,
+        "phase_ms_source": "a separate pass of the same steps with a HIP event after every library "
+                           "call (outside the timed region)",
+        "routing": {"kept_pairs": R_kept, "max_rows": int(kept.max()), "min_rows": int(kept.min())},
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or {"mixtral_bf16": 1024, "finegrained_shared_bf16": 2048,
+                                    "capacity_balance_bf16": 2048, "decode_bf16": 64}[cfg.name]
+        out["cpu_baseline"] = cpu_baseline_backward(inp, dy_h, cfg, n_tok, c_bal, c_z)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.backward:
+        return main_backward(args)
 
     import numpy as np
     import torch
