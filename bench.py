@@ -232,7 +232,7 @@ def main_backward(args):
     ex_marks = []
 
     def mark_experts(name):
-        if name in ("weights_t", "experts_bwd"):
+        if name in ("route_bwd", "experts_bwd"):  # enqueued right before / after the call
             ev = torch.cuda.Event(enable_timing=True)
             ev.record(stream)
             ex_marks[-1].append(ev)
@@ -284,8 +284,8 @@ def main_backward(args):
     roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
             "kernel": "moe_expert_swiglu_backward (dgrad with SiLU-backward epilogue, dgrad of "
-                      "the gate/up input, three K-grouped weight-gradient GEMMs, operand "
-                      "transposes)",
+                      "the gate/up input, three weight-gradient GEMMs over each expert's rows, "
+                      "the row gather of x)",
             "per_launch": {"flops": ex_flops, "avg_ms": ex_ms}}
     ceil = measured_ceilings(torch, None)
     roof["measured_peak"] = ceil["mfma_bf16_tflops"]
@@ -307,8 +307,7 @@ def main_backward(args):
                 "the workload's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
-                   "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)",
-                   "weights_t_per_step": True},
+                   "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "measured_ceilings": ceil,
         "step_tflops": step_flops / (ms * 1e-3) / 1e12,

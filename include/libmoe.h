@@ -295,17 +295,17 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
  * gets no gradient from the output but stays in the renormalising softmax.
  *
  * A layer step: moe_expert_gate_up_train + moe_expert_down (forward, keeping
- * the pre-activations uv and the expert rows y_perm) ... then
- *   moe_combine_backward        dgate from dy and y_perm
+ * the pre-activations uv, the hidden activation hid and the expert rows
+ * y_perm), then
+ *   moe_combine_backward        dgate, and dout = gate * dy per kept row
  *   moe_route_backward          dlogits
- *   moe_expert_weights_t        transposed weight copies (once per weight update)
- *   moe_expert_swiglu_backward  routed experts (a_rows = row_pair, row_gate =
- *                               topk_gate) and shared experts (a_rows = NULL)
+ *   moe_expert_swiglu_backward  routed experts (dout rows, a = x gathered
+ *                               through row_pair) and shared experts (dout = dy)
  *   moe_router_backward         router weights, logit bias, dx (accumulate)
  *   moe_combine(da_perm, NULL gates, shared_y = the accumulated dx) -> dx
  * Every gradient output is fp32 and written (not accumulated) unless stated.
- * The bf16 expert kernels keep u, v, [du | dv] and the gated hidden
- * activation in bf16 (rounded to nearest even) between GEMMs.
+ * The bf16 expert kernels keep u, v and [du | dv] in bf16 (rounded to
+ * nearest even) between GEMMs.
  */
 
 /* moe_expert_gate_up_train: moe_expert_gate_up that also keeps the
@@ -319,56 +319,53 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
                                       const void* w_up, void* hid, void* uv, void* ws,
                                       size_t ws_bytes, void* stream);
 
-/* moe_expert_weights_t: the transposed weight copies the input-gradient GEMMs
- * read (the backward contracts over the weights' leading axis):
- *   w_down_t[g] = w_down[g]^T                     [G, h, d]
- *   w_gu_t[g]   = [w_gate[g]^T | w_up[g]^T]       [G, d, 2h]
- * bf16 only, d % 64 == 0, h % 64 == 0.  They stay valid until the weights
- * change, so a caller that runs several backward passes per weight update
- * makes them once. */
-moe_status_t moe_expert_weights_t(const void* w_gate, const void* w_up, const void* w_down, int dt,
-                                  int d, int h, int G, void* w_down_t, void* w_gu_t,
-                                  void* stream);
-
 /* moe_expert_swiglu_backward: gradients of G SwiGLU experts over row groups
  * (same group semantics, gather and limits as moe_expert_swiglu).  For row r
- * of group g with s_r = row_gate[a_rows ? a_rows[r] : r] (1 if row_gate is
- * NULL) and dy_r = dy[a_rows[r] / a_rows_div] (or dy[r]):
- *   u, v    = uv[r, 0:h], uv[r, h:2h]      (from moe_expert_gate_up_train)
- *   dhid    = s_r dy_r . w_down[g]                               ([h])
+ * of group g with a_r = a[a_rows[r] / a_rows_div] (or a[r]) and dout_r the
+ * upstream gradient of the row's expert output (gate already applied):
+ *   u, v    = uv[r, 0:h], uv[r, h:2h]     (from moe_expert_gate_up_train)
+ *   hid_r   = hid[r]                       (SiLU(u) * v, from the same call)
+ *   dhid    = dout_r . w_down[g]                                 ([h])
  *   du      = dhid * v * SiLU'(u),  dv = dhid * SiLU(u)
  *   da[r]   = du . w_gate[g] + dv . w_up[g]                      ([d], fp32)
  *   dw_gate[g] = sum_r du_r^T a_r,  dw_up[g] = sum_r dv_r^T a_r  ([h, d], fp32)
- *   dw_down[g] = sum_r s_r dy_r^T (SiLU(u_r) * v_r)              ([d, h], fp32)
+ *   dw_down[g] = sum_r dout_r^T hid_r                            ([d, h], fp32)
  * with SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z).  A group without rows
- * gets zero weight gradients.  Routed experts: a = x, a_rows = row_pair,
- * a_rows_div = k, row_gate = topk_gate.  Shared experts: a = x, a_rows =
- * NULL, row_gate = NULL, G = 1 (concatenated hidden axis).
- * dt must be bf16; additionally 4 d h < 2^32.  da [max_rows, d] fp32 (rows
- * past group_offset[G] untouched).  w_down_t, w_gu_t from moe_expert_weights_t.
- * Workspace: moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt)
- * bytes (tile table, split-K partials, and the transposed bf16 operands of
- * the weight gradients: about (2 d + 3 h) (max_rows + 64 G) + 4 h max_rows
- * bytes); contents need no initialisation and are dead after the call. */
-size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt);
+ * gets zero weight gradients.  The weights are the forward's (w_gate, w_up
+ * [G, h, d], w_down [G, d, h]); the kernels read them along their leading
+ * axis directly (no transposed copies).  Routed experts: a = x, a_rows =
+ * row_pair, a_rows_div = k, dout from moe_combine_backward.  Shared experts:
+ * a = x, a_rows = NULL, dout = dy, G = 1 (concatenated hidden axis).
+ * dt must be bf16; additionally 4 d h < 2^32.  dout, uv, hid in dt with rows
+ * in group order ([max_rows, *]); da [max_rows, d] fp32 (rows past
+ * group_offset[G] untouched).
+ * Workspace: moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt,
+ * a_rows != NULL) bytes (tile table, split-K partials, a zero row, the
+ * gathered rows of a when a_rows is given, and [du | dv] in bf16: about
+ * 2 max_rows (2h + d) bytes plus 64 MiB); contents need no initialisation
+ * and are dead after the call. */
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,
+                                            int gather);
 moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
                                         const int32_t* group_offset, int64_t max_rows,
-                                        const int32_t* a_rows, int a_rows_div, const void* dy,
-                                        const float* row_gate, const void* uv,
-                                        const void* w_down_t, const void* w_gu_t, float* da,
+                                        const int32_t* a_rows, int a_rows_div, const void* dout,
+                                        const void* uv, const void* hid, const void* w_gate,
+                                        const void* w_up, const void* w_down, float* da,
                                         float* dw_gate, float* dw_up, float* dw_down, void* ws,
                                         size_t ws_bytes, void* stream);
 
 /* moe_combine_backward: the gate gradients of the combine,
  *   dgate[t, j] = sum_i dy[t, i] * y_perm[pair_row[t*k+j], i]   (fp32)
- * and 0 for a dropped pair (pair_row < 0).  Source: "The gating network"
- * (y = sum_j g_j Expert_j(x)).  dy [T, d] in dy_dt; y_perm [*, d] in y_dt
- * (the expert rows moe_expert_down wrote); dgate [T, k] fp32.
- * (The input gradient of the expert rows, g * dy, is formed inside
- * moe_expert_swiglu_backward through row_gate.) */
+ * and 0 for a dropped pair (pair_row < 0); with dout non-NULL also the
+ * upstream gradient of every kept expert row,
+ *   dout[pair_row[t*k+j], :] = topk_gate[t, j] * dy[t, :]       (dy_dt)
+ * Source: "The gating network" (y = sum_j g_j Expert_j(x)).  dy [T, d] in
+ * dy_dt; y_perm [*, d] in y_dt (the expert rows moe_expert_down wrote);
+ * topk_gate [T, k] fp32 (needed with dout); dgate [T, k] fp32; dout [*, d]
+ * or NULL (rows of dropped pairs do not exist; other rows untouched). */
 moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
-                                  const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
-                                  void* stream);
+                                  const int32_t* pair_row, const float* topk_gate, int64_t T, int k,
+                                  int d, float* dgate, void* dout, void* stream);
 
 /* moe_route_backward: dJ/dlogits [T, E] fp32,
  *   dl[t,e] = g_tj (dgate_tj - sum_i g_ti dgate_ti)    for e = topk_idx[t,j]

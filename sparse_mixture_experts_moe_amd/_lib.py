@@ -63,11 +63,10 @@ _SIGS = {
     "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_gate_up_train": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
                                       _sz, _p]),
-    "moe_expert_weights_t": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p]),
-    "moe_expert_swiglu_backward_workspace": (_sz, [_i64, _i, _i, _i, _i]),
+    "moe_expert_swiglu_backward_workspace": (_sz, [_i64, _i, _i, _i, _i, _i]),
     "moe_expert_swiglu_backward": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
-                                        _p, _p, _p, _p, _p, _sz, _p]),
-    "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _i64, _i, _i, _p, _p]),
+                                        _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _p, _i64, _i, _i, _p, _p, _p]),
     "moe_route_backward": (_i, [_p, _p, _p, _p, _p, _i64, _i, _i, _f, _f, _f, _p, _p]),
     "moe_router_backward_workspace": (_sz, [_i64, _i, _i]),
     "moe_router_backward": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
@@ -324,30 +323,16 @@ def moe_expert_gate_up_train(a, group_offset, max_rows, w_gate, w_up, *, a_rows=
     return hid, uv
 
 
-def moe_expert_weights_t(w_gate, w_up, w_down, *, w_down_t=None, w_gu_t=None, stream=None):
-    """Transposed weight copies w_down_t [G, h, d] and w_gu_t [G, d, 2h]."""
-    G, h, d = w_gate.shape
-    dev = w_gate.device
-    if w_down_t is None:
-        w_down_t = torch.empty((G, h, d), dtype=w_gate.dtype, device=dev)
-    if w_gu_t is None:
-        w_gu_t = torch.empty((G, d, 2 * h), dtype=w_gate.dtype, device=dev)
-    _contig(w_gate, w_up, w_down, w_down_t, w_gu_t)
-    _check(_L.moe_expert_weights_t(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _dt(w_gate), d, h, G,
-                                   _ptr(w_down_t), _ptr(w_gu_t), _stream(stream)))
-    return w_down_t, w_gu_t
+def moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt, gather=False) -> int:
+    return _L.moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt, 1 if gather else 0)
 
 
-def moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt) -> int:
-    return _L.moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt)
-
-
-def moe_expert_swiglu_backward(a, group_offset, max_rows, dy, uv, w_down_t, w_gu_t, *,
-                               a_rows=None, a_rows_div=1, row_gate=None, da=None, dw_gate=None,
-                               dw_up=None, dw_down=None, ws=None, stream=None):
+def moe_expert_swiglu_backward(a, group_offset, max_rows, dout, uv, hid, w_gate, w_up, w_down, *,
+                               a_rows=None, a_rows_div=1, da=None, dw_gate=None, dw_up=None,
+                               dw_down=None, ws=None, stream=None):
     """Gradients of the grouped SwiGLU experts: da [max_rows, d] and dw_gate,
     dw_up [G, h, d], dw_down [G, d, h] (all fp32)."""
-    G, h, d = w_down_t.shape
+    G, h, d = w_gate.shape
     dev = a.device
     f32 = torch.float32
     da = torch.empty((max_rows, d), dtype=f32, device=dev) if da is None else da
@@ -355,27 +340,32 @@ def moe_expert_swiglu_backward(a, group_offset, max_rows, dy, uv, w_down_t, w_gu
     dw_up = torch.empty((G, h, d), dtype=f32, device=dev) if dw_up is None else dw_up
     dw_down = torch.empty((G, d, h), dtype=f32, device=dev) if dw_down is None else dw_down
     if ws is None:
-        ws = torch.empty(max(moe_expert_swiglu_backward_workspace(max_rows, d, h, G, _dt(a)), 1),
-                         dtype=torch.uint8, device=dev)
-    _contig(a, group_offset, dy, uv, w_down_t, w_gu_t, a_rows, row_gate, da, dw_gate, dw_up,
+        n = moe_expert_swiglu_backward_workspace(max_rows, d, h, G, _dt(a), a_rows is not None)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _contig(a, group_offset, dout, uv, hid, w_gate, w_up, w_down, a_rows, da, dw_gate, dw_up,
             dw_down, ws)
     _check(_L.moe_expert_swiglu_backward(_ptr(a), _dt(a), d, h, G, _ptr(group_offset), max_rows,
-                                         _ptr(a_rows), a_rows_div, _ptr(dy), _ptr(row_gate),
-                                         _ptr(uv), _ptr(w_down_t), _ptr(w_gu_t), _ptr(da),
-                                         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ws),
-                                         ws.numel(), _stream(stream)))
+                                         _ptr(a_rows), a_rows_div, _ptr(dout), _ptr(uv),
+                                         _ptr(hid), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                         _ptr(da), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
     return da, dw_gate, dw_up, dw_down
 
 
-def moe_combine_backward(dy, y_perm, pair_row, k, *, dgate=None, stream=None):
-    """dgate[t, j] = <dy[t], y_perm[pair_row[t k + j]]> (0 for dropped pairs)."""
+def moe_combine_backward(dy, y_perm, pair_row, k, topk_gate=None, *, dgate=None, dout=None,
+                         want_dout=False, stream=None):
+    """dgate[t, j] = <dy[t], y_perm[pair_row[t k + j]]> (0 for dropped pairs) and,
+    with ``want_dout`` (or a given dout), dout[pair_row[t k + j]] = g[t, j] dy[t]."""
     T, d = dy.shape
     if dgate is None:
         dgate = torch.empty((T, k), dtype=torch.float32, device=dy.device)
-    _contig(dy, y_perm, pair_row, dgate)
+    if want_dout and dout is None:
+        dout = torch.empty((T * k, d), dtype=dy.dtype, device=dy.device)
+    _contig(dy, y_perm, pair_row, topk_gate, dgate, dout)
     _check(_L.moe_combine_backward(_ptr(dy), _dt(dy), _ptr(y_perm), _dt(y_perm), _ptr(pair_row),
-                                   T, k, d, _ptr(dgate), _stream(stream)))
-    return dgate
+                                   _ptr(topk_gate), T, k, d, _ptr(dgate), _ptr(dout),
+                                   _stream(stream)))
+    return dgate, dout
 
 
 def moe_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, alpha=0.01,

@@ -54,19 +54,36 @@ __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 
 // ---------------------------------------------------------------------------
-// dgate[t, j] = sum_i dy[t, i] * y[pair_row[t k + j], i], 0 for a dropped pair.
+// dgate[t, j] = sum_i dy[t, i] * y[pair_row[t k + j], i], 0 for a dropped pair,
+// and (with dout) the upstream gradient of the kept pair's expert row,
+// dout[pair_row[t k + j]] = gate[t, j] * dy[t] (in dy's dtype).
 // One wave per token (four per workgroup); each lane takes 8 consecutive
 // columns per step; slots go in batches of 8 and the lane partials of each
 // slot are added by a butterfly.
 // ---------------------------------------------------------------------------
 constexpr int kGradSlots = 8;
 
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+__device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+
 template <typename DT, typename YT>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restrict__ dy,
                                                                const YT* __restrict__ y,
                                                                const int32_t* __restrict__ pair_row,
+                                                               const float* __restrict__ gate,
                                                                int64_t T, int k, int d,
-                                                               float* __restrict__ dgate) {
+                                                               float* __restrict__ dgate,
+                                                               DT* __restrict__ dout) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (t >= T) return;
@@ -74,10 +91,11 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restr
   const DT* dyr = dy + t * d;
   for (int j0 = 0; j0 < k; j0 += kGradSlots) {
     int rows[kGradSlots];
-    float acc[kGradSlots];
+    float acc[kGradSlots], gs[kGradSlots];
 #pragma unroll
     for (int u = 0; u < kGradSlots; ++u) {
       rows[u] = j0 + u < k ? pr[j0 + u] : -1;
+      gs[u] = (dout && rows[u] >= 0) ? gate[t * k + j0 + u] : 0.0f;
       acc[u] = 0.0f;
     }
     if ((d & 7) == 0) {
@@ -91,14 +109,23 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restr
           load8(y + static_cast<int64_t>(rows[u]) * d + c, v);
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[u] = fmaf(g[i], v[i], acc[u]);
+          if (dout) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = gs[u] * g[i];
+            store8(dout + static_cast<int64_t>(rows[u]) * d + c, o);
+          }
         }
       }
     } else {
       for (int c = lane; c < d; c += kWave) {
         const float g = load1(dyr + c);
 #pragma unroll
-        for (int u = 0; u < kGradSlots; ++u)
-          if (rows[u] >= 0) acc[u] = fmaf(g, load1(y + static_cast<int64_t>(rows[u]) * d + c), acc[u]);
+        for (int u = 0; u < kGradSlots; ++u) {
+          if (rows[u] < 0) continue;
+          acc[u] = fmaf(g, load1(y + static_cast<int64_t>(rows[u]) * d + c), acc[u]);
+          if (dout) store1(dout + static_cast<int64_t>(rows[u]) * d + c, gs[u] * g);
+        }
       }
     }
 #pragma unroll
@@ -331,13 +358,13 @@ hipError_t router_backward_typed(const void* x, const void* w, const float* dl, 
 }  // namespace
 
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,
-                                   const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
-                                   hipStream_t stream) {
+                                   const int32_t* pair_row, const float* gate, int64_t T, int k,
+                                   int d, float* dgate, void* dout, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((T + 3) / 4);
-#define MOE_CB(DT, YT)                                                                       \
-  combine_backward_kernel<DT, YT><<<grid, 256, 0, stream>>>(static_cast<const DT*>(dy),      \
-                                                            static_cast<const YT*>(y), pair_row, \
-                                                            T, k, d, dgate)
+#define MOE_CB(DT, YT)                                                                         \
+  combine_backward_kernel<DT, YT><<<grid, 256, 0, stream>>>(                                   \
+      static_cast<const DT*>(dy), static_cast<const YT*>(y), pair_row, gate, T, k, d, dgate,   \
+      static_cast<DT*>(dout))
   if (dy_bf16 && y_bf16) MOE_CB(uint16_t, uint16_t);
   else if (dy_bf16) MOE_CB(uint16_t, float);
   else if (y_bf16) MOE_CB(float, uint16_t);

@@ -458,46 +458,93 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
+// Operand storage of the bf16 tiles.
+//   kOpRows:  rows of the operand (tile rows for A, weight rows for B) are
+//             contiguous along K (the forward's layout; A rows may be gathered).
+//   kOpSlabT: B only; the expert's weight slab is stored K-major, [K][N] with
+//             rows of N elements (the input-gradient GEMMs read the forward's
+//             weights this way); K slices below OpArgs::nk1 come from B0's
+//             slab, the rest from B1's.
+//   kOpRowsT: K-major data rows: K runs over the rows r0 .. rend - 1 of a
+//             row-major buffer whose columns are the tile's M (A, row length
+//             lda) or N (B, row length ldb); K rows past rend read the zero
+//             row (the weight gradients contract over an expert's rows).
+// A K-major stage is read with ds_read_b64_tr_b16: within each 16-lane group
+// lane s passes the address of 4 consecutive columns x0 + 4 (s mod 4) of row
+// k0 + s / 4 and receives column x0 + s of rows k0 .. k0 + 3, which is the
+// MFMA operand layout (a lane holds one column and consecutive k).
+constexpr int kOpRows = 0;
+constexpr int kOpSlabT = 1;
+constexpr int kOpRowsT = 2;
+
+struct OpArgs {
+  int nk1;               // kOpSlabT: K slices taken from B0
+  int r0, rend;          // kOpRowsT: row range of the K axis
+  int lda, ldb;          // kOpRowsT: row lengths of A and B
+  int a_cols;            // kOpRowsT: columns of A (the GEMM's M)
+  const uint16_t* zero;  // kOpRowsT: a row of zeros, at least as long as any row read
+};
+
+// Chunk swizzle of a K-major stage with rows of X columns: the half-wave of a
+// transposed read covers 4 rows x 64 bytes, which land on distinct bank
+// groups (rows of 256 and 512 bytes: XOR of bits 2-3 of the chunk with k mod
+// 4; rows of 128 bytes: bit 2 with bit 1 of k).
+__device__ __forceinline__ int swz_kmajor(int k, int X) {
+  return X >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
+
+// LDS element offset of this lane's first transposed read of the 32-column
+// fragment at column xb (k step 0); the second read is 4 rows further.
+__device__ __forceinline__ int kmajor_frag(int xb, int X, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int x = xb + 16 * (g & 1) + 4 * (sl & 3);
+  const int k = 8 * (g >> 1) + (sl >> 2);
+  return k * X + (((x >> 3) ^ swz_kmajor(k, X)) << 3) + (x & 7);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Fragment of 8 consecutive k (rows p, p + 1, ... of a K-major stage) for this
+// lane's column: two transposed reads of 4 rows each.
+__device__ __forceinline__ bf16x8 read_kmajor(const uint16_t* p, int X) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  lds_i16x4* q0 = (lds_i16x4*)((__attribute__((address_space(3))) uint16_t*)(p));
+  lds_i16x4* q1 = (lds_i16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 4 * X));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Epilogue modes of the bf16 tiles.
 //   kEpiNone:    C = A B^T (fused: C = SiLU(gate) * up).
 //   kEpiSaveUV:  fused only; also keeps the two pre-activations of every
 //                output, uv[r, c] = gate sum and uv[r, N + c] = up sum (bf16),
 //                for the backward pass.
-//   kEpiSiluBwd: unfused, N = h, A rows = the upstream gradient rows of the
-//                tile's pairs; the accumulator is dhid / s_r with s_r the
-//                pair's gate (row_gate[a_rows[r]], or row_gate[r] without a
-//                gather, or 1 without row_gate).  With u, v read back from uv:
-//                  du = s dhid_acc v SiLU'(u),  dv = s dhid_acc SiLU(u)
-//                written to dab[r] = [du | dv] (row layout) and to the
-//                transposed buffers dabT[c][kc] (du), dabT[N + c][kc] (dv) and
-//                ghidT[c][kc] = s SiLU(u) v, where kc = kofs[g] + r - off[g]
-//                is the row's column in the K-grouped layout of the weight
-//                gradients.  C is not written.
+//   kEpiSiluBwd: unfused, N = h, the accumulator is dhid = dout W_down; with
+//                u, v read back from uv:
+//                  du = dhid v SiLU'(u),  dv = dhid SiLU(u)
+//                written to dab[r] = [du | dv] (bf16).  C is not written.
 constexpr int kEpiNone = 0;
 constexpr int kEpiSaveUV = 1;
 constexpr int kEpiSiluBwd = 2;
 
 struct EpiArgs {
-  uint16_t* uv;                  // [rows, 2N]
-  const float* row_gate;         // per pair, or NULL
-  const int32_t* a_rows;         // the tile's row gather (pair of each row), or NULL
-  const int32_t* off;            // group offsets [G + 1]
-  const int32_t* kofs;           // first transposed column of each group [G + 1]
-  int64_t kt;                    // columns of the transposed buffers
-  uint16_t* dab;                 // [rows, 2N]
-  uint16_t* dabT;                // [2N, kt]
-  uint16_t* ghidT;               // [N, kt]
+  uint16_t* uv;   // [rows, 2N]
+  uint16_t* dab;  // [rows, 2N]
 };
 
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
 // waves form a WM x WN grid, each wave a (BM/WM) x (BN/WN) block of MFMA
 // tiles.  The LDS rings are laid out for kTileM rows of A whatever BM is.
-template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename OutT, int kEpi>
+template <int BM, int WM, int WN, int BN, int SA, int SB, bool kFused, typename OutT, int kEpi,
+          int kAM = kOpRows, int kBM = kOpRows>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const Tile2& tile, int ks0, int nk, uint16_t* smem, OutT* __restrict__ C,
-    float* __restrict__ part_out, const EpiArgs& ep) {
+    float* __restrict__ part_out, const EpiArgs& ep, const OpArgs& oa = OpArgs{}) {
   static_assert(WM * WN == 4, "four waves");
   static_assert(kEpi == kEpiNone || (kEpi == kEpiSaveUV) == kFused, "epilogue mode");
   constexpr int MT = BM / WM / 32;            // 32-row MFMA tiles per wave
@@ -525,48 +572,106 @@ __device__ __forceinline__ void gemm_tile(
   const int lrow = lane >> 3;
   const int gchunk = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
 
+  // K-major operands (kAM / kBM != kOpRows): a stage holds 64 K rows of the
+  // tile's X = BM (A) or BN (B) columns, row-major, 16-byte chunk c of row k
+  // at slot c ^ swz_kmajor(k, X); copy j of a wave fills 1 KB = 512 / X rows.
+  // Each lane copies the same global chunk column in every copy (the swizzle
+  // depends on k mod 4 only, and each copy advances k by a multiple of 4).
+  constexpr int AXR = 512 / BM, BXR = 512 / BN;  // K rows per 1 KB copy
+  const int a_kr0 = wave * AXR + lane / (BM / 8);
+  const int b_kr0 = wave * BXR + lane / (BN / 8);
+  const int a_kcol = tile.m0 + 8 * ((lane % (BM / 8)) ^ swz_kmajor(a_kr0, BM));
+  const int b_kcol = tile.n0 + 8 * ((lane % (BN / 8)) ^ swz_kmajor(b_kr0, BN));
+
   int src[AP];
-#pragma unroll
-  for (int j = 0; j < AP; ++j) {
-    const int r = tile.m0 + 8 * (4 * j + wave) + lrow;
-    src[j] = r < tile.row_end ? r : tile.row_end - 1;  // rows past the group: valid row, unused
-  }
-  if (a_rows) {  // gather: all index loads first, then the divisions
-#pragma unroll
-    for (int j = 0; j < AP; ++j) src[j] = a_rows[src[j]];
-#pragma unroll
-    for (int j = 0; j < AP; ++j) src[j] /= a_div;
-  }
   const uint16_t* ap[AP];
+  if constexpr (kAM == kOpRows) {
 #pragma unroll
-  for (int j = 0; j < AP; ++j) ap[j] = A + static_cast<int64_t>(src[j]) * K + gchunk * 8;
+    for (int j = 0; j < AP; ++j) {
+      const int r = tile.m0 + 8 * (4 * j + wave) + lrow;
+      src[j] = r < tile.row_end ? r : tile.row_end - 1;  // rows past the group: valid row, unused
+    }
+    if (a_rows) {  // gather: all index loads first, then the divisions
+#pragma unroll
+      for (int j = 0; j < AP; ++j) src[j] = a_rows[src[j]];
+#pragma unroll
+      for (int j = 0; j < AP; ++j) src[j] /= a_div;
+    }
+#pragma unroll
+    for (int j = 0; j < AP; ++j) ap[j] = A + static_cast<int64_t>(src[j]) * K + gchunk * 8;
+  }
   // B copies: the expert's weight slab (gate rows for j < BP/2 of a fused
   // tile, up rows after) is uniform, the row offset within it per lane
   uint32_t boff[BP];
+  if constexpr (kBM == kOpRows) {
 #pragma unroll
-  for (int j = 0; j < BP; ++j) {
-    const int r = 8 * (4 * j + wave) + lrow;
-    int n = tile.n0 + ((kFused && r >= BN / 2) ? r - BN / 2 : r);
-    n = n < N ? n : N - 1;
-    boff[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K * 2) + gchunk * 16;
+    for (int j = 0; j < BP; ++j) {
+      const int r = 8 * (4 * j + wave) + lrow;
+      int n = tile.n0 + ((kFused && r >= BN / 2) ? r - BN / 2 : r);
+      n = n < N ? n : N - 1;
+      boff[j] = static_cast<uint32_t>(n) * static_cast<uint32_t>(K * 2) + gchunk * 16;
+    }
+  } else if constexpr (kBM == kOpSlabT) {
+    // K-major weight slab: lane offset of copy j in bytes (columns past N
+    // read a valid column, unused)
+    const int col = b_kcol < N ? b_kcol : N - 8;
+#pragma unroll
+    for (int j = 0; j < BP; ++j)
+      boff[j] = (static_cast<uint32_t>(b_kr0 + 4 * j * BXR) * static_cast<uint32_t>(N) +
+                 static_cast<uint32_t>(col)) * 2u;
   }
   const uint16_t* bslab0 = B0 + tile.g * b_stride;
   const uint16_t* bslab1 = (kFused ? B1 : B0) + tile.g * b_stride;
+  if constexpr (kBM == kOpSlabT) bslab1 = B1 + tile.g * b_stride;
   static_assert(!kFused || sizeof(OutT) == 2, "split-K partials are for the unfused GEMM");
+  static_assert(!kFused || (kAM == kOpRows && kBM == kOpRows), "fused tiles read row-major operands");
 
   // this tile covers K slices ks0 .. ks0 + nk - 1 (all of K unless split)
+  if constexpr (kAM == kOpRows) {
 #pragma unroll
-  for (int j = 0; j < AP; ++j) ap[j] += ks0 * kBK;
-  bslab0 += ks0 * kBK;
-  bslab1 += ks0 * kBK;
+    for (int j = 0; j < AP; ++j) ap[j] += ks0 * kBK;
+  }
+  if constexpr (kBM == kOpRows) {
+    bslab0 += ks0 * kBK;
+    bslab1 += ks0 * kBK;
+  }
+  // K-major data rows (kOpRowsT): global row of K slice ks, copy j; rows past
+  // the range read the zero row
+  const int a_col = a_kcol < oa.a_cols ? a_kcol : oa.a_cols - 8;
+  const int b_col = b_kcol < N ? b_kcol : N - 8;
+  auto rows_t_ptr = [&](const uint16_t* base, int ld, int col, int kr, int ks) {
+    const int row = oa.r0 + (ks0 + ks) * kBK + kr;
+    return row < oa.rend ? base + static_cast<int64_t>(row) * ld + col : oa.zero + col;
+  };
+  // K-major weight slab: slices below nk1 from B0, the rest from B1
+  auto slab_t_base = [&](int ks) {
+    const int kg = ks0 + ks;
+    return kg < oa.nk1 ? bslab0 + static_cast<int64_t>(kg) * kBK * N
+                       : bslab1 + static_cast<int64_t>(kg - oa.nk1) * kBK * N;
+  };
   // copy K slice `ks` (clamped into range: surplus copies reload the last slice
   // into a stage nobody reads again, which keeps the loop branch-free)
 #define MOE_COPY_A(j, stage, ks)                                                     \
-  dma_lds16(ap[(j)] + ((ks) < nk ? (ks) : nk - 1) * kBK,                             \
-            As + (stage) * kTileM * kBK + 8 * (4 * (j) + wave_u) * kBK)
+  do {                                                                               \
+    const int ksc_ = (ks) < nk ? (ks) : nk - 1;                                      \
+    uint16_t* dst_ = As + (stage) * kTileM * kBK + 8 * (4 * (j) + wave_u) * kBK;     \
+    if constexpr (kAM == kOpRows)                                                    \
+      dma_lds16(ap[(j)] + ksc_ * kBK, dst_);                                         \
+    else                                                                             \
+      dma_lds16(rows_t_ptr(A, oa.lda, a_col, a_kr0 + 4 * (j) * AXR, ksc_), dst_);    \
+  } while (0)
 #define MOE_COPY_B(j, stage, ks)                                                     \
-  dma_lds16_s(((kFused && (j) >= BP / 2) ? bslab1 : bslab0) + ((ks) < nk ? (ks) : nk - 1) * kBK, \
-              boff[(j)], Bs + (stage) * BN * kBK + 8 * (4 * (j) + wave_u) * kBK)
+  do {                                                                               \
+    const int ksc_ = (ks) < nk ? (ks) : nk - 1;                                      \
+    uint16_t* dst_ = Bs + (stage) * BN * kBK + 8 * (4 * (j) + wave_u) * kBK;         \
+    if constexpr (kBM == kOpRows)                                                    \
+      dma_lds16_s(((kFused && (j) >= BP / 2) ? bslab1 : bslab0) + ksc_ * kBK, boff[(j)], \
+                  dst_);                                                             \
+    else if constexpr (kBM == kOpSlabT)                                              \
+      dma_lds16_s(slab_t_base(ksc_), boff[(j)], dst_);                               \
+    else                                                                             \
+      dma_lds16(rows_t_ptr(B0, oa.ldb, b_col, b_kr0 + 4 * (j) * BXR, ksc_), dst_);   \
+  } while (0)
 
   f32x16 acc[MT][NT];
 #pragma unroll
@@ -576,10 +681,15 @@ __device__ __forceinline__ void gemm_tile(
 
   // LDS element offsets of this lane's fragments for k step 0; step s is the
   // same offset XOR (s << 4), as the swizzle flips only chunk bits
+  // (K-major stages: the offset of the first transposed read of step 0;
+  // step s adds 16 s rows, the second read 4 rows)
   int aoff[MT], boffl[NT];
   const int khalf = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) aoff[i] = swz64(wm * (BM / WM) + i * 32 + (lane & 31), khalf);
+  for (int i = 0; i < MT; ++i) {
+    const int x = wm * (BM / WM) + i * 32;
+    aoff[i] = kAM == kOpRows ? swz64(x + (lane & 31), khalf) : kmajor_frag(x, BM, lane);
+  }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     int row;
@@ -589,7 +699,7 @@ __device__ __forceinline__ void gemm_tile(
     } else {
       row = wn * (BN / WN) + j * 32;
     }
-    boffl[j] = swz64(row + (lane & 31), khalf);
+    boffl[j] = kBM == kOpRows ? swz64(row + (lane & 31), khalf) : kmajor_frag(row, BN, lane);
   }
 
   // read r < MT is A fragment r, else B fragment r - MT, of k step `step`
@@ -597,12 +707,18 @@ __device__ __forceinline__ void gemm_tile(
   do {                                                                               \
     if ((r) < MT) {                                                                  \
       const int i_ = (r) < MT ? (r) : 0;                                             \
-      F##a[i_] = *reinterpret_cast<const bf16x8*>(As + (sa) * kTileM * kBK +         \
-                                                  (aoff[i_] ^ ((step) << 4)));       \
+      const uint16_t* base_ = As + (sa) * kTileM * kBK;                              \
+      if constexpr (kAM == kOpRows)                                                  \
+        F##a[i_] = *reinterpret_cast<const bf16x8*>(base_ + (aoff[i_] ^ ((step) << 4))); \
+      else                                                                           \
+        F##a[i_] = read_kmajor(base_ + aoff[i_] + (step) * 16 * BM, BM);             \
     } else {                                                                         \
       const int j_ = (r) >= MT ? (r) - MT : 0;                                       \
-      F##b[j_] = *reinterpret_cast<const bf16x8*>(Bs + (sb) * BN * kBK +             \
-                                                  (boffl[j_] ^ ((step) << 4)));      \
+      const uint16_t* base_ = Bs + (sb) * BN * kBK;                                  \
+      if constexpr (kBM == kOpRows)                                                  \
+        F##b[j_] = *reinterpret_cast<const bf16x8*>(base_ + (boffl[j_] ^ ((step) << 4))); \
+      else                                                                           \
+        F##b[j_] = read_kmajor(base_ + boffl[j_] + (step) * 16 * BN, BN);            \
     }                                                                                \
   } while (0)
 // acc[i][j] accumulates the transposed product of m-block i and n-block j
@@ -682,6 +798,43 @@ __device__ __forceinline__ void gemm_tile(
   // every lane stores runs of four columns (N % 64 == 0 keeps a run whole)
   const int row0 = tile.m0 + wm * (BM / WM) + (lane & 31);
   const int cq = 4 * (lane >> 5);
+  if constexpr (kEpi == kEpiSiluBwd) {
+    // dab[r] = [du | dv] from the accumulator (dhid) and the kept u, v
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = row0 + i * 32;
+      if (row >= tile.row_end) continue;
+      const uint16_t* urow = ep.uv + static_cast<int64_t>(row) * (2 * N);
+      uint16_t* drow = ep.dab + static_cast<int64_t>(row) * (2 * N);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int cb = tile.n0 + wn * (BN / WN) + j * 32 + cq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = cb + 8 * q;
+          if (col >= N) continue;
+          const u32x2 ur = *reinterpret_cast<const u32x2*>(urow + col);
+          const u32x2 vr = *reinterpret_cast<const u32x2*>(urow + N + col);
+          float du[4], dv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t uw = ur[e >> 1], vw = vr[e >> 1];
+            const float u = __uint_as_float((e & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
+            const float v = __uint_as_float((e & 1) ? (vw & 0xFFFF0000u) : (vw << 16));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-u));  // 0 once exp overflows
+            const float dh = acc[i][j][4 * q + e];
+            du[e] = dh * v * (sg * (1.0f + u * (1.0f - sg)));
+            dv[e] = dh * (u * sg);
+          }
+          *reinterpret_cast<u32x2*>(drow + col) =
+              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          *reinterpret_cast<u32x2*>(drow + N + col) =
+              u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int row = row0 + i * 32;
@@ -709,47 +862,6 @@ __device__ __forceinline__ void gemm_tile(
                 u32x2{pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3])};
             *reinterpret_cast<u32x2*>(urow + N + col) =
                 u32x2{pack_bf16x2(ua[4 * q], ua[4 * q + 1]), pack_bf16x2(ua[4 * q + 2], ua[4 * q + 3])};
-          }
-        }
-      }
-    } else if constexpr (kEpi == kEpiSiluBwd) {
-      const int64_t pr = ep.a_rows ? ep.a_rows[row] : row;
-      const float sr = ep.row_gate ? ep.row_gate[pr] : 1.0f;
-      const int64_t kc = ep.kofs[tile.g] + (row - ep.off[tile.g]);
-      const uint16_t* urow = ep.uv + static_cast<int64_t>(row) * (2 * N);
-      uint16_t* drow = ep.dab + static_cast<int64_t>(row) * (2 * N);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int cb = tile.n0 + wn * (BN / WN) + j * 32 + cq;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = cb + 8 * q;
-          if (col >= N) continue;
-          const u32x2 ur = *reinterpret_cast<const u32x2*>(urow + col);
-          const u32x2 vr = *reinterpret_cast<const u32x2*>(urow + N + col);
-          float du[4], dv[4], gh[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t uw = ur[e >> 1], vw = vr[e >> 1];
-            const float u = __uint_as_float((e & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
-            const float v = __uint_as_float((e & 1) ? (vw & 0xFFFF0000u) : (vw << 16));
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-u));  // 0 once exp overflows
-            const float si = u * sg;
-            const float dh = sr * acc[i][j][4 * q + e];
-            du[e] = dh * v * (sg * (1.0f + u * (1.0f - sg)));
-            dv[e] = dh * si;
-            gh[e] = sr * (si * v);
-          }
-          *reinterpret_cast<u32x2*>(drow + col) =
-              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-          *reinterpret_cast<u32x2*>(drow + N + col) =
-              u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t c = col + e;
-            ep.dabT[c * ep.kt + kc] = f32_to_bf16_bits(du[e]);
-            ep.dabT[(N + c) * ep.kt + kc] = f32_to_bf16_bits(dv[e]);
-            ep.ghidT[c * ep.kt + kc] = f32_to_bf16_bits(gh[e]);
           }
         }
       }
@@ -822,12 +934,12 @@ __device__ __forceinline__ int next_work(const int32_t* __restrict__ runs, int32
 // runs).  tt: the tile-table workspace (mstart first); skw: split-K
 // workspace (kSkUnits fp32 256 x 256 tiles) or NULL (no split); ncu: compute
 // units of the device, as given to tile_table_kernel.
-template <bool kFused, typename OutT, int kEpi>
+template <bool kFused, typename OutT, int kEpi, int kBM = kOpRows>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, int64_t b_stride, int K,
     int N, const int32_t* __restrict__ off, int32_t* __restrict__ tt, int G, int ntn,
-    OutT* __restrict__ C, float* __restrict__ skw, int ncu, EpiArgs ep) {
+    OutT* __restrict__ C, float* __restrict__ skw, int ncu, EpiArgs ep, OpArgs oa) {
   constexpr int BN = 256;
   extern __shared__ __align__(16) uint16_t smem[];
   const int32_t* mstart = tt;
@@ -843,9 +955,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       if (u.count == 0) {
         t.n0 = u.nt0 * (BN / 2);
         const Tile2 tile = classify(t);
-        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, 0, K / kBK,
-                                                              smem, C, nullptr, ep);
+                                                              smem, C, nullptr, ep, oa);
         continue;
       }
       for (int s = 0; s < u.count; ++s) {
@@ -853,13 +965,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
         t.n0 = (u.nt0 + s) * (BN / 2);
         const Tile2 tile = classify(t);
         if (tile.cls == 1)
-          gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+          gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                                 b_stride, K, N, tile, 0, K / kBK,
-                                                                smem, C, nullptr, ep);
+                                                                smem, C, nullptr, ep, oa);
         else
-          gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+          gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                                b_stride, K, N, tile, 0, K / kBK,
-                                                               smem, C, nullptr, ep);
+                                                               smem, C, nullptr, ep, oa);
       }
     }
   } else {
@@ -881,17 +993,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       }
       const Tile2 tile = classify(tile_at(L, off, mstart, G, ntn, kTileM, BN));
       if (tile.cls == 0) {
-        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+        gemm_tile<256, 2, 2, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, ks0, nk,
-                                                              smem, C, part_out, ep);
+                                                              smem, C, part_out, ep, oa);
       } else if (tile.cls == 1) {
-        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+        gemm_tile<128, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                               b_stride, K, N, tile, ks0, nk,
-                                                              smem, C, part_out, ep);
+                                                              smem, C, part_out, ep, oa);
       } else {
-        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi>(A, a_rows, a_div, B0, B1,
+        gemm_tile<64, 1, 4, BN, kRingA, kRingB, kFused, OutT, kEpi, kOpRows, kBM>(A, a_rows, a_div, B0, B1,
                                                              b_stride, K, N, tile, ks0, nk,
-                                                             smem, C, part_out, ep);
+                                                             smem, C, part_out, ep, oa);
       }
     }
   }
@@ -1237,7 +1349,8 @@ hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
-      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu, ep);
+      s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu, ep,
+      OpArgs{});
   return hipGetLastError();
 }
 
@@ -1252,7 +1365,7 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
   kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
-      static_cast<OutT*>(s.y), s.sk_ws, ncu, EpiArgs{});
+      static_cast<OutT*>(s.y), s.sk_ws, ncu, EpiArgs{}, OpArgs{});
   if (s.sk_ws)
     sk_reduce_kernel<OutT><<<kSkUnits * 32, 256, 0, stream>>>(
         s.sk_ws, s.group_offset, s.mstart, s.G, ntn, s.h, s.d, ncu, static_cast<OutT*>(s.y));
@@ -1331,141 +1444,47 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
 bool skinny(const SwigluArgs& s) { return s.max_rows <= static_cast<int64_t>(s.G) * 64; }
 
 // ---------------------------------------------------------------------------
-// Backward pass of the experts (bf16).  With dout_r = s_r dy_r (s_r the
-// pair's gate), per group g:
+// Backward pass of the experts (bf16).  With dout_r the upstream gradient of
+// row r's expert output (the gate already applied), per group g:
 //   dhid = dout W_down[g]                           (dgrad 1, K = d, N = h)
 //   du = dhid v SiLU'(u),  dv = dhid SiLU(u)        (its epilogue)
 //   da = du W_gate[g] + dv W_up[g]                  (dgrad 2, K = 2h, N = d)
-//   dW_down[g] = sum_r dy_r^T (s_r hid_r)           (weight gradients, K = rows)
+//   dW_down[g] = sum_r dout_r^T hid_r               (weight gradients, K = rows)
 //   dW_gate[g] = sum_r du_r^T a_r,  dW_up[g] = sum_r dv_r^T a_r
-// The two input-gradient GEMMs contract over the weights' leading axis, so
-// they run on transposed weight copies (w_down_t [G, h, d], w_gu_t [G, d, 2h]
-// = [W_gate^T | W_up^T]) with the forward's grouped kernel.  The weight
-// gradients contract over the rows of a group: their operands are laid out
-// transposed, [features, kt], each group's rows in a run of columns that
-// starts at kofs[g] and is padded with zeros to a multiple of 64, so that
-// every group is a whole number of K slices of the same tiled kernel.
+// The input-gradient GEMMs contract over the weights' leading axis: they read
+// the forward's weights K-major (kOpSlabT, W_gate's slab for the first h/64
+// slices of dgrad 2 and W_up's after).  The weight gradients contract over a
+// group's rows: both operands are read K-major from the row-major buffers
+// (kOpRowsT), so no operand is ever transposed in memory.
 // ---------------------------------------------------------------------------
-constexpr int kTr = 64;  // transpose tile
 
-__host__ __device__ constexpr int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
-
-// kofs[g] = sum over g' < g of pad64(rows of g'), g = 0..G (one thread: G is small)
-__global__ void kofs_kernel(const int32_t* __restrict__ off, int G, int32_t* __restrict__ kofs) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int32_t acc = 0;
-  for (int g = 0; g < G; ++g) {
-    kofs[g] = acc;
-    acc += static_cast<int32_t>(pad64(off[g + 1] - off[g]));
-  }
-  kofs[G] = acc;
-}
-
-// out[g][c][col_off + r] = in[g][r][c] for in [G][R][C] (R, C multiples of
-// 64); out rows hold ld elements.  A 64 x 64 tile goes through LDS with
-// 16-byte loads and stores.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
-                                                             int R, int C,
-                                                             uint16_t* __restrict__ out, int ld,
-                                                             int col_off) {
-  __shared__ __align__(16) uint16_t t[kTr][kTr + 8];
-  const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr;
-  const uint16_t* src = in + static_cast<int64_t>(blockIdx.z) * R * C;
-  uint16_t* dst = out + static_cast<int64_t>(blockIdx.z) * C * ld;
-  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
-    const int r = i / 8, ch = i % 8;
-    *reinterpret_cast<u32x4*>(&t[r][ch * 8]) =
-        *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r0 + r) * C + c0 + ch * 8);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
-    const int c = i / 8, ch = i % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = static_cast<uint32_t>(t[ch * 8 + 2 * u][c]) |
-             (static_cast<uint32_t>(t[ch * 8 + 2 * u + 1][c]) << 16);
-    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c0 + c) * ld + col_off + r0 + ch * 8) =
-        u32x4{w[0], w[1], w[2], w[3]};
+// xs[r] = a[a_rows[r] / a_div] for r < off[G]: 16-byte copies, one row per
+// workgroup pass.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ a,
+                                                          const int32_t* __restrict__ a_rows,
+                                                          int a_div,
+                                                          const int32_t* __restrict__ off, int G,
+                                                          int d, uint16_t* __restrict__ xs) {
+  const int rows = off[G];
+  const int per = d / 8;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+       i < static_cast<int64_t>(rows) * per; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / per;
+    const int c = static_cast<int>(i - r * per) * 8;
+    const int64_t sr = a_rows[r] / a_div;
+    *reinterpret_cast<u32x4*>(xs + r * d + c) = *reinterpret_cast<const u32x4*>(a + sr * d + c);
   }
 }
 
-// Group of transposed column kc: the last g with kofs[g] <= kc (kc < kofs[G]).
-__device__ __forceinline__ int kgroup(const int32_t* __restrict__ kofs, int G, int kc) {
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (kofs[mid] <= kc) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// K-grouped transposed gather: out_z[i][kofs[g] + r - off[g]] = src_z[row(r)][i]
-// for r in group g, row(r) = a_rows[r] / a_div (or r), i < d; padding
-// columns are zero.  z = blockIdx.z selects (src0, out0) or (src1, out1).
-__global__ __launch_bounds__(256) void gather_transpose_kernel(
-    const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
-    const int32_t* __restrict__ a_rows, int a_div, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ kofs, int G, int d, uint16_t* __restrict__ out0,
-    uint16_t* __restrict__ out1, int64_t kt) {
-  __shared__ __align__(16) uint16_t t[kTr][kTr + 8];
-  const int kc0 = blockIdx.x * kTr;
-  if (kc0 >= kofs[G]) return;
-  const uint16_t* src = blockIdx.z ? src1 : src0;
-  uint16_t* out = blockIdx.z ? out1 : out0;
-  const int g = kgroup(kofs, G, kc0);
-  const int r_base = off[g] + (kc0 - kofs[g]), r_end = off[g + 1];
-  const int i0 = blockIdx.y * kTr;
-  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
-    const int rr = i / 8, ch = i % 8;
-    const int r = r_base + rr;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < r_end) {
-      const int64_t sr = a_rows ? a_rows[r] / a_div : r;
-      v = *reinterpret_cast<const u32x4*>(src + sr * d + i0 + ch * 8);
-    }
-    *reinterpret_cast<u32x4*>(&t[rr][ch * 8]) = v;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTr * kTr / 8; i += 256) {
-    const int c = i / 8, ch = i % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = static_cast<uint32_t>(t[ch * 8 + 2 * u][c]) |
-             (static_cast<uint32_t>(t[ch * 8 + 2 * u + 1][c]) << 16);
-    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(i0 + c) * kt + kc0 + ch * 8) =
-        u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
-// Zeroes the padding columns [kofs[g] + rows_g, kofs[g+1]) of rows0 rows of
-// p0 and rows1 rows of p1 (both [*, kt]); block (g, 64-row block).
-__global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ off,
-                                                       const int32_t* __restrict__ kofs,
-                                                       uint16_t* __restrict__ p0, int rows0,
-                                                       uint16_t* __restrict__ p1, int rows1,
-                                                       int64_t kt) {
-  const int g = blockIdx.x;
-  const int c0 = kofs[g] + (off[g + 1] - off[g]), c1 = kofs[g + 1];
-  if (c0 >= c1) return;
-  for (int i = threadIdx.x; i < kTr * kTr; i += 256) {
-    const int rr = i / kTr, c = i % kTr;
-    if (c0 + c >= c1) continue;
-    const int row = blockIdx.y * kTr + rr;
-    if (row < rows0) p0[row * kt + c0 + c] = 0;
-    else if (row - rows0 < rows1) p1[(row - rows0) * kt + c0 + c] = 0;
-  }
-}
-
-// Weight gradients: for every group g, C_g = A[:, cols_g] B[:, cols_g]^T with
-// A [M, kt], B [N, kt] and C_g [M, N] (fp32) at C + g M N; cols_g = the
-// group's (zero-padded) K slices.  One workgroup per output tile (tiles of a
-// group in the banded order, groups in order, contiguous runs per XCD); a
-// group without rows gets zeros.
+// Weight gradients: for every group g, C_g[M, N] = sum over the group's rows r
+// of A[r, :M]^T B[r, :N] (fp32, at C + g M N), A and B row-major with rows of
+// lda and ldb elements.  One workgroup per output tile (tiles of a group in
+// the banded order, groups in order, contiguous runs per XCD); a group
+// without rows gets zeros.
 __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int kt, int M, int N,
-    const int32_t* __restrict__ kofs, int G, int mtn, int ntn, float* __restrict__ C) {
+    const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, int M,
+    int N, const int32_t* __restrict__ off, int G, int mtn, int ntn,
+    const uint16_t* __restrict__ zero, float* __restrict__ C) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int per = mtn * ntn, total = G * per, nw8 = (total + 7) & ~7;
   const int L = xcd_run(blockIdx.x, nw8);
@@ -1486,7 +1505,8 @@ __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
   }
   const Tile2 tile = classify(Tile{0, mt * kTileM, M, nt * 256});
   float* Cg = C + static_cast<int64_t>(g) * M * N;
-  const int ks0 = kofs[g] / kBK, nk = (kofs[g + 1] - kofs[g]) / kBK;
+  const int r0 = off[g], r1 = off[g + 1];
+  const int nk = (r1 - r0 + kBK - 1) / kBK;
   if (nk == 0) {
     const int rows = min(kTileM, M - tile.m0);
     for (int i = threadIdx.x; i < rows * 64; i += kThreads) {
@@ -1498,25 +1518,56 @@ __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
     return;
   }
   const EpiArgs ep{};
+  OpArgs oa{};
+  oa.r0 = r0;
+  oa.rend = r1;
+  oa.lda = lda;
+  oa.ldb = ldb;
+  oa.a_cols = M;
+  oa.zero = zero;
   if (tile.cls == 0)
-    gemm_tile<256, 2, 2, 256, kRingA, kRingB, false, float, kEpiNone>(
-        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+    gemm_tile<256, 2, 2, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+        A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
   else if (tile.cls == 1)
-    gemm_tile<128, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone>(
-        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+    gemm_tile<128, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+        A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
   else
-    gemm_tile<64, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone>(
-        A, nullptr, 1, B, nullptr, 0, kt, N, tile, ks0, nk, smem, Cg, nullptr, ep);
+    gemm_tile<64, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+        A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
 }
 
-hipError_t wgrad_bf16(const uint16_t* A, const uint16_t* B, int64_t kt, int M, int N,
-                      const int32_t* kofs, int G, float* C, hipStream_t stream) {
+hipError_t wgrad_bf16(const uint16_t* A, int lda, const uint16_t* B, int ldb, int M, int N,
+                      const int32_t* off, int G, const uint16_t* zero, float* C,
+                      hipStream_t stream) {
   const int mtn = (M + kTileM - 1) / kTileM, ntn = (N + 255) / 256;
   const int64_t total = static_cast<int64_t>(G) * mtn * ntn;
   auto kern = wgrad_bf16_kernel;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<static_cast<unsigned>((total + 7) & ~7), kThreads, kGemmLds, stream>>>(
-      A, B, static_cast<int>(kt), M, N, kofs, G, mtn, ntn, C);
+      A, lda, B, ldb, M, N, off, G, mtn, ntn, zero, C);
+  return hipGetLastError();
+}
+
+// Input-gradient GEMM: C[r] = A[r] . W[g]^(K-major) for the rows of each group,
+// W's slab [K][N] per group (slices >= nk1 from B1), persistent like the
+// forward's down projection (split-K of the last round when skw is given).
+template <int kEpi, typename OutT>
+hipError_t dgrad_bf16(const uint16_t* A, int K, int N, const uint16_t* B0, const uint16_t* B1,
+                      int64_t b_stride, int nk1, const int32_t* off, int G, int32_t* tt,
+                      OutT* C, float* skw, const EpiArgs& ep, hipStream_t stream) {
+  const int ntn = (N + 255) / 256;
+  const int ncu = compute_units();
+  tile_table_kernel<<<1, 1024, 0, stream>>>(off, G, kTileM, ntn, false, tt, tt, ncu, K / kBK,
+                                            skw != nullptr);
+  OpArgs oa{};
+  oa.nk1 = nk1;
+  auto kern = gemm_bf16_kernel<false, OutT, kEpi, kOpSlabT>;
+  ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
+  kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(A, nullptr, 1, B0, B1, b_stride, K,
+                                                              N, off, tt, G, ntn, C, skw, ncu, ep,
+                                                              oa);
+  if (skw)
+    sk_reduce_kernel<OutT><<<kSkUnits * 32, 256, 0, stream>>>(skw, off, tt, G, ntn, K, N, ncu, C);
   return hipGetLastError();
 }
 
@@ -1548,83 +1599,47 @@ hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
   return s.y_bf16 ? down_bf16<uint16_t>(s, stream) : down_bf16<float>(s, stream);
 }
 
-int64_t backward_kt(int64_t max_rows, int G) { return pad64(max_rows) + 64 * static_cast<int64_t>(G); }
-
-hipError_t launch_weights_t(const void* w_gate, const void* w_up, const void* w_down, int d, int h,
-                            int G, void* w_down_t, void* w_gu_t, hipStream_t stream) {
-  const auto* wg = static_cast<const uint16_t*>(w_gate);
-  const auto* wu = static_cast<const uint16_t*>(w_up);
-  const auto* wd = static_cast<const uint16_t*>(w_down);
-  auto* wdt = static_cast<uint16_t*>(w_down_t);
-  auto* wgut = static_cast<uint16_t*>(w_gu_t);
-  const unsigned G_ = static_cast<unsigned>(G);
-  // w_down [G, d, h] -> [G, h, d]; w_gate, w_up [G, h, d] -> halves of [G, d, 2h]
-  transpose_bf16_kernel<<<dim3(h / kTr, d / kTr, G_), 256, 0, stream>>>(wd, d, h, wdt, d, 0);
-  transpose_bf16_kernel<<<dim3(d / kTr, h / kTr, G_), 256, 0, stream>>>(wg, h, d, wgut, 2 * h, 0);
-  transpose_bf16_kernel<<<dim3(d / kTr, h / kTr, G_), 256, 0, stream>>>(wu, h, d, wgut, 2 * h, h);
-  return hipGetLastError();
-}
-
 hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
   const int d = b.d, h = b.h, G = b.G;
-  const int64_t kt = b.kt;
-  kofs_kernel<<<1, 64, 0, stream>>>(b.group_offset, G, b.kofs);
-  // transposed activations for the weight gradients, and their zero padding
-  gather_transpose_kernel<<<dim3(static_cast<unsigned>(kt / kTr), d / kTr, 2), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(b.a), static_cast<const uint16_t*>(b.dy), b.a_rows, b.a_div,
-      b.group_offset, b.kofs, G, d, b.xs_t, b.dy_t, kt);
-  zero_pad_kernel<<<dim3(static_cast<unsigned>(G), (3 * h + kTr - 1) / kTr), 256, 0, stream>>>(
-      b.group_offset, b.kofs, b.dab_t, 2 * h, b.ghid_t, h, kt);
-  // dgrad 1 with the SiLU backward epilogue, then dgrad 2 (no rows: only the
-  // zero weight gradients below)
+  const auto* a = static_cast<const uint16_t*>(b.a);
+  const auto* dout = static_cast<const uint16_t*>(b.dout);
+  const auto* hid = static_cast<const uint16_t*>(b.hid);
+  const auto* wg = static_cast<const uint16_t*>(b.w_gate);
+  const auto* wu = static_cast<const uint16_t*>(b.w_up);
+  const auto* wd = static_cast<const uint16_t*>(b.w_down);
+  // a row of zeros (max(d, 2h) bf16) for the K tails of the weight gradients
+  hipError_t e = launch_fill_i32(reinterpret_cast<int32_t*>(b.zero), std::max(d, 2 * h) / 2, 0,
+                                 stream);
+  if (e != hipSuccess) return e;
+  const uint16_t* xs = a;
+  if (b.a_rows && b.max_rows > 0) {
+    const int64_t n = b.max_rows * (d / 8);
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 16384));
+    gather_rows_kernel<<<grid, 256, 0, stream>>>(a, b.a_rows, b.a_div, b.group_offset, G, d,
+                                                 b.xs);
+    xs = b.xs;
+  }
   if (b.max_rows > 0) {
-    const int ntn = (h + 255) / 256;
-    const int ncu = compute_units();
-    tile_table_kernel<<<1, 1024, 0, stream>>>(b.group_offset, G, kTileM, ntn, false, b.mstart,
-                                              b.mstart, ncu, d / kBK, false);
+    // dgrad 1 (dhid = dout W_down, K-major W_down) with the SiLU backward epilogue
     EpiArgs ep{};
     ep.uv = const_cast<uint16_t*>(static_cast<const uint16_t*>(b.uv));
-    ep.row_gate = b.row_gate;
-    ep.a_rows = b.a_rows;
-    ep.off = b.group_offset;
-    ep.kofs = b.kofs;
-    ep.kt = kt;
     ep.dab = b.dab;
-    ep.dabT = b.dab_t;
-    ep.ghidT = b.ghid_t;
-    auto kern = gemm_bf16_kernel<false, uint16_t, kEpiSiluBwd>;
-    ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-    kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
-        static_cast<const uint16_t*>(b.dy), b.a_rows, b.a_div,
-        static_cast<const uint16_t*>(b.w_down_t), nullptr, static_cast<int64_t>(h) * d, d, h,
-        b.group_offset, b.mstart, G, ntn, static_cast<uint16_t*>(nullptr), nullptr, ncu, ep);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dgrad 2: da = [du | dv] w_gu_t^T, the forward's down-projection path with K = 2h
-  if (b.max_rows > 0) {
-    SwigluArgs s2{};
-    s2.bf16 = true;
-    s2.d = d;
-    s2.h = 2 * h;
-    s2.G = G;
-    s2.group_offset = b.group_offset;
-    s2.max_rows = b.max_rows;
-    s2.w_down = b.w_gu_t;
-    s2.y = b.da;
-    s2.y_bf16 = false;
-    s2.hid = b.dab;
-    s2.mstart = b.mstart;
-    s2.sk_ws = b.sk_ws;
-    e = launch_down(s2, stream);
+    e = dgrad_bf16<kEpiSiluBwd, uint16_t>(dout, d, h, wd, wd, static_cast<int64_t>(d) * h,
+                                          d / kBK, b.group_offset, G, b.mstart, nullptr, nullptr,
+                                          ep, stream);
+    if (e != hipSuccess) return e;
+    // dgrad 2: da = du W_gate + dv W_up (K = 2h over the two K-major slabs)
+    e = dgrad_bf16<kEpiNone, float>(b.dab, 2 * h, d, wg, wu, static_cast<int64_t>(h) * d, h / kBK,
+                                    b.group_offset, G, b.mstart, b.da, b.sk_ws, EpiArgs{},
+                                    stream);
     if (e != hipSuccess) return e;
   }
   // weight gradients
-  e = wgrad_bf16(b.dy_t, b.ghid_t, kt, d, h, b.kofs, G, b.dw_down, stream);
-  if (e == hipSuccess) e = wgrad_bf16(b.dab_t, b.xs_t, kt, h, d, b.kofs, G, b.dw_gate, stream);
-  if (e == hipSuccess)
-    e = wgrad_bf16(b.dab_t + static_cast<int64_t>(h) * kt, b.xs_t, kt, h, d, b.kofs, G, b.dw_up,
-                   stream);
+  e = wgrad_bf16(dout, d, hid, h, d, h, b.group_offset, G, b.zero, b.dw_down, stream);
+  if (e == hipSuccess) e = wgrad_bf16(b.dab, 2 * h, xs, d, h, d, b.group_offset, G, b.zero,
+                                      b.dw_gate, stream);
+  if (e == hipSuccess) e = wgrad_bf16(b.dab + h, 2 * h, xs, d, h, d, b.group_offset, G, b.zero,
+                                      b.dw_up, stream);
   return e;
 }
 

@@ -66,11 +66,12 @@ struct SwigluBwdArgs {
   int64_t max_rows;
   const int32_t* a_rows;
   int a_div;
-  const void* dy;           // upstream gradient rows, gathered like a
-  const float* row_gate;    // per pair (a_rows[r]) or per row, or NULL (1)
+  const void* dout;         // [max_rows, d] upstream gradient of each row's expert output
   const void* uv;           // [max_rows, 2h] pre-activations of the forward
-  const void* w_down_t;     // [G, h, d]
-  const void* w_gu_t;       // [G, d, 2h]
+  const void* hid;          // [max_rows, h] hidden activation of the forward
+  const void* w_gate;       // [G, h, d]
+  const void* w_up;         // [G, h, d]
+  const void* w_down;       // [G, d, h]
   float* da;                // [max_rows, d]
   float* dw_gate;           // [G, h, d]
   float* dw_up;             // [G, h, d]
@@ -78,18 +79,10 @@ struct SwigluBwdArgs {
   // workspace
   int32_t* mstart;          // tile table
   float* sk_ws;             // split-K partial tiles
-  int32_t* kofs;            // [G + 1]
-  int64_t kt;               // backward_kt(max_rows, G)
-  uint16_t* xs_t;           // [d, kt]
-  uint16_t* dy_t;           // [d, kt]
+  uint16_t* zero;           // [max(d, 2h)] zeros
+  uint16_t* xs;             // [max_rows, d] gathered rows (when a_rows is given)
   uint16_t* dab;            // [max_rows, 2h]
-  uint16_t* dab_t;          // [2h, kt]
-  uint16_t* ghid_t;         // [h, kt]
 };
-// columns of the K-grouped transposed operands of the weight gradients
-int64_t backward_kt(int64_t max_rows, int G);
-hipError_t launch_weights_t(const void* w_gate, const void* w_up, const void* w_down, int d, int h,
-                            int G, void* w_down_t, void* w_gu_t, hipStream_t stream);
 hipError_t launch_expert_backward(const SwigluBwdArgs& args, hipStream_t stream);
 
 // combine.hip
@@ -99,8 +92,8 @@ hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, c
 
 // backward.hip: combine, gate/router and router-linear gradients
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,
-                                   const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
-                                   hipStream_t stream);
+                                   const int32_t* pair_row, const float* gate, int64_t T, int k,
+                                   int d, float* dgate, void* dout, hipStream_t stream);
 hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
                                  const float* dgate, const int32_t* count, int64_t T, int E, int k,
                                  float alpha, float c_bal, float c_z, float* dlogits,

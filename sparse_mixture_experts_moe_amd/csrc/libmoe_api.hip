@@ -398,65 +398,42 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
   return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up_train");
 }
 
-moe_status_t moe_expert_weights_t(const void* w_gate, const void* w_up, const void* w_down, int dt,
-                                  int d, int h, int G, void* w_down_t, void* w_gu_t,
-                                  void* stream) {
-  if (d < 1 || h < 1 || G < 1) return fail(MOE_EINVAL, "moe_expert_weights_t: need d, h, G >= 1");
-  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: bf16 only");
-  if (d % 64 != 0 || h % 64 != 0)
-    return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: needs d %% 64 == 0 and h %% 64 == 0");
-  if (G > 65535) return fail(MOE_EUNSUPPORTED, "moe_expert_weights_t: G > 65535");
-  if (!w_gate || !w_up || !w_down || !w_down_t || !w_gu_t)
-    return fail(MOE_EINVAL, "moe_expert_weights_t: NULL pointer");
-  return hip_status(moe::launch_weights_t(w_gate, w_up, w_down, d, h, G, w_down_t, w_gu_t,
-                                          as_stream(stream)),
-                    "moe_expert_weights_t");
-}
-
 namespace {
 
 struct BwdLayout {
-  size_t table, sk, kofs, xs_t, dy_t, dab, dab_t, ghid_t, total;
-  int64_t kt;
+  size_t table, sk, zero, xs, dab, total;
 };
 
-BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G) {
+BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G, bool gather) {
   BwdLayout L{};
-  L.kt = moe::backward_kt(max_rows, G);
-  const size_t kt = static_cast<size_t>(L.kt);
   size_t o = 0;
   L.table = o;
   o += tile_table_bytes(G);
   L.sk = o;
   o += moe::split_k_workspace_bytes();
-  L.kofs = o;
-  o += align256(sizeof(int32_t) * (static_cast<size_t>(G) + 1));
-  L.xs_t = o;
-  o += align256(2 * static_cast<size_t>(d) * kt);
-  L.dy_t = o;
-  o += align256(2 * static_cast<size_t>(d) * kt);
+  L.zero = o;
+  o += align256(2 * static_cast<size_t>(d > 2 * h ? d : 2 * h));
+  L.xs = o;
+  if (gather) o += align256(2 * static_cast<size_t>(max_rows) * d);
   L.dab = o;
   o += align256(2 * static_cast<size_t>(max_rows) * 2 * h);
-  L.dab_t = o;
-  o += align256(2 * static_cast<size_t>(2 * h) * kt);
-  L.ghid_t = o;
-  o += align256(2 * static_cast<size_t>(h) * kt);
   L.total = o;
   return L;
 }
 
 }  // namespace
 
-size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt) {
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,
+                                            int gather) {
   if (max_rows < 0 || d < 1 || h < 1 || G < 1 || dt != MOE_BF16) return 0;
-  return bwd_layout(max_rows, d, h, G).total;
+  return bwd_layout(max_rows, d, h, G, gather != 0).total;
 }
 
 moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
                                         const int32_t* group_offset, int64_t max_rows,
-                                        const int32_t* a_rows, int a_rows_div, const void* dy,
-                                        const float* row_gate, const void* uv,
-                                        const void* w_down_t, const void* w_gu_t, float* da,
+                                        const int32_t* a_rows, int a_rows_div, const void* dout,
+                                        const void* uv, const void* hid, const void* w_gate,
+                                        const void* w_up, const void* w_down, float* da,
                                         float* dw_gate, float* dw_up, float* dw_down, void* ws,
                                         size_t ws_bytes, void* stream) {
   const char* fn = "moe_expert_swiglu_backward";
@@ -464,18 +441,17 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   if (st != MOE_OK) return st;
   if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: bf16 only", fn);
   if (static_cast<int64_t>(d) * h * 4 > static_cast<int64_t>(UINT32_MAX))
-    return fail(MOE_EUNSUPPORTED, "%s: 4 d h over 2^32 (transposed gate/up weights)", fn);
-  const BwdLayout L = bwd_layout(max_rows, d, h, G);
-  if (static_cast<int64_t>(d > h ? d : h) * L.kt * 2 > static_cast<int64_t>(UINT32_MAX) ||
-      L.kt > INT32_MAX / 2)
-    return fail(MOE_EUNSUPPORTED, "%s: too many rows for 32-bit operand offsets", fn);
-  if (G > 65535) return fail(MOE_EUNSUPPORTED, "%s: G > 65535", fn);
-  if (!dw_gate || !dw_up || !dw_down || !w_down_t || !w_gu_t)
+    return fail(MOE_EUNSUPPORTED, "%s: 4 d h over 2^32", fn);
+  if (static_cast<int64_t>(G) * ((d + 255) / 256) * ((h + 255) / 256) > INT32_MAX / 2)
+    return fail(MOE_EUNSUPPORTED, "%s: too many weight-gradient tiles", fn);
+  if (!w_gate || !w_up || !w_down || !dw_gate || !dw_up || !dw_down)
     return fail(MOE_EINVAL, "%s: NULL pointer", fn);
-  if (max_rows > 0 && (!a || !dy || !uv || !da)) return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if (max_rows > 0 && (!a || !dout || !uv || !hid || !da))
+    return fail(MOE_EINVAL, "%s: NULL pointer", fn);
   if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "%s: a_rows_div < 1", fn);
+  const BwdLayout L = bwd_layout(max_rows, d, h, G, a_rows != nullptr);
   if (ws_bytes < L.total || !ws)
-    return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", ws_bytes, L.total);
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
   moe::SwigluBwdArgs b{};
   b.a = a;
@@ -486,39 +462,37 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   b.max_rows = max_rows;
   b.a_rows = a_rows;
   b.a_div = a_rows ? a_rows_div : 1;
-  b.dy = dy;
-  b.row_gate = row_gate;
+  b.dout = dout;
   b.uv = uv;
-  b.w_down_t = w_down_t;
-  b.w_gu_t = w_gu_t;
+  b.hid = hid;
+  b.w_gate = w_gate;
+  b.w_up = w_up;
+  b.w_down = w_down;
   b.da = da;
   b.dw_gate = dw_gate;
   b.dw_up = dw_up;
   b.dw_down = dw_down;
   b.mstart = reinterpret_cast<int32_t*>(w + L.table);
   b.sk_ws = reinterpret_cast<float*>(w + L.sk);
-  b.kofs = reinterpret_cast<int32_t*>(w + L.kofs);
-  b.kt = L.kt;
-  b.xs_t = reinterpret_cast<uint16_t*>(w + L.xs_t);
-  b.dy_t = reinterpret_cast<uint16_t*>(w + L.dy_t);
+  b.zero = reinterpret_cast<uint16_t*>(w + L.zero);
+  b.xs = a_rows ? reinterpret_cast<uint16_t*>(w + L.xs) : nullptr;
   b.dab = reinterpret_cast<uint16_t*>(w + L.dab);
-  b.dab_t = reinterpret_cast<uint16_t*>(w + L.dab_t);
-  b.ghid_t = reinterpret_cast<uint16_t*>(w + L.ghid_t);
   return hip_status(moe::launch_expert_backward(b, as_stream(stream)), fn);
 }
 
 moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
-                                  const int32_t* pair_row, int64_t T, int k, int d, float* dgate,
-                                  void* stream) {
+                                  const int32_t* pair_row, const float* topk_gate, int64_t T, int k,
+                                  int d, float* dgate, void* dout, void* stream) {
   if (T < 0 || k < 1 || d < 1)
     return fail(MOE_EINVAL, "moe_combine_backward: need T >= 0, k >= 1, d >= 1");
   if (!valid_dtype(dy_dt) || !valid_dtype(y_dt))
     return fail(MOE_EINVAL, "moe_combine_backward: dtype");
   if (T == 0) return ok();
-  if (!dy || !y_perm || !pair_row || !dgate)
+  if (!dy || !y_perm || !pair_row || !dgate || (dout && !topk_gate))
     return fail(MOE_EINVAL, "moe_combine_backward: NULL pointer");
   return hip_status(moe::launch_combine_backward(dy, dy_dt == MOE_BF16, y_perm, y_dt == MOE_BF16,
-                                                 pair_row, T, k, d, dgate, as_stream(stream)),
+                                                 pair_row, topk_gate, T, k, d, dgate, dout,
+                                                 as_stream(stream)),
                     "moe_combine_backward");
 }
 

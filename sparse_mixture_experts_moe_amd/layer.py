@@ -109,15 +109,15 @@ class MoELayer:
         f32 = torch.float32
         b["uv"] = torch.empty((R, 2 * h), dtype=x.dtype, device=dev)
         b["dgate"] = torch.empty((T, k), dtype=f32, device=dev)
+        b["dout"] = torch.empty((R, d), dtype=x.dtype, device=dev)
         b["dlogits"] = torch.empty((T, E), dtype=f32, device=dev)
-        b["w_down_t"] = torch.empty((E, h, d), dtype=x.dtype, device=dev)
-        b["w_gu_t"] = torch.empty((E, d, 2 * h), dtype=x.dtype, device=dev)
         b["da"] = torch.empty((R, d), dtype=f32, device=dev)
         b["dw_gate"] = torch.empty((E, h, d), dtype=f32, device=dev)
         b["dw_up"] = torch.empty((E, h, d), dtype=f32, device=dev)
         b["dw_down"] = torch.empty((E, d, h), dtype=f32, device=dev)
-        b["bwd_ws"] = torch.empty(max(1, _lib.moe_expert_swiglu_backward_workspace(R, d, h, E, dt)),
-                                  dtype=torch.uint8, device=dev)
+        b["bwd_ws"] = torch.empty(
+            max(1, _lib.moe_expert_swiglu_backward_workspace(R, d, h, E, dt, True)),
+            dtype=torch.uint8, device=dev)
         b["dw_router"] = torch.empty((E, d), dtype=f32, device=dev)
         b["dlogit_bias"] = torch.empty(E, dtype=f32, device=dev)
         b["dx_acc"] = torch.empty((T, d), dtype=f32, device=dev)
@@ -128,13 +128,11 @@ class MoELayer:
             Hs = self.shared[0].shape[1]
             b["shared_hid"] = torch.empty((T, Hs), dtype=x.dtype, device=dev)
             b["shared_uv"] = torch.empty((T, 2 * Hs), dtype=x.dtype, device=dev)
-            b["shared_w_down_t"] = torch.empty((1, Hs, d), dtype=x.dtype, device=dev)
-            b["shared_w_gu_t"] = torch.empty((1, d, 2 * Hs), dtype=x.dtype, device=dev)
             b["shared_dw_gate"] = torch.empty((1, Hs, d), dtype=f32, device=dev)
             b["shared_dw_up"] = torch.empty((1, Hs, d), dtype=f32, device=dev)
             b["shared_dw_down"] = torch.empty((1, d, Hs), dtype=f32, device=dev)
             b["shared_bwd_ws"] = torch.empty(
-                max(1, _lib.moe_expert_swiglu_backward_workspace(T, d, Hs, 1, dt)),
+                max(1, _lib.moe_expert_swiglu_backward_workspace(T, d, Hs, 1, dt, False)),
                 dtype=torch.uint8, device=dev)
         return b
 
@@ -218,14 +216,11 @@ class MoELayer:
 
     __call__ = forward
 
-    def backward(self, dy, coef_balance=0.0, coef_z=0.0, stream=None, mark=None,
-                 weights_t=True):
+    def backward(self, dy, coef_balance=0.0, coef_z=0.0, stream=None, mark=None):
         """Gradients after ``forward(x, train=True)`` on the same x: fills and
         returns the buffer dict with dx [T, d], dw_router, dlogit_bias (when the
         layer has a logit bias), dw_gate, dw_up, dw_down, and shared_dw_* (fp32),
-        plus the intermediates dgate and dlogits.  ``weights_t`` False reuses the
-        transposed weight copies of the previous call (valid while the weights
-        are unchanged)."""
+        plus the intermediates dgate, dout and dlogits."""
         T = dy.shape[0]
         b = self._bufs[(T, dy.dtype, dy.device)]
         if "x" not in b:
@@ -233,33 +228,24 @@ class MoELayer:
         x = b["x"]
         k, E = self.k, self.E
         mark = mark or (lambda name: None)
-        _lib.moe_combine_backward(dy, b["y_perm"], b["pair_row"], k, dgate=b["dgate"],
-                                  stream=stream)
+        _lib.moe_combine_backward(dy, b["y_perm"], b["pair_row"], k, b["topk_gate"],
+                                  dgate=b["dgate"], dout=b["dout"], stream=stream)
         mark("combine_bwd")
         _lib.moe_route_backward(b["logits"], b["topk_idx"], b["topk_gate"], b["dgate"],
                                 b["expert_count"], self.alpha, coef_balance, coef_z,
                                 dlogits=b["dlogits"], stream=stream)
         mark("route_bwd")
-        if weights_t:
-            _lib.moe_expert_weights_t(self.w_gate, self.w_up, self.w_down,
-                                      w_down_t=b["w_down_t"], w_gu_t=b["w_gu_t"], stream=stream)
-            if self.shared is not None:
-                sg, su, sd = self.shared
-                _lib.moe_expert_weights_t(sg, su, sd, w_down_t=b["shared_w_down_t"],
-                                          w_gu_t=b["shared_w_gu_t"], stream=stream)
-            mark("weights_t")
         _lib.moe_expert_swiglu_backward(
-            x, b["expert_offset"], T * k, dy, b["uv"], b["w_down_t"], b["w_gu_t"],
-            a_rows=b["row_pair"], a_rows_div=k, row_gate=b["topk_gate"], da=b["da"],
-            dw_gate=b["dw_gate"], dw_up=b["dw_up"], dw_down=b["dw_down"], ws=b["bwd_ws"],
-            stream=stream)
+            x, b["expert_offset"], T * k, b["dout"], b["uv"], b["hid"], self.w_gate, self.w_up,
+            self.w_down, a_rows=b["row_pair"], a_rows_div=k, da=b["da"], dw_gate=b["dw_gate"],
+            dw_up=b["dw_up"], dw_down=b["dw_down"], ws=b["bwd_ws"], stream=stream)
         mark("experts_bwd")
         if self.shared is not None:
+            sg, su, sd = self.shared
             _lib.moe_expert_swiglu_backward(
-                x, b["shared_off"], T, dy, b["shared_uv"], b["shared_w_down_t"],
-                b["shared_w_gu_t"], da=b["dx_acc"], dw_gate=b["shared_dw_gate"],
-                dw_up=b["shared_dw_up"], dw_down=b["shared_dw_down"], ws=b["shared_bwd_ws"],
-                stream=stream)
+                x, b["shared_off"], T, dy, b["shared_uv"], b["shared_hid"], sg, su, sd,
+                da=b["dx_acc"], dw_gate=b["shared_dw_gate"], dw_up=b["shared_dw_up"],
+                dw_down=b["shared_dw_down"], ws=b["shared_bwd_ws"], stream=stream)
             mark("shared_bwd")
         _lib.moe_router_backward(x, self.w_router, b["dlogits"], dw_router=b["dw_router"],
                                  dlogit_bias=b["dlogit_bias"] if self.logit_bias is not None else None,
