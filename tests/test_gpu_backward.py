@@ -217,3 +217,122 @@ def test_expert_backward_groups(sizes, d, h, gather):
                                 ("dw_up", dwu_h[g], ref[2]), ("dw_down", dwd_h[g], ref[3])):
             err = normwise(got, want)
             assert err <= 2e-2, (g, name, err)
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _silu_grad(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "finegrained_shared_bf16"])
+def test_backward_full_size_sampled(name):
+    """The training step at a workload's full size, in the bench's launch
+    configuration (two streams), checked on samples the oracle computes one
+    by one: gate and input gradients of sampled tokens, sampled entries of
+    every expert weight gradient, and the logit and router-weight gradients in
+    full on the GPU's own gate gradients."""
+    from moe_inputs import WORKLOADS
+    cfg = WORKLOADS[name]
+    c_bal, c_z = 1.0, 1e-3
+    _say(f"[case] full-size backward {name}: generating inputs")
+    inp = generate(cfg)
+    dy_h = generate_dy(cfg)
+    layer = build_layer(inp)
+    x = to_device(inp["x"])
+    dy = to_device(dy_h)
+    _say(f"[case] full-size backward {name}: running")
+    res = layer.forward(x, train=True)
+    layer.backward(dy, c_bal, c_z)
+    torch.cuda.synchronize()
+    _say(f"[case] full-size backward {name}: checking")
+    T, E, k, d, h = cfg.T, cfg.E, cfg.k, cfg.d, cfg.h
+    xf, wr = as_f32(inp["x"]), as_f32(inp["w_router"])
+    dyf = as_f32(dy_h)
+    gl = host(res["logits"])
+    idx = host(res["topk_idx"]).astype(np.int64)
+    gate = host(res["topk_gate"]).astype(np.float64)
+    pair_row = host(res["pair_row"]).reshape(T, k)
+    count = host(res["expert_count"])
+    off = host(res["expert_offset"])
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(T, size=12, replace=False))
+    W = {}
+
+    def weights(e):
+        if e not in W:
+            W[e] = (inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+        return W[e]
+
+    # gate and input gradients of the sampled tokens (routed part + router part)
+    gdg = host(res["dgate"])
+    gdx = host(res["dx"])
+    dl_rows = oracle.gate_logit_grad(gl[toks], idx[toks], gdg[toks])
+    dl_rows = dl_rows + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)[toks]
+    dl_rows = dl_rows + c_z * oracle.z_loss_logit_grad(gl)[toks]
+    dg_ref = np.zeros((toks.size, k))
+    dx_ref = dl_rows @ wr.astype(np.float64)
+    for n, t in enumerate(toks):
+        for j in range(k):
+            if pair_row[t, j] < 0:
+                continue
+            wg, wu, wd = weights(int(idx[t, j]))
+            xt = xf[t].astype(np.float64)
+            dg_ref[n, j] = float(dyf[t] @ oracle.swiglu(xt[None], wg, wu, wd)[0])
+            dxs, _, _, _ = oracle.swiglu_backward(xt[None], wg, wu, wd, gate[t, j] * dyf[t][None])
+            dx_ref[n] += dxs[0]
+    for s in shared_list(inp):
+        dxs, _, _, _ = oracle.swiglu_backward(xf[toks], s[0], s[1], s[2], dyf[toks])
+        dx_ref += dxs
+    errs = {"dgate": normwise(gdg[toks], dg_ref), "dx": normwise(gdx[toks], dx_ref)}
+
+    # logits and router weights on the GPU's gate gradients (fp32 kernels)
+    dl_same = oracle.gate_logit_grad(gl, idx, gdg)
+    dl_same = dl_same + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)
+    dl_same = dl_same + c_z * oracle.z_loss_logit_grad(gl)
+    gdl = host(res["dlogits"])
+    errs["dlogits_same_in"] = normwise(gdl, dl_same)
+    _, dwr_same, _ = oracle.router_linear_backward(xf, wr, gdl)
+    errs["dw_router_same_in"] = normwise(host(res["dw_router"]), dwr_same)
+
+    # sampled weight-gradient entries of a few experts (all of each expert's rows)
+    row_pair = host(res["row_pair"])
+    dwg, dwu, dwd = res["dw_gate"], res["dw_up"], res["dw_down"]
+    worst = {"dw_gate": 0.0, "dw_up": 0.0, "dw_down": 0.0}
+    for e in (int(v) for v in rng.choice(E, size=min(3, E), replace=False)):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r0 == r1:
+            assert float(dwg[e].abs().max()) == 0.0
+            continue
+        pairs = row_pair[r0:r1].astype(np.int64)
+        xs = xf[pairs // k].astype(np.float64)
+        dout = gate.reshape(-1)[pairs][:, None] * dyf[pairs // k]
+        wg, wu, wd = weights(e)
+        cols = rng.choice(h, size=6, replace=False)   # hidden units
+        feats = rng.choice(d, size=6, replace=False)  # model-width features
+        u = xs @ wg[cols].T.astype(np.float64)
+        v = xs @ wu[cols].T.astype(np.float64)
+        dh = dout @ wd[:, cols].astype(np.float64)
+        du = dh * v * _silu_grad(u)
+        dv = dh * _silu(u)
+        ref_g = du.T @ xs[:, feats]
+        ref_u = dv.T @ xs[:, feats]
+        ref_d = dout[:, feats].T @ (_silu(u) * v)
+        ci = torch.from_numpy(cols).cuda()
+        fi = torch.from_numpy(feats).cuda()
+        got_g = host(dwg[e].index_select(0, ci).index_select(1, fi))
+        got_u = host(dwu[e].index_select(0, ci).index_select(1, fi))
+        got_d = host(dwd[e].index_select(0, fi).index_select(1, ci))
+        # scale of each expert's gradient: its largest entry in the full GPU result
+        for key, got, ref, full in (("dw_gate", got_g, ref_g, dwg[e]), ("dw_up", got_u, ref_u, dwu[e]),
+                                    ("dw_down", got_d, ref_d, dwd[e])):
+            scale = float(full.abs().max())
+            worst[key] = max(worst[key], float(np.max(np.abs(got - ref))) / scale)
+    errs.update(worst)
+    _say(f"[ok] full-size backward {name}: " + ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+    assert errs["dlogits_same_in"] <= 1e-5 and errs["dw_router_same_in"] <= 1e-5, errs
+    for key in ("dgate", "dx", "dw_gate", "dw_up", "dw_down"):
+        assert errs[key] <= 2e-2, errs
