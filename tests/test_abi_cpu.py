@@ -170,3 +170,51 @@ def test_probes_reject():
     assert C.moe_probe_read(FAKE, 0, 4, FAKE, None) == L.MOE_EINVAL
     assert C.moe_probe_read(FAKE, 1024, 0, FAKE, None) == L.MOE_EINVAL
     assert C.moe_probe_read(FAKE, 1024, 4, None, None) == L.MOE_EINVAL
+
+
+def test_backward_rejects():
+    F32, BF = L.MOE_F32, L.MOE_BF16
+    # expert backward: bf16 only, shapes, pointers, workspace
+    ws = L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, BF, True)
+    assert ws > 0 and L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, F32, True) == 0
+    assert ws > L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, BF, False)
+    args = [FAKE, BF, 128, 256, 4, FAKE, 1000, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    s = C.moe_expert_swiglu_backward(*args[:1], F32, *args[2:])
+    assert s == L.MOE_EUNSUPPORTED and "bf16" in _err()
+    s = C.moe_expert_swiglu_backward(*args[:2], 100, *args[3:])
+    assert s == L.MOE_EUNSUPPORTED and "% 64" in _err()
+    s = C.moe_expert_swiglu_backward(*args[:9], None, *args[10:])
+    assert s == L.MOE_EINVAL
+    s = C.moe_expert_swiglu_backward(*args[:20], ws - 1, None)
+    assert s == L.MOE_EWORKSPACE
+    s = C.moe_expert_swiglu_backward(*args[:8], 0, *args[9:])
+    assert s == L.MOE_EINVAL and "a_rows_div" in _err()
+    # training gate/up: bf16 only, uv required
+    s = C.moe_expert_gate_up_train(FAKE, F32, 128, 256, 4, FAKE, 100, None, 1, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, 1 << 30, None)
+    assert s == L.MOE_EUNSUPPORTED
+    s = C.moe_expert_gate_up_train(FAKE, BF, 128, 256, 4, FAKE, 100, None, 1, FAKE, FAKE, FAKE,
+                                   None, FAKE, 1 << 30, None)
+    assert s == L.MOE_EINVAL
+    # combine backward: dout needs the gates
+    s = C.moe_combine_backward(FAKE, BF, FAKE, BF, FAKE, None, 10, 2, 64, FAKE, FAKE, None)
+    assert s == L.MOE_EINVAL
+    assert C.moe_combine_backward(FAKE, 7, FAKE, BF, FAKE, FAKE, 10, 2, 64, FAKE, None, None) == L.MOE_EINVAL
+    assert C.moe_combine_backward(None, BF, None, BF, None, None, 0, 2, 64, None, None, None) == L.MOE_OK
+    # route backward: k <= E, counts needed with the balance term
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4, 5, 0.01, 0.0, 0.0, FAKE,
+                                None) == L.MOE_EINVAL
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, None, 10, 8, 2, 0.01, 1.0, 0.0, FAKE,
+                                None) == L.MOE_EINVAL
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 300, 2, 0.01, 1.0, 0.0, FAKE,
+                                None) == L.MOE_EUNSUPPORTED
+    # router backward: workspace only with dw_router
+    need = L.moe_router_backward_workspace(4096, 1024, 8)
+    assert need > 0
+    s = C.moe_router_backward(FAKE, FAKE, BF, FAKE, 4096, 1024, 8, FAKE, None, None, 0, FAKE,
+                              need - 1, None)
+    assert s == L.MOE_EWORKSPACE
+    s = C.moe_router_backward(None, FAKE, BF, FAKE, 4096, 1024, 8, FAKE, None, None, 0, FAKE,
+                              need, None)
+    assert s == L.MOE_EINVAL
