@@ -1,5 +1,5 @@
 """CPU oracle for the sparse Mixture-of-Experts feed-forward layer (forward and
-backward passes).
+backward passes, and the per-step load-balancing updates).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -45,4 +45,10 @@ from .moe_backward import (  # noqa: F401
     silu_grad,
     swiglu_backward,
     z_loss_logit_grad,
+)
+from .moe_balance import (  # noqa: F401
+    adaptive_capacity,
+    balance_update,
+    load_ema,
+    selection_bias_update,
 )

@@ -138,6 +138,9 @@ def dispatch(idx, E, cap=UNLIMITED):
     pairs past the budget are dropped.  [Every] "What you still pay for": a
     token travels to the expert it was assigned.  Reading used: an expert's
     pairs are ranked in token order and its first ``cap`` pairs are kept.
+    ``cap`` is UNLIMITED, one budget for every expert, or a sequence of E
+    per-expert budgets ([MoDE] "Adaptive Capacity Factors": capacity per
+    expert).
 
     Returns a dict of int64 arrays:
       count    [E]    routed pairs per expert, before the drop
@@ -154,11 +157,13 @@ def dispatch(idx, E, cap=UNLIMITED):
     rank = np.zeros(R, dtype=np.int64)
     pair_row = np.full(R, -1, dtype=np.int64)
     members = []
+    per_expert = cap is not UNLIMITED and np.ndim(cap) == 1
     for e in range(E):
         pairs_e = np.nonzero(flat == e)[0]  # ascending pair id == ascending token id
         count[e] = pairs_e.size
         rank[pairs_e] = np.arange(pairs_e.size)
-        keep_e = pairs_e if cap is UNLIMITED else pairs_e[:cap]
+        cap_e = int(cap[e]) if per_expert else cap
+        keep_e = pairs_e if cap_e is UNLIMITED else pairs_e[:cap_e]
         kept[e] = keep_e.size
         members.append(keep_e)
     offset = np.zeros(E + 1, dtype=np.int64)
