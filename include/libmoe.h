@@ -170,6 +170,41 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
                          int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
                          void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute_budgets: moe_permute with one budget per expert,
+ *   kept(p) = rank(p) < expert_capacity[topk_idx[p]]
+ * (expert_capacity [E] int32 on the device, each >= 0; everything else as
+ * moe_permute).  Source: Zen MoDE, section "Adaptive Capacity Factors"
+ * (capacity per expert); the budgets typically come from moe_balance_update. */
+moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int E,
+                                 const int32_t* expert_capacity, const void* x, int dt, int d,
+                                 int32_t* expert_count, int32_t* expert_offset, int32_t* pair_row,
+                                 int32_t* row_pair, void* x_perm, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* moe_balance_update: the per-step load-balancing updates, from the pre-drop
+ * counts of the last step (expert_count of moe_permute, T tokens, k slots):
+ *   select_bias[e] += bias_step * sign(T k - E expert_count[e])   (float32)
+ *       (an overloaded expert's selection bias falls, an underloaded one's
+ *       rises; unchanged at the mean load), if select_bias is not NULL;
+ *   load_ema[e] = ema_decay * load_ema[e] + (1 - ema_decay) * f[e],
+ *       f[e] = expert_count[e] / (T k) (each product and the sum rounded to
+ *       float32, f rounded once from the exact quotient);
+ *   expert_capacity[e] = clamp(ceil(C_e T k / E), 0, T) with
+ *       C_e = cf_base + gamma (load_ema[e] - 1/E) on the updated load_ema,
+ *       in float64, if expert_capacity is not NULL.
+ * Sources: Zen-Max, section "Auxiliary-Loss-Free Load Balancing" (bias moved
+ * after each step against the load deviation); Zen MoDE, section "Adaptive
+ * Capacity Factors" (C_e(t) = C_base + gamma (fbar_e - 1/N_E) from rolling
+ * load statistics).  The pages give neither the step size, the rolling
+ * window nor gamma: they are the arguments (ema_decay in [0, 1]; 0 uses this
+ * step's load alone).  Every operation is a fixed IEEE sequence: results are
+ * bit-reproducible.  select_bias, load_ema [E] fp32 in/out; expert_count [E]
+ * int32; expert_capacity [E] int32 out. */
+moe_status_t moe_balance_update(const int32_t* expert_count, int64_t T, int k, int E,
+                                float* select_bias, float bias_step, float* load_ema,
+                                float ema_decay, double cf_base, double gamma,
+                                int32_t* expert_capacity, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* moe_expert_swiglu: G SwiGLU experts over contiguous row groups.
  *

@@ -51,6 +51,9 @@ _SIGS = {
     "moe_route": (_i, [_p, _p, _i, _i64, _i, _i, _i, _p, _p, _u, _p, _p, _p, _p, _sz, _p]),
     "moe_permute_workspace": (_sz, [_i64, _i, _i]),
     "moe_permute": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_permute_budgets": (_i, [_p, _i64, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz,
+                                 _p]),
+    "moe_balance_update": (_i, [_p, _i64, _i, _i, _p, _f, _p, _f, _d, _d, _p, _p]),
     "moe_expert_swiglu_workspace": (_sz, [_i64, _i, _i, _i, _i]),
     "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
                                _sz, _p]),
@@ -194,6 +197,53 @@ def moe_permute(topk_idx, E, capacity=-1, x=None, *, expert_count=None, expert_o
                           _ptr(expert_count), _ptr(expert_offset), _ptr(pair_row),
                           _ptr(row_pair), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
     return expert_count, expert_offset, pair_row, row_pair, x_perm
+
+
+def moe_permute_budgets(topk_idx, E, expert_capacity, x=None, *, expert_count=None,
+                        expert_offset=None, pair_row=None, row_pair=None, x_perm=None, ws=None,
+                        stream=None):
+    """moe_permute with a per-expert budget (expert_capacity [E] int32 on the device)."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    R = T * k
+    if expert_count is None:
+        expert_count = torch.empty(E, dtype=torch.int32, device=dev)
+    if expert_offset is None:
+        expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pair_row is None:
+        pair_row = torch.empty(R, dtype=torch.int32, device=dev)
+    if row_pair is None:
+        row_pair = torch.empty(R, dtype=torch.int32, device=dev)
+    dt, d = MOE_F32, 0
+    if x is not None:
+        dt, d = _dt(x), x.shape[1]
+        if x_perm is None:
+            x_perm = torch.empty((R, d), dtype=x.dtype, device=dev)
+    nws = moe_permute_workspace(T, k, E)
+    if ws is None:
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _contig(topk_idx, expert_capacity, x, expert_count, expert_offset, pair_row, row_pair, x_perm,
+            ws)
+    _check(_L.moe_permute_budgets(_ptr(topk_idx), T, k, E, _ptr(expert_capacity), _ptr(x), dt, d,
+                                  _ptr(expert_count), _ptr(expert_offset), _ptr(pair_row),
+                                  _ptr(row_pair), _ptr(x_perm), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return expert_count, expert_offset, pair_row, row_pair, x_perm
+
+
+def moe_balance_update(expert_count, T, k, load_ema, *, select_bias=None, bias_step=0.0,
+                       ema_decay=0.0, cf_base=1.0, gamma=0.0, expert_capacity=None,
+                       want_capacity=True, stream=None):
+    """Per-step updates (in place on select_bias and load_ema); returns the
+    per-expert budgets (int32 [E]) when ``want_capacity``."""
+    E = expert_count.numel()
+    if want_capacity and expert_capacity is None:
+        expert_capacity = torch.empty(E, dtype=torch.int32, device=expert_count.device)
+    _contig(expert_count, load_ema, select_bias, expert_capacity)
+    _check(_L.moe_balance_update(_ptr(expert_count), T, k, E, _ptr(select_bias), float(bias_step),
+                                 _ptr(load_ema), float(ema_decay), float(cf_base), float(gamma),
+                                 _ptr(expert_capacity), _stream(stream)))
+    return expert_capacity
 
 
 def moe_expert_swiglu_workspace(max_rows, d, h, G, dt) -> int:

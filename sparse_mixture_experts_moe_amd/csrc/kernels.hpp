@@ -27,7 +27,8 @@ hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int 
 int64_t permute_chunks(int64_t R);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int64_t cap,
-                          const void* x, int elem_bytes, int d, int32_t* count, int32_t* offset,
+                          const int32_t* cap_e, const void* x, int elem_bytes, int d,
+                          int32_t* count, int32_t* offset,
                           int32_t* pair_row, int32_t* row_pair, void* x_perm,
                           int32_t* local_rank, int32_t* hist, hipStream_t stream);
 
@@ -102,6 +103,11 @@ size_t router_backward_workspace_bytes(int64_t T, int d, int E);
 hipError_t launch_router_backward(const void* x, const void* w_router, bool bf16, const float* dl,
                                   int64_t T, int d, int E, float* dw_router, float* dlogit_bias,
                                   float* dx, bool dx_accumulate, void* ws, hipStream_t stream);
+
+// balance.hip: per-step load-balancing updates
+hipError_t launch_balance_update(const int32_t* count, int64_t T, int k, int E, float* select_bias,
+                                 float bias_step, float* f_bar, float decay, double cf_base,
+                                 double gamma, int32_t* capacity, hipStream_t stream);
 
 // stats.hip
 int64_t stats_blocks(int64_t T);

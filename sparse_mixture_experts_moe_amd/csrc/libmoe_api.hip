@@ -223,10 +223,65 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
   int32_t* local_rank = static_cast<int32_t*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                              align256(sizeof(int32_t) * static_cast<size_t>(T * k)));
-  return hip_status(moe::launch_permute(topk_idx, T, k, E, capacity, x, elem_bytes(dt), d,
+  return hip_status(moe::launch_permute(topk_idx, T, k, E, capacity, nullptr, x, elem_bytes(dt), d,
                                         expert_count, expert_offset, pair_row, row_pair, x_perm,
                                         local_rank, hist, as_stream(stream)),
                     "moe_permute");
+}
+
+moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int E,
+                                 const int32_t* expert_capacity, const void* x, int dt, int d,
+                                 int32_t* expert_count, int32_t* expert_offset, int32_t* pair_row,
+                                 int32_t* row_pair, void* x_perm, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!expert_capacity) return fail(MOE_EINVAL, "moe_permute_budgets: NULL expert_capacity");
+  if (T < 0) return fail(MOE_EINVAL, "moe_permute_budgets: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_permute_budgets: need 1 <= k <= E");
+  if (!expert_count || !expert_offset) return fail(MOE_EINVAL, "moe_permute_budgets: NULL pointer");
+  if (T > 0 && (!topk_idx || !pair_row || !row_pair))
+    return fail(MOE_EINVAL, "moe_permute_budgets: NULL pointer");
+  if (x && (!x_perm || d < 1 || !valid_dtype(dt)))
+    return fail(MOE_EINVAL, "moe_permute_budgets: gather needs x_perm, d >= 1 and a valid dtype");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_permute_budgets: E > %d", moe::kMaxExperts);
+  if (T * k > INT32_MAX) return fail(MOE_EUNSUPPORTED, "moe_permute_budgets: T*k exceeds int32");
+  const size_t need = moe_permute_workspace(T, k, E);
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_EWORKSPACE, "moe_permute_budgets: workspace %zu < %zu bytes", ws_bytes, need);
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_i32(expert_count, E, 0, as_stream(stream));
+    if (e == hipSuccess) e = moe::launch_fill_i32(expert_offset, E + 1, 0, as_stream(stream));
+    return hip_status(e, "moe_permute_budgets");
+  }
+  int32_t* local_rank = static_cast<int32_t*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                             align256(sizeof(int32_t) * static_cast<size_t>(T * k)));
+  return hip_status(moe::launch_permute(topk_idx, T, k, E, -1, expert_capacity, x,
+                                        elem_bytes(dt), d, expert_count, expert_offset, pair_row,
+                                        row_pair, x_perm, local_rank, hist, as_stream(stream)),
+                    "moe_permute_budgets");
+}
+
+moe_status_t moe_balance_update(const int32_t* expert_count, int64_t T, int k, int E,
+                                float* select_bias, float bias_step, float* load_ema,
+                                float ema_decay, double cf_base, double gamma,
+                                int32_t* expert_capacity, void* stream) {
+  if (T < 1 || k < 1 || E < 1 || k > E)
+    return fail(MOE_EINVAL, "moe_balance_update: need T >= 1 and 1 <= k <= E");
+  if (!expert_count || !load_ema) return fail(MOE_EINVAL, "moe_balance_update: NULL pointer");
+  if (!std::isfinite(bias_step) || !std::isfinite(ema_decay) || !std::isfinite(cf_base) ||
+      !std::isfinite(gamma))
+    return fail(MOE_EINVAL, "moe_balance_update: non-finite step, decay, cf_base or gamma");
+  if (ema_decay < 0.0f || ema_decay > 1.0f)
+    return fail(MOE_EINVAL, "moe_balance_update: ema_decay outside [0, 1]");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_balance_update: E > %d", moe::kMaxExperts);
+  if (T > INT32_MAX || T * k > (int64_t{1} << 53))
+    return fail(MOE_EUNSUPPORTED, "moe_balance_update: T too large");
+  return hip_status(moe::launch_balance_update(expert_count, T, k, E, select_bias, bias_step,
+                                               load_ema, ema_decay, cf_base, gamma,
+                                               expert_capacity, as_stream(stream)),
+                    "moe_balance_update");
 }
 
 // ---------------------------------------------------------------------------

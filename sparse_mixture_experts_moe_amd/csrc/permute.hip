@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
 // count[e]; offset[0..E] = exclusive scan of min(count, cap).
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ hist, int nchunk,
                                                             int E, int64_t cap,
+                                                            const int32_t* __restrict__ cap_e,
                                                             int32_t* __restrict__ count,
                                                             int32_t* __restrict__ offset) {
   __shared__ int part[kScanThreads];
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
     }
     if (seg == segs - 1) {
       count[col] = pre;
-      kept[col] = (cap >= 0 && pre > cap) ? static_cast<int>(cap) : pre;
+      const int64_t c = cap_e ? static_cast<int64_t>(cap_e[col]) : cap;  // per-expert budget
+      kept[col] = (c >= 0 && pre > c) ? static_cast<int>(c) : pre;
     }
   }
   __syncthreads();
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, int64_t R,
                                                       int E, int64_t cap,
+                                                      const int32_t* __restrict__ cap_e,
                                                       const int32_t* __restrict__ local_rank,
                                                       const int32_t* __restrict__ hist,
                                                       const int32_t* __restrict__ offset,
@@ -153,7 +156,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     if (p >= R) break;
     const int e = idx[p];
     const int r = hist[chunk * E + e] + local_rank[p];
-    const bool kept = cap < 0 || r < cap;
+    const int64_t c = cap_e ? static_cast<int64_t>(cap_e[e]) : cap;
+    const bool kept = c < 0 || r < c;
     const int row = offset[e] + r;
     pair_row[p] = kept ? row : -1;
     if (kept) row_pair[row] = static_cast<int32_t>(p);
@@ -201,18 +205,19 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream)
 }
 
 hipError_t launch_permute(const int32_t* idx, int64_t T, int k, int E, int64_t cap,
-                          const void* x, int elem_bytes, int d, int32_t* count, int32_t* offset,
+                          const int32_t* cap_e, const void* x, int elem_bytes, int d,
+                          int32_t* count, int32_t* offset,
                           int32_t* pair_row, int32_t* row_pair, void* x_perm,
                           int32_t* local_rank, int32_t* hist, hipStream_t stream) {
   const int64_t R = T * k;
   const int64_t nchunk = permute_chunks(R);
   rank_kernel<<<static_cast<unsigned>(nchunk), kRankThreads, 0, stream>>>(idx, R, E, local_rank,
                                                                           hist);
-  scan_kernel<<<1, kScanThreads, 0, stream>>>(hist, static_cast<int>(nchunk), E, cap, count,
-                                              offset);
-  scatter_kernel<<<static_cast<unsigned>(nchunk), 256, 0, stream>>>(idx, R, E, cap, local_rank,
-                                                                   hist, offset, pair_row,
-                                                                   row_pair);
+  scan_kernel<<<1, kScanThreads, 0, stream>>>(hist, static_cast<int>(nchunk), E, cap, cap_e,
+                                              count, offset);
+  scatter_kernel<<<static_cast<unsigned>(nchunk), 256, 0, stream>>>(idx, R, E, cap, cap_e,
+                                                                   local_rank, hist, offset,
+                                                                   pair_row, row_pair);
   if (x != nullptr) {
     const int64_t row_bytes = static_cast<int64_t>(d) * elem_bytes;
     gather_kernel<<<static_cast<unsigned>((R + 3) / 4), 256, 0, stream>>>(

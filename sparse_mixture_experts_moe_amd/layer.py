@@ -27,14 +27,22 @@ from . import _lib
 class MoELayer:
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
                  select_bias=None, capacity=-1, alpha=0.01, gather="fused",
-                 overlap_shared=True):
+                 overlap_shared=True, balance=None):
         """Weights are device tensors: w_router [E, d]; w_gate, w_up [E, h, d];
         w_down [E, d, h]; ``shared`` is None or (gate [Hs, d], up [Hs, d],
         down [d, Hs]) with the shared experts concatenated along the hidden
         axis.  ``capacity`` < 0 means unlimited.  ``gather`` is "fused" (the
         first expert GEMM reads token rows through the permutation) or "copy"
         (moe_permute writes an expert-ordered copy of x first).  ``overlap_shared``
-        runs the shared experts on a second stream."""
+        runs the shared experts on a second stream.
+
+        ``balance`` turns on the per-step load-balancing updates that
+        ``update_balance()`` applies after a step: a dict with ``bias_step``
+        (the selection-bias step; the layer then owns a selection bias, zero
+        if none was given), ``ema_decay``, and, for adaptive per-expert
+        capacity, ``cf_base`` and ``gamma`` (the budgets start at
+        moe_capacity(cf_base) and follow C_e = cf_base + gamma (fbar_e - 1/E)
+        from the first update on)."""
         if gather not in ("fused", "copy"):
             raise ValueError("gather must be 'fused' or 'copy'")
         self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
@@ -52,6 +60,15 @@ class MoELayer:
         self.overlap_shared = overlap_shared
         self._bufs = {}
         self._side = {}
+        self.balance = dict(balance) if balance else None
+        self.load_ema = None
+        self.expert_capacity = None
+        if self.balance:
+            dev = w_router.device
+            self.load_ema = torch.full((self.E,), 1.0 / self.E, dtype=torch.float32, device=dev)
+            if self.balance.get("bias_step", 0.0) and self.select_bias is None:
+                self.select_bias = torch.zeros(self.E, dtype=torch.float32, device=dev)
+        self._last_T = None
 
     def _buffers(self, x):
         T = x.shape[0]
@@ -179,11 +196,25 @@ class MoELayer:
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
                        ws=b["route_ws"], stream=stream)
         mark("route")
-        _lib.moe_permute(b["topk_idx"], E, self.capacity,
-                         x if self.gather == "copy" else None,
-                         expert_count=b["expert_count"], expert_offset=b["expert_offset"],
-                         pair_row=b["pair_row"], row_pair=b["row_pair"], x_perm=b["x_perm"],
-                         ws=b["perm_ws"], stream=stream)
+        if self.balance and "gamma" in self.balance:
+            if self.expert_capacity is None or self._last_T != T:
+                c0 = _lib.moe_capacity(self.balance["cf_base"], T, k, E)
+                self.expert_capacity = torch.full((E,), min(c0, T) if c0 >= 0 else T,
+                                                  dtype=torch.int32, device=x.device)
+            _lib.moe_permute_budgets(b["topk_idx"], E, self.expert_capacity,
+                                     x if self.gather == "copy" else None,
+                                     expert_count=b["expert_count"],
+                                     expert_offset=b["expert_offset"], pair_row=b["pair_row"],
+                                     row_pair=b["row_pair"], x_perm=b["x_perm"], ws=b["perm_ws"],
+                                     stream=stream)
+        else:
+            _lib.moe_permute(b["topk_idx"], E, self.capacity,
+                             x if self.gather == "copy" else None,
+                             expert_count=b["expert_count"], expert_offset=b["expert_offset"],
+                             pair_row=b["pair_row"], row_pair=b["row_pair"], x_perm=b["x_perm"],
+                             ws=b["perm_ws"], stream=stream)
+        self._last_T = T
+        self._last_counts = b["expert_count"]
         mark("permute")
         if self.gather == "copy":
             a, a_rows = b["x_perm"], None
@@ -215,6 +246,24 @@ class MoELayer:
         return b
 
     __call__ = forward
+
+    def update_balance(self, stream=None):
+        """The per-step load-balancing updates from the last forward's counts
+        (selection bias, rolling load, per-expert budgets for the next step)."""
+        if not self.balance:
+            raise RuntimeError("the layer was built without balance updates")
+        cfg = self.balance
+        adaptive = "gamma" in cfg
+        if adaptive and self.expert_capacity is None:
+            self.expert_capacity = torch.empty(self.E, dtype=torch.int32,
+                                               device=self._last_counts.device)
+        _lib.moe_balance_update(self._last_counts, self._last_T, self.k, self.load_ema,
+                                select_bias=self.select_bias if cfg.get("bias_step", 0.0) else None,
+                                bias_step=cfg.get("bias_step", 0.0),
+                                ema_decay=cfg.get("ema_decay", 0.0),
+                                cf_base=cfg.get("cf_base", 1.0), gamma=cfg.get("gamma", 0.0),
+                                expert_capacity=self.expert_capacity if adaptive else None,
+                                want_capacity=adaptive, stream=stream)
 
     def backward(self, dy, coef_balance=0.0, coef_z=0.0, stream=None, mark=None):
         """Gradients after ``forward(x, train=True)`` on the same x: fills and

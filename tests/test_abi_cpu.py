@@ -218,3 +218,29 @@ def test_backward_rejects():
     s = C.moe_router_backward(None, FAKE, BF, FAKE, 4096, 1024, 8, FAKE, None, None, 0, FAKE,
                               need, None)
     assert s == L.MOE_EINVAL
+
+
+def test_balance_rejects():
+    # the budgets are required; bad k
+    s = C.moe_permute_budgets(FAKE, 100, 2, 8, None, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
+                              FAKE, 1 << 20, None)
+    assert s == L.MOE_EINVAL and "expert_capacity" in _err()
+    s = C.moe_permute_budgets(FAKE, 100, 9, 8, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
+                              FAKE, 1 << 20, None)
+    assert s == L.MOE_EINVAL
+    ws = L.moe_permute_workspace(100, 2, 8)
+    s = C.moe_permute_budgets(FAKE, 100, 2, 8, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
+                              FAKE, ws - 1, None)
+    assert s == L.MOE_EWORKSPACE
+    # update: finite arguments, decay in [0, 1], a rolling-load buffer
+    nan = float("nan")
+    assert C.moe_balance_update(FAKE, 100, 2, 8, None, 0.1, FAKE, 0.5, nan, 1.0, None,
+                                None) == L.MOE_EINVAL
+    assert C.moe_balance_update(FAKE, 100, 2, 8, None, 0.1, FAKE, 1.5, 1.0, 1.0, None,
+                                None) == L.MOE_EINVAL
+    assert C.moe_balance_update(FAKE, 100, 2, 8, None, 0.1, None, 0.5, 1.0, 1.0, None,
+                                None) == L.MOE_EINVAL
+    assert C.moe_balance_update(FAKE, 0, 2, 8, None, 0.1, FAKE, 0.5, 1.0, 1.0, None,
+                                None) == L.MOE_EINVAL
+    assert C.moe_balance_update(FAKE, 100, 2, 300, None, 0.1, FAKE, 0.5, 1.0, 1.0, None,
+                                None) == L.MOE_EUNSUPPORTED
