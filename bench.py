@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared experts in line on the layer's stream instead of "
                          "overlapping them on a second stream")
+    ap.add_argument("--balance", action="store_true",
+                    help="apply the per-step load-balancing updates after every step "
+                         "(selection-bias step 1e-3, rolling-load decay 0.9, adaptive per-expert "
+                         "budgets with C_base = the workload's capacity factor or 1 and gamma = E)")
     ap.add_argument("--backward", action="store_true",
                     help="time training steps instead: forward (keeping the pre-activations) "
                          "plus the backward pass of <dy, y> + loss + 1e-3 zloss")
@@ -344,10 +348,28 @@ def main():
     print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     layer = layer_from_inputs(inp, args.gather)
     layer.overlap_shared = not args.serial_shared
+    balance = None
+    if args.balance:
+        balance = dict(bias_step=1e-3, ema_decay=0.9, cf_base=cfg.cf if cfg.cf > 0 else 1.0,
+                       gamma=float(cfg.E))
+        layer = type(layer)(layer.w_router, layer.w_gate, layer.w_up, layer.w_down, cfg.k,
+                            shared=None if layer.shared is None else
+                            tuple(w[0] for w in layer.shared),
+                            logit_bias=layer.logit_bias, select_bias=layer.select_bias,
+                            alpha=cfg.alpha, gather=args.gather,
+                            overlap_shared=not args.serial_shared, balance=balance)
     x = to_device(inp["x"])
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+
+    def step(mark=None):
+        res_ = layer(x, mark=mark)
+        if balance:
+            layer.update_balance()
+            if mark:
+                mark("balance_update")
+        return res_
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -357,7 +379,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     for _ in range(args.warmup):
-        layer(x)
+        step()
     torch.cuda.synchronize()
 
     # Timed region: K steps with only the two events the roofline needs, around
@@ -379,7 +401,7 @@ def main():
     t_host = time.perf_counter()
     for _ in range(args.steps):
         gu_marks.append([])
-        res = layer(x, mark=mark_gate_up)
+        res = step(mark_gate_up)
     end.record(stream)
     host_ms = (time.perf_counter() - t_host) * 1e3 / args.steps  # enqueue cost per step
     torch.cuda.synchronize()
@@ -407,7 +429,7 @@ def main():
         ev0 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         marks.append([("start", ev0)])
-        layer(x, mark=mark)
+        step(mark)
     torch.cuda.synchronize()
     layer.overlap_shared = overlap
     phases = {}
@@ -490,7 +512,8 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
                    "gather": args.gather, "parallelism": "none (1 GPU)",
-                   "shared_overlap": bool(cfg.n_shared and layer.overlap_shared)},
+                   "shared_overlap": bool(cfg.n_shared and layer.overlap_shared),
+                   **({"balance": balance} if balance else {})},
         "roofline": roof,
         "measured_ceilings": ceil,
         "expert_gemm_mfma_util": expert_flops / (expert_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
