@@ -339,13 +339,13 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
  *   moe_router_backward         router weights, logit bias, dx (accumulate)
  *   moe_combine(da_perm, NULL gates, shared_y = the accumulated dx) -> dx
  * Every gradient output is fp32 and written (not accumulated) unless stated.
- * The bf16 expert kernels keep u, v and [du | dv] in bf16 (rounded to
- * nearest even) between GEMMs.
+ * The bf16 expert kernels keep u, v and du, dv in bf16 (rounded to nearest
+ * even) between GEMMs.
  */
 
 /* moe_expert_gate_up_train: moe_expert_gate_up that also keeps the
- * pre-activations for the backward pass:
- *   uv[r, 0:h] = a_r . w_gate[g]^T,  uv[r, h:2h] = a_r . w_up[g]^T
+ * pre-activations for the backward pass, interleaved per hidden unit:
+ *   uv[r, 2c] = a_r . w_gate[g][c],  uv[r, 2c + 1] = a_r . w_up[g][c]
  * uv [max_rows, 2h] bf16.  bf16 only (MOE_EUNSUPPORTED otherwise); runs the
  * tiled kernel at every row count.  Workspace: moe_expert_group_workspace(G). */
 moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
@@ -358,7 +358,7 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
  * (same group semantics, gather and limits as moe_expert_swiglu).  For row r
  * of group g with a_r = a[a_rows[r] / a_rows_div] (or a[r]) and dout_r the
  * upstream gradient of the row's expert output (gate already applied):
- *   u, v    = uv[r, 0:h], uv[r, h:2h]     (from moe_expert_gate_up_train)
+ *   u, v    = uv[r, 0::2], uv[r, 1::2]    (from moe_expert_gate_up_train)
  *   hid_r   = hid[r]                       (SiLU(u) * v, from the same call)
  *   dhid    = dout_r . w_down[g]                                 ([h])
  *   du      = dhid * v * SiLU'(u),  dv = dhid * SiLU(u)
@@ -376,7 +376,7 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
  * group_offset[G] untouched).
  * Workspace: moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt,
  * a_rows != NULL) bytes (tile table, split-K partials, a zero row, the
- * gathered rows of a when a_rows is given, and [du | dv] in bf16: about
+ * gathered rows of a when a_rows is given, and du, dv interleaved in bf16: about
  * 2 max_rows (2h + d) bytes plus 64 MiB); contents need no initialisation
  * and are dead after the call. */
 size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,

@@ -463,8 +463,10 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
 //             contiguous along K (the forward's layout; A rows may be gathered).
 //   kOpSlabT: B only; the expert's weight slab is stored K-major, [K][N] with
 //             rows of N elements (the input-gradient GEMMs read the forward's
-//             weights this way); K slices below OpArgs::nk1 come from B0's
-//             slab, the rest from B1's.
+//             weights this way).
+//   kOpSlabI: B only; K-major like kOpSlabT, with the even K rows 2i from row
+//             i of B0's slab and the odd rows 2i + 1 from row i of B1's (the
+//             gate and up weights against the interleaved (du, dv) columns).
 //   kOpRowsT: K-major data rows: K runs over the rows r0 .. rend - 1 of a
 //             row-major buffer whose columns are the tile's M (A, row length
 //             lda) or N (B, row length ldb); K rows past rend read the zero
@@ -476,9 +478,9 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
 constexpr int kOpRows = 0;
 constexpr int kOpSlabT = 1;
 constexpr int kOpRowsT = 2;
+constexpr int kOpSlabI = 3;
 
 struct OpArgs {
-  int nk1;               // kOpSlabT: K slices taken from B0
   int r0, rend;          // kOpRowsT: row range of the K axis
   int lda, ldb;          // kOpRowsT: row lengths of A and B
   int a_cols;            // kOpRowsT: columns of A (the GEMM's M)
@@ -520,19 +522,25 @@ __device__ __forceinline__ bf16x8 read_kmajor(const uint16_t* p, int X) {
 // Epilogue modes of the bf16 tiles.
 //   kEpiNone:    C = A B^T (fused: C = SiLU(gate) * up).
 //   kEpiSaveUV:  fused only; also keeps the two pre-activations of every
-//                output, uv[r, c] = gate sum and uv[r, N + c] = up sum (bf16),
-//                for the backward pass.
+//                output, uv[r, 2c] = gate sum and uv[r, 2c + 1] = up sum
+//                (bf16), for the backward pass.
 //   kEpiSiluBwd: unfused, N = h, the accumulator is dhid = dout W_down; with
 //                u, v read back from uv:
 //                  du = dhid v SiLU'(u),  dv = dhid SiLU(u)
-//                written to dab[r] = [du | dv] (bf16).  C is not written.
+//                written to dab[r, 2c] = du, dab[r, 2c + 1] = dv (bf16).  C
+//                is not written.
+//   kEpiRowPairs: unfused fp32; even output rows 2m go to C row m, odd rows
+//                2m + 1 to row m of c_odd (the gate and up weight gradients of
+//                one GEMM over the interleaved (du, dv) columns).
 constexpr int kEpiNone = 0;
 constexpr int kEpiSaveUV = 1;
 constexpr int kEpiSiluBwd = 2;
+constexpr int kEpiRowPairs = 3;
 
 struct EpiArgs {
   uint16_t* uv;   // [rows, 2N]
   uint16_t* dab;  // [rows, 2N]
+  float* c_odd;   // kEpiRowPairs
 };
 
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
@@ -622,7 +630,14 @@ __device__ __forceinline__ void gemm_tile(
   }
   const uint16_t* bslab0 = B0 + tile.g * b_stride;
   const uint16_t* bslab1 = (kFused ? B1 : B0) + tile.g * b_stride;
-  if constexpr (kBM == kOpSlabT) bslab1 = B1 + tile.g * b_stride;
+  // interleaved slabs: each lane's K rows have one parity in every copy (the
+  // copies advance k by a multiple of 4), so it always reads one slab
+  const uint16_t* bi_lane = nullptr;
+  if constexpr (kBM == kOpSlabI) {
+    const int col = b_kcol < N ? b_kcol : N - 8;
+    bi_lane = ((b_kr0 & 1) ? B1 : B0) + tile.g * b_stride + static_cast<int64_t>(b_kr0 >> 1) * N +
+              col;
+  }
   static_assert(!kFused || sizeof(OutT) == 2, "split-K partials are for the unfused GEMM");
   static_assert(!kFused || (kAM == kOpRows && kBM == kOpRows), "fused tiles read row-major operands");
 
@@ -643,12 +658,7 @@ __device__ __forceinline__ void gemm_tile(
     const int row = oa.r0 + (ks0 + ks) * kBK + kr;
     return row < oa.rend ? base + static_cast<int64_t>(row) * ld + col : oa.zero + col;
   };
-  // K-major weight slab: slices below nk1 from B0, the rest from B1
-  auto slab_t_base = [&](int ks) {
-    const int kg = ks0 + ks;
-    return kg < oa.nk1 ? bslab0 + static_cast<int64_t>(kg) * kBK * N
-                       : bslab1 + static_cast<int64_t>(kg - oa.nk1) * kBK * N;
-  };
+  auto slab_t_base = [&](int ks) { return bslab0 + static_cast<int64_t>(ks0 + ks) * kBK * N; };
   // copy K slice `ks` (clamped into range: surplus copies reload the last slice
   // into a stage nobody reads again, which keeps the loop branch-free)
 #define MOE_COPY_A(j, stage, ks)                                                     \
@@ -669,6 +679,9 @@ __device__ __forceinline__ void gemm_tile(
                   dst_);                                                             \
     else if constexpr (kBM == kOpSlabT)                                              \
       dma_lds16_s(slab_t_base(ksc_), boff[(j)], dst_);                               \
+    else if constexpr (kBM == kOpSlabI)                                              \
+      dma_lds16(bi_lane + (static_cast<int64_t>(ks0 + ksc_) * (kBK / 2) + 2 * (j) * BXR) * N, \
+                dst_);                                                               \
     else                                                                             \
       dma_lds16(rows_t_ptr(B0, oa.ldb, b_col, b_kr0 + 4 * (j) * BXR, ksc_), dst_);   \
   } while (0)
@@ -799,7 +812,7 @@ __device__ __forceinline__ void gemm_tile(
   const int row0 = tile.m0 + wm * (BM / WM) + (lane & 31);
   const int cq = 4 * (lane >> 5);
   if constexpr (kEpi == kEpiSiluBwd) {
-    // dab[r] = [du | dv] from the accumulator (dhid) and the kept u, v
+    // dab[r] = (du, dv) pairs from the accumulator (dhid) and the kept (u, v)
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int row = row0 + i * 32;
@@ -813,23 +826,17 @@ __device__ __forceinline__ void gemm_tile(
         for (int q = 0; q < 4; ++q) {
           const int col = cb + 8 * q;
           if (col >= N) continue;
-          const u32x2 ur = *reinterpret_cast<const u32x2*>(urow + col);
-          const u32x2 vr = *reinterpret_cast<const u32x2*>(urow + N + col);
-          float du[4], dv[4];
+          const u32x4 uv = *reinterpret_cast<const u32x4*>(urow + 2 * col);
+          uint32_t o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t uw = ur[e >> 1], vw = vr[e >> 1];
-            const float u = __uint_as_float((e & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
-            const float v = __uint_as_float((e & 1) ? (vw & 0xFFFF0000u) : (vw << 16));
+            const float u = __uint_as_float(uv[e] << 16);
+            const float v = __uint_as_float(uv[e] & 0xFFFF0000u);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-u));  // 0 once exp overflows
             const float dh = acc[i][j][4 * q + e];
-            du[e] = dh * v * (sg * (1.0f + u * (1.0f - sg)));
-            dv[e] = dh * (u * sg);
+            o[e] = pack_bf16x2(dh * v * (sg * (1.0f + u * (1.0f - sg))), dh * (u * sg));
           }
-          *reinterpret_cast<u32x2*>(drow + col) =
-              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-          *reinterpret_cast<u32x2*>(drow + N + col) =
-              u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+          *reinterpret_cast<u32x4*>(drow + 2 * col) = u32x4{o[0], o[1], o[2], o[3]};
         }
       }
     }
@@ -840,6 +847,9 @@ __device__ __forceinline__ void gemm_tile(
     const int row = row0 + i * 32;
     if (row >= tile.row_end) continue;
     OutT* crow = C + static_cast<int64_t>(row) * N;
+    if constexpr (kEpi == kEpiRowPairs)
+      crow = reinterpret_cast<OutT*>(row & 1 ? ep.c_odd : reinterpret_cast<float*>(C)) +
+             static_cast<int64_t>(row >> 1) * N;
     if constexpr (kFused) {
 #pragma unroll
       for (int j = 0; j < NT / 2; ++j) {
@@ -855,13 +865,13 @@ __device__ __forceinline__ void gemm_tile(
           u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(crow + col) = pk;
           if constexpr (kEpi == kEpiSaveUV) {
-            uint16_t* urow = ep.uv + static_cast<int64_t>(row) * (2 * N);
+            // (u, v) pairs of the four columns: one 16-byte store
             const f32x16& ga = acc[i][j];
             const f32x16& ua = acc[i][j + NT / 2];
-            *reinterpret_cast<u32x2*>(urow + col) =
-                u32x2{pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3])};
-            *reinterpret_cast<u32x2*>(urow + N + col) =
-                u32x2{pack_bf16x2(ua[4 * q], ua[4 * q + 1]), pack_bf16x2(ua[4 * q + 2], ua[4 * q + 3])};
+            *reinterpret_cast<u32x4*>(ep.uv + static_cast<int64_t>(row) * (2 * N) + 2 * col) =
+                u32x4{pack_bf16x2(ga[4 * q], ua[4 * q]), pack_bf16x2(ga[4 * q + 1], ua[4 * q + 1]),
+                      pack_bf16x2(ga[4 * q + 2], ua[4 * q + 2]),
+                      pack_bf16x2(ga[4 * q + 3], ua[4 * q + 3])};
           }
         }
       }
@@ -1478,13 +1488,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 
 // Weight gradients: for every group g, C_g[M, N] = sum over the group's rows r
 // of A[r, :M]^T B[r, :N] (fp32, at C + g M N), A and B row-major with rows of
-// lda and ldb elements.  One workgroup per output tile (tiles of a group in
+// lda and ldb elements; with kPairs the even rows of C_g go to C and the odd
+// rows to C_odd (M / 2 rows each, at g M N / 2).  One workgroup per output tile (tiles of a group in
 // the banded order, groups in order, contiguous runs per XCD); a group
 // without rows gets zeros.
+template <bool kPairs>
 __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, int M,
     int N, const int32_t* __restrict__ off, int G, int mtn, int ntn,
-    const uint16_t* __restrict__ zero, float* __restrict__ C) {
+    const uint16_t* __restrict__ zero, float* __restrict__ C, float* __restrict__ C_odd) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int per = mtn * ntn, total = G * per, nw8 = (total + 7) & ~7;
   const int L = xcd_run(blockIdx.x, nw8);
@@ -1504,20 +1516,24 @@ __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
     mt = lead + (local - nt * mtail);
   }
   const Tile2 tile = classify(Tile{0, mt * kTileM, M, nt * 256});
-  float* Cg = C + static_cast<int64_t>(g) * M * N;
+  // this group's output (row pairs: M / 2 rows in each of C and C_odd)
+  const int64_t gsz = static_cast<int64_t>(kPairs ? M / 2 : M) * N;
+  float* Cg = C + g * gsz;
+  EpiArgs ep{};
+  ep.c_odd = kPairs ? C_odd + g * gsz : nullptr;
   const int r0 = off[g], r1 = off[g + 1];
   const int nk = (r1 - r0 + kBK - 1) / kBK;
   if (nk == 0) {
     const int rows = min(kTileM, M - tile.m0);
     for (int i = threadIdx.x; i < rows * 64; i += kThreads) {
-      const int r = i / 64, c = tile.n0 + (i % 64) * 4;
-      if (c < N)
-        *reinterpret_cast<f32x4*>(Cg + static_cast<int64_t>(tile.m0 + r) * N + c) =
-            f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int r = tile.m0 + i / 64, c = tile.n0 + (i % 64) * 4;
+      if (c >= N) continue;
+      float* dst = kPairs ? (r & 1 ? ep.c_odd : Cg) + static_cast<int64_t>(r >> 1) * N
+                          : Cg + static_cast<int64_t>(r) * N;
+      *reinterpret_cast<f32x4*>(dst + c) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     return;
   }
-  const EpiArgs ep{};
   OpArgs oa{};
   oa.r0 = r0;
   oa.rend = r1;
@@ -1526,46 +1542,48 @@ __global__ __launch_bounds__(kThreads) void wgrad_bf16_kernel(
   oa.a_cols = M;
   oa.zero = zero;
   if (tile.cls == 0)
-    gemm_tile<256, 2, 2, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+    gemm_tile<256, 2, 2, 256, kRingA, kRingB, false, float, kPairs ? kEpiRowPairs : kEpiNone, kOpRowsT,
+              kOpRowsT>(
         A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
   else if (tile.cls == 1)
-    gemm_tile<128, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+    gemm_tile<128, 1, 4, 256, kRingA, kRingB, false, float, kPairs ? kEpiRowPairs : kEpiNone, kOpRowsT,
+              kOpRowsT>(
         A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
   else
-    gemm_tile<64, 1, 4, 256, kRingA, kRingB, false, float, kEpiNone, kOpRowsT, kOpRowsT>(
+    gemm_tile<64, 1, 4, 256, kRingA, kRingB, false, float, kPairs ? kEpiRowPairs : kEpiNone, kOpRowsT,
+              kOpRowsT>(
         A, nullptr, 1, B, nullptr, 0, 0, N, tile, 0, nk, smem, Cg, nullptr, ep, oa);
 }
 
 hipError_t wgrad_bf16(const uint16_t* A, int lda, const uint16_t* B, int ldb, int M, int N,
-                      const int32_t* off, int G, const uint16_t* zero, float* C,
+                      const int32_t* off, int G, const uint16_t* zero, float* C, float* C_odd,
                       hipStream_t stream) {
   const int mtn = (M + kTileM - 1) / kTileM, ntn = (N + 255) / 256;
   const int64_t total = static_cast<int64_t>(G) * mtn * ntn;
-  auto kern = wgrad_bf16_kernel;
+  auto kern = C_odd ? wgrad_bf16_kernel<true> : wgrad_bf16_kernel<false>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<static_cast<unsigned>((total + 7) & ~7), kThreads, kGemmLds, stream>>>(
-      A, lda, B, ldb, M, N, off, G, mtn, ntn, zero, C);
+      A, lda, B, ldb, M, N, off, G, mtn, ntn, zero, C, C_odd);
   return hipGetLastError();
 }
 
-// Input-gradient GEMM: C[r] = A[r] . W[g]^(K-major) for the rows of each group,
-// W's slab [K][N] per group (slices >= nk1 from B1), persistent like the
-// forward's down projection (split-K of the last round when skw is given).
-template <int kEpi, typename OutT>
+// Input-gradient GEMM: C[r] = A[r] . W[g] for the rows of each group, W read
+// K-major (kBM = kOpSlabT: one slab [K][N] per group; kOpSlabI: the K rows
+// alternate between B0's and B1's slabs), persistent like the forward's down
+// projection (split-K of the last round when skw is given).
+template <int kEpi, int kBM, typename OutT>
 hipError_t dgrad_bf16(const uint16_t* A, int K, int N, const uint16_t* B0, const uint16_t* B1,
-                      int64_t b_stride, int nk1, const int32_t* off, int G, int32_t* tt,
-                      OutT* C, float* skw, const EpiArgs& ep, hipStream_t stream) {
+                      int64_t b_stride, const int32_t* off, int G, int32_t* tt, OutT* C,
+                      float* skw, const EpiArgs& ep, hipStream_t stream) {
   const int ntn = (N + 255) / 256;
   const int ncu = compute_units();
   tile_table_kernel<<<1, 1024, 0, stream>>>(off, G, kTileM, ntn, false, tt, tt, ncu, K / kBK,
                                             skw != nullptr);
-  OpArgs oa{};
-  oa.nk1 = nk1;
-  auto kern = gemm_bf16_kernel<false, OutT, kEpi, kOpSlabT>;
+  auto kern = gemm_bf16_kernel<false, OutT, kEpi, kBM>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
   kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(A, nullptr, 1, B0, B1, b_stride, K,
                                                               N, off, tt, G, ntn, C, skw, ncu, ep,
-                                                              oa);
+                                                              OpArgs{});
   if (skw)
     sk_reduce_kernel<OutT><<<kSkUnits * 32, 256, 0, stream>>>(skw, off, tt, G, ntn, K, N, ncu, C);
   return hipGetLastError();
@@ -1624,22 +1642,23 @@ hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
     EpiArgs ep{};
     ep.uv = const_cast<uint16_t*>(static_cast<const uint16_t*>(b.uv));
     ep.dab = b.dab;
-    e = dgrad_bf16<kEpiSiluBwd, uint16_t>(dout, d, h, wd, wd, static_cast<int64_t>(d) * h,
-                                          d / kBK, b.group_offset, G, b.mstart, nullptr, nullptr,
-                                          ep, stream);
+    e = dgrad_bf16<kEpiSiluBwd, kOpSlabT, uint16_t>(dout, d, h, wd, wd,
+                                                    static_cast<int64_t>(d) * h, b.group_offset,
+                                                    G, b.mstart, nullptr, nullptr, ep, stream);
     if (e != hipSuccess) return e;
-    // dgrad 2: da = du W_gate + dv W_up (K = 2h over the two K-major slabs)
-    e = dgrad_bf16<kEpiNone, float>(b.dab, 2 * h, d, wg, wu, static_cast<int64_t>(h) * d, h / kBK,
-                                    b.group_offset, G, b.mstart, b.da, b.sk_ws, EpiArgs{},
-                                    stream);
+    // dgrad 2: da = du W_gate + dv W_up, K = 2h over the interleaved (du, dv)
+    // columns and the two K-major slabs
+    e = dgrad_bf16<kEpiNone, kOpSlabI, float>(b.dab, 2 * h, d, wg, wu,
+                                              static_cast<int64_t>(h) * d, b.group_offset, G,
+                                              b.mstart, b.da, b.sk_ws, EpiArgs{}, stream);
     if (e != hipSuccess) return e;
   }
-  // weight gradients
-  e = wgrad_bf16(dout, d, hid, h, d, h, b.group_offset, G, b.zero, b.dw_down, stream);
-  if (e == hipSuccess) e = wgrad_bf16(b.dab, 2 * h, xs, d, h, d, b.group_offset, G, b.zero,
-                                      b.dw_gate, stream);
-  if (e == hipSuccess) e = wgrad_bf16(b.dab + h, 2 * h, xs, d, h, d, b.group_offset, G, b.zero,
-                                      b.dw_up, stream);
+  // weight gradients: dW_down, then dW_gate and dW_up as one GEMM over the
+  // interleaved (du, dv) columns (even output rows to dW_gate, odd to dW_up)
+  e = wgrad_bf16(dout, d, hid, h, d, h, b.group_offset, G, b.zero, b.dw_down, nullptr, stream);
+  if (e == hipSuccess)
+    e = wgrad_bf16(b.dab, 2 * h, xs, d, 2 * h, d, b.group_offset, G, b.zero, b.dw_gate, b.dw_up,
+                   stream);
   return e;
 }
 
