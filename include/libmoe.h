@@ -82,6 +82,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 /* moe_route flag: skip the router GEMM and read the logits the caller put in
  * `logits` (used to test selection on identical logits). */
 #define MOE_ROUTE_LOGITS_IN 1u
+/* moe_route flag: the selection key is the routing probability plus the
+ * selection bias, key = softmax(logits[t,:])[e] + select_bias[e], as Zen-Max
+ * writes it (section "Auxiliary-Loss-Free Load Balancing", s_ij =
+ * softmax(x_i W_g)_j + b_j), instead of the default logit plus bias. */
+#define MOE_ROUTE_BIAS_ON_PROBS 2u
 
 /* Limits of these kernels (MOE_EUNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 256
@@ -126,7 +131,11 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E);
  *   moe_balance_stats see it).
  * select_bias [E] fp32 or NULL: selection key only.
  * flags: MOE_ROUTE_LOGITS_IN reads `logits` instead of computing them
- *   (x and w_router may then be NULL; logit_bias is ignored).
+ *   (x and w_router may then be NULL; logit_bias is ignored);
+ *   MOE_ROUTE_BIAS_ON_PROBS selects on key = p[t,e] + select_bias[e] with
+ *   p[t,:] = softmax(logits[t,:]) over all E experts (fp32: p_e =
+ *   exp(l_e - m) / sum, m the row maximum; then one fp32 add), same ties
+ *   and order rule; the gates are unchanged.
  * logits [T,E] fp32 out (in with LOGITS_IN); topk_idx [T,k] int32 out;
  * topk_gate [T,k] fp32 out.
  * Limits: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK; for bf16

@@ -31,6 +31,7 @@ from .moe_oracle import (  # noqa: F401
     router_logits,
     router_z_loss,
     selection_keys,
+    selection_keys_on_probs,
     silu,
     swiglu,
     top_k,

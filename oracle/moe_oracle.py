@@ -58,6 +58,20 @@ def router_logits(x, w_router, logit_bias=None):
     return l
 
 
+def selection_keys_on_probs(logits, select_bias=None):
+    """The selection key as [Max] "Auxiliary-Loss-Free Load Balancing" writes
+    it: s_j = softmax(x W_g)_j + b_j, the routing probability over all experts
+    plus the per-expert bias.  The probabilities are computed in float64,
+    rounded to float32, and the bias is added in float32 (the precision of
+    the decision, as for ``selection_keys``)."""
+    l = _f64(logits)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    if select_bias is None:
+        return p
+    return (p + np.asarray(select_bias, dtype=np.float32)[None, :]).astype(np.float32)
+
+
 def selection_keys(logits, select_bias=None):
     """The value that decides expert membership.
 

@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("LIBMOE_PATH", os.path.join(_HERE, "lib", "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
+MOE_ROUTE_BIAS_ON_PROBS = 2
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
 
@@ -136,9 +137,10 @@ def moe_route_workspace(T, d, E, k, dt) -> int:
 
 
 def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None, topk_idx=None,
-              topk_gate=None, logits_in=False, ws=None, stream=None):
+              topk_gate=None, logits_in=False, bias_on_probs=False, ws=None, stream=None):
     """Router logits, top-k experts and renormalised gates.  With
-    ``logits_in`` the given ``logits`` [T, E] are used instead of x W_r^T."""
+    ``logits_in`` the given ``logits`` [T, E] are used instead of x W_r^T;
+    ``bias_on_probs`` selects on softmax probability + selection bias."""
     if logits_in:
         T, E = logits.shape
         dt, d = MOE_F32, 0
@@ -159,7 +161,9 @@ def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None,
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _contig(x, w_router, logit_bias, select_bias, logits, topk_idx, topk_gate, ws)
     _check(_L.moe_route(_ptr(x), _ptr(w_router), dt, T, d, E, k, _ptr(logit_bias),
-                        _ptr(select_bias), MOE_ROUTE_LOGITS_IN if logits_in else 0,
+                        _ptr(select_bias),
+                        (MOE_ROUTE_LOGITS_IN if logits_in else 0) |
+                        (MOE_ROUTE_BIAS_ON_PROBS if bias_on_probs else 0),
                         _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), ws.numel(),
                         _stream(stream)))
     return logits, topk_idx, topk_gate

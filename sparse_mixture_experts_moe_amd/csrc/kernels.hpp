@@ -20,8 +20,8 @@ size_t route_lds_bytes(int E, int k);
 size_t route_workspace_bytes(int64_t T, int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
                         const float* logit_bias, const float* select_bias, bool logits_in,
-                        float* logits, int32_t* topk_idx, float* topk_gate, void* ws,
-                        hipStream_t stream);
+                        bool prob_keys, float* logits, int32_t* topk_idx, float* topk_gate,
+                        void* ws, hipStream_t stream);
 
 // permute.hip
 int64_t permute_chunks(int64_t R);

@@ -168,7 +168,9 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
                        unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
                        void* ws, size_t ws_bytes, void* stream) {
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
-  if (flags & ~MOE_ROUTE_LOGITS_IN) return fail(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
+  const bool prob_keys = (flags & MOE_ROUTE_BIAS_ON_PROBS) != 0;
+  if (flags & ~(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_BIAS_ON_PROBS))
+    return fail(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
   if (T < 0) return fail(MOE_EINVAL, "moe_route: T < 0");
   if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_route: need 1 <= k <= E");
   if (!valid_dtype(dt)) return fail(MOE_EINVAL, "moe_route: bad dtype %d", dt);
@@ -185,8 +187,8 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
   if (ws_bytes < need || (need && !ws))
     return fail(MOE_EWORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(moe::launch_route(x, w_router, dt == MOE_BF16, T, d, E, k, logit_bias,
-                                      select_bias, logits_in, logits, topk_idx, topk_gate, ws,
-                                      as_stream(stream)),
+                                      select_bias, logits_in, prob_keys, logits, topk_idx,
+                                      topk_gate, ws, as_stream(stream)),
                     "moe_route");
 }
 

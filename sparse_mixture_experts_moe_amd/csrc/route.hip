@@ -1,5 +1,6 @@
 // Router: logits = x . w_router^T (+ logit_bias), top-k selection on
-// key = logit + select_bias (ties to the lower expert index), and gates that
+// key = logit + select_bias (ties to the lower expert index; or, on request,
+// key = softmax probability + select_bias), and gates that
 // renormalise the softmax over the selected logits.
 //
 // Sources: "Every parameter, every token", section "The gating network";
@@ -170,7 +171,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // mode: 0 = logits are in `logits` (caller's or written by the logits kernel
 // with KS = 1); 1 = sum KS partial tiles from `part` and add logit_bias;
 // 2 = fp32 inputs, compute with FMA.
-template <int KK>  // keys per lane: experts q, q+8, ... below 8 KK >= E
+// kProb: the selection key is the softmax probability plus the selection
+// bias (instead of the logit plus the bias).
+template <int KK, bool kProb>  // keys per lane: experts q, q+8, ... below 8 KK >= E
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     int mode, const float* __restrict__ xf, const float* __restrict__ wf,
     const float* __restrict__ part, int KS, int64_t T, int d, int E, int k,
@@ -283,12 +286,41 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   const float* row = lg + tt * ldl;
   constexpr int kKeys = KK;
   uint64_t code[kKeys];  // 0: no candidate
+  if constexpr (kProb) {
+    // p_e = exp(l_e - m) / sum_e' exp(l_e' - m) over all experts (the eight
+    // lanes' partial sums added by a fixed butterfly), key = p_e + b_e
+    float ex[kKeys];
+    float m = -__builtin_inff();
 #pragma unroll
-  for (int u = 0; u < kKeys; ++u) {
-    const int e = q + u * kLanesPerTok;
-    code[u] = (active && e < E)
-                  ? rank_code(select_bias ? __fadd_rn(row[e], sb[e]) : row[e], e)
-                  : uint64_t{0};
+    for (int u = 0; u < kKeys; ++u) {
+      const int e = q + u * kLanesPerTok;
+      ex[u] = (active && e < E) ? row[e] : -__builtin_inff();
+      m = fmaxf(m, ex[u]);
+    }
+    m = max8_f32(m);
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kKeys; ++u) {
+      const int e = q + u * kLanesPerTok;
+      ex[u] = (active && e < E) ? expf(ex[u] - m) : 0.0f;
+      s += ex[u];
+    }
+    s = sum8_f32(s);
+#pragma unroll
+    for (int u = 0; u < kKeys; ++u) {
+      const int e = q + u * kLanesPerTok;
+      const float pe = ex[u] / s;
+      code[u] = (active && e < E) ? rank_code(select_bias ? __fadd_rn(pe, sb[e]) : pe, e)
+                                  : uint64_t{0};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kKeys; ++u) {
+      const int e = q + u * kLanesPerTok;
+      code[u] = (active && e < E)
+                    ? rank_code(select_bias ? __fadd_rn(row[e], sb[e]) : row[e], e)
+                    : uint64_t{0};
+    }
   }
   // pass j: the first candidate ranking after pass j-1's winner (branch-free)
   uint64_t prev = ~uint64_t{0};
@@ -348,15 +380,20 @@ size_t route_workspace_bytes(int64_t T, int d, int E, bool bf16) {
 
 hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
                         const float* logit_bias, const float* select_bias, bool logits_in,
-                        float* logits, int32_t* topk_idx, float* topk_gate, void* ws,
-                        hipStream_t stream) {
+                        bool prob_keys, float* logits, int32_t* topk_idx, float* topk_gate,
+                        void* ws, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
   const size_t lds = route_lds_bytes(E, k);
   // the logits tile can exceed the default 64 KB dynamic LDS limit
-  const void* sel_fn = E <= 32 ? reinterpret_cast<const void*>(route_select_kernel<4>)
-                       : E <= 64 ? reinterpret_cast<const void*>(route_select_kernel<8>)
-                       : E <= 128 ? reinterpret_cast<const void*>(route_select_kernel<16>)
-                                  : reinterpret_cast<const void*>(route_select_kernel<32>);
+  const void* sel_fn =
+      prob_keys ? (E <= 32   ? reinterpret_cast<const void*>(route_select_kernel<4, true>)
+                   : E <= 64  ? reinterpret_cast<const void*>(route_select_kernel<8, true>)
+                   : E <= 128 ? reinterpret_cast<const void*>(route_select_kernel<16, true>)
+                              : reinterpret_cast<const void*>(route_select_kernel<32, true>))
+                : (E <= 32   ? reinterpret_cast<const void*>(route_select_kernel<4, false>)
+                   : E <= 64  ? reinterpret_cast<const void*>(route_select_kernel<8, false>)
+                   : E <= 128 ? reinterpret_cast<const void*>(route_select_kernel<16, false>)
+                              : reinterpret_cast<const void*>(route_select_kernel<32, false>));
   ensure_dynamic_lds(sel_fn, static_cast<int>(lds));
   int mode = 0, ks = 1;
   if (!logits_in && bf16) {
@@ -373,15 +410,22 @@ hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int 
   } else if (!logits_in) {
     mode = 2;
   }
-#define MOE_SELECT(KK)                                                                    \
-  route_select_kernel<KK><<<blocks, kThreads, lds, stream>>>(                              \
+#define MOE_SELECT(KK, P)                                                                 \
+  route_select_kernel<KK, P><<<blocks, kThreads, lds, stream>>>(                           \
       mode, static_cast<const float*>(x), static_cast<const float*>(w),                     \
       static_cast<const float*>(ws), ks, T, d, E, k, logit_bias, select_bias, logits,       \
       topk_idx, topk_gate)
-  if (E <= 32) MOE_SELECT(4);
-  else if (E <= 64) MOE_SELECT(8);
-  else if (E <= 128) MOE_SELECT(16);
-  else MOE_SELECT(32);
+#define MOE_SELECT_E(P)                 \
+  if (E <= 32) MOE_SELECT(4, P);        \
+  else if (E <= 64) MOE_SELECT(8, P);   \
+  else if (E <= 128) MOE_SELECT(16, P); \
+  else MOE_SELECT(32, P)
+  if (prob_keys) {
+    MOE_SELECT_E(true);
+  } else {
+    MOE_SELECT_E(false);
+  }
+#undef MOE_SELECT_E
 #undef MOE_SELECT
   return hipGetLastError();
 }

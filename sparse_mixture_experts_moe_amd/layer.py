@@ -27,14 +27,15 @@ from . import _lib
 class MoELayer:
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
                  select_bias=None, capacity=-1, alpha=0.01, gather="fused",
-                 overlap_shared=True, balance=None):
+                 overlap_shared=True, balance=None, bias_on_probs=False):
         """Weights are device tensors: w_router [E, d]; w_gate, w_up [E, h, d];
         w_down [E, d, h]; ``shared`` is None or (gate [Hs, d], up [Hs, d],
         down [d, Hs]) with the shared experts concatenated along the hidden
         axis.  ``capacity`` < 0 means unlimited.  ``gather`` is "fused" (the
         first expert GEMM reads token rows through the permutation) or "copy"
         (moe_permute writes an expert-ordered copy of x first).  ``overlap_shared``
-        runs the shared experts on a second stream.
+        runs the shared experts on a second stream.  ``bias_on_probs`` adds
+        the selection bias to the routing probability instead of the logit.
 
         ``balance`` turns on the per-step load-balancing updates that
         ``update_balance()`` applies after a step: a dict with ``bias_step``
@@ -60,6 +61,7 @@ class MoELayer:
         self.overlap_shared = overlap_shared
         self._bufs = {}
         self._side = {}
+        self.bias_on_probs = bias_on_probs
         self.balance = dict(balance) if balance else None
         self.load_ema = None
         self.expert_capacity = None
@@ -194,7 +196,7 @@ class MoELayer:
             shared_done.record(side)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
-                       ws=b["route_ws"], stream=stream)
+                       bias_on_probs=self.bias_on_probs, ws=b["route_ws"], stream=stream)
         mark("route")
         if self.balance and "gamma" in self.balance:
             if self.expert_capacity is None or self._last_T != T:

@@ -308,3 +308,44 @@ def test_shared_overlap_matches_serial():
         torch.cuda.synchronize()
         outs.append(host(res["out"]).copy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("E,k,scale", [(8, 2, 1.0), (64, 6, 3.0), (256, 8, 0.3), (5, 5, 1.0)])
+def test_route_bias_on_probs(E, k, scale):
+    """Selection on softmax probability + selection bias (Zen-Max,
+    "Auxiliary-Loss-Free Load Balancing").  The GPU's fp32 probabilities may
+    differ from the oracle's correctly rounded ones in the last bits, so the
+    selection is checked for validity against the oracle's keys: every chosen
+    expert's key is at least every unchosen one's (to 4e-7 of the largest key)
+    and slots go in descending key order; where the oracle's k-th and
+    (k+1)-th keys are more than that apart, the chosen set is exactly the
+    oracle's.  Gates are the renormalised softmax of the chosen logits."""
+    from sparse_mixture_experts_moe_amd import _lib as L
+    _say(f"[case] bias on probabilities E={E} k={k}")
+    rng = np.random.default_rng(E + k)
+    T = 777
+    logits = (rng.standard_normal((T, E)) * scale).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.05).astype(np.float32)
+    lg = torch.from_numpy(logits).cuda()
+    _, idx, gate = L.moe_route(None, None, k, None, torch.from_numpy(bias).cuda(), logits=lg,
+                               logits_in=True, bias_on_probs=True)
+    torch.cuda.synchronize()
+    idx = host(idx).astype(np.int64)
+    keys = oracle.selection_keys_on_probs(logits, bias).astype(np.float64)
+    tol = 4e-7 * float(np.max(np.abs(keys)))
+    exact = 0
+    for t in range(T):
+        chosen = keys[t, idx[t]]
+        others = np.delete(keys[t], idx[t])
+        assert len(set(idx[t].tolist())) == k
+        if others.size:
+            assert chosen.min() >= others.max() - tol, t
+        assert np.all(np.diff(chosen) <= tol), t
+        ref = oracle.top_k(keys[t:t + 1], k)[0]
+        srt = np.sort(keys[t])[::-1]
+        if k == E or srt[k - 1] - srt[k] > tol:
+            assert set(ref.tolist()) == set(idx[t].tolist()), t
+            exact += 1
+    assert exact >= T * 0.9
+    g = oracle.gates(logits, idx)
+    assert float(np.max(np.abs(host(gate) - g))) <= 1e-6
