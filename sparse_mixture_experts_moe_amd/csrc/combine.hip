@@ -79,17 +79,23 @@ struct Vec8<float> {
   static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 };
 
-template <typename YT, typename OT>
-__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
-                                                      const int32_t* __restrict__ pair_row,
-                                                      const float* __restrict__ gate, int k,
-                                                      int d, const YT* __restrict__ shared,
-                                                      OT* __restrict__ out) {
+// Workgroup (t, y) covers the whole row of token t (gridDim.y = 1) or its
+// columns [8 BLOCK y, 8 BLOCK (y + 1)) (gridDim.y column chunks, so that a few
+// tokens still fill the device).
+template <typename YT, typename OT, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y,
+                                                        const int32_t* __restrict__ pair_row,
+                                                        const float* __restrict__ gate, int k,
+                                                        int d, const YT* __restrict__ shared,
+                                                        OT* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int32_t* pr = pair_row + t * k;
   const float* g = gate ? gate + t * k : nullptr;  // NULL: every gate is 1
   if ((d & 7) == 0) {
-    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    const int cw = gridDim.y == 1 ? d : BLOCK * 8;  // columns of this workgroup
+    const int c0 = static_cast<int>(blockIdx.y) * cw;
+    const int cend = min(d, c0 + cw);
+    for (int c = c0 + threadIdx.x * 8; c < cend; c += BLOCK * 8) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       typename Vec8<YT>::Raw sh{};
       if (shared) sh = Vec8<YT>::load_raw(shared + t * d + c);
@@ -120,7 +126,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
       Vec8<OT>::store(out + t * d + c, acc);
     }
   } else {
-    for (int c = threadIdx.x; c < d; c += 256) {
+    if (blockIdx.y != 0) return;
+    for (int c = threadIdx.x; c < d; c += BLOCK) {
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) {
         const int row = pr[j];
@@ -133,12 +140,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   }
 }
 
+// Enough workgroups for the device: whole rows per 256-thread workgroup when
+// there are many tokens; for a few tokens (decode), 64-thread workgroups on
+// 512-column chunks of a row.
 template <typename YT, typename OT>
 hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_t T, int k, int d,
                         const void* shared, void* out, hipStream_t stream) {
-  combine_kernel<YT, OT><<<static_cast<unsigned>(T), 256, 0, stream>>>(
-      static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
-      static_cast<OT*>(out));
+  if (T >= 1024 || (d & 7) != 0) {
+    combine_kernel<YT, OT, 256><<<dim3(static_cast<unsigned>(T), 1), 256, 0, stream>>>(
+        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
+        static_cast<OT*>(out));
+  } else {
+    const unsigned chunks = static_cast<unsigned>((d + 511) / 512);
+    combine_kernel<YT, OT, 64><<<dim3(static_cast<unsigned>(T), chunks), 64, 0, stream>>>(
+        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
+        static_cast<OT*>(out));
+  }
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@ count and reused afterwards, so repeated calls allocate nothing.
 
 The shared experts depend on x alone, so by default they run on a second
 stream (default priority) from the start of the call, overlapping the routing
-and the routed experts; the combine waits for them.
+and the routed experts; the balance statistics follow them there once the
+routing is done, and the combine waits for both.
 
 The layer output excludes the residual ("Every parameter, every token",
 section "The gating network": the weighted sum is added back to the residual
@@ -155,6 +156,10 @@ class MoELayer:
                 dtype=torch.uint8, device=dev)
         return b
 
+    def _stats(self, b, k, stream):
+        _lib.moe_balance_stats(b["logits"], b["expert_count"], k, self.alpha, f=b["f"], P=b["P"],
+                               loss=b["loss"], zloss=b["zloss"], ws=b["stats_ws"], stream=stream)
+
     def _shared_forward(self, x, b, train, stream):
         sg, su, sd = self.shared
         T = x.shape[0]
@@ -192,8 +197,6 @@ class MoELayer:
             x_ready.record(main)
             side.wait_event(x_ready)
             shared_y = self._shared_forward(x, b, train, side)
-            shared_done = torch.cuda.Event()
-            shared_done.record(side)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
                        bias_on_probs=self.bias_on_probs, ws=b["route_ws"], stream=stream)
@@ -218,6 +221,15 @@ class MoELayer:
         self._last_T = T
         self._last_counts = b["expert_count"]
         mark("permute")
+        if shared_y is not None:
+            # the balance statistics need only the logits and the counts: on
+            # the side stream, after the shared experts, beside the routed GEMMs
+            routed = torch.cuda.Event()
+            routed.record(main)
+            side.wait_event(routed)
+            self._stats(b, k, side)
+            shared_done = torch.cuda.Event()
+            shared_done.record(side)
         if self.gather == "copy":
             a, a_rows = b["x_perm"], None
         else:
@@ -242,9 +254,9 @@ class MoELayer:
         _lib.moe_combine(b["y_perm"], b["pair_row"], b["topk_gate"], shared_y, out=b["out"],
                          stream=stream)
         mark("combine")
-        _lib.moe_balance_stats(b["logits"], b["expert_count"], k, self.alpha, f=b["f"], P=b["P"],
-                               loss=b["loss"], zloss=b["zloss"], ws=b["stats_ws"], stream=stream)
-        mark("stats")
+        if shared_done is None:
+            self._stats(b, k, stream)
+            mark("stats")
         return b
 
     __call__ = forward

@@ -295,7 +295,8 @@ def test_layer_full_size(name):
 
 
 def test_shared_overlap_matches_serial():
-    """The shared experts on a second stream give the same bits as in line."""
+    """The shared experts (and then the balance statistics) on a second stream
+    give the same bits as in line."""
     inp = generate(SMALL["finegrained_small"])
     _say("[case] shared experts overlapped vs in line")
     layer = build_layer(inp)
@@ -306,8 +307,10 @@ def test_shared_overlap_matches_serial():
         for _ in range(3):  # back-to-back calls reuse the buffers
             res = layer(x)
         torch.cuda.synchronize()
-        outs.append(host(res["out"]).copy())
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+        outs.append({key: host(res[key]).copy() for key in ("out", "f", "P", "loss", "zloss")})
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+        assert np.array_equal(outs[1][key], outs[2][key]), key
 
 
 @pytest.mark.parametrize("E,k,scale", [(8, 2, 1.0), (64, 6, 3.0), (256, 8, 0.3), (5, 5, 1.0)])
