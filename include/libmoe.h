@@ -355,8 +355,8 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
 /* moe_expert_gate_up_train: moe_expert_gate_up that also keeps the
  * pre-activations for the backward pass, interleaved per hidden unit:
  *   uv[r, 2c] = a_r . w_gate[g][c],  uv[r, 2c + 1] = a_r . w_up[g][c]
- * uv [max_rows, 2h] bf16.  bf16 only (MOE_EUNSUPPORTED otherwise); runs the
- * tiled kernel at every row count.  Workspace: moe_expert_group_workspace(G). */
+ * uv [max_rows, 2h] in dtype dt.  The bf16 path runs the tiled kernel at
+ * every row count.  Workspace: moe_expert_group_workspace(G). */
 moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
                                       const int32_t* group_offset, int64_t max_rows,
                                       const int32_t* a_rows, int a_rows_div, const void* w_gate,
@@ -380,7 +380,8 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
  * axis directly (no transposed copies).  Routed experts: a = x, a_rows =
  * row_pair, a_rows_div = k, dout from moe_combine_backward.  Shared experts:
  * a = x, a_rows = NULL, dout = dy, G = 1 (concatenated hidden axis).
- * dt must be bf16; additionally 4 d h < 2^32.  dout, uv, hid in dt with rows
+ * bf16 additionally needs 4 d h < 2^32 (fp32 runs plain FMA tiles).  dout,
+ * uv, hid in dt with rows
  * in group order ([max_rows, *]); da [max_rows, d] fp32 (rows past
  * group_offset[G] untouched).
  * Workspace: moe_expert_swiglu_backward_workspace(max_rows, d, h, G, dt,

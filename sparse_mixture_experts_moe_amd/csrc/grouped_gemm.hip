@@ -1277,7 +1277,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ a_rows, int a_div,
     const float* __restrict__ B0, const float* __restrict__ B1, int64_t b_stride, int K, int N,
     const int32_t* __restrict__ off, const int32_t* __restrict__ mstart, int G, int ntn,
-    void* __restrict__ Cv, bool out_bf16) {
+    void* __restrict__ Cv, bool out_bf16, float* __restrict__ uv) {
   Tile tile;
   if (!decode_tile(off, mstart, G, ntn, kF32Tile, kF32Tile, tile)) return;
   __shared__ float As[kF32K][kF32Tile + 1];
@@ -1331,6 +1331,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
       if (col >= N) continue;
       const float v = kFused ? silu_f32(cg[i][j]) * cu[i][j] : cg[i][j];
       const int64_t o = static_cast<int64_t>(row) * N + col;
+      if (kFused && uv) {  // pre-activations for the backward pass, (u, v) pairs
+        uv[2 * o] = cg[i][j];
+        uv[2 * o + 1] = cu[i][j];
+      }
       if (out_bf16) static_cast<uint16_t*>(Cv)[o] = f32_to_bf16_bits(v);
       else static_cast<float*>(Cv)[o] = v;
     }
@@ -1390,7 +1394,7 @@ hipError_t gate_up_f32(const SwigluArgs& s, hipStream_t stream) {
   gemm_f32_kernel<true><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.a), s.a_rows, s.a_div, static_cast<const float*>(s.w_gate),
       static_cast<const float*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h, s.group_offset,
-      s.mstart, s.G, ntn, s.hid, false);
+      s.mstart, s.G, ntn, s.hid, false, static_cast<float*>(s.uv));
   return hipGetLastError();
 }
 
@@ -1402,7 +1406,7 @@ hipError_t down_f32(const SwigluArgs& s, hipStream_t stream) {
   gemm_f32_kernel<false><<<static_cast<unsigned>(round_up(mt_ub * ntn, 8)), kThreads, 0, stream>>>(
       static_cast<const float*>(s.hid), nullptr, 1, static_cast<const float*>(s.w_down), nullptr,
       static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn, s.y,
-      s.y_bf16);
+      s.y_bf16, nullptr);
   return hipGetLastError();
 }
 
@@ -1447,6 +1451,137 @@ hipError_t skinny_bf16(const SwigluArgs& s, int K, int N, const void* a, const i
                                                    N, static_cast<OutT*>(out));
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 backward GEMMs: 64 x 64 tiles of plain FMAs through LDS, K steps of 16.
+//   f32_dgrad_kernel: for the rows of each group, C[r, n] = sum_k A[r, k] B(k, n)
+//     with B read K-major, B(k, n) = B0[g][k][n] or, kInter, the rows
+//     alternating between B0[g][k / 2] (even k) and B1[g][k / 2] (odd k);
+//     kSilu: the SiLU-backward epilogue on the interleaved (u, v) -> (du, dv).
+//   f32_wgrad_kernel: for each group g, C_g[m, n] = sum over its rows r of
+//     A[r][m] B[row(r)][n], row(r) = b_rows[r] / b_div (or r); kPairs sends
+//     the even rows of C_g to C and the odd rows to C_odd.
+// ---------------------------------------------------------------------------
+template <bool kInter, bool kSilu>
+__global__ __launch_bounds__(kThreads) void f32_dgrad_kernel(
+    const float* __restrict__ A, int K, const float* __restrict__ B0, const float* __restrict__ B1,
+    int64_t b_stride, int N, const int32_t* __restrict__ off, const int32_t* __restrict__ mstart,
+    int G, int ntn, float* __restrict__ C, const float* __restrict__ uv, float* __restrict__ dab) {
+  Tile tile;
+  if (!decode_tile(off, mstart, G, ntn, kF32Tile, kF32Tile, tile)) return;
+  __shared__ float As[kF32K][kF32Tile + 1];
+  __shared__ float Bs[kF32K][kF32Tile + 1];
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  const float* b0 = B0 + tile.g * b_stride;
+  const float* b1 = kInter ? B1 + tile.g * b_stride : b0;
+  for (int k0 = 0; k0 < K; k0 += kF32K) {
+    for (int i = tid; i < kF32K * kF32Tile; i += kThreads) {
+      const int r = i / kF32K, kk = i % kF32K;
+      const int kg = k0 + kk;
+      int row = tile.m0 + r;
+      row = row < tile.row_end ? row : tile.row_end - 1;
+      As[kk][r] = kg < K ? A[static_cast<int64_t>(row) * K + kg] : 0.0f;
+      const int kb = i / kF32Tile, c = i % kF32Tile;  // B: consecutive threads along n
+      const int kgb = k0 + kb;
+      int n = tile.n0 + c;
+      n = n < N ? n : N - 1;
+      float bv = 0.0f;
+      if (kgb < K) {
+        if constexpr (kInter) bv = ((kgb & 1) ? b1 : b0)[static_cast<int64_t>(kgb >> 1) * N + n];
+        else bv = b0[static_cast<int64_t>(kgb) * N + n];
+      }
+      Bs[kb][c] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kF32K; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile.m0 + ty * 4 + i;
+    if (row >= tile.row_end) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = tile.n0 + tx * 4 + j;
+      if (col >= N) continue;
+      const int64_t o = static_cast<int64_t>(row) * N + col;
+      if constexpr (kSilu) {
+        const float u = uv[2 * o], v = uv[2 * o + 1];
+        const float sg = 1.0f / (1.0f + expf(-u));
+        dab[2 * o] = acc[i][j] * v * (sg * (1.0f + u * (1.0f - sg)));
+        dab[2 * o + 1] = acc[i][j] * (u * sg);
+      } else {
+        C[o] = acc[i][j];
+      }
+    }
+  }
+}
+
+template <bool kPairs>
+__global__ __launch_bounds__(kThreads) void f32_wgrad_kernel(
+    const float* __restrict__ A, int lda, const float* __restrict__ B, int ldb,
+    const int32_t* __restrict__ b_rows, int b_div, int M, int N,
+    const int32_t* __restrict__ off, int mtn, int ntn, float* __restrict__ C,
+    float* __restrict__ C_odd) {
+  const int per = mtn * ntn;
+  const int g = blockIdx.x / per;
+  const int local = blockIdx.x - g * per;
+  const int m0 = (local / ntn) * kF32Tile, n0 = (local % ntn) * kF32Tile;
+  const int r0 = off[g], r1 = off[g + 1];
+  __shared__ float As[kF32K][kF32Tile + 1];
+  __shared__ float Bs[kF32K][kF32Tile + 1];
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  for (int k0 = r0; k0 < r1; k0 += kF32K) {
+    for (int i = tid; i < kF32K * kF32Tile; i += kThreads) {
+      const int kk = i / kF32Tile, c = i % kF32Tile;
+      const int r = k0 + kk;
+      const bool in = r < r1;
+      const int64_t br = in ? (b_rows ? b_rows[r] / b_div : r) : 0;
+      As[kk][c] = (in && m0 + c < M) ? A[static_cast<int64_t>(r) * lda + m0 + c] : 0.0f;
+      Bs[kk][c] = (in && n0 + c < N) ? B[br * ldb + n0 + c] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kF32K; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const int64_t gsz = static_cast<int64_t>(kPairs ? M / 2 : M) * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+    float* crow = kPairs ? (m & 1 ? C_odd : C) + g * gsz + static_cast<int64_t>(m >> 1) * N
+                         : C + g * gsz + static_cast<int64_t>(m) * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < N) crow[n] = acc[i][j];
+    }
+  }
 }
 
 // Groups averaging at most 64 rows stream weights through the skinny kernel;
@@ -1617,7 +1752,50 @@ hipError_t launch_down(const SwigluArgs& s, hipStream_t stream) {
   return s.y_bf16 ? down_bf16<uint16_t>(s, stream) : down_bf16<float>(s, stream);
 }
 
+hipError_t launch_expert_backward_f32(const SwigluBwdArgs& b, hipStream_t stream) {
+  const int d = b.d, h = b.h, G = b.G;
+  const auto* a = static_cast<const float*>(b.a);
+  const auto* dout = static_cast<const float*>(b.dout);
+  const auto* hid = static_cast<const float*>(b.hid);
+  const auto* uv = static_cast<const float*>(b.uv);
+  const auto* wg = static_cast<const float*>(b.w_gate);
+  const auto* wu = static_cast<const float*>(b.w_up);
+  const auto* wd = static_cast<const float*>(b.w_down);
+  float* dab = reinterpret_cast<float*>(b.dab);
+  if (b.max_rows > 0) {
+    const int64_t mt_ub = (b.max_rows + kF32Tile - 1) / kF32Tile + G;
+    tile_table_kernel<<<1, 1024, 0, stream>>>(b.group_offset, G, kF32Tile, 0, false, b.mstart,
+                                              nullptr, 0, 0, false);
+    // dgrad 1 (W_down read K-major) with the SiLU backward epilogue
+    const int ntn1 = (h + kF32Tile - 1) / kF32Tile;
+    f32_dgrad_kernel<false, true>
+        <<<static_cast<unsigned>(round_up(mt_ub * ntn1, 8)), kThreads, 0, stream>>>(
+            dout, d, wd, wd, static_cast<int64_t>(d) * h, h, b.group_offset, b.mstart, G, ntn1,
+            nullptr, uv, dab);
+    // dgrad 2 over the interleaved (du, dv) and the alternating gate/up rows
+    const int ntn2 = (d + kF32Tile - 1) / kF32Tile;
+    f32_dgrad_kernel<true, false>
+        <<<static_cast<unsigned>(round_up(mt_ub * ntn2, 8)), kThreads, 0, stream>>>(
+            dab, 2 * h, wg, wu, static_cast<int64_t>(h) * d, d, b.group_offset, b.mstart, G, ntn2,
+            b.da, nullptr, nullptr);
+  }
+  // weight gradients over each group's rows
+  {
+    const int mtn = (d + kF32Tile - 1) / kF32Tile, ntn = (h + kF32Tile - 1) / kF32Tile;
+    f32_wgrad_kernel<false><<<static_cast<unsigned>(G * mtn * ntn), kThreads, 0, stream>>>(
+        dout, d, hid, h, nullptr, 1, d, h, b.group_offset, mtn, ntn, b.dw_down, nullptr);
+  }
+  {
+    const int mtn = (2 * h + kF32Tile - 1) / kF32Tile, ntn = (d + kF32Tile - 1) / kF32Tile;
+    f32_wgrad_kernel<true><<<static_cast<unsigned>(G * mtn * ntn), kThreads, 0, stream>>>(
+        dab, 2 * h, a, d, b.a_rows, b.a_div, 2 * h, d, b.group_offset, mtn, ntn, b.dw_gate,
+        b.dw_up);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
+  if (!b.bf16) return launch_expert_backward_f32(b, stream);
   const int d = b.d, h = b.h, G = b.G;
   const auto* a = static_cast<const uint16_t*>(b.a);
   const auto* dout = static_cast<const uint16_t*>(b.dout);
@@ -1641,14 +1819,14 @@ hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
     // dgrad 1 (dhid = dout W_down, K-major W_down) with the SiLU backward epilogue
     EpiArgs ep{};
     ep.uv = const_cast<uint16_t*>(static_cast<const uint16_t*>(b.uv));
-    ep.dab = b.dab;
+    ep.dab = static_cast<uint16_t*>(b.dab);
     e = dgrad_bf16<kEpiSiluBwd, kOpSlabT, uint16_t>(dout, d, h, wd, wd,
                                                     static_cast<int64_t>(d) * h, b.group_offset,
                                                     G, b.mstart, nullptr, nullptr, ep, stream);
     if (e != hipSuccess) return e;
     // dgrad 2: da = du W_gate + dv W_up, K = 2h over the interleaved (du, dv)
     // columns and the two K-major slabs
-    e = dgrad_bf16<kEpiNone, kOpSlabI, float>(b.dab, 2 * h, d, wg, wu,
+    e = dgrad_bf16<kEpiNone, kOpSlabI, float>(static_cast<const uint16_t*>(b.dab), 2 * h, d, wg, wu,
                                               static_cast<int64_t>(h) * d, b.group_offset, G,
                                               b.mstart, b.da, b.sk_ws, EpiArgs{}, stream);
     if (e != hipSuccess) return e;
@@ -1657,7 +1835,7 @@ hipError_t launch_expert_backward(const SwigluBwdArgs& b, hipStream_t stream) {
   // interleaved (du, dv) columns (even output rows to dW_gate, odd to dW_up)
   e = wgrad_bf16(dout, d, hid, h, d, h, b.group_offset, G, b.zero, b.dw_down, nullptr, stream);
   if (e == hipSuccess)
-    e = wgrad_bf16(b.dab, 2 * h, xs, d, 2 * h, d, b.group_offset, G, b.zero, b.dw_gate, b.dw_up,
+    e = wgrad_bf16(static_cast<const uint16_t*>(b.dab), 2 * h, xs, d, 2 * h, d, b.group_offset, G, b.zero, b.dw_gate, b.dw_up,
                    stream);
   return e;
 }

@@ -47,7 +47,7 @@ struct SwigluArgs {
   void* y;
   bool y_bf16;
   void* hid;        // [max_rows, h] in the compute dtype
-  void* uv;         // bf16 gate/up only: [max_rows, 2h] pre-activations kept, or NULL
+  void* uv;         // gate/up only: [max_rows, 2h] pre-activations kept (interleaved), or NULL
   int32_t* mstart;  // workspace: tile table (tile_table_bytes(G))
   float* sk_ws;     // workspace: split-K partial tiles (down projection), or NULL
 };
@@ -62,6 +62,7 @@ hipError_t launch_down(const SwigluArgs& args, hipStream_t stream);
 // backward pass of the experts (bf16)
 struct SwigluBwdArgs {
   const void* a;
+  bool bf16;                // else fp32 (every tensor below in the same dtype)
   int d, h, G;
   const int32_t* group_offset;
   int64_t max_rows;
@@ -82,7 +83,7 @@ struct SwigluBwdArgs {
   float* sk_ws;             // split-K partial tiles
   uint16_t* zero;           // [max(d, 2h)] zeros
   uint16_t* xs;             // [max_rows, d] gathered rows (when a_rows is given)
-  uint16_t* dab;            // [max_rows, 2h]
+  void* dab;                // [max_rows, 2h] interleaved (du, dv)
 };
 hipError_t launch_expert_backward(const SwigluBwdArgs& args, hipStream_t stream);
 

@@ -428,7 +428,6 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
                                       size_t ws_bytes, void* stream) {
   moe_status_t st = check_experts("moe_expert_gate_up_train", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
-  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "moe_expert_gate_up_train: bf16 only");
   if (max_rows == 0) return ok();
   if (!a || !w_gate || !w_up || !hid || !uv)
     return fail(MOE_EINVAL, "moe_expert_gate_up_train: NULL pointer");
@@ -438,7 +437,7 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
                 moe_expert_group_workspace(G));
   moe::SwigluArgs s{};
   s.a = a;
-  s.bf16 = true;
+  s.bf16 = dt == MOE_BF16;
   s.d = d;
   s.h = h;
   s.G = G;
@@ -461,19 +460,19 @@ struct BwdLayout {
   size_t table, sk, zero, xs, dab, total;
 };
 
-BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G, bool gather) {
+BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G, bool gather, bool bf16) {
   BwdLayout L{};
   size_t o = 0;
   L.table = o;
   o += tile_table_bytes(G);
   L.sk = o;
-  o += moe::split_k_workspace_bytes();
+  if (bf16) o += moe::split_k_workspace_bytes();
   L.zero = o;
-  o += align256(2 * static_cast<size_t>(d > 2 * h ? d : 2 * h));
+  if (bf16) o += align256(2 * static_cast<size_t>(d > 2 * h ? d : 2 * h));
   L.xs = o;
-  if (gather) o += align256(2 * static_cast<size_t>(max_rows) * d);
+  if (bf16 && gather) o += align256(2 * static_cast<size_t>(max_rows) * d);
   L.dab = o;
-  o += align256(2 * static_cast<size_t>(max_rows) * 2 * h);
+  o += align256((bf16 ? 2 : 4) * static_cast<size_t>(max_rows) * 2 * h);
   L.total = o;
   return L;
 }
@@ -482,8 +481,8 @@ BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G, bool gather) {
 
 size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,
                                             int gather) {
-  if (max_rows < 0 || d < 1 || h < 1 || G < 1 || dt != MOE_BF16) return 0;
-  return bwd_layout(max_rows, d, h, G, gather != 0).total;
+  if (max_rows < 0 || d < 1 || h < 1 || G < 1 || !valid_dtype(dt)) return 0;
+  return bwd_layout(max_rows, d, h, G, gather != 0, dt == MOE_BF16).total;
 }
 
 moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
@@ -496,8 +495,7 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   const char* fn = "moe_expert_swiglu_backward";
   moe_status_t st = check_experts(fn, dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
-  if (dt != MOE_BF16) return fail(MOE_EUNSUPPORTED, "%s: bf16 only", fn);
-  if (static_cast<int64_t>(d) * h * 4 > static_cast<int64_t>(UINT32_MAX))
+  if (dt == MOE_BF16 && static_cast<int64_t>(d) * h * 4 > static_cast<int64_t>(UINT32_MAX))
     return fail(MOE_EUNSUPPORTED, "%s: 4 d h over 2^32", fn);
   if (static_cast<int64_t>(G) * ((d + 255) / 256) * ((h + 255) / 256) > INT32_MAX / 2)
     return fail(MOE_EUNSUPPORTED, "%s: too many weight-gradient tiles", fn);
@@ -506,12 +504,13 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   if (max_rows > 0 && (!a || !dout || !uv || !hid || !da))
     return fail(MOE_EINVAL, "%s: NULL pointer", fn);
   if (a_rows && a_rows_div < 1) return fail(MOE_EINVAL, "%s: a_rows_div < 1", fn);
-  const BwdLayout L = bwd_layout(max_rows, d, h, G, a_rows != nullptr);
+  const BwdLayout L = bwd_layout(max_rows, d, h, G, a_rows != nullptr, dt == MOE_BF16);
   if (ws_bytes < L.total || !ws)
     return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
   moe::SwigluBwdArgs b{};
   b.a = a;
+  b.bf16 = dt == MOE_BF16;
   b.d = d;
   b.h = h;
   b.G = G;
@@ -532,8 +531,8 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   b.mstart = reinterpret_cast<int32_t*>(w + L.table);
   b.sk_ws = reinterpret_cast<float*>(w + L.sk);
   b.zero = reinterpret_cast<uint16_t*>(w + L.zero);
-  b.xs = a_rows ? reinterpret_cast<uint16_t*>(w + L.xs) : nullptr;
-  b.dab = reinterpret_cast<uint16_t*>(w + L.dab);
+  b.xs = (a_rows && dt == MOE_BF16) ? reinterpret_cast<uint16_t*>(w + L.xs) : nullptr;
+  b.dab = w + L.dab;
   return hip_status(moe::launch_expert_backward(b, as_stream(stream)), fn);
 }
 

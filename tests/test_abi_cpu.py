@@ -174,14 +174,15 @@ def test_probes_reject():
 
 def test_backward_rejects():
     F32, BF = L.MOE_F32, L.MOE_BF16
-    # expert backward: bf16 only, shapes, pointers, workspace
+    # expert backward: dtype, shapes, pointers, workspace
     ws = L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, BF, True)
-    assert ws > 0 and L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, F32, True) == 0
+    assert ws > 0 and L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, F32, True) > 0
+    assert L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, 7, True) == 0
     assert ws > L.moe_expert_swiglu_backward_workspace(1000, 128, 256, 4, BF, False)
     args = [FAKE, BF, 128, 256, 4, FAKE, 1000, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
             FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
-    s = C.moe_expert_swiglu_backward(*args[:1], F32, *args[2:])
-    assert s == L.MOE_EUNSUPPORTED and "bf16" in _err()
+    s = C.moe_expert_swiglu_backward(*args[:1], 7, *args[2:])
+    assert s == L.MOE_EINVAL
     s = C.moe_expert_swiglu_backward(*args[:2], 100, *args[3:])
     assert s == L.MOE_EUNSUPPORTED and "% 64" in _err()
     s = C.moe_expert_swiglu_backward(*args[:9], None, *args[10:])
@@ -190,10 +191,7 @@ def test_backward_rejects():
     assert s == L.MOE_EWORKSPACE
     s = C.moe_expert_swiglu_backward(*args[:8], 0, *args[9:])
     assert s == L.MOE_EINVAL and "a_rows_div" in _err()
-    # training gate/up: bf16 only, uv required
-    s = C.moe_expert_gate_up_train(FAKE, F32, 128, 256, 4, FAKE, 100, None, 1, FAKE, FAKE, FAKE,
-                                   FAKE, FAKE, 1 << 30, None)
-    assert s == L.MOE_EUNSUPPORTED
+    # training gate/up: uv required
     s = C.moe_expert_gate_up_train(FAKE, BF, 128, 256, 4, FAKE, 100, None, 1, FAKE, FAKE, FAKE,
                                    None, FAKE, 1 << 30, None)
     assert s == L.MOE_EINVAL
