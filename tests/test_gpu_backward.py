@@ -348,3 +348,63 @@ def test_backward_full_size_sampled(name):
     assert errs["dlogits_same_in"] <= 1e-5 and errs["dw_router_same_in"] <= 1e-5, errs
     for key in ("dgate", "dx", "dw_gate", "dw_up", "dw_down"):
         assert errs[key] <= 2e-2, errs
+
+
+@pytest.mark.parametrize("T,E,k,d,dt,c_bal,c_z", [
+    (1, 1, 1, 64, "bf16", 1.0, 1.0),
+    (333, 256, 32, 96, "f32", 1.0, 0.01),
+    (1000, 200, 7, 160, "bf16", 0.5, 0.0),
+    (4099, 8, 2, 256, "bf16", 0.0, 0.001),
+])
+def test_routing_backward_shapes(T, E, k, d, dt, c_bal, c_z):
+    """moe_combine_backward, moe_route_backward and moe_router_backward alone,
+    from the smallest to the largest expert count and k, with dropped pairs,
+    against the oracle on the same inputs (fp32 arithmetic: 1e-5)."""
+    from sparse_mixture_experts_moe_amd import _lib
+    from moe_inputs import bf16_bits_rne
+    _say(f"[case] routing backward T={T} E={E} k={k} d={d} {dt}")
+    rng = np.random.default_rng(T + E + k)
+
+    def cast(a):
+        return a.astype(np.float32) if dt == "f32" else Bf16(bf16_bits_rne(a.astype(np.float32)))
+
+    x = cast(rng.standard_normal((T, d)))
+    wr = cast(rng.standard_normal((E, d)) / np.sqrt(d))
+    dy = cast(rng.standard_normal((T, d)))
+    logits = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx = oracle.top_k(logits, k)
+    gate = oracle.gates(logits, idx).astype(np.float32)
+    cap = max(1, (T * k) // (2 * E))
+    disp = oracle.dispatch(idx, E, cap)
+    R = int(disp["offset"][-1])
+    y_rows = cast(rng.standard_normal((max(R, 1), d)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    pair_row = dev(disp["pair_row"].astype(np.int32))
+    dgate, dout = _lib.moe_combine_backward(to_device(dy), to_device(y_rows), pair_row, k,
+                                            dev(gate), want_dout=True)
+    count = dev(disp["count"].astype(np.int32))
+    dl = _lib.moe_route_backward(dev(logits), dev(idx.astype(np.int32)), dev(gate), dgate, count,
+                                 0.01, c_bal, c_z)
+    dw, db, dx = _lib.moe_router_backward(to_device(x), to_device(wr), dl)
+    torch.cuda.synchronize()
+    xf, wrf, dyf, yf = as_f32(x), as_f32(wr), as_f32(dy), as_f32(y_rows)
+    pr = disp["pair_row"].reshape(T, k)
+    dg_ref = np.where(pr >= 0, np.einsum("td,tkd->tk", dyf.astype(np.float64),
+                                         yf[np.maximum(pr, 0)].astype(np.float64)), 0.0)
+    assert normwise(host(dgate), dg_ref) <= 1e-5
+    kept_pairs = np.nonzero(disp["pair_row"] >= 0)[0]
+    want = gate.reshape(-1)[kept_pairs][:, None].astype(np.float64) * dyf[kept_pairs // k]
+    got = host(dout)[disp["pair_row"][kept_pairs]]
+    assert normwise(got, want) <= (1e-6 if dt == "f32" else 4e-3)
+    gdg = host(dgate)
+    dl_ref = oracle.gate_logit_grad(logits, idx, gdg)
+    if c_bal:
+        dl_ref = dl_ref + c_bal * oracle.balance_logit_grad(logits, disp["count"], k, 0.01)
+    if c_z:
+        dl_ref = dl_ref + c_z * oracle.z_loss_logit_grad(logits)
+    gdl = host(dl)
+    assert normwise(gdl, dl_ref) <= 1e-5
+    dx_ref, dw_ref, db_ref = oracle.router_linear_backward(xf, wrf, gdl)
+    assert normwise(host(dx), dx_ref) <= 1e-5
+    assert normwise(host(dw), dw_ref) <= 1e-5
+    assert normwise(host(db), db_ref) <= 1e-5
