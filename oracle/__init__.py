@@ -1,5 +1,6 @@
 """CPU oracle for the sparse Mixture-of-Experts feed-forward layer (forward and
-backward passes, and the per-step load-balancing updates).
+backward passes, the per-step load-balancing updates, and the ReLU-routing and
+zero-computation-expert variants).
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -52,4 +53,11 @@ from .moe_balance import (  # noqa: F401
     balance_update,
     load_ema,
     selection_bias_update,
+)
+from .moe_variants import (  # noqa: F401
+    bypass_kind,
+    bypass_output,
+    forward_bypass,
+    forward_relu,
+    relu_route,
 )

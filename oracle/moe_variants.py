@@ -1,0 +1,151 @@
+"""Plain float64 oracle of two routing variants of the sparse MoE layer:
+ReLU routing and zero-computation (zero, copy and constant) experts.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Source: "Zen MoDE: Mixture of Distilled Experts Architecture", section
+"Router" (the router adopts ReLU gating, which gives each token an adaptive
+number of experts instead of a fixed top-K, and zero-computation experts, of
+three kinds: zero, copy and constant, which let a token skip the FFN
+compute), and the same page's "Related Work" (both taken from earlier
+published work).  The page names the mechanisms without equations; the
+readings used are stated in each function.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .moe_oracle import UNLIMITED, balance_stats, dispatch, gates, moe_output, router_logits, top_k
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# ReLU routing
+# ---------------------------------------------------------------------------
+def relu_route(logits, k_max):
+    """ReLU gating: (topk_idx int32 [T, k_max], topk_gate float64 [T, k_max]).
+
+    Reading used: the gate of expert e is max(l_e, 0), so a token uses exactly
+    the experts whose logit is positive (a zero logit gives a zero gate and is
+    not used), with no renormalisation.  The token's slots hold its positive
+    experts in descending logit order (equal logits: lower index first); at
+    most ``k_max`` of them are kept (the largest), and unused slots hold
+    expert -1 with gate 0.
+    """
+    l = _f64(logits)
+    T, E = l.shape
+    if not 1 <= k_max <= E:
+        raise ValueError("need 1 <= k_max <= E")
+    idx = np.full((T, k_max), -1, dtype=np.int32)
+    g = np.zeros((T, k_max), dtype=np.float64)
+    for t in range(T):
+        pos = [e for e in range(E) if l[t, e] > 0]
+        pos.sort(key=lambda e: (-l[t, e], e))
+        for j, e in enumerate(pos[:k_max]):
+            idx[t, j] = e
+            g[t, j] = l[t, e]
+    return idx, g
+
+
+def forward_relu(x, w_router, w_gate, w_up, w_down, k_max, shared=(), logit_bias=None,
+                 cap=UNLIMITED, alpha=0.01, logits=None, tokens=None):
+    """The layer with ReLU routing: y = shared + sum over used slots g_j E_j(x).
+
+    Dispatch and capacity are the plain layer's (an unused slot is never
+    routed, so it takes no budget); the balance statistics keep their plain
+    definitions with f_e = count_e / (T k_max).
+    """
+    if logits is None:
+        logits = router_logits(x, w_router, logit_bias)
+    idx, g = relu_route(logits, k_max)
+    E = np.asarray(w_router).shape[0]
+    disp = dispatch(idx, E, cap)
+    y = moe_output(x, idx, g, disp["pair_row"], w_gate, w_up, w_down, shared, tokens)
+    f, P, loss = balance_stats(logits, disp["count"], k_max, alpha)
+    return dict(logits=logits, topk_idx=idx, topk_gate=g, y=y, f=f, P=P, loss=loss, **disp)
+
+
+# ---------------------------------------------------------------------------
+# Zero-computation experts
+# ---------------------------------------------------------------------------
+def bypass_kind(e, E_ffn, n_zero, n_copy, n_const):
+    """Kind of router expert e: ("ffn", e), ("zero", i), ("copy", i) or ("const", i).
+
+    Reading used for the numbering: the router scores E_ffn FFN experts
+    followed by n_zero zero experts, n_copy copy experts and n_const constant
+    experts, in that order.
+    """
+    if 0 <= e < E_ffn:
+        return "ffn", e
+    i = e - E_ffn
+    if 0 <= i < n_zero:
+        return "zero", i
+    i -= n_zero
+    if 0 <= i < n_copy:
+        return "copy", i
+    i -= n_copy
+    if 0 <= i < n_const:
+        return "const", i
+    raise ValueError(f"expert {e} out of range")
+
+
+def bypass_output(x, idx, gate, E_ffn, n_zero, n_copy, const_rows, tokens=None):
+    """The zero-computation experts' share of the output, float64 [len(tokens), d].
+
+    Readings used: a zero expert outputs the zero vector, a copy expert outputs
+    its input token x_t unchanged, and constant expert c outputs a fixed
+    (trainable) vector v_c of width d, whatever the token.  Each enters the
+    gate-weighted sum like any other selected expert.
+    """
+    x = _f64(x)
+    T, d = x.shape
+    idx = np.asarray(idx, dtype=np.int64)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    const_rows = _f64(const_rows).reshape(-1, d)
+    n_const = const_rows.shape[0]
+    g = _f64(gate)
+    y = np.zeros((tokens.size, d), dtype=np.float64)
+    for i, t in enumerate(tokens):
+        for j in range(idx.shape[1]):
+            kind, c = bypass_kind(int(idx[t, j]), E_ffn, n_zero, n_copy, n_const)
+            if kind == "copy":
+                y[i] += g[t, j] * x[t]
+            elif kind == "const":
+                y[i] += g[t, j] * const_rows[c]
+    return y
+
+
+def forward_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_rows,
+                   shared=(), logit_bias=None, cap=UNLIMITED, alpha=0.01, logits=None,
+                   tokens=None):
+    """The layer with zero-computation experts after its E_ffn FFN experts.
+
+    Routing is the plain top-k over all E = E_ffn + n_zero + n_copy + n_const
+    router experts with softmax gates renormalised over the k selected.
+    Readings used: only the FFN experts run on rows, so only they have a token
+    budget (``cap`` applies to them; a zero-computation expert never drops a
+    pair), and the balance statistics are taken over all E router experts
+    (count_e before any drop).
+    """
+    if logits is None:
+        logits = router_logits(x, w_router, logit_bias)
+    E = np.asarray(w_router).shape[0]
+    E_ffn = np.asarray(w_gate).shape[0]
+    n_const = _f64(const_rows).reshape(-1, np.asarray(x).shape[1]).shape[0]
+    if E_ffn + n_zero + n_copy + n_const != E:
+        raise ValueError("router rows must be E_ffn + n_zero + n_copy + n_const")
+    idx = top_k(logits, k)
+    g = gates(logits, idx)
+    caps = np.zeros(E, dtype=np.int64)
+    ffn_cap = np.iinfo(np.int64).max if cap is UNLIMITED else int(cap)
+    caps[:E_ffn] = ffn_cap
+    disp = dispatch(idx, E, caps)
+    y = moe_output(x, idx, g, disp["pair_row"], w_gate, w_up, w_down, shared, tokens)
+    y = y + bypass_output(x, idx, g, E_ffn, n_zero, n_copy, const_rows, tokens)
+    f, P, loss = balance_stats(logits, disp["count"], k, alpha)
+    return dict(logits=logits, topk_idx=idx, topk_gate=g, y=y, f=f, P=P, loss=loss, **disp)

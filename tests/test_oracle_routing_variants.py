@@ -1,0 +1,260 @@
+"""Pins of the routing-variant oracle (ReLU routing, zero-computation
+experts) from "Zen MoDE: Mixture of Distilled Experts Architecture", section
+"Router": worked values, closed forms, special cases that reduce to the plain
+layer, and pure-Python brute force from the definitions (``tests/brute.py``
+style loops, written here without the oracle's code).  The last test plants
+plausible mistakes in the oracle (on the CPU) and checks that a pin fails."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_variants as mv
+from tests import brute
+
+E_FFN, D, H = 5, 8, 6
+
+
+def _layer(seed, E_router, k_scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((7, D))
+    wr = rng.standard_normal((E_router, D)) * k_scale
+    wg = rng.standard_normal((E_FFN, H, D)) / math.sqrt(D)
+    wu = rng.standard_normal((E_FFN, H, D)) / math.sqrt(D)
+    wd = rng.standard_normal((E_FFN, D, H)) / math.sqrt(H)
+    return rng, x, wr, wg, wu, wd
+
+
+def _expert(x_row, wg, wu, wd, e):
+    return brute.expert(list(x_row), wg[e].tolist(), wu[e].tolist(), wd[e].tolist())
+
+
+# ---------------------------------------------------------------- ReLU routing
+def test_relu_route_worked():
+    """Positive logits only, descending, ties to the lower index, -1 padding."""
+    logits = np.array([[2.0, -1.0, 0.0, 3.0], [-1.0, -2.0, -3.0, -4.0], [1.0, 1.0, 1.0, 1.0],
+                       [0.5, 4.0, 0.25, -0.0]])
+    idx, g = oracle.relu_route(logits, 4)
+    assert idx.tolist() == [[3, 0, -1, -1], [-1, -1, -1, -1], [0, 1, 2, 3], [1, 0, 2, -1]]
+    assert g.tolist() == [[3, 2, 0, 0], [0, 0, 0, 0], [1, 1, 1, 1], [4, 0.5, 0.25, 0]]
+
+
+def test_relu_route_k_max_keeps_largest():
+    idx, g = oracle.relu_route(np.array([[3.0, 5.0, 4.0, 1.0], [2.0, 2.0, 2.0, 7.0]]), 2)
+    assert idx.tolist() == [[1, 2], [3, 0]]
+    assert g.tolist() == [[5, 4], [7, 2]]
+
+
+def test_relu_route_closed_forms():
+    """With k_max = E every positive expert is used: the used count equals the
+    number of positive logits and the gates sum to sum_e max(l_e, 0)."""
+    rng = np.random.default_rng(1)
+    logits = rng.standard_normal((200, 9))
+    idx, g = oracle.relu_route(logits, 9)
+    assert np.array_equal((idx >= 0).sum(axis=1), (logits > 0).sum(axis=1))
+    np.testing.assert_allclose(g.sum(axis=1), np.maximum(logits, 0).sum(axis=1), rtol=1e-15)
+    assert np.all(g[idx < 0] == 0)
+    for t in range(200):
+        used = idx[t][idx[t] >= 0]
+        assert np.all(np.diff(logits[t, used]) <= 0)
+        assert np.array_equal(g[t, :used.size], logits[t, used])
+
+
+def test_forward_relu_brute():
+    """y_t = sum over all experts of max(l_te, 0) E_e(x_t) (k_max = E, no
+    budget), written as a loop over experts, not over slots."""
+    rng, x, wr, wg, wu, wd = _layer(2, E_FFN)
+    res = oracle.forward_relu(x, wr, wg, wu, wd, E_FFN)
+    logits = x @ wr.T
+    for t in range(x.shape[0]):
+        want = [0.0] * D
+        for e in range(E_FFN):
+            if logits[t, e] > 0:
+                out = _expert(x[t], wg, wu, wd, e)
+                want = [a + logits[t, e] * b for a, b in zip(want, out)]
+        np.testing.assert_allclose(res["y"][t], want, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_relu_budget_and_stats():
+    """Unused slots take no budget: the count per expert is the number of
+    tokens with a positive logit there (k_max = E); a budget keeps the first
+    tokens in token order; f uses T k_max."""
+    rng, x, wr, wg, wu, wd = _layer(3, E_FFN)
+    logits = x @ wr.T
+    res = oracle.forward_relu(x, wr, wg, wu, wd, E_FFN, cap=2)
+    assert np.array_equal(res["count"], (logits > 0).sum(axis=0))
+    assert np.array_equal(res["kept"], np.minimum((logits > 0).sum(axis=0), 2))
+    pr = res["pair_row"].reshape(7, E_FFN)
+    for e in range(E_FFN):
+        toks = [t for t in range(7) if logits[t, e] > 0]
+        kept_toks = sorted(t for t in range(7) for j in range(E_FFN)
+                           if res["topk_idx"][t, j] == e and pr[t, j] >= 0)
+        assert kept_toks == toks[:2]
+    np.testing.assert_allclose(res["f"], res["count"] / (7 * E_FFN))
+
+
+def test_forward_relu_all_negative_is_shared_only():
+    rng, x, wr, wg, wu, wd = _layer(4, E_FFN)
+    sh = (rng.standard_normal((4, D)), rng.standard_normal((4, D)), rng.standard_normal((D, 4)))
+    logits = -np.abs(rng.standard_normal((7, E_FFN))) - 0.1
+    res = oracle.forward_relu(x, wr, wg, wu, wd, 3, shared=[sh], logits=logits)
+    assert np.all(res["topk_idx"] == -1) and res["offset"][-1] == 0
+    np.testing.assert_allclose(res["y"], oracle.swiglu(x, *sh), rtol=1e-14)
+
+
+# ------------------------------------------------- zero-computation experts
+def test_bypass_numbering():
+    kinds = [oracle.bypass_kind(e, 3, 2, 1, 2) for e in range(8)]
+    assert kinds == [("ffn", 0), ("ffn", 1), ("ffn", 2), ("zero", 0), ("zero", 1), ("copy", 0),
+                     ("const", 0), ("const", 1)]
+    with pytest.raises(ValueError):
+        oracle.bypass_kind(8, 3, 2, 1, 2)
+
+
+def _forced_logits(T, E, choice, second=None):
+    lg = np.zeros((T, E))
+    lg[:, choice] = 5.0
+    if second is not None:
+        lg[:, second] = 4.0
+    return lg
+
+
+def test_bypass_copy_is_identity():
+    """Every token on a copy expert with k = 1: y = x exactly, no FFN rows."""
+    rng, x, _, wg, wu, wd = _layer(5, 0)
+    n_zero, n_copy, cv = 1, 2, rng.standard_normal((1, D))
+    E = E_FFN + n_zero + n_copy + 1
+    wr = np.zeros((E, D))
+    res = oracle.forward_bypass(x, wr, wg, wu, wd, 1, n_zero, n_copy, cv,
+                                logits=_forced_logits(7, E, E_FFN + n_zero + 1))
+    assert np.array_equal(res["y"], x)
+    assert res["offset"][-1] == 0 and np.all(res["pair_row"] == -1)
+    assert res["count"][E_FFN + n_zero + 1] == 7
+
+
+def test_bypass_constant_and_zero():
+    """A constant expert gives its vector; a zero expert gives nothing, and the
+    FFN expert beside it keeps its renormalised gate."""
+    rng, x, _, wg, wu, wd = _layer(6, 0)
+    cv = rng.standard_normal((2, D))
+    E = E_FFN + 1 + 1 + 2
+    res = oracle.forward_bypass(x, np.zeros((E, D)), wg, wu, wd, 1, 1, 1, cv,
+                                logits=_forced_logits(7, E, E - 1))
+    np.testing.assert_allclose(res["y"], np.broadcast_to(cv[1], (7, D)), rtol=0, atol=0)
+    res = oracle.forward_bypass(x, np.zeros((E, D)), wg, wu, wd, 2, 1, 1, cv,
+                                logits=_forced_logits(7, E, 2, second=E_FFN))
+    g0 = 1.0 / (1.0 + math.exp(-1.0))
+    for t in range(7):
+        want = [g0 * v for v in _expert(x[t], wg, wu, wd, 2)]
+        np.testing.assert_allclose(res["y"][t], want, rtol=1e-12, atol=1e-14)
+
+
+def _brute_bypass(x, logits, k, wg, wu, wd, n_zero, n_copy, cv, cap):
+    """Per-token definition: softmax over the k best (ties low), kinds by
+    position, budget per FFN expert in token order."""
+    T, E = logits.shape
+    used = [0] * E_FFN
+    y = []
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        m = max(logits[t, e] for e in order)
+        w = [math.exp(logits[t, e] - m) for e in order]
+        s = sum(w)
+        acc = [0.0] * D
+        for e, wj in zip(order, w):
+            g = wj / s
+            if e < E_FFN:
+                if cap is not None and used[e] >= cap:
+                    used[e] += 1
+                    continue
+                used[e] += 1
+                out = _expert(x[t], wg, wu, wd, e)
+            elif e < E_FFN + n_zero:
+                out = [0.0] * D
+            elif e < E_FFN + n_zero + n_copy:
+                out = list(x[t])
+            else:
+                out = list(cv[e - E_FFN - n_zero - n_copy])
+            acc = [a + g * b for a, b in zip(acc, out)]
+        y.append(acc)
+    return np.array(y)
+
+
+@pytest.mark.parametrize("k,cap,seed", [(1, None, 7), (2, None, 8), (3, 1, 9), (4, 2, 10)])
+def test_forward_bypass_brute(k, cap, seed):
+    n_zero, n_copy, n_const = 2, 1, 2
+    E = E_FFN + n_zero + n_copy + n_const
+    rng, x, wr, wg, wu, wd = _layer(seed, E, k_scale=0.8)
+    cv = rng.standard_normal((n_const, D))
+    res = oracle.forward_bypass(x, wr, wg, wu, wd, k, n_zero, n_copy, cv, cap=cap)
+    want = _brute_bypass(x, x @ wr.T, k, wg, wu, wd, n_zero, n_copy, cv, cap)
+    np.testing.assert_allclose(res["y"], want, rtol=1e-12, atol=1e-12)
+    # statistics over all router experts, counts before any drop
+    idx = res["topk_idx"]
+    assert np.array_equal(res["count"], np.bincount(idx.ravel(), minlength=E))
+    assert math.isclose(res["f"].sum(), 1.0, rel_tol=1e-15)
+    assert np.all(res["kept"][E_FFN:] == 0)
+
+
+def test_forward_bypass_without_bypass_is_plain_layer():
+    rng, x, wr, wg, wu, wd = _layer(11, E_FFN)
+    a = oracle.forward_bypass(x, wr, wg, wu, wd, 2, 0, 0, np.zeros((0, D)), cap=2)
+    b = oracle.forward(x, wr, wg, wu, wd, 2, cap=2)
+    assert np.array_equal(a["y"], b["y"])
+    assert np.array_equal(a["pair_row"], b["pair_row"])
+
+
+# ------------------------------------------------------------- mutations
+def _relu_keeps_zero(logits, k_max):
+    l = np.asarray(logits, dtype=np.float64)
+    idx, g = mv.__dict__["_orig_relu_route"](np.where(l == 0, 1e-300, l), k_max)
+    return idx, np.where(idx >= 0, np.take_along_axis(l, np.maximum(idx, 0), 1), 0.0)
+
+
+def _relu_renormalised(logits, k_max):
+    idx, g = mv.__dict__["_orig_relu_route"](logits, k_max)
+    s = g.sum(axis=1, keepdims=True)
+    return idx, np.where(s > 0, g / np.where(s > 0, s, 1), 0.0)
+
+
+def _kind_copy_const_swapped(e, E_ffn, n_zero, n_copy, n_const):
+    kind, i = mv.__dict__["_orig_bypass_kind"](e, E_ffn, n_zero, n_copy, n_const)
+    if kind == "copy" and n_const:
+        return "const", 0
+    return kind, i
+
+
+def _bypass_output_no_gate(x, idx, gate, *a, **kw):
+    return mv.__dict__["_orig_bypass_output"](x, idx, np.ones_like(np.asarray(gate)), *a, **kw)
+
+
+MUTATIONS = {
+    "relu keeps a zero logit": ("relu_route", _relu_keeps_zero),
+    "relu gates renormalised": ("relu_route", _relu_renormalised),
+    "copy and constant swapped": ("bypass_kind", _kind_copy_const_swapped),
+    "bypass ignores its gate": ("bypass_output", _bypass_output_no_gate),
+}
+
+PIN_TESTS = [
+    test_relu_route_worked, test_relu_route_closed_forms, test_forward_relu_brute,
+    test_bypass_copy_is_identity, test_bypass_constant_and_zero,
+    lambda: test_forward_bypass_brute(2, None, 8), lambda: test_forward_bypass_brute(3, 1, 9),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    fn_name, bad = MUTATIONS[name]
+    monkeypatch.setitem(mv.__dict__, f"_orig_{fn_name}", getattr(mv, fn_name))
+    monkeypatch.setattr(mv, fn_name, bad)
+    if fn_name == "relu_route":
+        monkeypatch.setattr(oracle, "relu_route", bad)
+    failed = 0
+    for pin in PIN_TESTS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin caught: {name}"
