@@ -26,6 +26,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec (1 GPU) + grouped-GEMM MFMA util % / HBM GB/s"
+BYPASS_COUNTS = (1, 1, 2)   # zero, copy and constant experts of --variant bypass
+RELU_K_MUL = 2              # --variant relu: at most RELU_K_MUL * k experts per token
 
 
 def parse():
@@ -45,6 +47,10 @@ def parse():
                     help="apply the per-step load-balancing updates after every step "
                          "(selection-bias step 1e-3, rolling-load decay 0.9, adaptive per-expert "
                          "budgets with C_base = the workload's capacity factor or 1 and gamma = E)")
+    ap.add_argument("--variant", choices=["relu", "bypass"], default=None,
+                    help="routing variant: ReLU routing (at most 2k experts per token, a logit "
+                         "offset that makes k positive on average) or zero-computation experts "
+                         "(1 zero, 1 copy, 2 constant after the FFN experts)")
     ap.add_argument("--backward", action="store_true",
                     help="time training steps instead: forward (keeping the pre-activations) "
                          "plus the backward pass of <dy, y> + loss + 1e-3 zloss")
@@ -142,10 +148,13 @@ def measured_ceilings(torch, gemm_shape):
     return res
 
 
-def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5):
+def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
     """The oracle as it stands, on the first n_tok tokens taken as a batch of
     their own (same shapes, weights, biases and capacity factor), repeated
-    until at least min_seconds of CPU work (at most max_passes passes)."""
+    until at least min_seconds of CPU work (at most max_passes passes).
+    ``variant`` = (kind, extras) runs the oracle of that routing variant."""
+    import numpy as np
+
     import oracle
     from moe_inputs import as_f32
     try:
@@ -163,15 +172,26 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5):
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle.forward(x, wr, inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k,
-                       shared=shared, logit_bias=inp["logit_bias"],
-                       select_bias=inp["select_bias"], cap=cap, alpha=cfg.alpha)
+        if variant is None:
+            oracle.forward(x, wr, inp["w_gate"], inp["w_up"], inp["w_down"], cfg.k,
+                           shared=shared, logit_bias=inp["logit_bias"],
+                           select_bias=inp["select_bias"], cap=cap, alpha=cfg.alpha)
+        elif variant[0] == "relu":
+            oracle.forward_relu(x, wr, inp["w_gate"], inp["w_up"], inp["w_down"],
+                                variant[1]["k_max"], shared=shared,
+                                logit_bias=variant[1]["logit_bias"], cap=cap, alpha=cfg.alpha)
+        else:
+            ex = variant[1]
+            oracle.forward_bypass(x, np.concatenate([wr, as_f32(ex["rows"])], 0), inp["w_gate"],
+                                  inp["w_up"], inp["w_down"], cfg.k, ex["n_zero"], ex["n_copy"],
+                                  as_f32(ex["const"]), shared=shared, cap=cap, alpha=cfg.alpha)
         dt += time.perf_counter() - t0
         passes += 1
     return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name} as one batch, "
-                      f"{passes} passes (float64 NumPy, {dt:.1f} s)"}
+            "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name}"
+                      f"{'' if variant is None else ' (' + variant[0] + ' variant)'} as one "
+                      f"batch, {passes} passes (float64 NumPy, {dt:.1f} s)"}
 
 
 def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max_passes=5):
@@ -347,8 +367,27 @@ def main():
     inp = generate(cfg)
     print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     layer = layer_from_inputs(inp, args.gather)
+    variant = None
+    if args.variant == "relu":
+        from moe_inputs import relu_logit_offset
+        from sparse_mixture_experts_moe_amd.workload import relu_layer_from_inputs, relu_logit_bias
+        off = relu_logit_offset(cfg, cfg.k)
+        k_max = min(cfg.E, RELU_K_MUL * cfg.k)
+        layer = relu_layer_from_inputs(inp, k_max, off, args.gather)
+        variant = ("relu", {"k_max": k_max, "logit_offset": off,
+                            "logit_bias": relu_logit_bias(inp, off)})
+    elif args.variant == "bypass":
+        from moe_inputs import generate_bypass
+        from sparse_mixture_experts_moe_amd.workload import bypass_layer_from_inputs
+        rows, const = generate_bypass(cfg, *BYPASS_COUNTS)
+        layer = bypass_layer_from_inputs(inp, rows, const, BYPASS_COUNTS[0], BYPASS_COUNTS[1],
+                                         args.gather)
+        variant = ("bypass", {"n_zero": BYPASS_COUNTS[0], "n_copy": BYPASS_COUNTS[1],
+                              "n_const": BYPASS_COUNTS[2], "rows": rows, "const": const})
     layer.overlap_shared = not args.serial_shared
     balance = None
+    if args.balance and variant:
+        raise SystemExit("--balance does not combine with --variant")
     if args.balance:
         balance = dict(bias_step=1e-3, ema_decay=0.9, cf_base=cfg.cf if cfg.cf > 0 else 1.0,
                        gamma=float(cfg.E))
@@ -462,7 +501,7 @@ def main():
                 "frac": achieved / peak}
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs
     # recorded in profiles/ (scaled by a plain copy of known size), or null
-    roof["traffic"] = recorded_traffic(cfg.name)
+    roof["traffic"] = None if variant else recorded_traffic(cfg.name)
     ceil = measured_ceilings(torch, None if cfg.name.startswith("decode") or cfg.dtype != "bf16"
                              else (R_kept, d, 2 * h))
     if roof["bound"] == "hbm":
@@ -513,7 +552,11 @@ def main():
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
                    "gather": args.gather, "parallelism": "none (1 GPU)",
                    "shared_overlap": bool(cfg.n_shared and layer.overlap_shared),
-                   **({"balance": balance} if balance else {})},
+                   **({"balance": balance} if balance else {}),
+                   **({"variant": {k_: v_ for k_, v_ in variant[1].items()
+                                   if k_ in ("k_max", "logit_offset", "n_zero", "n_copy",
+                                             "n_const")} | {"kind": variant[0]}}
+                      if variant else {})},
         "roofline": roof,
         "measured_ceilings": ceil,
         "expert_gemm_mfma_util": expert_flops / (expert_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -532,7 +575,7 @@ def main():
         n_tok = args.cpu_tokens or {"tiny_f32": 64, "mixtral_bf16": 4096,
                                     "finegrained_shared_bf16": 8192,
                                     "capacity_balance_bf16": 8192, "decode_bf16": 64}[cfg.name]
-        out["cpu_baseline"] = cpu_baseline(inp, cfg, n_tok)
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, n_tok, variant=variant)
     print(json.dumps(out), flush=True)
 
 

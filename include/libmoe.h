@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -87,6 +87,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * writes it (section "Auxiliary-Loss-Free Load Balancing", s_ij =
  * softmax(x_i W_g)_j + b_j), instead of the default logit plus bias. */
 #define MOE_ROUTE_BIAS_ON_PROBS 2u
+/* moe_route flag: ReLU routing ("Zen MoDE", section "Router": ReLU gating
+ * gives each token an adaptive number of experts instead of a fixed top-k).
+ * Reading: the gate of expert e is max(logits[t,e], 0) with no
+ * renormalisation; a token's slots hold, of its k largest logits, those above
+ * zero, in descending order (ties to the lower index), topk_gate = the logit;
+ * the remaining slots are empty: topk_idx = -1, topk_gate = 0.  k is then the
+ * most experts a token may use.  Not combinable with select_bias or
+ * MOE_ROUTE_BIAS_ON_PROBS. */
+#define MOE_ROUTE_RELU 4u
 
 /* Limits of these kernels (MOE_EUNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 256
@@ -167,7 +176,9 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
  * still pay for" (a token travels to its assigned expert).  Reading: an
  * expert keeps its first `capacity` pairs in token order.
  *
- * topk_idx [T,k] int32 (values in [0,E)); capacity < 0 means unlimited.
+ * topk_idx [T,k] int32; a slot whose expert lies outside [0,E) (the empty
+ * slots of MOE_ROUTE_RELU hold -1) is not routed: it is not counted, takes
+ * no budget and gets pair_row -1.  capacity < 0 means unlimited.
  * x [T,d] in dtype dt, or NULL to skip the gather (x_perm then unused).
  * Outputs (int32): expert_count [E], expert_offset [E+1], pair_row [T*k],
  * row_pair [T*k]; x_perm [T*k, d] dtype dt.
@@ -296,6 +307,31 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
 moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
                          const float* topk_gate, int64_t T, int k, int d,
                          const void* shared_y, void* out, int out_dt, void* stream);
+
+/* moe_combine_bypass: moe_combine for a router whose experts past the first
+ * E_ffn are zero-computation experts ("Zen MoDE", section "Router": zero,
+ * copy and constant experts let a token skip the FFN compute).  Router ids
+ * E_ffn .. E_ffn+n_zero-1 are zero experts, the next n_copy copy experts, the
+ * next n_const constant experts.  Slot j of token t adds, in slot order,
+ *   topk_gate[t,j] * y_perm[pair_row[t*k+j], :]   if topk_idx[t,j] < E_ffn
+ *                                                 and pair_row >= 0,
+ *   nothing                                       for a zero expert,
+ *   topk_gate[t,j] * x[t, :]                      for a copy expert,
+ *   topk_gate[t,j] * const_rows[c, :]             for constant expert c,
+ * then the shared term, rounded once (readings: zero outputs 0, copy outputs
+ * its input, constant c outputs a fixed row v_c; the gates are the plain
+ * top-k softmax over all router experts).  The FFN experts' rows come from
+ * moe_permute_budgets with a budget of 0 for the zero-computation experts,
+ * so they take no rows; their pair_row is not read.
+ * topk_idx [T,k] int32; x [T,d] and const_rows [n_const,d] in y_dt (x may be
+ * NULL when n_copy == 0, const_rows when n_const == 0); other arguments as
+ * moe_combine.  Ids at or past E_ffn+n_zero+n_copy+n_const contribute
+ * nothing. */
+moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pair_row,
+                                const int32_t* topk_idx, const float* topk_gate, int64_t T,
+                                int k, int d, int E_ffn, int n_zero, int n_copy, int n_const,
+                                const void* x, const void* const_rows, const void* shared_y,
+                                void* out, int out_dt, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* moe_balance_stats: Switch balance statistics and the router z-loss.

@@ -160,3 +160,26 @@ def generate_dy(cfg: MoEConfig, seed: int = 0):
     tid = 4 + 3 * cfg.E + 3 * cfg.n_shared
     z = _draw(seed, cfg.cid, tid, (cfg.T, cfg.d), 1.0, cfg.dtype)
     return Bf16(z) if cfg.dtype == "bf16" else z
+
+
+def generate_bypass(cfg: MoEConfig, n_zero: int, n_copy: int, n_const: int, seed: int = 0):
+    """Inputs of the zero-computation experts added to workload ``cfg``: their
+    router rows [n_zero + n_copy + n_const, d] (drawn like w_router, to be
+    appended after its E rows) and the constant experts' rows [n_const, d],
+    N(0, 1).  Returned in the workload's dtype (``Bf16`` for bf16)."""
+    tid = 5 + 3 * cfg.E + 3 * cfg.n_shared
+    n = n_zero + n_copy + n_const
+    rows = _draw(seed, cfg.cid, tid, (n, cfg.d), cfg.sigma_in, cfg.dtype)
+    const = _draw(seed, cfg.cid, tid + 1, (n_const, cfg.d), 1.0, cfg.dtype)
+    wrap = (lambda a: Bf16(a)) if cfg.dtype == "bf16" else (lambda a: a)
+    return wrap(rows), wrap(const)
+
+
+def relu_logit_offset(cfg: MoEConfig, k_mean: float) -> float:
+    """The constant logit bias -tau that makes k_mean of the E logits of a
+    token positive on average, for ReLU routing on untrained random weights:
+    a logit of this generator is N(0, d sigma_in^2), so tau = sigma z with
+    z the (1 - k_mean / E) normal quantile."""
+    from statistics import NormalDist
+    sigma = math.sqrt(cfg.d) * cfg.sigma_in
+    return -sigma * NormalDist().inv_cdf(1.0 - k_mean / cfg.E)

@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 MOE_ROUTE_BIAS_ON_PROBS = 2
+MOE_ROUTE_RELU = 4
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 32
 
@@ -63,6 +64,8 @@ _SIGS = {
     "moe_expert_gate_up": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_down": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _p, _i, _p, _sz, _p]),
     "moe_combine": (_i, [_p, _i, _p, _p, _i64, _i, _i, _p, _p, _i, _p]),
+    "moe_combine_bypass": (_i, [_p, _i, _p, _p, _p, _i64, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
+                                _i, _p]),
     "moe_balance_stats_workspace": (_sz, [_i64, _i]),
     "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_gate_up_train": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
@@ -137,10 +140,13 @@ def moe_route_workspace(T, d, E, k, dt) -> int:
 
 
 def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None, topk_idx=None,
-              topk_gate=None, logits_in=False, bias_on_probs=False, ws=None, stream=None):
+              topk_gate=None, logits_in=False, bias_on_probs=False, relu=False, ws=None,
+              stream=None):
     """Router logits, top-k experts and renormalised gates.  With
     ``logits_in`` the given ``logits`` [T, E] are used instead of x W_r^T;
-    ``bias_on_probs`` selects on softmax probability + selection bias."""
+    ``bias_on_probs`` selects on softmax probability + selection bias;
+    ``relu`` is ReLU routing (at most k experts with a positive logit, gate =
+    logit, empty slots -1 / 0)."""
     if logits_in:
         T, E = logits.shape
         dt, d = MOE_F32, 0
@@ -163,7 +169,8 @@ def moe_route(x, w_router, k, logit_bias=None, select_bias=None, *, logits=None,
     _check(_L.moe_route(_ptr(x), _ptr(w_router), dt, T, d, E, k, _ptr(logit_bias),
                         _ptr(select_bias),
                         (MOE_ROUTE_LOGITS_IN if logits_in else 0) |
-                        (MOE_ROUTE_BIAS_ON_PROBS if bias_on_probs else 0),
+                        (MOE_ROUTE_BIAS_ON_PROBS if bias_on_probs else 0) |
+                        (MOE_ROUTE_RELU if relu else 0),
                         _ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(ws), ws.numel(),
                         _stream(stream)))
     return logits, topk_idx, topk_gate
@@ -329,6 +336,27 @@ def moe_combine(y_perm, pair_row, topk_gate, shared_y=None, *, out=None, out_dty
         raise TypeError("shared_y must have the dtype of y_perm")
     _check(_L.moe_combine(_ptr(y_perm), _dt(y_perm), _ptr(pair_row), _ptr(topk_gate), T, k, d,
                           _ptr(shared_y), _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def moe_combine_bypass(y_perm, pair_row, topk_idx, topk_gate, e_ffn, n_zero, n_copy, x=None,
+                       const_rows=None, shared_y=None, *, out=None, out_dtype=None, stream=None):
+    """moe_combine with zero-computation experts after the first ``e_ffn``
+    router experts: ``n_zero`` zero, ``n_copy`` copy (add g x[t]) and
+    ``const_rows.shape[0]`` constant experts (add g const_rows[c])."""
+    T, k = topk_gate.shape
+    d = y_perm.shape[1]
+    n_const = 0 if const_rows is None else const_rows.shape[0]
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype or y_perm.dtype, device=y_perm.device)
+    _contig(y_perm, pair_row, topk_idx, topk_gate, x, const_rows, shared_y, out)
+    for t in (x, const_rows, shared_y):
+        if t is not None and (t.dtype != y_perm.dtype or t.shape[-1] != d):
+            raise TypeError("x, const_rows and shared_y need the dtype and width of y_perm")
+    _check(_L.moe_combine_bypass(_ptr(y_perm), _dt(y_perm), _ptr(pair_row), _ptr(topk_idx),
+                                 _ptr(topk_gate), T, k, d, e_ffn, n_zero, n_copy, n_const, _ptr(x),
+                                 _ptr(const_rows), _ptr(shared_y), _ptr(out), _dt(out),
+                                 _stream(stream)))
     return out
 
 

@@ -1,13 +1,18 @@
 // Combine: out[t] = shared_y[t] + sum over kept slots j of g[t,j] * y_perm[pair_row[t*k+j]],
 // accumulated in fp32 in slot order and rounded once.  Without gates (g = 1)
 // the same kernel adds the input gradients of a token's kept pairs in the
-// backward pass.
+// backward pass.  With zero-computation experts (router experts past the
+// E_ffn FFN experts: zero, then copy, then constant) a slot on such an expert
+// contributes g times nothing, the token's own input row, or the expert's
+// constant row.
 //
 // Sources: "Every parameter, every token", sections "The gating network"
 // (the output is the gate-weighted sum of the selected experts), "A budget"
 // (a dropped pair contributes nothing) and "A shared expert"; "Zen-Max:
 // Maximum Capability via Mixture-of-Experts Architecture", section
-// "Fine-Grained Expert Architecture" (shared experts are added).
+// "Fine-Grained Expert Architecture" (shared experts are added); "Zen MoDE:
+// Mixture of Distilled Experts Architecture", section "Router" (zero, copy
+// and constant experts that skip the FFN).
 //
 // HBM-bound: one workgroup per token, each lane handles 8 consecutive
 // columns per step (16-byte bf16 loads and stores); the rows of up to
@@ -82,12 +87,41 @@ struct Vec8<float> {
 // Workgroup (t, y) covers the whole row of token t (gridDim.y = 1) or its
 // columns [8 BLOCK y, 8 BLOCK (y + 1)) (gridDim.y column chunks, so that a few
 // tokens still fill the device).
-template <typename YT, typename OT, int BLOCK>
+// Zero-computation experts: router ids e_ffn .. e_ffn + n_zero - 1 are zero
+// experts, the next n_copy copy experts, the next n_const constant experts
+// (rows of cvec).
+template <typename YT>
+struct Bypass {
+  const int32_t* idx;
+  int e_ffn, n_zero, n_copy, n_const;
+  const YT* x;
+  const YT* cvec;
+};
+
+// The source row of slot j of token t (NULL: contributes nothing).
+template <typename YT, bool kBypass>
+__device__ __forceinline__ const YT* slot_row(const YT* y, const int32_t* pr, int j, int64_t t,
+                                              int k, int d, const Bypass<YT>& bp) {
+  if constexpr (kBypass) {
+    const int e = bp.idx[t * k + j] - bp.e_ffn;
+    if (e >= 0) {
+      if (e < bp.n_zero) return nullptr;
+      if (e < bp.n_zero + bp.n_copy) return bp.x + t * d;
+      const int c = e - bp.n_zero - bp.n_copy;
+      return c < bp.n_const ? bp.cvec + static_cast<int64_t>(c) * d : nullptr;
+    }
+  }
+  const int row = pr[j];
+  return row >= 0 ? y + static_cast<int64_t>(row) * d : nullptr;
+}
+
+template <typename YT, typename OT, int BLOCK, bool kBypass = false>
 __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y,
                                                         const int32_t* __restrict__ pair_row,
                                                         const float* __restrict__ gate, int k,
                                                         int d, const YT* __restrict__ shared,
-                                                        OT* __restrict__ out) {
+                                                        OT* __restrict__ out,
+                                                        Bypass<YT> bp = Bypass<YT>{}) {
   const int64_t t = blockIdx.x;
   const int32_t* pr = pair_row + t * k;
   const float* g = gate ? gate + t * k : nullptr;  // NULL: every gate is 1
@@ -100,16 +134,16 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y
       typename Vec8<YT>::Raw sh{};
       if (shared) sh = Vec8<YT>::load_raw(shared + t * d + c);
       for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
-        int rows[kSlotBatch];
+        const YT* src[kSlotBatch];
         typename Vec8<YT>::Raw raw[kSlotBatch];
 #pragma unroll
         for (int u = 0; u < kSlotBatch; ++u) {
-          rows[u] = j0 + u < k ? pr[j0 + u] : -1;
-          if (rows[u] >= 0) raw[u] = Vec8<YT>::load_raw(y + static_cast<int64_t>(rows[u]) * d + c);
+          src[u] = j0 + u < k ? slot_row<YT, kBypass>(y, pr, j0 + u, t, k, d, bp) : nullptr;
+          if (src[u]) raw[u] = Vec8<YT>::load_raw(src[u] + c);
         }
 #pragma unroll
         for (int u = 0; u < kSlotBatch; ++u) {
-          if (rows[u] < 0) continue;  // dropped (or past k): contributes nothing
+          if (!src[u]) continue;  // dropped, a zero expert, or past k: contributes nothing
           const float gj = g ? g[j0 + u] : 1.0f;
           float v[8];
           Vec8<YT>::unpack(raw[u], v);
@@ -130,9 +164,9 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y
     for (int c = threadIdx.x; c < d; c += BLOCK) {
       float acc = 0.0f;
       for (int j = 0; j < k; ++j) {
-        const int row = pr[j];
-        if (row < 0) continue;
-        acc = fmaf(g ? g[j] : 1.0f, Vec8<YT>::load1(y + static_cast<int64_t>(row) * d + c), acc);
+        const YT* src = slot_row<YT, kBypass>(y, pr, j, t, k, d, bp);
+        if (!src) continue;
+        acc = fmaf(g ? g[j] : 1.0f, Vec8<YT>::load1(src + c), acc);
       }
       if (shared) acc += Vec8<YT>::load1(shared + t * d + c);
       Vec8<OT>::store1(out + t * d + c, acc);
@@ -143,20 +177,38 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y
 // Enough workgroups for the device: whole rows per 256-thread workgroup when
 // there are many tokens; for a few tokens (decode), 64-thread workgroups on
 // 512-column chunks of a row.
-template <typename YT, typename OT>
+template <typename YT, typename OT, bool kBypass>
 hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_t T, int k, int d,
-                        const void* shared, void* out, hipStream_t stream) {
+                        const void* shared, void* out, const BypassArgs* bpa, hipStream_t stream) {
+  Bypass<YT> bp{};
+  if (bpa)
+    bp = Bypass<YT>{bpa->topk_idx, bpa->e_ffn, bpa->n_zero, bpa->n_copy, bpa->n_const,
+                    static_cast<const YT*>(bpa->x), static_cast<const YT*>(bpa->const_rows)};
   if (T >= 1024 || (d & 7) != 0) {
-    combine_kernel<YT, OT, 256><<<dim3(static_cast<unsigned>(T), 1), 256, 0, stream>>>(
+    combine_kernel<YT, OT, 256, kBypass><<<dim3(static_cast<unsigned>(T), 1), 256, 0, stream>>>(
         static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
-        static_cast<OT*>(out));
+        static_cast<OT*>(out), bp);
   } else {
     const unsigned chunks = static_cast<unsigned>((d + 511) / 512);
-    combine_kernel<YT, OT, 64><<<dim3(static_cast<unsigned>(T), chunks), 64, 0, stream>>>(
+    combine_kernel<YT, OT, 64, kBypass><<<dim3(static_cast<unsigned>(T), chunks), 64, 0, stream>>>(
         static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
-        static_cast<OT*>(out));
+        static_cast<OT*>(out), bp);
   }
   return hipGetLastError();
+}
+
+template <bool kBypass>
+hipError_t launch_any(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
+                      int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
+                      const BypassArgs* bp, hipStream_t stream) {
+  if (y_bf16) {
+    return out_bf16
+               ? launch_typed<uint16_t, uint16_t, kBypass>(y, pair_row, gate, T, k, d, shared, out, bp, stream)
+               : launch_typed<uint16_t, float, kBypass>(y, pair_row, gate, T, k, d, shared, out, bp, stream);
+  }
+  return out_bf16
+             ? launch_typed<float, uint16_t, kBypass>(y, pair_row, gate, T, k, d, shared, out, bp, stream)
+             : launch_typed<float, float, kBypass>(y, pair_row, gate, T, k, d, shared, out, bp, stream);
 }
 
 }  // namespace
@@ -164,12 +216,15 @@ hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_
 hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
                           int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
                           hipStream_t stream) {
-  if (y_bf16) {
-    return out_bf16 ? launch_typed<uint16_t, uint16_t>(y, pair_row, gate, T, k, d, shared, out, stream)
-                    : launch_typed<uint16_t, float>(y, pair_row, gate, T, k, d, shared, out, stream);
-  }
-  return out_bf16 ? launch_typed<float, uint16_t>(y, pair_row, gate, T, k, d, shared, out, stream)
-                  : launch_typed<float, float>(y, pair_row, gate, T, k, d, shared, out, stream);
+  return launch_any<false>(y, y_bf16, pair_row, gate, T, k, d, shared, out, out_bf16, nullptr,
+                           stream);
+}
+
+hipError_t launch_combine_bypass(const void* y, bool y_bf16, const int32_t* pair_row,
+                                 const float* gate, int64_t T, int k, int d, const void* shared,
+                                 void* out, bool out_bf16, const BypassArgs& bp,
+                                 hipStream_t stream) {
+  return launch_any<true>(y, y_bf16, pair_row, gate, T, k, d, shared, out, out_bf16, &bp, stream);
 }
 
 }  // namespace moe

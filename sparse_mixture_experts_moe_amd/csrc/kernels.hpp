@@ -20,8 +20,8 @@ size_t route_lds_bytes(int E, int k);
 size_t route_workspace_bytes(int64_t T, int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
                         const float* logit_bias, const float* select_bias, bool logits_in,
-                        bool prob_keys, float* logits, int32_t* topk_idx, float* topk_gate,
-                        void* ws, hipStream_t stream);
+                        bool prob_keys, bool relu, float* logits, int32_t* topk_idx,
+                        float* topk_gate, void* ws, hipStream_t stream);
 
 // permute.hip
 int64_t permute_chunks(int64_t R);
@@ -91,6 +91,19 @@ hipError_t launch_expert_backward(const SwigluBwdArgs& args, hipStream_t stream)
 hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* pair_row, const float* gate,
                           int64_t T, int k, int d, const void* shared, void* out, bool out_bf16,
                           hipStream_t stream);
+// Zero-computation experts of moe_combine_bypass (router ids past e_ffn:
+// n_zero zero, n_copy copy, n_const constant experts; x and const_rows in the
+// dtype of y).
+struct BypassArgs {
+  const int32_t* topk_idx;
+  int e_ffn, n_zero, n_copy, n_const;
+  const void* x;
+  const void* const_rows;
+};
+hipError_t launch_combine_bypass(const void* y, bool y_bf16, const int32_t* pair_row,
+                                 const float* gate, int64_t T, int k, int d, const void* shared,
+                                 void* out, bool out_bf16, const BypassArgs& bp,
+                                 hipStream_t stream);
 
 // backward.hip: combine, gate/router and router-linear gradients
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,

@@ -169,8 +169,11 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
                        void* ws, size_t ws_bytes, void* stream) {
   const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
   const bool prob_keys = (flags & MOE_ROUTE_BIAS_ON_PROBS) != 0;
-  if (flags & ~(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_BIAS_ON_PROBS))
+  const bool relu = (flags & MOE_ROUTE_RELU) != 0;
+  if (flags & ~(MOE_ROUTE_LOGITS_IN | MOE_ROUTE_BIAS_ON_PROBS | MOE_ROUTE_RELU))
     return fail(MOE_EINVAL, "moe_route: unknown flags 0x%x", flags);
+  if (relu && (prob_keys || select_bias))
+    return fail(MOE_EINVAL, "moe_route: ReLU routing takes no selection bias");
   if (T < 0) return fail(MOE_EINVAL, "moe_route: T < 0");
   if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_route: need 1 <= k <= E");
   if (!valid_dtype(dt)) return fail(MOE_EINVAL, "moe_route: bad dtype %d", dt);
@@ -187,7 +190,7 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
   if (ws_bytes < need || (need && !ws))
     return fail(MOE_EWORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(moe::launch_route(x, w_router, dt == MOE_BF16, T, d, E, k, logit_bias,
-                                      select_bias, logits_in, prob_keys, logits, topk_idx,
+                                      select_bias, logits_in, prob_keys, relu, logits, topk_idx,
                                       topk_gate, ws, as_stream(stream)),
                     "moe_route");
 }
@@ -416,6 +419,32 @@ moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
   return hip_status(moe::launch_combine(y_perm, y_dt == MOE_BF16, pair_row, topk_gate, T, k, d,
                                         shared_y, out, out_dt == MOE_BF16, as_stream(stream)),
                     "moe_combine");
+}
+
+moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pair_row,
+                                const int32_t* topk_idx, const float* topk_gate, int64_t T,
+                                int k, int d, int E_ffn, int n_zero, int n_copy, int n_const,
+                                const void* x, const void* const_rows, const void* shared_y,
+                                void* out, int out_dt, void* stream) {
+  if (T < 0 || k < 1 || d < 1)
+    return fail(MOE_EINVAL, "moe_combine_bypass: need T >= 0, k >= 1, d >= 1");
+  if (E_ffn < 0 || n_zero < 0 || n_copy < 0 || n_const < 0)
+    return fail(MOE_EINVAL, "moe_combine_bypass: negative expert count");
+  if (static_cast<int64_t>(E_ffn) + n_zero + n_copy + n_const > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_combine_bypass: more than %d router experts",
+                moe::kMaxExperts);
+  if (!valid_dtype(y_dt) || !valid_dtype(out_dt))
+    return fail(MOE_EINVAL, "moe_combine_bypass: dtype");
+  if (T == 0) return ok();
+  if (!pair_row || !topk_idx || !out || (E_ffn > 0 && !y_perm))
+    return fail(MOE_EINVAL, "moe_combine_bypass: NULL pointer");
+  if ((n_copy > 0 && !x) || (n_const > 0 && !const_rows))
+    return fail(MOE_EINVAL, "moe_combine_bypass: NULL x or const_rows");
+  const moe::BypassArgs bp{topk_idx, E_ffn, n_zero, n_copy, n_const, x, const_rows};
+  return hip_status(moe::launch_combine_bypass(y_perm, y_dt == MOE_BF16, pair_row, topk_gate, T,
+                                               k, d, shared_y, out, out_dt == MOE_BF16, bp,
+                                               as_stream(stream)),
+                    "moe_combine_bypass");
 }
 
 // ---------------------------------------------------------------------------

@@ -42,8 +42,11 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t p = base + s * 64 + lane;
-    const bool valid = p < R;
-    const int e = valid ? idx[p] : -1;
+    // a slot whose expert lies outside [0, E) (an empty slot of ReLU routing)
+    // is not routed
+    const int e_raw = p < R ? idx[p] : -1;
+    const bool valid = static_cast<unsigned>(e_raw) < static_cast<unsigned>(E);
+    const int e = valid ? e_raw : -1;
     // lanes holding the same expert: the lanes that agree with this one on
     // every bit of the expert id (one ballot per bit, constant time)
     uint64_t mine = __ballot(valid);
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const int32_t* __res
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int64_t p = base + s * 64 + lane;
-    if (p < R) {
+    if (p < R && my_e[s] >= 0) {
       int add = 0;
       for (int w = 0; w < wave; ++w) add += cnt[w][my_e[s]];
       local_rank[p] = my_r[s] + add;
@@ -155,6 +158,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     const int64_t p = chunk * kChunk + i;
     if (p >= R) break;
     const int e = idx[p];
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {  // not routed
+      pair_row[p] = -1;
+      if (p >= total) row_pair[p] = -1;
+      continue;
+    }
     const int r = hist[chunk * E + e] + local_rank[p];
     const int64_t c = cap_e ? static_cast<int64_t>(cap_e[e]) : cap;
     const bool kept = c < 0 || r < c;

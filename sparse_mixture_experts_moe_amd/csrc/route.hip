@@ -1,11 +1,14 @@
 // Router: logits = x . w_router^T (+ logit_bias), top-k selection on
 // key = logit + select_bias (ties to the lower expert index; or, on request,
 // key = softmax probability + select_bias), and gates that
-// renormalise the softmax over the selected logits.
+// renormalise the softmax over the selected logits.  ReLU routing instead
+// keeps, of the k largest logits, those above zero, with gate = logit, and
+// leaves the remaining slots empty (expert -1, gate 0).
 //
 // Sources: "Every parameter, every token", section "The gating network";
 // "Zen MoDE: Mixture of Distilled Experts Architecture", section "Router
-// Architecture" (standard router equation); "Zen-Max: Maximum Capability via
+// Architecture" (standard router equation) and section "Router" (ReLU gating,
+// an adaptive expert count per token); "Zen-Max: Maximum Capability via
 // Mixture-of-Experts Architecture", section "Auxiliary-Loss-Free Load
 // Balancing" (selection-only bias).
 //
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // bias (instead of the logit plus the bias).
 template <int KK, bool kProb>  // keys per lane: experts q, q+8, ... below 8 KK >= E
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
-    int mode, const float* __restrict__ xf, const float* __restrict__ wf,
+    int mode, int relu, const float* __restrict__ xf, const float* __restrict__ wf,
     const float* __restrict__ part, int KS, int64_t T, int d, int E, int k,
     const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
@@ -337,8 +340,19 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   }
   __syncthreads();
 
+  // ---- ReLU gates: the selected experts with a positive logit, gate = the
+  // logit; the slots after them (the order is by descending logit) are empty
+  if (active && relu) {
+    for (int j = q; j < k; j += kLanesPerTok) {
+      const int e = sel[tt * k + j];
+      const float l = row[e];
+      const bool use = l > 0.0f;
+      topk_idx[(t0 + tt) * k + j] = use ? e : -1;
+      topk_gate[(t0 + tt) * k + j] = use ? l : 0.0f;
+    }
+  }
   // ---- gates: softmax over the selected (unbiased) logits ----
-  if (active) {
+  if (active && !relu) {
     float m = -__builtin_inff();
     for (int j = 0; j < k; ++j) m = fmaxf(m, row[sel[tt * k + j]]);
     float s = 0.0f;
@@ -380,8 +394,8 @@ size_t route_workspace_bytes(int64_t T, int d, int E, bool bf16) {
 
 hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int d, int E, int k,
                         const float* logit_bias, const float* select_bias, bool logits_in,
-                        bool prob_keys, float* logits, int32_t* topk_idx, float* topk_gate,
-                        void* ws, hipStream_t stream) {
+                        bool prob_keys, bool relu, float* logits, int32_t* topk_idx,
+                        float* topk_gate, void* ws, hipStream_t stream) {
   const unsigned blocks = static_cast<unsigned>((T + kTokPerBlock - 1) / kTokPerBlock);
   const size_t lds = route_lds_bytes(E, k);
   // the logits tile can exceed the default 64 KB dynamic LDS limit
@@ -412,7 +426,7 @@ hipError_t launch_route(const void* x, const void* w, bool bf16, int64_t T, int 
   }
 #define MOE_SELECT(KK, P)                                                                 \
   route_select_kernel<KK, P><<<blocks, kThreads, lds, stream>>>(                           \
-      mode, static_cast<const float*>(x), static_cast<const float*>(w),                     \
+      mode, relu ? 1 : 0, static_cast<const float*>(x), static_cast<const float*>(w),       \
       static_cast<const float*>(ws), ks, T, d, E, k, logit_bias, select_bias, logits,       \
       topk_idx, topk_gate)
 #define MOE_SELECT_E(P)                 \

@@ -28,7 +28,8 @@ from . import _lib
 class MoELayer:
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
                  select_bias=None, capacity=-1, alpha=0.01, gather="fused",
-                 overlap_shared=True, balance=None, bias_on_probs=False):
+                 overlap_shared=True, balance=None, bias_on_probs=False, relu=False,
+                 bypass=None):
         """Weights are device tensors: w_router [E, d]; w_gate, w_up [E, h, d];
         w_down [E, d, h]; ``shared`` is None or (gate [Hs, d], up [Hs, d],
         down [d, Hs]) with the shared experts concatenated along the hidden
@@ -44,12 +45,36 @@ class MoELayer:
         if none was given), ``ema_decay``, and, for adaptive per-expert
         capacity, ``cf_base`` and ``gamma`` (the budgets start at
         moe_capacity(cf_base) and follow C_e = cf_base + gamma (fbar_e - 1/E)
-        from the first update on)."""
+        from the first update on).
+
+        ``relu`` routes with ReLU gates (at most k experts per token, those
+        with a positive logit; no selection bias).  ``bypass`` adds
+        zero-computation experts after the FFN experts: a dict with
+        ``n_zero``, ``n_copy`` and ``const_rows`` ([n_const, d] in the dtype
+        of x, or None); w_router then has E + n_zero + n_copy + n_const rows.
+        Both variants are forward-only and take no balance updates."""
         if gather not in ("fused", "copy"):
             raise ValueError("gather must be 'fused' or 'copy'")
         self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
         self.E, self.h, self.d = w_gate.shape
+        self.E_router = w_router.shape[0]
         self.k = k
+        self.relu = bool(relu)
+        self.bypass = None
+        if bypass is not None:
+            cr = bypass.get("const_rows")
+            self.bypass = dict(n_zero=int(bypass.get("n_zero", 0)),
+                               n_copy=int(bypass.get("n_copy", 0)), const_rows=cr,
+                               n_const=0 if cr is None else int(cr.shape[0]))
+            nz = self.bypass["n_zero"] + self.bypass["n_copy"] + self.bypass["n_const"]
+            if self.E + nz != self.E_router:
+                raise ValueError("w_router needs E + n_zero + n_copy + n_const rows")
+        elif self.E_router != self.E:
+            raise ValueError("w_router and the expert weights disagree on E")
+        if (self.relu or self.bypass) and balance:
+            raise ValueError("the routing variants take no balance updates")
+        if self.relu and (select_bias is not None or bias_on_probs):
+            raise ValueError("ReLU routing takes no selection bias")
         self.shared = None
         if shared is not None:
             sg, su, sd = shared
@@ -79,7 +104,7 @@ class MoELayer:
         b = self._bufs.get(key)
         if b is not None:
             return b
-        dev, E, k, d, h = x.device, self.E, self.k, self.d, self.h
+        dev, E, k, d, h = x.device, self.E_router, self.k, self.d, self.h
         R = T * k
         dt = _lib._dt(x)
         b = dict(
@@ -98,7 +123,7 @@ class MoELayer:
                                 device=dev),
             hid=torch.empty((R, h), dtype=x.dtype, device=dev),
             y_perm=torch.empty((R, d), dtype=x.dtype, device=dev),
-            table_ws=torch.empty(_lib.moe_expert_down_workspace(E), dtype=torch.uint8,
+            table_ws=torch.empty(_lib.moe_expert_down_workspace(self.E), dtype=torch.uint8,
                                  device=dev),
             out=torch.empty((T, d), dtype=x.dtype, device=dev),
             f=torch.empty(E, dtype=torch.float32, device=dev),
@@ -108,6 +133,11 @@ class MoELayer:
             stats_ws=torch.empty(max(1, _lib.moe_balance_stats_workspace(T, E)),
                                  dtype=torch.uint8, device=dev),
         )
+        if self.bypass is not None:
+            # the zero-computation experts take no rows: budget 0
+            cap = self.capacity if self.capacity >= 0 else T
+            b["bypass_caps"] = torch.tensor([min(cap, T)] * self.E + [0] * (E - self.E),
+                                            dtype=torch.int32, device=dev)
         if self.shared is not None:
             Hs = self.shared[0].shape[1]
             b["shared_off"] = torch.tensor([0, T], dtype=torch.int32, device=dev)
@@ -199,9 +229,18 @@ class MoELayer:
             shared_y = self._shared_forward(x, b, train, side)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
-                       bias_on_probs=self.bias_on_probs, ws=b["route_ws"], stream=stream)
+                       bias_on_probs=self.bias_on_probs, relu=self.relu, ws=b["route_ws"],
+                       stream=stream)
         mark("route")
-        if self.balance and "gamma" in self.balance:
+        E = self.E_router
+        if self.bypass is not None:
+            _lib.moe_permute_budgets(b["topk_idx"], E, b["bypass_caps"],
+                                     x if self.gather == "copy" else None,
+                                     expert_count=b["expert_count"],
+                                     expert_offset=b["expert_offset"], pair_row=b["pair_row"],
+                                     row_pair=b["row_pair"], x_perm=b["x_perm"], ws=b["perm_ws"],
+                                     stream=stream)
+        elif self.balance and "gamma" in self.balance:
             if self.expert_capacity is None or self._last_T != T:
                 c0 = _lib.moe_capacity(self.balance["cf_base"], T, k, E)
                 self.expert_capacity = torch.full((E,), min(c0, T) if c0 >= 0 else T,
@@ -234,16 +273,17 @@ class MoELayer:
             a, a_rows = b["x_perm"], None
         else:
             a, a_rows = x, b["row_pair"]
+        off = b["expert_offset"] if self.bypass is None else b["expert_offset"][:self.E + 1]
         if train:
-            _lib.moe_expert_gate_up_train(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
+            _lib.moe_expert_gate_up_train(a, off, T * k, self.w_gate, self.w_up,
                                           a_rows=a_rows, a_rows_div=k, hid=b["hid"], uv=b["uv"],
                                           ws=b["table_ws"], stream=stream)
         else:
-            _lib.moe_expert_gate_up(a, b["expert_offset"], T * k, self.w_gate, self.w_up,
+            _lib.moe_expert_gate_up(a, off, T * k, self.w_gate, self.w_up,
                                     a_rows=a_rows, a_rows_div=k, hid=b["hid"], ws=b["table_ws"],
                                     stream=stream)
         mark("gate_up")
-        _lib.moe_expert_down(b["hid"], b["expert_offset"], T * k, self.w_down, y=b["y_perm"],
+        _lib.moe_expert_down(b["hid"], off, T * k, self.w_down, y=b["y_perm"],
                              ws=b["table_ws"], stream=stream)
         mark("down")
         if self.shared is not None and not self.overlap_shared:
@@ -251,8 +291,14 @@ class MoELayer:
             mark("shared")
         if shared_done is not None:
             main.wait_event(shared_done)
-        _lib.moe_combine(b["y_perm"], b["pair_row"], b["topk_gate"], shared_y, out=b["out"],
-                         stream=stream)
+        if self.bypass is not None:
+            bp = self.bypass
+            _lib.moe_combine_bypass(b["y_perm"], b["pair_row"], b["topk_idx"], b["topk_gate"],
+                                    self.E, bp["n_zero"], bp["n_copy"], x, bp["const_rows"],
+                                    shared_y, out=b["out"], stream=stream)
+        else:
+            _lib.moe_combine(b["y_perm"], b["pair_row"], b["topk_gate"], shared_y, out=b["out"],
+                             stream=stream)
         mark("combine")
         if shared_done is None:
             self._stats(b, k, stream)
@@ -284,6 +330,8 @@ class MoELayer:
         returns the buffer dict with dx [T, d], dw_router, dlogit_bias (when the
         layer has a logit bias), dw_gate, dw_up, dw_down, and shared_dw_* (fp32),
         plus the intermediates dgate, dout and dlogits."""
+        if self.relu or self.bypass is not None:
+            raise NotImplementedError("the routing variants are forward-only")
         T = dy.shape[0]
         b = self._bufs[(T, dy.dtype, dy.device)]
         if "x" not in b:

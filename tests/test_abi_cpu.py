@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert L.moe_status_string(L.MOE_OK) == "ok"
     assert L.moe_status_string(L.MOE_EWORKSPACE) == "workspace too small"
     assert L.moe_status_string(99) == "unknown status"
@@ -89,8 +89,15 @@ def test_route_rejects():
     assert s == L.MOE_EINVAL
     s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 64, 33, None, None, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EUNSUPPORTED
-    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None, 4, FAKE, FAKE, FAKE, None, 0, None)
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None, 8, FAKE, FAKE, FAKE, None, 0, None)
     assert s == L.MOE_EINVAL and "flags" in _err()
+    # ReLU routing takes no selection bias, on the logits or on the probabilities
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, FAKE, L.MOE_ROUTE_RELU, FAKE, FAKE,
+                    FAKE, None, 0, None)
+    assert s == L.MOE_EINVAL and "ReLU" in _err()
+    s = C.moe_route(FAKE, FAKE, L.MOE_F32, 64, 128, 8, 2, None, None,
+                    L.MOE_ROUTE_RELU | L.MOE_ROUTE_BIAS_ON_PROBS, FAKE, FAKE, FAKE, None, 0, None)
+    assert s == L.MOE_EINVAL and "ReLU" in _err()
     # T = 0 is a no-op that enqueues nothing
     assert C.moe_route(FAKE, FAKE, L.MOE_F32, 0, 128, 8, 2, None, None, 0, FAKE, FAKE, FAKE,
                        None, 0, None) == L.MOE_OK
@@ -242,3 +249,26 @@ def test_balance_rejects():
                                 None) == L.MOE_EINVAL
     assert C.moe_balance_update(FAKE, 100, 2, 300, None, 0.1, FAKE, 0.5, 1.0, 1.0, None,
                                 None) == L.MOE_EUNSUPPORTED
+
+
+def test_combine_bypass_rejects():
+    f = C.moe_combine_bypass
+    args = lambda **kw: dict(dict(y=FAKE, ydt=L.MOE_BF16, pr=FAKE, idx=FAKE, g=FAKE, T=16, k=2,  # noqa: E731
+                                  d=64, ef=8, nz=1, nc=1, nk=2, x=FAKE, cr=FAKE, sh=None, out=FAKE,
+                                  odt=L.MOE_BF16), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["y"], a["ydt"], a["pr"], a["idx"], a["g"], a["T"], a["k"], a["d"], a["ef"],
+                 a["nz"], a["nc"], a["nk"], a["x"], a["cr"], a["sh"], a["out"], a["odt"], None)
+    assert call(k=0) == L.MOE_EINVAL
+    assert call(nz=-1) == L.MOE_EINVAL and "negative" in _err()
+    assert call(ef=250, nk=7) == L.MOE_EUNSUPPORTED
+    assert call(ydt=5) == L.MOE_EINVAL
+    assert call(idx=None) == L.MOE_EINVAL
+    assert call(x=None) == L.MOE_EINVAL and "x or const_rows" in _err()
+    assert call(cr=None) == L.MOE_EINVAL
+    assert call(T=0, idx=None, x=None) == L.MOE_OK
+    # no copy or constant experts: x and const_rows may be NULL (checked only)
+    assert call(T=0, nc=0, nk=0, x=None, cr=None) == L.MOE_OK
+
