@@ -477,11 +477,16 @@ def main():
             phases.setdefault(name, []).append(a.elapsed_time(b))
     phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
 
+    # routing structure over the FFN experts (the zero-computation experts of
+    # the bypass variant take no rows; ReLU routing leaves slots empty)
+    E_ffn = layer.E
     counts = res["expert_count"].cpu().numpy()
-    offs = res["expert_offset"].cpu().numpy()
+    offs = res["expert_offset"].cpu().numpy()[:E_ffn + 1]
     kept = offs[1:] - offs[:-1]
     R_kept = int(offs[-1])
     touched = int(np.sum(kept > 0))
+    used_slots = int((res["topk_idx"].cpu().numpy() >= 0).sum())
+    bypass_pairs = int(counts[E_ffn:].sum())
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
     esz = 2 if cfg.dtype == "bf16" else 4
 
@@ -567,9 +572,13 @@ def main():
                            "call (outside the timed region)",
         "phase_hbm_gbs": phase_gbs,
         "host_enqueue_ms_per_step": host_ms,
-        "routing": {"kept_pairs": R_kept, "dropped_pairs": T * k - R_kept,
+        "routing": {"kept_pairs": R_kept, "dropped_pairs": used_slots - bypass_pairs - R_kept,
                     "touched_experts": touched, "max_rows": int(kept.max()),
-                    "min_rows": int(kept.min()), "max_demand": int(counts.max())},
+                    "min_rows": int(kept.min()), "max_demand": int(counts[:E_ffn].max()),
+                    **({"experts_per_token": used_slots / T,
+                        "empty_slots": T * layer.k - used_slots} if args.variant == "relu"
+                       else {}),
+                    **({"bypass_pairs": bypass_pairs} if args.variant == "bypass" else {})},
     }
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or {"tiny_f32": 64, "mixtral_bf16": 4096,
