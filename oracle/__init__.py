@@ -55,9 +55,12 @@ from .moe_balance import (  # noqa: F401
     selection_bias_update,
 )
 from .moe_variants import (  # noqa: F401
+    backward_relu,
     bypass_kind,
     bypass_output,
     forward_bypass,
     forward_relu,
+    objective_relu,
+    relu_gate_logit_grad,
     relu_route,
 )

@@ -149,3 +149,80 @@ def forward_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_r
     y = y + bypass_output(x, idx, g, E_ffn, n_zero, n_copy, const_rows, tokens)
     f, P, loss = balance_stats(logits, disp["count"], k, alpha)
     return dict(logits=logits, topk_idx=idx, topk_gate=g, y=y, f=f, P=P, loss=loss, **disp)
+
+
+# ---------------------------------------------------------------------------
+# ReLU routing: backward
+# ---------------------------------------------------------------------------
+def relu_gate_logit_grad(logits, idx, dgate):
+    """dJ/dlogits [T, E] through ReLU gates.
+
+    A used slot's gate is the logit itself (positive), so dl_e = dgate for
+    the expert in that slot; an expert a token does not use gets nothing
+    (reading: the ReLU's derivative is taken as 0 at a zero logit, which is
+    never used; an expert with a positive logit that the k_max limit left out
+    is off, like an unselected expert of top-k routing).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    dg = _f64(dgate)
+    dl = np.zeros(np.asarray(logits).shape)
+    T, k = idx.shape
+    for t in range(T):
+        for j in range(k):
+            if idx[t, j] >= 0:
+                dl[t, idx[t, j]] += dg[t, j]
+    return dl
+
+
+def backward_relu(x, w_router, w_gate, w_up, w_down, k_max, dy, shared=(), logit_bias=None,
+                  cap=UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0, logits=None):
+    """dJ of the ReLU-routed layer, J = <dy, y> + c_bal loss + c_z zloss, in
+    reverse order of ``forward_relu``: the combine, the experts on their kept
+    rows, the ReLU gates, the auxiliary losses, the linear router.  Returns
+    the dict of ``moe_backward.backward``."""
+    from .moe_backward import (balance_logit_grad, gate_grad, router_linear_backward,
+                               swiglu_backward, z_loss_logit_grad)
+    x, dy = _f64(x), _f64(dy)
+    fw = forward_relu(x, w_router, w_gate, w_up, w_down, k_max, shared=shared,
+                      logit_bias=logit_bias, cap=cap, alpha=alpha, logits=logits)
+    idx, g, pr = fw["topk_idx"], fw["topk_gate"], fw["pair_row"]
+    T, d = x.shape
+    E = np.asarray(w_router).shape[0]
+    dgate = gate_grad(dy, x, idx, pr, w_gate, w_up, w_down)
+    dx = np.zeros((T, d))
+    dwg, dwu, dwd = (np.zeros(np.shape(w)) for w in (w_gate, w_up, w_down))
+    prk = np.asarray(pr, dtype=np.int64).reshape(T, k_max)
+    for e in range(E):
+        rows, slots = np.nonzero((idx == e) & (prk >= 0))
+        if rows.size == 0:
+            continue
+        dout = g[rows, slots][:, None] * dy[rows]
+        dxs, dwg[e], dwu[e], dwd[e] = swiglu_backward(x[rows], w_gate[e], w_up[e], w_down[e], dout)
+        np.add.at(dx, rows, dxs)
+    dshared = []
+    for (sg, su, sd) in shared:
+        dxs, a, b, c = swiglu_backward(x, sg, su, sd, dy)
+        dx += dxs
+        dshared.append((a, b, c))
+    lg = fw["logits"]
+    dlogits = relu_gate_logit_grad(lg, idx, dgate)
+    if c_bal:
+        dlogits = dlogits + c_bal * balance_logit_grad(lg, fw["count"], k_max, alpha)
+    if c_z:
+        dlogits = dlogits + c_z * z_loss_logit_grad(lg)
+    dxr, dwr, dlb = router_linear_backward(x, w_router, dlogits)
+    dx += dxr
+    return dict(dx=dx, dw_router=dwr, dlogit_bias=dlb, dw_gate=dwg, dw_up=dwu, dw_down=dwd,
+                dshared=dshared, dgate=dgate, dlogits=dlogits, fwd=fw)
+
+
+def objective_relu(x, w_router, w_gate, w_up, w_down, k_max, dy, shared=(), logit_bias=None,
+                   cap=UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0):
+    """J = sum(dy * y) + c_bal * loss + c_z * zloss of the ReLU-routed layer
+    from its forward alone, and the selection it used."""
+    from .moe_oracle import router_z_loss
+    fw = forward_relu(x, w_router, w_gate, w_up, w_down, k_max, shared=shared,
+                      logit_bias=logit_bias, cap=cap, alpha=alpha)
+    J = (float(np.sum(_f64(dy) * fw["y"])) + c_bal * fw["loss"] +
+         c_z * router_z_loss(fw["logits"]))
+    return J, fw["topk_idx"]

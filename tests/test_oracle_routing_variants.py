@@ -9,6 +9,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import moe_variants as mv
@@ -258,3 +259,116 @@ def test_mutation_is_caught(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"no pin caught: {name}"
+
+
+# ------------------------------------------------------ ReLU routing backward
+RELU_BWD_CASES = [
+    # T, d, E, h, k_max, cap, n_shared, c_bal, c_z, seed
+    (7, 5, 4, 3, 4, None, 0, 0.0, 0.0, 21),
+    (9, 4, 6, 3, 2, 3, 1, 1.0, 0.0, 22),
+    (8, 6, 5, 4, 3, 2, 0, 0.5, 0.3, 23),
+]
+
+
+def _relu_setup(case):
+    T, d, E, h, k_max, cap, ns, cb, cz, seed = case
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    wg = rng.standard_normal((E, h, d)) / math.sqrt(d)
+    wu = rng.standard_normal((E, h, d)) / math.sqrt(d)
+    wd = rng.standard_normal((E, d, h)) / math.sqrt(h)
+    shared = [(rng.standard_normal((4, d)), rng.standard_normal((4, d)),
+               rng.standard_normal((d, 4))) for _ in range(ns)]
+    lb = 0.5 * rng.standard_normal(E)
+    dy = rng.standard_normal((T, d))
+    params = dict(x=x, w_router=wr, w_gate=wg, w_up=wu, w_down=wd, logit_bias=lb)
+    kw = dict(shared=shared, cap=cap, alpha=0.01, c_bal=cb, c_z=cz)
+    return params, k_max, dy, kw
+
+
+def _relu_J(params, k_max, dy, kw):
+    p = params
+    return oracle.objective_relu(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], k_max,
+                                 dy, logit_bias=p["logit_bias"], **kw)
+
+
+@pytest.mark.parametrize("case", RELU_BWD_CASES)
+def test_relu_backward_finite_differences(case):
+    """Every gradient of the ReLU-routed layer equals the central difference
+    of its forward objective along random directions (selection fixed)."""
+    params, k_max, dy, kw = _relu_setup(case)
+    p = params
+    g = oracle.backward_relu(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], k_max,
+                             dy, logit_bias=p["logit_bias"], **kw)
+    _, idx0 = _relu_J(params, k_max, dy, kw)
+    assert np.any(idx0 < 0) or case[4] < case[2]  # the case exercises empty or left-out slots
+    rng = np.random.default_rng(5)
+    eps = 1e-6
+    names = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up",
+             "w_down": "dw_down", "logit_bias": "dlogit_bias"}
+    for name, gname in names.items():
+        for _ in range(2):
+            V = rng.standard_normal(params[name].shape)
+            Jp, ip = _relu_J(dict(params, **{name: params[name] + eps * V}), k_max, dy, kw)
+            Jm, im = _relu_J(dict(params, **{name: params[name] - eps * V}), k_max, dy, kw)
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "selection moved"
+            ana = float(np.sum(g[gname] * V))
+            assert abs((Jp - Jm) / (2 * eps) - ana) <= 1e-6 * (1.0 + abs(ana)), (name, ana)
+
+
+def test_relu_backward_autograd():
+    """The ReLU-routed layer written in PyTorch as a sum over all experts of
+    relu(l) E(x) (k_max = E, no budget), differentiated by autograd."""
+    F = torch.nn.functional
+    params, k_max, dy, kw = _relu_setup((6, 4, 5, 3, 5, None, 0, 0.0, 0.0, 31))
+    p = params
+    g = oracle.backward_relu(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], k_max,
+                             dy, logit_bias=p["logit_bias"], **kw)
+    tp = {n: torch.tensor(v, requires_grad=True) for n, v in params.items()}
+    logits = tp["x"] @ tp["w_router"].T + tp["logit_bias"]
+    y = torch.zeros_like(tp["x"])
+    for e in range(5):
+        out = F.linear(F.silu(F.linear(tp["x"], tp["w_gate"][e])) * F.linear(tp["x"], tp["w_up"][e]),
+                       tp["w_down"][e])
+        y = y + torch.relu(logits[:, e:e + 1]) * out
+    torch.sum(torch.as_tensor(dy) * y).backward()
+    for n, gn in (("x", "dx"), ("w_router", "dw_router"), ("logit_bias", "dlogit_bias"),
+                  ("w_gate", "dw_gate"), ("w_down", "dw_down")):
+        np.testing.assert_allclose(g[gn], tp[n].grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_relu_gate_logit_grad_worked():
+    """Used slots pass dgate to their expert's logit; empty slots and unused
+    experts get nothing."""
+    idx = np.array([[2, 0, -1], [-1, -1, -1]])
+    dg = np.array([[0.5, -2.0, 7.0], [1.0, 1.0, 1.0]])
+    dl = oracle.relu_gate_logit_grad(np.zeros((2, 4)), idx, dg)
+    assert dl.tolist() == [[-2.0, 0.0, 0.5, 0.0], [0.0, 0.0, 0.0, 0.0]]
+
+
+def _relu_grad_through_softmax(logits, idx, dgate):
+    from oracle.moe_backward import gate_logit_grad
+    idx = np.asarray(idx, dtype=np.int64)
+    safe = np.where(idx >= 0, idx, np.argmax(np.asarray(logits), axis=1)[:, None])
+    return gate_logit_grad(logits, safe, np.where(idx >= 0, dgate, 0.0))
+
+
+def _relu_grad_counts_empty_slots(logits, idx, dgate):
+    dl = mv.__dict__["_orig_relu_gate_logit_grad"](logits, idx, dgate)
+    dl[:, 0] += np.sum(np.where(np.asarray(idx) < 0, 1.0, 0.0), axis=1)
+    return dl
+
+
+MUTATIONS["relu backward through a softmax"] = ("relu_gate_logit_grad", _relu_grad_through_softmax)
+MUTATIONS["relu backward feeds empty slots"] = ("relu_gate_logit_grad",
+                                                _relu_grad_counts_empty_slots)
+PIN_TESTS += [lambda: test_relu_backward_finite_differences(RELU_BWD_CASES[1]),
+              lambda: test_relu_backward_finite_differences(RELU_BWD_CASES[2]),
+              test_relu_gate_logit_grad_worked]
+
+
+@pytest.mark.parametrize("name", ["relu backward through a softmax",
+                                  "relu backward feeds empty slots"])
+def test_backward_mutation_is_caught(name, monkeypatch):
+    test_mutation_is_caught(name, monkeypatch)
