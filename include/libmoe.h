@@ -457,11 +457,16 @@ moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm,
  * pre-drop counts of moe_permute).  Sources: "The gating network" (softmax
  * over the selected set), Zen MoDE "Auxiliary Load Balancing Loss", Zen-Max
  * "MoE-Specific Training Stability".  expert_count may be NULL when
- * coef_balance == 0. */
+ * coef_balance == 0.
+ * flags: 0, or MOE_ROUTE_RELU for the ReLU-routed forward (its gate is the
+ * logit on a used slot, so the gate term becomes dl[t,e] = dgate_tj for
+ * e = topk_idx[t,j] >= 0; empty slots (-1) contribute nothing; the balance
+ * and z-loss terms are unchanged, k being the most experts per token). */
 moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
                                 const float* topk_gate, const float* dgate,
-                                const int32_t* expert_count, int64_t T, int E, int k, float alpha,
-                                float coef_balance, float coef_z, float* dlogits, void* stream);
+                                const int32_t* expert_count, int64_t T, int E, int k,
+                                unsigned flags, float alpha, float coef_balance, float coef_z,
+                                float* dlogits, void* stream);
 
 /* moe_router_backward: gradients of logits = x w_router^T + logit_bias:
  *   dw_router[e, i] = sum_t dlogits[t, e] x[t, i]       [E, d] fp32

@@ -74,7 +74,7 @@ _SIGS = {
     "moe_expert_swiglu_backward": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
                                         _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _p, _i64, _i, _i, _p, _p, _p]),
-    "moe_route_backward": (_i, [_p, _p, _p, _p, _p, _i64, _i, _i, _f, _f, _f, _p, _p]),
+    "moe_route_backward": (_i, [_p, _p, _p, _p, _p, _i64, _i, _i, _u, _f, _f, _f, _p, _p]),
     "moe_router_backward_workspace": (_sz, [_i64, _i, _i]),
     "moe_router_backward": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
     "moe_probe_mfma_bf16": (_i, [_p, _i, _i, _p, _p]),
@@ -451,15 +451,17 @@ def moe_combine_backward(dy, y_perm, pair_row, k, topk_gate=None, *, dgate=None,
 
 
 def moe_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, alpha=0.01,
-                       coef_balance=0.0, coef_z=0.0, *, dlogits=None, stream=None):
-    """dJ/dlogits through the renormalised gates, the balance loss and the z-loss."""
+                       coef_balance=0.0, coef_z=0.0, *, relu=False, dlogits=None, stream=None):
+    """dJ/dlogits through the renormalised gates (or, with ``relu``, the ReLU
+    gates), the balance loss and the z-loss."""
     T, E = logits.shape
     k = topk_idx.shape[1]
     if dlogits is None:
         dlogits = torch.empty((T, E), dtype=torch.float32, device=logits.device)
     _contig(logits, topk_idx, topk_gate, dgate, expert_count, dlogits)
     _check(_L.moe_route_backward(_ptr(logits), _ptr(topk_idx), _ptr(topk_gate), _ptr(dgate),
-                                 _ptr(expert_count), T, E, k, float(alpha), float(coef_balance),
+                                 _ptr(expert_count), T, E, k, MOE_ROUTE_RELU if relu else 0,
+                                 float(alpha), float(coef_balance),
                                  float(coef_z), _ptr(dlogits), _stream(stream)))
     return dlogits
 

@@ -147,8 +147,8 @@ template <int KK>  // experts per lane: 64 KK >= E
 __global__ __launch_bounds__(256) void route_backward_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const float* __restrict__ dgate,
-    const int32_t* __restrict__ count, int64_t T, int E, int k, float alpha, float c_bal,
-    float c_z, float* __restrict__ dl) {
+    const int32_t* __restrict__ count, int64_t T, int E, int k, int relu, float alpha,
+    float c_bal, float c_z, float* __restrict__ dl) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (t >= T) return;
@@ -188,13 +188,15 @@ __global__ __launch_bounds__(256) void route_backward_kernel(
   const float* gr = gate + t * k;
   const float* dgr = dgate + t * k;
   float inner = 0.0f;
-  for (int j = 0; j < k; ++j) inner = fmaf(gr[j], dgr[j], inner);
+  for (int j = 0; !relu && j < k; ++j) inner = fmaf(gr[j], dgr[j], inner);
   float out[KK];
 #pragma unroll
   for (int u = 0; u < KK; ++u) out[u] = cb * v[u] * (f[u] - fp) + cz * v[u];
   for (int j = 0; j < k; ++j) {
     const int e = ir[j];
-    const float gt = gr[j] * (dgr[j] - inner);
+    // ReLU gate = logit on a used slot (an empty slot holds -1 and matches
+    // no expert); softmax gate: g_j (dg_j - sum_i g_i dg_i)
+    const float gt = relu ? dgr[j] : gr[j] * (dgr[j] - inner);
 #pragma unroll
     for (int u = 0; u < KK; ++u)
       if (e == lane + u * kWave) out[u] += gt;
@@ -374,13 +376,13 @@ hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, 
 }
 
 hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
-                                 const float* dgate, const int32_t* count, int64_t T, int E, int k,
+                                 const float* dgate, const int32_t* count, int64_t T, int E, int k, bool relu,
                                  float alpha, float c_bal, float c_z, float* dlogits,
                                  hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((T + 3) / 4);
 #define MOE_RB(KK)                                                                          \
   route_backward_kernel<KK><<<grid, 256, 0, stream>>>(logits, idx, gate, dgate, count, T, E, k, \
-                                                      alpha, c_bal, c_z, dlogits)
+                                                      relu ? 1 : 0, alpha, c_bal, c_z, dlogits)
   if (E <= 64) MOE_RB(1);
   else if (E <= 128) MOE_RB(2);
   else MOE_RB(4);

@@ -110,7 +110,7 @@ hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, 
                                    const int32_t* pair_row, const float* gate, int64_t T, int k,
                                    int d, float* dgate, void* dout, hipStream_t stream);
 hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
-                                 const float* dgate, const int32_t* count, int64_t T, int E, int k,
+                                 const float* dgate, const int32_t* count, int64_t T, int E, int k, bool relu,
                                  float alpha, float c_bal, float c_z, float* dlogits,
                                  hipStream_t stream);
 size_t router_backward_workspace_bytes(int64_t T, int d, int E);

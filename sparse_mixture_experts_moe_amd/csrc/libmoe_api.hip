@@ -583,8 +583,10 @@ moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm,
 
 moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
                                 const float* topk_gate, const float* dgate,
-                                const int32_t* expert_count, int64_t T, int E, int k, float alpha,
-                                float coef_balance, float coef_z, float* dlogits, void* stream) {
+                                const int32_t* expert_count, int64_t T, int E, int k,
+                                unsigned flags, float alpha, float coef_balance, float coef_z,
+                                float* dlogits, void* stream) {
+  if (flags & ~MOE_ROUTE_RELU) return fail(MOE_EINVAL, "moe_route_backward: unknown flags 0x%x", flags);
   if (T < 0) return fail(MOE_EINVAL, "moe_route_backward: T < 0");
   if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_route_backward: need 1 <= k <= E");
   if (E > moe::kMaxExperts)
@@ -594,8 +596,8 @@ moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
       (coef_balance != 0.0f && !expert_count))
     return fail(MOE_EINVAL, "moe_route_backward: NULL pointer");
   return hip_status(moe::launch_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, T,
-                                               E, k, alpha, coef_balance, coef_z, dlogits,
-                                               as_stream(stream)),
+                                               E, k, (flags & MOE_ROUTE_RELU) != 0, alpha,
+                                               coef_balance, coef_z, dlogits, as_stream(stream)),
                     "moe_route_backward");
 }
 

@@ -52,7 +52,8 @@ class MoELayer:
         zero-computation experts after the FFN experts: a dict with
         ``n_zero``, ``n_copy`` and ``const_rows`` ([n_const, d] in the dtype
         of x, or None); w_router then has E + n_zero + n_copy + n_const rows.
-        Both variants are forward-only and take no balance updates."""
+        Neither variant takes balance updates; the zero-computation experts
+        are forward-only."""
         if gather not in ("fused", "copy"):
             raise ValueError("gather must be 'fused' or 'copy'")
         self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
@@ -330,8 +331,8 @@ class MoELayer:
         returns the buffer dict with dx [T, d], dw_router, dlogit_bias (when the
         layer has a logit bias), dw_gate, dw_up, dw_down, and shared_dw_* (fp32),
         plus the intermediates dgate, dout and dlogits."""
-        if self.relu or self.bypass is not None:
-            raise NotImplementedError("the routing variants are forward-only")
+        if self.bypass is not None:
+            raise NotImplementedError("the zero-computation experts are forward-only")
         T = dy.shape[0]
         b = self._bufs[(T, dy.dtype, dy.device)]
         if "x" not in b:
@@ -344,7 +345,7 @@ class MoELayer:
         mark("combine_bwd")
         _lib.moe_route_backward(b["logits"], b["topk_idx"], b["topk_gate"], b["dgate"],
                                 b["expert_count"], self.alpha, coef_balance, coef_z,
-                                dlogits=b["dlogits"], stream=stream)
+                                relu=self.relu, dlogits=b["dlogits"], stream=stream)
         mark("route_bwd")
         _lib.moe_expert_swiglu_backward(
             x, b["expert_offset"], T * k, b["dout"], b["uv"], b["hid"], self.w_gate, self.w_up,

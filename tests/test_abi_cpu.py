@@ -208,12 +208,18 @@ def test_backward_rejects():
     assert C.moe_combine_backward(FAKE, 7, FAKE, BF, FAKE, FAKE, 10, 2, 64, FAKE, None, None) == L.MOE_EINVAL
     assert C.moe_combine_backward(None, BF, None, BF, None, None, 0, 2, 64, None, None, None) == L.MOE_OK
     # route backward: k <= E, counts needed with the balance term
-    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4, 5, 0.01, 0.0, 0.0, FAKE,
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 4, 5, 0, 0.01, 0.0, 0.0, FAKE,
                                 None) == L.MOE_EINVAL
-    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, None, 10, 8, 2, 0.01, 1.0, 0.0, FAKE,
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, None, 10, 8, 2, 0, 0.01, 1.0, 0.0, FAKE,
                                 None) == L.MOE_EINVAL
-    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 300, 2, 0.01, 1.0, 0.0, FAKE,
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 300, 2, 0, 0.01, 1.0, 0.0, FAKE,
                                 None) == L.MOE_EUNSUPPORTED
+    # the only flag is MOE_ROUTE_RELU
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 8, 2, L.MOE_ROUTE_LOGITS_IN, 0.01,
+                                1.0, 0.0, FAKE, None) == L.MOE_EINVAL
+    assert "flags" in _err()
+    assert C.moe_route_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2, L.MOE_ROUTE_RELU, 0.01,
+                                1.0, 0.0, FAKE, None) == L.MOE_OK
     # router backward: workspace only with dw_router
     need = L.moe_router_backward_workspace(4096, 1024, 8)
     assert need > 0
