@@ -194,9 +194,11 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
                       f"batch, {passes} passes (float64 NumPy, {dt:.1f} s)"}
 
 
-def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max_passes=5):
+def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max_passes=5,
+                          relu=None):
     """The backward oracle as it stands (its forward included) on the first
-    n_tok tokens as a batch of their own, repeated until min_seconds."""
+    n_tok tokens as a batch of their own, repeated until min_seconds.
+    ``relu`` = (k_max, logit_bias) runs the ReLU-routed layer's oracle."""
     import oracle
     from moe_inputs import as_f32
     try:
@@ -216,14 +218,20 @@ def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle.backward(x, wr, wg, wu, wd, cfg.k, dyf, shared=shared,
-                        logit_bias=inp["logit_bias"], select_bias=inp["select_bias"], cap=cap,
-                        alpha=cfg.alpha, c_bal=c_bal, c_z=c_z)
+        if relu is None:
+            oracle.backward(x, wr, wg, wu, wd, cfg.k, dyf, shared=shared,
+                            logit_bias=inp["logit_bias"], select_bias=inp["select_bias"], cap=cap,
+                            alpha=cfg.alpha, c_bal=c_bal, c_z=c_z)
+        else:
+            oracle.backward_relu(x, wr, wg, wu, wd, relu[0], dyf, shared=shared,
+                                 logit_bias=relu[1], cap=cap, alpha=cfg.alpha, c_bal=c_bal,
+                                 c_z=c_z)
         dt += time.perf_counter() - t0
         passes += 1
     return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name} as one batch, forward and "
+            "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name}"
+                      f"{'' if relu is None else ' (relu variant)'} as one batch, forward and "
                       f"backward, {passes} passes (float64 NumPy, {dt:.1f} s)"}
 
 
@@ -243,6 +251,17 @@ def main_backward(args):
     inp = generate(cfg)
     dy_h = generate_dy(cfg)
     layer = layer_from_inputs(inp, args.gather)
+    relu = None
+    if args.variant == "bypass":
+        print(json.dumps({"error": "the zero-computation experts are forward-only"}), flush=True)
+        sys.exit(2)
+    if args.variant == "relu":
+        from moe_inputs import relu_logit_offset
+        from sparse_mixture_experts_moe_amd.workload import relu_layer_from_inputs, relu_logit_bias
+        off = relu_logit_offset(cfg, cfg.k)
+        k_max = min(cfg.E, RELU_K_MUL * cfg.k)
+        layer = relu_layer_from_inputs(inp, k_max, off, args.gather)
+        relu = (k_max, relu_logit_bias(inp, off))
     layer.overlap_shared = not args.serial_shared
     x = to_device(inp["x"])
     dy = to_device(dy_h)
@@ -331,7 +350,8 @@ def main_backward(args):
                 "the workload's shape)",
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
-                   "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)"},
+                   "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)",
+                   **({"variant": {"kind": "relu", "k_max": relu[0]}} if relu else {})},
         "roofline": roof,
         "measured_ceilings": ceil,
         "step_tflops": step_flops / (ms * 1e-3) / 1e12,
@@ -343,7 +363,7 @@ def main_backward(args):
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or {"mixtral_bf16": 1024, "finegrained_shared_bf16": 2048,
                                     "capacity_balance_bf16": 2048, "decode_bf16": 64}[cfg.name]
-        out["cpu_baseline"] = cpu_baseline_backward(inp, dy_h, cfg, n_tok, c_bal, c_z)
+        out["cpu_baseline"] = cpu_baseline_backward(inp, dy_h, cfg, n_tok, c_bal, c_z, relu=relu)
     print(json.dumps(out), flush=True)
 
 
