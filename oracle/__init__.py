@@ -55,11 +55,14 @@ from .moe_balance import (  # noqa: F401
     selection_bias_update,
 )
 from .moe_variants import (  # noqa: F401
+    backward_bypass,
     backward_relu,
+    bypass_gate_grad,
     bypass_kind,
     bypass_output,
     forward_bypass,
     forward_relu,
+    objective_bypass,
     objective_relu,
     relu_gate_logit_grad,
     relu_route,

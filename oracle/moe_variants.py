@@ -226,3 +226,92 @@ def objective_relu(x, w_router, w_gate, w_up, w_down, k_max, dy, shared=(), logi
     J = (float(np.sum(_f64(dy) * fw["y"])) + c_bal * fw["loss"] +
          c_z * router_z_loss(fw["logits"]))
     return J, fw["topk_idx"]
+
+
+# ---------------------------------------------------------------------------
+# Zero-computation experts: backward
+# ---------------------------------------------------------------------------
+def bypass_gate_grad(dy, x, idx, E_ffn, n_zero, n_copy, const_rows):
+    """dJ/d(gate) [T, k] of the zero-computation slots (0 on FFN slots):
+    <dy_t, x_t> for a copy expert, <dy_t, v_c> for constant expert c, 0 for
+    a zero expert (y = sum_j g_j out_j, so dJ/dg_j = <dy, out_j>)."""
+    dy, x = _f64(dy), _f64(x)
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    const_rows = _f64(const_rows).reshape(-1, x.shape[1])
+    dg = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            kind, c = bypass_kind(int(idx[t, j]), E_ffn, n_zero, n_copy, const_rows.shape[0])
+            if kind == "copy":
+                dg[t, j] = float(dy[t] @ x[t])
+            elif kind == "const":
+                dg[t, j] = float(dy[t] @ const_rows[c])
+    return dg
+
+
+def backward_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_rows, dy,
+                    shared=(), logit_bias=None, cap=UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0,
+                    logits=None):
+    """dJ of the layer with zero-computation experts, in reverse order of
+    ``forward_bypass``.  Besides the plain layer's gradients: a copy slot
+    passes g dy_t to dx_t, constant expert c collects dconst[c] = sum over
+    its slots of g dy_t, and every slot's gate gradient enters the softmax
+    over all router experts.  Returns the dict of ``moe_backward.backward``
+    plus ``dconst`` [n_const, d]."""
+    from .moe_backward import (balance_logit_grad, gate_grad, gate_logit_grad,
+                               router_linear_backward, swiglu_backward, z_loss_logit_grad)
+    x, dy = _f64(x), _f64(dy)
+    fw = forward_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_rows,
+                        shared=shared, logit_bias=logit_bias, cap=cap, alpha=alpha, logits=logits)
+    idx, g, pr = fw["topk_idx"], fw["topk_gate"], fw["pair_row"]
+    T, d = x.shape
+    E_ffn = np.asarray(w_gate).shape[0]
+    cr = _f64(const_rows).reshape(-1, d)
+    dgate = gate_grad(dy, x, idx, pr, w_gate, w_up, w_down)  # FFN slots (pair_row >= 0)
+    dgate = dgate + bypass_gate_grad(dy, x, idx, E_ffn, n_zero, n_copy, cr)
+    dx = np.zeros((T, d))
+    dwg, dwu, dwd = (np.zeros(np.shape(w)) for w in (w_gate, w_up, w_down))
+    prk = np.asarray(pr, dtype=np.int64).reshape(T, k)
+    for e in range(E_ffn):
+        rows, slots = np.nonzero((idx == e) & (prk >= 0))
+        if rows.size == 0:
+            continue
+        dout = g[rows, slots][:, None] * dy[rows]
+        dxs, dwg[e], dwu[e], dwd[e] = swiglu_backward(x[rows], w_gate[e], w_up[e], w_down[e], dout)
+        np.add.at(dx, rows, dxs)
+    dconst = np.zeros_like(cr)
+    for t in range(T):
+        for j in range(k):
+            kind, c = bypass_kind(int(idx[t, j]), E_ffn, n_zero, n_copy, cr.shape[0])
+            if kind == "copy":
+                dx[t] += g[t, j] * dy[t]
+            elif kind == "const":
+                dconst[c] += g[t, j] * dy[t]
+    dshared = []
+    for (sg, su, sd) in shared:
+        dxs, a, b, c = swiglu_backward(x, sg, su, sd, dy)
+        dx += dxs
+        dshared.append((a, b, c))
+    lg = fw["logits"]
+    dlogits = gate_logit_grad(lg, idx, dgate)
+    if c_bal:
+        dlogits = dlogits + c_bal * balance_logit_grad(lg, fw["count"], k, alpha)
+    if c_z:
+        dlogits = dlogits + c_z * z_loss_logit_grad(lg)
+    dxr, dwr, dlb = router_linear_backward(x, w_router, dlogits)
+    dx += dxr
+    return dict(dx=dx, dw_router=dwr, dlogit_bias=dlb, dw_gate=dwg, dw_up=dwu, dw_down=dwd,
+                dconst=dconst, dshared=dshared, dgate=dgate, dlogits=dlogits, fwd=fw)
+
+
+def objective_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_rows, dy,
+                     shared=(), logit_bias=None, cap=UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0):
+    """J = sum(dy * y) + c_bal * loss + c_z * zloss of the layer with
+    zero-computation experts, and the selection it used."""
+    from .moe_oracle import router_z_loss
+    fw = forward_bypass(x, w_router, w_gate, w_up, w_down, k, n_zero, n_copy, const_rows,
+                        shared=shared, logit_bias=logit_bias, cap=cap, alpha=alpha)
+    J = (float(np.sum(_f64(dy) * fw["y"])) + c_bal * fw["loss"] +
+         c_z * router_z_loss(fw["logits"]))
+    return J, fw["topk_idx"]

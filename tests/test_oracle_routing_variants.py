@@ -372,3 +372,109 @@ PIN_TESTS += [lambda: test_relu_backward_finite_differences(RELU_BWD_CASES[1]),
                                   "relu backward feeds empty slots"])
 def test_backward_mutation_is_caught(name, monkeypatch):
     test_mutation_is_caught(name, monkeypatch)
+
+
+# ------------------------------------------- zero-computation experts backward
+BYPASS_BWD_CASES = [
+    # T, d, E_ffn, h, k, n_zero, n_copy, n_const, cap, n_shared, c_bal, c_z, seed
+    (7, 5, 4, 3, 2, 1, 1, 2, None, 0, 0.0, 0.0, 41),
+    (9, 4, 3, 3, 3, 2, 1, 1, 2, 1, 1.0, 0.0, 42),
+    (8, 6, 2, 4, 2, 0, 2, 2, 3, 0, 0.5, 0.3, 43),
+]
+
+
+def _bypass_setup(case):
+    T, d, E_ffn, h, k, nz, nc, nk, cap, ns, cb, cz, seed = case
+    rng = np.random.default_rng(seed)
+    E = E_ffn + nz + nc + nk
+    params = dict(x=rng.standard_normal((T, d)), w_router=rng.standard_normal((E, d)),
+                  w_gate=rng.standard_normal((E_ffn, h, d)) / math.sqrt(d),
+                  w_up=rng.standard_normal((E_ffn, h, d)) / math.sqrt(d),
+                  w_down=rng.standard_normal((E_ffn, d, h)) / math.sqrt(h),
+                  const_rows=rng.standard_normal((nk, d)))
+    shared = [(rng.standard_normal((4, d)), rng.standard_normal((4, d)),
+               rng.standard_normal((d, 4))) for _ in range(ns)]
+    dy = rng.standard_normal((T, d))
+    kw = dict(shared=shared, cap=cap, alpha=0.01, c_bal=cb, c_z=cz)
+    return params, (k, nz, nc), dy, kw
+
+
+def _bypass_J(params, kk, dy, kw):
+    p = params
+    k, nz, nc = kk
+    return oracle.objective_bypass(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], k,
+                                   nz, nc, p["const_rows"], dy, **kw)
+
+
+@pytest.mark.parametrize("case", BYPASS_BWD_CASES)
+def test_bypass_backward_finite_differences(case):
+    """Every gradient of the layer with zero-computation experts, the
+    constant rows' included, equals the central difference of its forward
+    objective along random directions (selection fixed)."""
+    params, kk, dy, kw = _bypass_setup(case)
+    p = params
+    g = oracle.backward_bypass(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], kk[0],
+                               kk[1], kk[2], p["const_rows"], dy, **kw)
+    _, idx0 = _bypass_J(params, kk, dy, kw)
+    assert np.any(idx0 >= p["w_gate"].shape[0])  # some slots reach zero-computation experts
+    rng = np.random.default_rng(6)
+    eps = 1e-6
+    names = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up",
+             "w_down": "dw_down", "const_rows": "dconst"}
+    for name, gname in names.items():
+        for _ in range(2):
+            V = rng.standard_normal(params[name].shape)
+            Jp, ip = _bypass_J(dict(params, **{name: params[name] + eps * V}), kk, dy, kw)
+            Jm, im = _bypass_J(dict(params, **{name: params[name] - eps * V}), kk, dy, kw)
+            assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "selection moved"
+            ana = float(np.sum(g[gname] * V))
+            assert abs((Jp - Jm) / (2 * eps) - ana) <= 1e-6 * (1.0 + abs(ana)), (name, ana)
+
+
+def test_bypass_backward_autograd():
+    """The layer written in PyTorch per token from the definitions (copy =
+    x, constant = v_c, zero = 0; softmax over the k selected), with the
+    selection fixed, differentiated by autograd."""
+    params, kk, dy, kw = _bypass_setup(BYPASS_BWD_CASES[0])
+    k, nz, nc = kk
+    p = params
+    g = oracle.backward_bypass(p["x"], p["w_router"], p["w_gate"], p["w_up"], p["w_down"], k, nz,
+                               nc, p["const_rows"], dy, **kw)
+    idx = g["fwd"]["topk_idx"]
+    F = torch.nn.functional
+    tp = {n: torch.tensor(v, requires_grad=True) for n, v in params.items()}
+    E_ffn = p["w_gate"].shape[0]
+    logits = tp["x"] @ tp["w_router"].T
+    J = 0.0
+    for t in range(p["x"].shape[0]):
+        sel = torch.as_tensor(idx[t].astype(np.int64))
+        gt = torch.softmax(logits[t, sel], dim=0)
+        for j, e in enumerate(idx[t]):
+            if e < E_ffn:
+                out = F.linear(F.silu(F.linear(tp["x"][t], tp["w_gate"][e])) *
+                               F.linear(tp["x"][t], tp["w_up"][e]), tp["w_down"][e])
+            elif e < E_ffn + nz:
+                continue
+            elif e < E_ffn + nz + nc:
+                out = tp["x"][t]
+            else:
+                out = tp["const_rows"][e - E_ffn - nz - nc]
+            J = J + gt[j] * torch.dot(torch.as_tensor(dy[t]), out)
+    J.backward()
+    for n, gn in (("x", "dx"), ("w_router", "dw_router"), ("const_rows", "dconst"),
+                  ("w_gate", "dw_gate"), ("w_down", "dw_down")):
+        np.testing.assert_allclose(g[gn], tp[n].grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _bypass_gate_grad_no_copy(dy, x, idx, E_ffn, n_zero, n_copy, const_rows):
+    return mv.__dict__["_orig_bypass_gate_grad"](dy, x, idx, E_ffn, n_zero + n_copy, 0, const_rows)
+
+
+MUTATIONS["bypass backward drops the copy gate gradient"] = ("bypass_gate_grad",
+                                                             _bypass_gate_grad_no_copy)
+PIN_TESTS += [lambda: test_bypass_backward_finite_differences(BYPASS_BWD_CASES[0]),
+              test_bypass_backward_autograd]
+
+
+def test_bypass_backward_mutation_is_caught(monkeypatch):
+    test_mutation_is_caught("bypass backward drops the copy gate gradient", monkeypatch)
