@@ -462,6 +462,34 @@ moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm,
  * logit on a used slot, so the gate term becomes dl[t,e] = dgate_tj for
  * e = topk_idx[t,j] >= 0; empty slots (-1) contribute nothing; the balance
  * and z-loss terms are unchanged, k being the most experts per token). */
+/* moe_combine_backward_bypass: moe_combine_backward for the layer with
+ * zero-computation experts (the forward's moe_combine_bypass; same router
+ * numbering).  dgate[t,j] = <dy[t], out_j> with out_j the slot's output row:
+ * y_perm[pair_row] for an FFN slot that ran, x[t] for a copy expert, the
+ * constant row for a constant expert, nothing (dgate 0) for a zero expert,
+ * a dropped pair or an id past the last; dout (optional) as
+ * moe_combine_backward, for the FFN slots that ran.  x and const_rows in
+ * y_dt.  Source: Zen MoDE, section "Router" (zero-computation experts). */
+moe_status_t moe_combine_backward_bypass(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+                                         const int32_t* pair_row, const int32_t* topk_idx,
+                                         const float* topk_gate, int64_t T, int k, int d,
+                                         int E_ffn, int n_zero, int n_copy, int n_const,
+                                         const void* x, const void* const_rows, float* dgate,
+                                         void* dout, void* stream);
+
+/* moe_bypass_backward: the rest of the zero-computation experts' backward,
+ *   dx_acc[t,:] += (sum of topk_gate[t,j] over t's copy slots) * dy[t,:]
+ *   dconst[c,:]  = sum over the slots on constant expert c of topk_gate * dy
+ * dx_acc [T,d] fp32 (accumulated; may be NULL when n_copy == 0), dconst
+ * [n_const,d] fp32 (written; may be NULL when n_const == 0), summed over
+ * fixed token ranges added in range order (deterministic).  Workspace:
+ * moe_bypass_backward_workspace(T, d, n_const) bytes. */
+size_t moe_bypass_backward_workspace(int64_t T, int d, int n_const);
+moe_status_t moe_bypass_backward(const void* dy, int dy_dt, const int32_t* topk_idx,
+                                 const float* topk_gate, int64_t T, int k, int d, int E_ffn,
+                                 int n_zero, int n_copy, int n_const, float* dx_acc, float* dconst,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
                                 const float* topk_gate, const float* dgate,
                                 const int32_t* expert_count, int64_t T, int E, int k,

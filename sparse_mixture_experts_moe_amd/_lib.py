@@ -74,6 +74,11 @@ _SIGS = {
     "moe_expert_swiglu_backward": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
                                         _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_combine_backward": (_i, [_p, _i, _p, _i, _p, _p, _i64, _i, _i, _p, _p, _p]),
+    "moe_combine_backward_bypass": (_i, [_p, _i, _p, _i, _p, _p, _p, _i64, _i, _i, _i, _i, _i, _i,
+                                         _p, _p, _p, _p, _p]),
+    "moe_bypass_backward_workspace": (_sz, [_i64, _i, _i]),
+    "moe_bypass_backward": (_i, [_p, _i, _p, _p, _i64, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz,
+                                 _p]),
     "moe_route_backward": (_i, [_p, _p, _p, _p, _p, _i64, _i, _i, _u, _f, _f, _f, _p, _p]),
     "moe_router_backward_workspace": (_sz, [_i64, _i, _i]),
     "moe_router_backward": (_i, [_p, _p, _i, _p, _i64, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
@@ -464,6 +469,44 @@ def moe_route_backward(logits, topk_idx, topk_gate, dgate, expert_count, alpha=0
                                  float(alpha), float(coef_balance),
                                  float(coef_z), _ptr(dlogits), _stream(stream)))
     return dlogits
+
+
+def moe_combine_backward_bypass(dy, y_perm, pair_row, topk_idx, topk_gate, e_ffn, n_zero, n_copy,
+                                x=None, const_rows=None, *, dgate=None, dout=None, stream=None):
+    """Gate gradients of every slot (FFN rows, copy = x, constant rows) and
+    the gated row gradients dout of the FFN slots that ran."""
+    T, k = topk_idx.shape
+    d = dy.shape[1]
+    n_const = 0 if const_rows is None else const_rows.shape[0]
+    if dgate is None:
+        dgate = torch.empty((T, k), dtype=torch.float32, device=dy.device)
+    _contig(dy, y_perm, pair_row, topk_idx, topk_gate, x, const_rows, dgate, dout)
+    _check(_L.moe_combine_backward_bypass(
+        _ptr(dy), _dt(dy), _ptr(y_perm), _dt(y_perm), _ptr(pair_row), _ptr(topk_idx),
+        _ptr(topk_gate), T, k, d, e_ffn, n_zero, n_copy, n_const, _ptr(x), _ptr(const_rows),
+        _ptr(dgate), _ptr(dout), _stream(stream)))
+    return dgate, dout
+
+
+def moe_bypass_backward_workspace(T, d, n_const) -> int:
+    return _L.moe_bypass_backward_workspace(T, d, n_const)
+
+
+def moe_bypass_backward(dy, topk_idx, topk_gate, e_ffn, n_zero, n_copy, n_const, *, dx_acc=None,
+                        dconst=None, ws=None, stream=None):
+    """dx_acc += (sum of the copy slots' gates) dy; dconst = the constant rows' gradient."""
+    T, k = topk_idx.shape
+    d = dy.shape[1]
+    if dconst is None and n_const:
+        dconst = torch.empty((n_const, d), dtype=torch.float32, device=dy.device)
+    if ws is None:
+        ws = torch.empty(max(1, moe_bypass_backward_workspace(T, d, n_const)), dtype=torch.uint8,
+                         device=dy.device)
+    _contig(dy, topk_idx, topk_gate, dx_acc, dconst, ws)
+    _check(_L.moe_bypass_backward(_ptr(dy), _dt(dy), _ptr(topk_idx), _ptr(topk_gate), T, k, d,
+                                  e_ffn, n_zero, n_copy, n_const, _ptr(dx_acc), _ptr(dconst),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return dx_acc, dconst
 
 
 def moe_router_backward_workspace(T, d, E) -> int:

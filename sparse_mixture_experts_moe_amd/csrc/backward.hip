@@ -76,26 +76,58 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
 __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 
-template <typename DT, typename YT>
+// Zero-computation experts (router ids from e_ffn on: n_zero zero, n_copy
+// copy, n_const constant experts): a copy slot's output is the token's x row,
+// a constant slot's the constant row, a zero slot's nothing.
+template <typename YT>
+struct BypassBwd {
+  const int32_t* idx;
+  int e_ffn, n_zero, n_copy, n_const;
+  const YT* x;
+  const YT* cvec;
+};
+
+template <typename DT, typename YT, bool kBypass>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restrict__ dy,
                                                                const YT* __restrict__ y,
                                                                const int32_t* __restrict__ pair_row,
                                                                const float* __restrict__ gate,
                                                                int64_t T, int k, int d,
                                                                float* __restrict__ dgate,
-                                                               DT* __restrict__ dout) {
+                                                               DT* __restrict__ dout,
+                                                               BypassBwd<YT> bp) {
   const int lane = threadIdx.x % kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (t >= T) return;
   const int32_t* pr = pair_row + t * k;
   const DT* dyr = dy + t * d;
   for (int j0 = 0; j0 < k; j0 += kGradSlots) {
-    int rows[kGradSlots];
+    int rows[kGradSlots];         // expert row of an FFN slot that ran, else -1
+    const YT* src[kGradSlots];    // the slot's output row (NULL: none)
     float acc[kGradSlots], gs[kGradSlots];
 #pragma unroll
     for (int u = 0; u < kGradSlots; ++u) {
-      rows[u] = j0 + u < k ? pr[j0 + u] : -1;
-      gs[u] = (dout && rows[u] >= 0) ? gate[t * k + j0 + u] : 0.0f;
+      const int j = j0 + u;
+      rows[u] = -1;
+      src[u] = nullptr;
+      bool ffn = true;
+      if constexpr (kBypass) {
+        const int e = j < k ? bp.idx[t * k + j] - bp.e_ffn : -1;
+        if (e >= 0) {
+          ffn = false;
+          if (e >= bp.n_zero && e < bp.n_zero + bp.n_copy) {
+            src[u] = bp.x + t * d;
+          } else if (e >= bp.n_zero + bp.n_copy) {
+            const int c = e - bp.n_zero - bp.n_copy;
+            if (c < bp.n_const) src[u] = bp.cvec + static_cast<int64_t>(c) * d;
+          }
+        }
+      }
+      if (ffn && j < k && pr[j] >= 0) {
+        rows[u] = pr[j];
+        src[u] = y + static_cast<int64_t>(rows[u]) * d;
+      }
+      gs[u] = (dout && rows[u] >= 0) ? gate[t * k + j] : 0.0f;
       acc[u] = 0.0f;
     }
     if ((d & 7) == 0) {
@@ -104,12 +136,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restr
         load8(dyr + c, g);
 #pragma unroll
         for (int u = 0; u < kGradSlots; ++u) {
-          if (rows[u] < 0) continue;
+          if (!src[u]) continue;
           float v[8];
-          load8(y + static_cast<int64_t>(rows[u]) * d + c, v);
+          load8(src[u] + c, v);
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[u] = fmaf(g[i], v[i], acc[u]);
-          if (dout) {
+          if (dout && rows[u] >= 0) {
             float o[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[i] = gs[u] * g[i];
@@ -122,18 +154,79 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const DT* __restr
         const float g = load1(dyr + c);
 #pragma unroll
         for (int u = 0; u < kGradSlots; ++u) {
-          if (rows[u] < 0) continue;
-          acc[u] = fmaf(g, load1(y + static_cast<int64_t>(rows[u]) * d + c), acc[u]);
-          if (dout) store1(dout + static_cast<int64_t>(rows[u]) * d + c, gs[u] * g);
+          if (!src[u]) continue;
+          acc[u] = fmaf(g, load1(src[u] + c), acc[u]);
+          if (dout && rows[u] >= 0) store1(dout + static_cast<int64_t>(rows[u]) * d + c, gs[u] * g);
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < kGradSlots; ++u) {
       const float s = wave_sum(acc[u]);
-      if (lane == 0 && j0 + u < k) dgate[t * k + j0 + u] = rows[u] >= 0 ? s : 0.0f;
+      if (lane == 0 && j0 + u < k) dgate[t * k + j0 + u] = src[u] ? s : 0.0f;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Zero-computation experts, the rest of their backward:
+//   dx_acc[t, :] += (sum of g[t, j] over the token's copy slots) dy[t, :]
+//   dconst[c, :]  = sum over the slots on constant expert c of g[t, j] dy[t, :]
+// The first is one wave per token; the second sums fixed token ranges into
+// partials (one workgroup per range, constant expert and 256 columns) that a
+// second kernel adds in range order.
+// ---------------------------------------------------------------------------
+template <typename DT>
+__global__ __launch_bounds__(256) void bypass_copy_dx_kernel(
+    const DT* __restrict__ dy, const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    int64_t T, int k, int d, int copy0, int copy1, float* __restrict__ dx) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  float gsum = 0.0f;
+  bool any = false;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e >= copy0 && e < copy1) {
+      gsum += gate[t * k + j];
+      any = true;
+    }
+  }
+  if (!any) return;
+  for (int c = lane; c < d; c += kWave) dx[t * d + c] += gsum * load1(dy + t * d + c);
+}
+
+constexpr int kConstCols = 256;
+
+template <typename DT>
+__global__ __launch_bounds__(kConstCols) void bypass_const_partial_kernel(
+    const DT* __restrict__ dy, const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    int64_t T, int k, int d, int const0, int n_const, int64_t tok_per, float* __restrict__ part) {
+  const int c = static_cast<int>(blockIdx.x) * kConstCols + threadIdx.x;
+  const int s = blockIdx.y, ce = blockIdx.z;
+  const int64_t t0 = s * tok_per;
+  const int64_t t1 = t0 + tok_per < T ? t0 + tok_per : T;
+  float acc = 0.0f;
+  for (int64_t t = t0; t < t1; ++t)
+    for (int j = 0; j < k; ++j)
+      if (idx[t * k + j] == const0 + ce && c < d) acc = fmaf(gate[t * k + j], load1(dy + t * d + c), acc);
+  if (c < d) part[(static_cast<int64_t>(s) * n_const + ce) * d + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void bypass_const_reduce_kernel(const float* __restrict__ part,
+                                                                  int splits, int n_const, int d,
+                                                                  float* __restrict__ dconst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(n_const) * d;
+  if (i >= n) return;
+  float acc = 0.0f;
+  for (int s = 0; s < splits; ++s) acc += part[s * n + i];
+  dconst[i] = acc;
+}
+
+int bypass_const_splits(int64_t T) {
+  const int64_t s = (T + 63) / 64;  // about 64 tokens per range, at most 64 ranges
+  return static_cast<int>(s < 1 ? 1 : (s > 64 ? 64 : s));
 }
 
 // ---------------------------------------------------------------------------
@@ -364,14 +457,71 @@ hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, 
                                    int d, float* dgate, void* dout, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((T + 3) / 4);
 #define MOE_CB(DT, YT)                                                                         \
-  combine_backward_kernel<DT, YT><<<grid, 256, 0, stream>>>(                                   \
+  combine_backward_kernel<DT, YT, false><<<grid, 256, 0, stream>>>(                            \
       static_cast<const DT*>(dy), static_cast<const YT*>(y), pair_row, gate, T, k, d, dgate,   \
-      static_cast<DT*>(dout))
+      static_cast<DT*>(dout), BypassBwd<YT>{})
   if (dy_bf16 && y_bf16) MOE_CB(uint16_t, uint16_t);
   else if (dy_bf16) MOE_CB(uint16_t, float);
   else if (y_bf16) MOE_CB(float, uint16_t);
   else MOE_CB(float, float);
 #undef MOE_CB
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward_bypass(const void* dy, bool dy_bf16, const void* y,
+                                          bool y_bf16, const int32_t* pair_row, const float* gate,
+                                          int64_t T, int k, int d, const BypassArgs& b,
+                                          float* dgate, void* dout, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+#define MOE_CB(DT, YT)                                                                         \
+  combine_backward_kernel<DT, YT, true><<<grid, 256, 0, stream>>>(                             \
+      static_cast<const DT*>(dy), static_cast<const YT*>(y), pair_row, gate, T, k, d, dgate,   \
+      static_cast<DT*>(dout),                                                                  \
+      BypassBwd<YT>{b.topk_idx, b.e_ffn, b.n_zero, b.n_copy, b.n_const,                        \
+                    static_cast<const YT*>(b.x), static_cast<const YT*>(b.const_rows)})
+  if (dy_bf16 && y_bf16) MOE_CB(uint16_t, uint16_t);
+  else if (dy_bf16) MOE_CB(uint16_t, float);
+  else if (y_bf16) MOE_CB(float, uint16_t);
+  else MOE_CB(float, float);
+#undef MOE_CB
+  return hipGetLastError();
+}
+
+size_t bypass_backward_workspace_bytes(int64_t T, int d, int n_const) {
+  return sizeof(float) * static_cast<size_t>(bypass_const_splits(T)) * n_const * d;
+}
+
+hipError_t launch_bypass_backward(const void* dy, bool dy_bf16, const int32_t* idx,
+                                  const float* gate, int64_t T, int k, int d, int e_ffn,
+                                  int n_zero, int n_copy, int n_const, float* dx_acc,
+                                  float* dconst, void* ws, hipStream_t stream) {
+  if (n_copy > 0 && dx_acc) {
+    const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+    const int c0 = e_ffn + n_zero, c1 = c0 + n_copy;
+    if (dy_bf16)
+      bypass_copy_dx_kernel<uint16_t><<<grid, 256, 0, stream>>>(
+          static_cast<const uint16_t*>(dy), idx, gate, T, k, d, c0, c1, dx_acc);
+    else
+      bypass_copy_dx_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(dy), idx,
+                                                             gate, T, k, d, c0, c1, dx_acc);
+  }
+  if (n_const > 0 && dconst) {
+    const int splits = bypass_const_splits(T);
+    const int64_t tok_per = (T + splits - 1) / splits;
+    const int const0 = e_ffn + n_zero + n_copy;
+    float* part = static_cast<float*>(ws);
+    dim3 grid(static_cast<unsigned>((d + kConstCols - 1) / kConstCols),
+              static_cast<unsigned>(splits), static_cast<unsigned>(n_const));
+    if (dy_bf16)
+      bypass_const_partial_kernel<uint16_t><<<grid, kConstCols, 0, stream>>>(
+          static_cast<const uint16_t*>(dy), idx, gate, T, k, d, const0, n_const, tok_per, part);
+    else
+      bypass_const_partial_kernel<float><<<grid, kConstCols, 0, stream>>>(
+          static_cast<const float*>(dy), idx, gate, T, k, d, const0, n_const, tok_per, part);
+    const int64_t n = static_cast<int64_t>(n_const) * d;
+    bypass_const_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
+        part, splits, n_const, d, dconst);
+  }
   return hipGetLastError();
 }
 

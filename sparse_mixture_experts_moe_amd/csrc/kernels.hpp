@@ -109,6 +109,16 @@ hipError_t launch_combine_bypass(const void* y, bool y_bf16, const int32_t* pair
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16, const void* y, bool y_bf16,
                                    const int32_t* pair_row, const float* gate, int64_t T, int k,
                                    int d, float* dgate, void* dout, hipStream_t stream);
+// Zero-computation experts in the backward pass (BypassArgs as in the combine).
+hipError_t launch_combine_backward_bypass(const void* dy, bool dy_bf16, const void* y,
+                                          bool y_bf16, const int32_t* pair_row, const float* gate,
+                                          int64_t T, int k, int d, const BypassArgs& b,
+                                          float* dgate, void* dout, hipStream_t stream);
+size_t bypass_backward_workspace_bytes(int64_t T, int d, int n_const);
+hipError_t launch_bypass_backward(const void* dy, bool dy_bf16, const int32_t* idx,
+                                  const float* gate, int64_t T, int k, int d, int e_ffn,
+                                  int n_zero, int n_copy, int n_const, float* dx_acc,
+                                  float* dconst, void* ws, hipStream_t stream);
 hipError_t launch_route_backward(const float* logits, const int32_t* idx, const float* gate,
                                  const float* dgate, const int32_t* count, int64_t T, int E, int k, bool relu,
                                  float alpha, float c_bal, float c_z, float* dlogits,

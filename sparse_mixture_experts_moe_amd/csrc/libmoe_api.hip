@@ -601,6 +601,64 @@ moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
                     "moe_route_backward");
 }
 
+static moe_status_t check_bypass(const char* fn, int64_t T, int k, int d, int E_ffn, int n_zero,
+                                 int n_copy, int n_const) {
+  if (T < 0 || k < 1 || d < 1) return fail(MOE_EINVAL, "%s: need T >= 0, k >= 1, d >= 1", fn);
+  if (E_ffn < 0 || n_zero < 0 || n_copy < 0 || n_const < 0)
+    return fail(MOE_EINVAL, "%s: negative expert count", fn);
+  if (static_cast<int64_t>(E_ffn) + n_zero + n_copy + n_const > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "%s: more than %d router experts", fn, moe::kMaxExperts);
+  return MOE_OK;
+}
+
+moe_status_t moe_combine_backward_bypass(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+                                         const int32_t* pair_row, const int32_t* topk_idx,
+                                         const float* topk_gate, int64_t T, int k, int d,
+                                         int E_ffn, int n_zero, int n_copy, int n_const,
+                                         const void* x, const void* const_rows, float* dgate,
+                                         void* dout, void* stream) {
+  const char* fn = "moe_combine_backward_bypass";
+  moe_status_t st = check_bypass(fn, T, k, d, E_ffn, n_zero, n_copy, n_const);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dy_dt) || !valid_dtype(y_dt)) return fail(MOE_EINVAL, "%s: dtype", fn);
+  if (T == 0) return ok();
+  if (!dy || !pair_row || !topk_idx || !dgate || (E_ffn > 0 && !y_perm) || (dout && !topk_gate))
+    return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if ((n_copy > 0 && !x) || (n_const > 0 && !const_rows))
+    return fail(MOE_EINVAL, "%s: NULL x or const_rows", fn);
+  const moe::BypassArgs bp{topk_idx, E_ffn, n_zero, n_copy, n_const, x, const_rows};
+  return hip_status(moe::launch_combine_backward_bypass(dy, dy_dt == MOE_BF16, y_perm,
+                                                        y_dt == MOE_BF16, pair_row, topk_gate, T, k,
+                                                        d, bp, dgate, dout, as_stream(stream)),
+                    fn);
+}
+
+size_t moe_bypass_backward_workspace(int64_t T, int d, int n_const) {
+  if (T < 0 || d < 1 || n_const < 0) return 0;
+  return align256(moe::bypass_backward_workspace_bytes(T, d, n_const));
+}
+
+moe_status_t moe_bypass_backward(const void* dy, int dy_dt, const int32_t* topk_idx,
+                                 const float* topk_gate, int64_t T, int k, int d, int E_ffn,
+                                 int n_zero, int n_copy, int n_const, float* dx_acc, float* dconst,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_bypass_backward";
+  moe_status_t st = check_bypass(fn, T, k, d, E_ffn, n_zero, n_copy, n_const);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dy_dt)) return fail(MOE_EINVAL, "%s: dtype", fn);
+  if (T == 0) return ok();
+  if (!dy || !topk_idx || !topk_gate) return fail(MOE_EINVAL, "%s: NULL pointer", fn);
+  if ((n_copy > 0 && !dx_acc) || (n_const > 0 && !dconst))
+    return fail(MOE_EINVAL, "%s: NULL dx_acc or dconst", fn);
+  const size_t need = n_const > 0 ? moe_bypass_backward_workspace(T, d, n_const) : 0;
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return hip_status(moe::launch_bypass_backward(dy, dy_dt == MOE_BF16, topk_idx, topk_gate, T, k, d,
+                                                E_ffn, n_zero, n_copy, n_const, dx_acc, dconst, ws,
+                                                as_stream(stream)),
+                    fn);
+}
+
 size_t moe_router_backward_workspace(int64_t T, int d, int E) {
   if (T < 0 || d < 1 || E < 1) return 0;
   return align256(moe::router_backward_workspace_bytes(T, d, E));

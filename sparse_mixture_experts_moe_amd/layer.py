@@ -52,8 +52,7 @@ class MoELayer:
         zero-computation experts after the FFN experts: a dict with
         ``n_zero``, ``n_copy`` and ``const_rows`` ([n_const, d] in the dtype
         of x, or None); w_router then has E + n_zero + n_copy + n_const rows.
-        Neither variant takes balance updates; the zero-computation experts
-        are forward-only."""
+        Neither variant takes balance updates."""
         if gather not in ("fused", "copy"):
             raise ValueError("gather must be 'fused' or 'copy'")
         self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
@@ -161,7 +160,8 @@ class MoELayer:
         b["uv"] = torch.empty((R, 2 * h), dtype=x.dtype, device=dev)
         b["dgate"] = torch.empty((T, k), dtype=f32, device=dev)
         b["dout"] = torch.empty((R, d), dtype=x.dtype, device=dev)
-        b["dlogits"] = torch.empty((T, E), dtype=f32, device=dev)
+        Er = self.E_router  # router experts (E plus any zero-computation experts)
+        b["dlogits"] = torch.empty((T, Er), dtype=f32, device=dev)
         b["da"] = torch.empty((R, d), dtype=f32, device=dev)
         b["dw_gate"] = torch.empty((E, h, d), dtype=f32, device=dev)
         b["dw_up"] = torch.empty((E, h, d), dtype=f32, device=dev)
@@ -169,12 +169,17 @@ class MoELayer:
         b["bwd_ws"] = torch.empty(
             max(1, _lib.moe_expert_swiglu_backward_workspace(R, d, h, E, dt, True)),
             dtype=torch.uint8, device=dev)
-        b["dw_router"] = torch.empty((E, d), dtype=f32, device=dev)
-        b["dlogit_bias"] = torch.empty(E, dtype=f32, device=dev)
+        b["dw_router"] = torch.empty((Er, d), dtype=f32, device=dev)
+        b["dlogit_bias"] = torch.empty(Er, dtype=f32, device=dev)
         b["dx_acc"] = torch.empty((T, d), dtype=f32, device=dev)
         b["dx"] = torch.empty((T, d), dtype=f32, device=dev)
-        b["router_ws"] = torch.empty(max(1, _lib.moe_router_backward_workspace(T, d, E)),
+        b["router_ws"] = torch.empty(max(1, _lib.moe_router_backward_workspace(T, d, Er)),
                                      dtype=torch.uint8, device=dev)
+        if self.bypass is not None:
+            nk = self.bypass["n_const"]
+            b["dconst"] = torch.empty((max(nk, 1), d), dtype=f32, device=dev)
+            b["bypass_ws"] = torch.empty(max(1, _lib.moe_bypass_backward_workspace(T, d, nk)),
+                                         dtype=torch.uint8, device=dev)
         if self.shared is not None:
             Hs = self.shared[0].shape[1]
             b["shared_hid"] = torch.empty((T, Hs), dtype=x.dtype, device=dev)
@@ -331,8 +336,6 @@ class MoELayer:
         returns the buffer dict with dx [T, d], dw_router, dlogit_bias (when the
         layer has a logit bias), dw_gate, dw_up, dw_down, and shared_dw_* (fp32),
         plus the intermediates dgate, dout and dlogits."""
-        if self.bypass is not None:
-            raise NotImplementedError("the zero-computation experts are forward-only")
         T = dy.shape[0]
         b = self._bufs[(T, dy.dtype, dy.device)]
         if "x" not in b:
@@ -340,15 +343,23 @@ class MoELayer:
         x = b["x"]
         k, E = self.k, self.E
         mark = mark or (lambda name: None)
-        _lib.moe_combine_backward(dy, b["y_perm"], b["pair_row"], k, b["topk_gate"],
-                                  dgate=b["dgate"], dout=b["dout"], stream=stream)
+        bp = self.bypass
+        if bp is not None:
+            _lib.moe_combine_backward_bypass(dy, b["y_perm"], b["pair_row"], b["topk_idx"],
+                                             b["topk_gate"], E, bp["n_zero"], bp["n_copy"], x,
+                                             bp["const_rows"], dgate=b["dgate"], dout=b["dout"],
+                                             stream=stream)
+        else:
+            _lib.moe_combine_backward(dy, b["y_perm"], b["pair_row"], k, b["topk_gate"],
+                                      dgate=b["dgate"], dout=b["dout"], stream=stream)
         mark("combine_bwd")
         _lib.moe_route_backward(b["logits"], b["topk_idx"], b["topk_gate"], b["dgate"],
                                 b["expert_count"], self.alpha, coef_balance, coef_z,
                                 relu=self.relu, dlogits=b["dlogits"], stream=stream)
         mark("route_bwd")
         _lib.moe_expert_swiglu_backward(
-            x, b["expert_offset"], T * k, b["dout"], b["uv"], b["hid"], self.w_gate, self.w_up,
+            x, b["expert_offset"][:E + 1], T * k, b["dout"], b["uv"], b["hid"], self.w_gate,
+            self.w_up,
             self.w_down, a_rows=b["row_pair"], a_rows_div=k, da=b["da"], dw_gate=b["dw_gate"],
             dw_up=b["dw_up"], dw_down=b["dw_down"], ws=b["bwd_ws"], stream=stream)
         mark("experts_bwd")
@@ -364,6 +375,13 @@ class MoELayer:
                                  dx=b["dx_acc"], accumulate_dx=self.shared is not None,
                                  want=("dw", "dx"), ws=b["router_ws"], stream=stream)
         mark("router_bwd")
+        if bp is not None:
+            # copy slots add g dy to dx; constant experts collect their rows' gradient
+            _lib.moe_bypass_backward(dy, b["topk_idx"], b["topk_gate"], E, bp["n_zero"],
+                                     bp["n_copy"], bp["n_const"], dx_acc=b["dx_acc"],
+                                     dconst=b["dconst"][:bp["n_const"]] if bp["n_const"] else None,
+                                     ws=b["bypass_ws"], stream=stream)
+            mark("bypass_bwd")
         _lib.moe_combine(b["da"], b["pair_row"], None, b["dx_acc"], out=b["dx"], k=k,
                          stream=stream)
         mark("dx")

@@ -278,3 +278,31 @@ def test_combine_bypass_rejects():
     # no copy or constant experts: x and const_rows may be NULL (checked only)
     assert call(T=0, nc=0, nk=0, x=None, cr=None) == L.MOE_OK
 
+
+def test_bypass_backward_rejects():
+    BF = L.MOE_BF16
+    f = C.moe_combine_backward_bypass
+    assert f(FAKE, BF, FAKE, BF, FAKE, FAKE, FAKE, 16, 0, 64, 8, 1, 1, 2, FAKE, FAKE, FAKE, None,
+             None) == L.MOE_EINVAL
+    assert f(FAKE, BF, FAKE, BF, FAKE, FAKE, FAKE, 16, 2, 64, 8, 1, 1, 2, None, FAKE, FAKE, None,
+             None) == L.MOE_EINVAL and "x or const_rows" in _err()
+    assert f(FAKE, BF, FAKE, BF, FAKE, None, FAKE, 16, 2, 64, 8, 1, 1, 2, FAKE, FAKE, FAKE, None,
+             None) == L.MOE_EINVAL
+    assert f(FAKE, BF, FAKE, BF, FAKE, FAKE, FAKE, 16, 2, 64, 250, 1, 1, 9, FAKE, FAKE, FAKE, None,
+             None) == L.MOE_EUNSUPPORTED
+    assert f(None, BF, None, BF, None, None, None, 0, 2, 64, 8, 1, 1, 2, None, None, None, None,
+             None) == L.MOE_OK
+    g = C.moe_bypass_backward
+    need = L.moe_bypass_backward_workspace(4096, 1024, 2)
+    assert need >= 2 * 1024 * 4
+    assert g(FAKE, BF, FAKE, FAKE, 4096, 2, 1024, 8, 1, 1, 2, FAKE, FAKE, FAKE, need - 1,
+             None) == L.MOE_EWORKSPACE
+    assert g(FAKE, BF, FAKE, FAKE, 4096, 2, 1024, 8, 1, 1, 2, None, FAKE, FAKE, need,
+             None) == L.MOE_EINVAL and "dx_acc" in _err()
+    assert g(FAKE, BF, FAKE, FAKE, 4096, 2, 1024, 8, 1, 1, 2, FAKE, None, FAKE, need,
+             None) == L.MOE_EINVAL
+    assert g(FAKE, 9, FAKE, FAKE, 4096, 2, 1024, 8, 1, 1, 2, FAKE, FAKE, FAKE, need,
+             None) == L.MOE_EINVAL
+    # no copy and no constant experts: nothing to do beyond the checks
+    assert g(FAKE, BF, FAKE, FAKE, 0, 2, 1024, 8, 1, 0, 0, None, None, None, 0, None) == L.MOE_OK
+
