@@ -195,10 +195,13 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
 
 
 def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max_passes=5,
-                          relu=None):
+                          relu=None, bypass=None):
     """The backward oracle as it stands (its forward included) on the first
     n_tok tokens as a batch of their own, repeated until min_seconds.
-    ``relu`` = (k_max, logit_bias) runs the ReLU-routed layer's oracle."""
+    ``relu`` = (k_max, logit_bias) runs the ReLU-routed layer's oracle,
+    ``bypass`` (the variant's dict) the one with zero-computation experts."""
+    import numpy as np
+
     import oracle
     from moe_inputs import as_f32
     try:
@@ -218,7 +221,12 @@ def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        if relu is None:
+        if bypass is not None:
+            oracle.backward_bypass(x, np.concatenate([wr, as_f32(bypass["rows"])], 0), wg, wu,
+                                   wd, cfg.k, bypass["n_zero"], bypass["n_copy"],
+                                   as_f32(bypass["const"]), dyf, shared=shared, cap=cap,
+                                   alpha=cfg.alpha, c_bal=c_bal, c_z=c_z)
+        elif relu is None:
             oracle.backward(x, wr, wg, wu, wd, cfg.k, dyf, shared=shared,
                             logit_bias=inp["logit_bias"], select_bias=inp["select_bias"], cap=cap,
                             alpha=cfg.alpha, c_bal=c_bal, c_z=c_z)
@@ -231,7 +239,8 @@ def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max
     return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name}"
-                      f"{'' if relu is None else ' (relu variant)'} as one batch, forward and "
+                      f"{' (relu variant)' if relu else (' (bypass variant)' if bypass else '')}"
+                      f" as one batch, forward and "
                       f"backward, {passes} passes (float64 NumPy, {dt:.1f} s)"}
 
 
@@ -251,10 +260,15 @@ def main_backward(args):
     inp = generate(cfg)
     dy_h = generate_dy(cfg)
     layer = layer_from_inputs(inp, args.gather)
-    relu = None
+    relu = bypass = None
     if args.variant == "bypass":
-        print(json.dumps({"error": "the zero-computation experts are forward-only"}), flush=True)
-        sys.exit(2)
+        from moe_inputs import generate_bypass
+        from sparse_mixture_experts_moe_amd.workload import bypass_layer_from_inputs
+        rows, const = generate_bypass(cfg, *BYPASS_COUNTS)
+        layer = bypass_layer_from_inputs(inp, rows, const, BYPASS_COUNTS[0], BYPASS_COUNTS[1],
+                                         args.gather)
+        bypass = {"n_zero": BYPASS_COUNTS[0], "n_copy": BYPASS_COUNTS[1],
+                  "n_const": BYPASS_COUNTS[2], "rows": rows, "const": const}
     if args.variant == "relu":
         from moe_inputs import relu_logit_offset
         from sparse_mixture_experts_moe_amd.workload import relu_layer_from_inputs, relu_logit_bias
@@ -351,7 +365,10 @@ def main_backward(args):
         "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "k": k, "h": h,
                    "n_shared": cfg.n_shared, "h_shared": cfg.h_shared, "cf": cfg.cf,
                    "coef_balance": c_bal, "coef_z": c_z, "parallelism": "none (1 GPU)",
-                   **({"variant": {"kind": "relu", "k_max": relu[0]}} if relu else {})},
+                   **({"variant": {"kind": "relu", "k_max": relu[0]}} if relu else {}),
+                   **({"variant": {"kind": "bypass", "n_zero": bypass["n_zero"],
+                                   "n_copy": bypass["n_copy"], "n_const": bypass["n_const"]}}
+                      if bypass else {})},
         "roofline": roof,
         "measured_ceilings": ceil,
         "step_tflops": step_flops / (ms * 1e-3) / 1e12,
@@ -363,7 +380,8 @@ def main_backward(args):
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or {"mixtral_bf16": 1024, "finegrained_shared_bf16": 2048,
                                     "capacity_balance_bf16": 2048, "decode_bf16": 64}[cfg.name]
-        out["cpu_baseline"] = cpu_baseline_backward(inp, dy_h, cfg, n_tok, c_bal, c_z, relu=relu)
+        out["cpu_baseline"] = cpu_baseline_backward(inp, dy_h, cfg, n_tok, c_bal, c_z, relu=relu,
+                                                    bypass=bypass)
     print(json.dumps(out), flush=True)
 
 

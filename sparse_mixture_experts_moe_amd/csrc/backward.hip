@@ -193,7 +193,18 @@ __global__ __launch_bounds__(256) void bypass_copy_dx_kernel(
     }
   }
   if (!any) return;
-  for (int c = lane; c < d; c += kWave) dx[t * d + c] += gsum * load1(dy + t * d + c);
+  if ((d & 7) == 0) {
+    for (int c = lane * 8; c < d; c += kWave * 8) {
+      float g[8], o[8];
+      load8(dy + t * d + c, g);
+      load8(dx + t * d + c, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = fmaf(gsum, g[i], o[i]);
+      store8(dx + t * d + c, o);
+    }
+  } else {
+    for (int c = lane; c < d; c += kWave) dx[t * d + c] += gsum * load1(dy + t * d + c);
+  }
 }
 
 constexpr int kConstCols = 256;
@@ -202,14 +213,31 @@ template <typename DT>
 __global__ __launch_bounds__(kConstCols) void bypass_const_partial_kernel(
     const DT* __restrict__ dy, const int32_t* __restrict__ idx, const float* __restrict__ gate,
     int64_t T, int k, int d, int const0, int n_const, int64_t tok_per, float* __restrict__ part) {
+  // the gates of this expert's slots, 64 tokens at a time, staged in LDS (0
+  // where the slot is on another expert), so the column loop waits on dy only
+  __shared__ float g_tok[64];
   const int c = static_cast<int>(blockIdx.x) * kConstCols + threadIdx.x;
   const int s = blockIdx.y, ce = blockIdx.z;
   const int64_t t0 = s * tok_per;
   const int64_t t1 = t0 + tok_per < T ? t0 + tok_per : T;
   float acc = 0.0f;
-  for (int64_t t = t0; t < t1; ++t)
-    for (int j = 0; j < k; ++j)
-      if (idx[t * k + j] == const0 + ce && c < d) acc = fmaf(gate[t * k + j], load1(dy + t * d + c), acc);
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    const int n = static_cast<int>(t1 - tb < 64 ? t1 - tb : 64);
+    if (threadIdx.x < 64) {
+      float gs = 0.0f;
+      if (static_cast<int>(threadIdx.x) < n) {
+        const int64_t t = tb + threadIdx.x;
+        for (int j = 0; j < k; ++j)
+          if (idx[t * k + j] == const0 + ce) gs += gate[t * k + j];
+      }
+      g_tok[threadIdx.x] = gs;
+    }
+    __syncthreads();
+    if (c < d)
+      for (int i = 0; i < n; ++i)
+        if (g_tok[i] != 0.0f) acc = fmaf(g_tok[i], load1(dy + (tb + i) * d + c), acc);
+    __syncthreads();
+  }
   if (c < d) part[(static_cast<int64_t>(s) * n_const + ce) * d + c] = acc;
 }
 
