@@ -330,7 +330,7 @@ def main_backward(args):
             phases.setdefault(name, []).append(a.elapsed_time(b))
     phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
 
-    offs = res["expert_offset"].cpu().numpy()
+    offs = res["expert_offset"].cpu().numpy()[:layer.E + 1]  # the FFN experts
     kept = offs[1:] - offs[:-1]
     R_kept = int(offs[-1])
     T, d, h, E, k = cfg.T, cfg.d, cfg.h, cfg.E, cfg.k
