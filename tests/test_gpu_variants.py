@@ -116,14 +116,15 @@ def _check_relu(inp, res, k_max, lb, tokens=None):
                                              ("mixtral_bf16", 512, 256, 384, 2),
                                              ("finegrained_shared_bf16", 700, 256, 128, 2),
                                              ("capacity_balance_bf16", 1024, 128, 128, 3)])
-def test_layer_relu(L, name, T, d, h, kmul):
+@pytest.mark.parametrize("gather", ["fused", "copy"])
+def test_layer_relu(L, name, T, d, h, kmul, gather):
     from sparse_mixture_experts_moe_amd.workload import relu_layer_from_inputs, relu_logit_bias
     cfg = small_case(name, T=T, d=d, h=h)
-    _say(f"[case] relu layer {name} T={T} d={d} h={h}")
+    _say(f"[case] relu layer {name} T={T} d={d} h={h} gather={gather}")
     inp = generate(cfg)
     off = relu_logit_offset(cfg, cfg.k)
     k_max = min(cfg.E, kmul * cfg.k)
-    layer = relu_layer_from_inputs(inp, k_max, off)
+    layer = relu_layer_from_inputs(inp, k_max, off, gather)
     res = layer(to_device(inp["x"]))
     torch.cuda.synchronize()
     err, mean_used, lo, hi = _check_relu(inp, res, k_max, relu_logit_bias(inp, off))
@@ -214,11 +215,12 @@ def _check_bypass(cfg, inp, res, rows, const, nz, nc, tokens=None):
     ("capacity_balance_bf16", 1024, 128, 128, (0, 3, 1)),
     ("decode_bf16", 64, 256, 128, (2, 0, 0)),
 ])
-def test_layer_bypass(L, name, T, d, h, counts):
+@pytest.mark.parametrize("gather", ["fused", "copy"])
+def test_layer_bypass(L, name, T, d, h, counts, gather):
     from sparse_mixture_experts_moe_amd.workload import bypass_layer_from_inputs
     cfg, inp, rows, const = _bypass_inputs(name, T, d, h, counts)
-    _say(f"[case] bypass layer {name} T={T} d={d} h={h} kinds={counts}")
-    layer = bypass_layer_from_inputs(inp, rows, const, counts[0], counts[1])
+    _say(f"[case] bypass layer {name} T={T} d={d} h={h} kinds={counts} gather={gather}")
+    layer = bypass_layer_from_inputs(inp, rows, const, counts[0], counts[1], gather)
     res = layer(to_device(inp["x"]))
     torch.cuda.synchronize()
     err, ffn_rows, bypass_pairs = _check_bypass(cfg, inp, res, rows, const, counts[0], counts[1])
