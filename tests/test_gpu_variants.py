@@ -134,7 +134,8 @@ def test_layer_relu(L, name, T, d, h, kmul, gather):
 # ---------------------------------------------------- zero-computation experts
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,k,nz,nc,nk,E_ffn", [(300, 128, 2, 1, 1, 2, 8), (65, 72, 4, 0, 2, 0, 5),
-                                                  (1500, 256, 8, 3, 0, 5, 60), (7, 8, 1, 0, 0, 3, 0)])
+                                                  (1500, 256, 8, 3, 0, 5, 60), (7, 8, 1, 0, 0, 3, 0),
+                                                  (33, 70, 3, 1, 1, 1, 4), (1100, 70, 2, 0, 1, 1, 3)])
 def test_combine_bypass(L, dt, T, d, k, nz, nc, nk, E_ffn):
     """moe_combine_bypass alone against the definition, with dropped FFN
     pairs, every kind of zero-computation expert and ids past the last."""
@@ -375,3 +376,69 @@ def test_layer_bypass_backward(L, name, T, d, h, counts, c_bal, c_z):
         errs[key] = worst
         assert worst <= tol, errs
     _say(f"[ok] bypass backward {name}: " + ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k,nz,nc,nk,E_ffn", [(300, 128, 2, 1, 1, 2, 8), (77, 70, 3, 1, 2, 1, 4),
+                                                  (5000, 64, 8, 2, 1, 3, 20), (9, 8, 1, 0, 0, 2, 2)])
+def test_bypass_backward_calls(L, dt, T, d, k, nz, nc, nk, E_ffn):
+    """moe_combine_backward_bypass and moe_bypass_backward alone against the
+    definitions: dgate per slot source, dout on the FFN rows that ran, the
+    copy slots' dx added to an accumulator, the constant rows' gradient."""
+    _say(f"[case] bypass backward calls {dt} T={T} d={d} k={k} kinds={nz},{nc},{nk} E_ffn={E_ffn}")
+    rng = np.random.default_rng(T * 3 + d + k)
+    E = E_ffn + nz + nc + nk
+    idx = np.stack([rng.choice(E + 1, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    gate = rng.random((T, k)).astype(np.float32)
+    caps = np.array([max(1, T * k // (2 * E))] * E_ffn + [0] * (E + 1 - E_ffn))
+    disp = oracle.dispatch(idx, E + 1, caps)
+    R = max(int(disp["offset"][-1]), 1)
+
+    def cast(a):
+        return a.astype(np.float32) if dt == "f32" else Bf16(bf16_bits_rne(a.astype(np.float32)))
+
+    y, x, cv, dy = (cast(rng.standard_normal(s)) for s in ((R, d), (T, d), (nk, d), (T, d)))
+    acc0 = rng.standard_normal((T, d)).astype(np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    pr = disp["pair_row"].astype(np.int32)
+    dout = torch.zeros((R, d), dtype=torch.float32 if dt == "f32" else torch.bfloat16,
+                       device="cuda")
+    dgate, _ = L.moe_combine_backward_bypass(to_device(dy), to_device(y), dev(pr), dev(idx),
+                                             dev(gate), E_ffn, nz, nc, to_device(x) if nc else None,
+                                             to_device(cv) if nk else None, dout=dout)
+    dx_acc = dev(acc0)
+    _, dconst = L.moe_bypass_backward(to_device(dy), dev(idx), dev(gate), E_ffn, nz, nc, nk,
+                                      dx_acc=dx_acc if nc else None)
+    torch.cuda.synchronize()
+    yf, xf, cf, dyf = (as_f32(a).astype(np.float64) for a in (y, x, cv, dy))
+    prk = pr.reshape(T, k)
+    want_dg = np.zeros((T, k))
+    want_dx = acc0.astype(np.float64).copy()
+    want_dc = np.zeros((nk, d))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e < E_ffn:
+                if prk[t, j] >= 0:
+                    want_dg[t, j] = dyf[t] @ yf[prk[t, j]]
+                continue
+            if e >= E:
+                continue
+            kind, c = oracle.bypass_kind(e, E_ffn, nz, nc, nk)
+            if kind == "copy":
+                want_dg[t, j] = dyf[t] @ xf[t]
+                want_dx[t] += gate[t, j] * dyf[t]
+            elif kind == "const":
+                want_dg[t, j] = dyf[t] @ cf[c]
+                want_dc[c] += gate[t, j] * dyf[t]
+    assert normwise(host(dgate), want_dg) <= 1e-5
+    kept = np.nonzero(pr >= 0)[0]
+    if kept.size:
+        got = host(dout)[pr[kept]]
+        want = gate.reshape(-1)[kept][:, None] * dyf[kept // k]
+        assert normwise(got, want) <= (1e-6 if dt == "f32" else 4e-3)
+    if nc:
+        assert normwise(host(dx_acc), want_dx) <= 1e-6
+    if nk:
+        assert normwise(host(dconst), want_dc) <= 1e-5
+
