@@ -182,18 +182,22 @@ def router_linear_backward(x, w_router, dlogits):
 # Whole layer
 # ---------------------------------------------------------------------------
 def backward(x, w_router, w_gate, w_up, w_down, k, dy, shared=(), logit_bias=None,
-             select_bias=None, cap=mo.UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0, logits=None):
+             select_bias=None, cap=mo.UNLIMITED, alpha=0.01, c_bal=0.0, c_z=0.0, logits=None,
+             topk_idx=None):
     """dJ for the whole layer, in reverse order of ``moe_oracle.forward``.
 
     If ``logits`` is given (e.g. float32 logits another implementation
     produced) the routing and every logit-dependent term use them, as in the
-    forward.  Returns a dict: dx, dw_router, dlogit_bias, dw_gate, dw_up,
+    forward; ``topk_idx``, if given, is the selection (as in the forward: the
+    selection key moves only the chosen set, so the gradient is the same
+    function of that set).  Returns a dict: dx, dw_router, dlogit_bias, dw_gate, dw_up,
     dw_down, dshared (a list of (dwg, dwu, dwd)), and the intermediates
     dgate [T, k] and dlogits [T, E], plus ``fwd`` (the forward's dict).
     """
     x, dy = _f64(x), _f64(dy)
     fw = mo.forward(x, w_router, w_gate, w_up, w_down, k, shared=shared, logit_bias=logit_bias,
-                    select_bias=select_bias, cap=cap, alpha=alpha, logits=logits)
+                    select_bias=select_bias, cap=cap, alpha=alpha, logits=logits,
+                    topk_idx=topk_idx)
     idx, g, pr = fw["topk_idx"], fw["topk_gate"], fw["pair_row"]
     T, d = x.shape
     E = np.asarray(w_router).shape[0]

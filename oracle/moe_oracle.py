@@ -293,18 +293,22 @@ def router_z_loss(logits):
 # Whole layer
 # ---------------------------------------------------------------------------
 def forward(x, w_router, w_gate, w_up, w_down, k, shared=(), logit_bias=None,
-            select_bias=None, cap=UNLIMITED, alpha=0.01, logits=None, tokens=None):
+            select_bias=None, cap=UNLIMITED, alpha=0.01, logits=None, tokens=None,
+            topk_idx=None):
     """The whole forward pass in the pages' order.
 
     If ``logits`` is given (e.g. the float32 logits another implementation
     produced) the routing, dispatch, output and statistics are computed from
-    them; otherwise from this oracle's own float64 logits.  Returns a dict with
-    every intermediate.
+    them; otherwise from this oracle's own float64 logits.  If ``topk_idx`` is
+    given, it is the selection (a selection made on other keys, such as the
+    routing probability plus the bias, whose validity the caller checks); the
+    gates, dispatch, output and statistics follow from it as usual.  Returns a
+    dict with every intermediate.
     """
     if logits is None:
         logits = router_logits(x, w_router, logit_bias)
     keys = selection_keys(logits, select_bias)
-    idx = top_k(keys, k)
+    idx = top_k(keys, k) if topk_idx is None else np.asarray(topk_idx, dtype=np.int32)
     g = gates(logits, idx)
     E = np.asarray(w_router).shape[0]
     disp = dispatch(idx, E, cap)

@@ -408,3 +408,48 @@ def test_routing_backward_shapes(T, E, k, d, dt, c_bal, c_z):
     assert normwise(host(dx), dx_ref) <= 1e-5
     assert normwise(host(dw), dw_ref) <= 1e-5
     assert normwise(host(db), db_ref) <= 1e-5
+
+
+def test_layer_backward_bias_on_probs():
+    """A training step whose selection adds the bias to the routing
+    probability: the GPU's selection is checked for validity on the
+    probability keys, then every gradient against the oracle's backward of
+    that selection (the key moves only the chosen set)."""
+    cfg = small_case("capacity_balance_bf16", T=2048, d=192, h=256)
+    _say(f"[case] backward with bias on probabilities {cfg}")
+    inp = generate(cfg)
+    dy_h = generate_dy(cfg)
+    base = build_layer(inp)
+    cap = oracle.capacity(cfg.cf, cfg.T, cfg.k, cfg.E)
+    layer = type(base)(base.w_router, base.w_gate, base.w_up, base.w_down, cfg.k,
+                       select_bias=base.select_bias, capacity=cap, alpha=cfg.alpha,
+                       bias_on_probs=True)
+    res = layer.forward(to_device(inp["x"]), train=True)
+    layer.backward(to_device(dy_h), 1.0, 0.1)
+    torch.cuda.synchronize()
+    gl = host(res["logits"])
+    idx = host(res["topk_idx"]).astype(np.int64)
+    keys = oracle.selection_keys_on_probs(gl, inp["select_bias"]).astype(np.float64)
+    chosen = np.take_along_axis(keys, idx, axis=1)
+    mask = np.ones_like(keys, dtype=bool)
+    np.put_along_axis(mask, idx, False, axis=1)
+    worst_other = np.where(mask, keys, -np.inf).max(axis=1)
+    tol = 4e-7 * np.abs(keys).max()
+    assert np.all(chosen.min(axis=1) >= worst_other - tol)
+    assert np.all(np.diff(chosen, axis=1) <= tol)
+    xf, wr = as_f32(inp["x"]), as_f32(inp["w_router"])
+    wg, wu, wd = as_f32(inp["w_gate"]), as_f32(inp["w_up"]), as_f32(inp["w_down"])
+    ref = oracle.backward(xf, wr, wg, wu, wd, cfg.k, as_f32(dy_h), cap=cap, alpha=cfg.alpha,
+                          c_bal=1.0, c_z=0.1, logits=gl, topk_idx=idx)
+    fw = ref["fwd"]
+    assert np.array_equal(host(res["pair_row"]), fw["pair_row"])
+    errs = {}
+    for key in ("dgate", "dlogits", "dx", "dw_router"):
+        errs[key] = normwise(host(res[key]), ref[key])
+        assert errs[key] <= 2e-2, errs
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        got = host(res[key])
+        worst = max(normwise(got[e], ref[key][e]) for e in range(cfg.E) if fw["kept"][e])
+        errs[key] = worst
+        assert worst <= 2e-2, errs
+    _say("[ok] bias on probabilities: " + ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))

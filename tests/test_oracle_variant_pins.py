@@ -40,3 +40,26 @@ def test_prob_keys_bias_shift():
     base = oracle.selection_keys_on_probs(logits)
     shifted = oracle.selection_keys_on_probs(logits, np.full(6, 0.5, np.float32))
     assert np.array_equal(shifted, (base + np.float32(0.5)).astype(np.float32))
+
+
+def test_given_selection_equals_own_selection():
+    """Passing the oracle's own selection as ``topk_idx`` changes nothing, and
+    a selection on probability keys flows through the forward and backward."""
+    rng = np.random.default_rng(8)
+    T, d, E, h, k = 6, 5, 4, 3, 2
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    wg = rng.standard_normal((E, h, d))
+    wu = rng.standard_normal((E, h, d))
+    wd = rng.standard_normal((E, d, h))
+    dy = rng.standard_normal((T, d))
+    sb = 0.4 * rng.standard_normal(E)
+    a = oracle.backward(x, wr, wg, wu, wd, k, dy, select_bias=sb, c_bal=1.0, c_z=0.1)
+    b = oracle.backward(x, wr, wg, wu, wd, k, dy, select_bias=sb, c_bal=1.0, c_z=0.1,
+                        topk_idx=a["fwd"]["topk_idx"])
+    for key in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dlogits"):
+        assert np.array_equal(a[key], b[key])
+    pk = oracle.top_k(oracle.selection_keys_on_probs(x @ wr.T, sb.astype(np.float32)), k)
+    c = oracle.backward(x, wr, wg, wu, wd, k, dy, c_bal=1.0, topk_idx=pk)
+    assert np.array_equal(c["fwd"]["topk_idx"], pk)
+    assert np.allclose(c["fwd"]["topk_gate"].sum(axis=1), 1.0)
