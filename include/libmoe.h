@@ -1,6 +1,7 @@
 /*
- * libmoe -- forward pass of a sparse Mixture-of-Experts feed-forward layer on
- * AMD Instinct MI355X (gfx950).
+ * libmoe -- a sparse Mixture-of-Experts feed-forward layer on AMD Instinct
+ * MI355X (gfx950): its forward pass, its backward pass, the per-step
+ * load-balancing updates and two routing variants.
  *
  * The layer, as the pages define it:
  *   - a linear router gives one logit per expert ("Every parameter, every
@@ -26,6 +27,13 @@
  * One layer call is five library calls on one stream:
  *   moe_route -> moe_permute -> moe_expert_swiglu (routed experts; and once
  *   more for the shared experts) -> moe_combine, plus moe_balance_stats.
+ * The backward pass, the balancing updates (moe_balance_update,
+ * moe_permute_budgets) and the routing variants (MOE_ROUTE_RELU: ReLU
+ * routing; moe_combine_bypass: zero, copy and constant experts, Zen MoDE,
+ * section "Router") are described where they are declared below.
+ *   - "Outputs are overwritten, never accumulated into" holds for every call
+ *     except where a declaration says "accumulated" (moe_router_backward's
+ *     dx on request, moe_bypass_backward's dx_acc).
  *
  * General contract
  *   - Every pointer is a DEVICE pointer unless marked (host).  Buffers are
