@@ -124,6 +124,13 @@ def test_layer_backward(name):
     assert errs["dlogits_same_in"] <= 1e-5, errs
     _, dwr_same, dlb_same = oracle.router_linear_backward(xf, wr, gdl)
     errs["dw_router_same_in"] = normwise(host(res["dw_router"]), dwr_same)
+    if nk:  # the constant rows' gradient, in full
+        dc_ref = np.zeros((nk, d))
+        for c in range(nk):
+            t_, j_ = np.nonzero(idx == E + nz + nc + c)
+            dc_ref[c] = (gate[t_, j_][:, None] * dyf[t_]).sum(axis=0)
+        errs["dconst"] = normwise(host(res["dconst"])[:nk], dc_ref)
+        assert errs["dconst"] <= 1e-5, errs
     assert errs["dw_router_same_in"] <= 1e-5, errs
     if inp["logit_bias"] is not None:
         errs["dlogit_bias_same_in"] = normwise(host(res["dlogit_bias"]), dlb_same)
@@ -240,29 +247,50 @@ def _silu_grad(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-@pytest.mark.parametrize("name", ["mixtral_bf16", "finegrained_shared_bf16"])
-def test_backward_full_size_sampled(name):
+@pytest.mark.parametrize("name,variant", [("mixtral_bf16", None), ("finegrained_shared_bf16", None),
+                                          ("mixtral_bf16", "relu"), ("mixtral_bf16", "bypass")])
+def test_backward_full_size_sampled(name, variant):
     """The training step at a workload's full size, in the bench's launch
-    configuration (two streams), checked on samples the oracle computes one
-    by one: gate and input gradients of sampled tokens, sampled entries of
+    configuration (two streams; for a routing variant, the one of
+    ``bench.py --backward --variant``), checked on samples the oracle computes
+    one by one: gate and input gradients of sampled tokens, sampled entries of
     every expert weight gradient, and the logit and router-weight gradients in
-    full on the GPU's own gate gradients."""
-    from moe_inputs import WORKLOADS
+    full on the GPU's own gate gradients (and the constant rows' gradient in
+    full)."""
+    from bench import BYPASS_COUNTS, RELU_K_MUL
+    from moe_inputs import WORKLOADS, generate_bypass, relu_logit_offset
+    from sparse_mixture_experts_moe_amd.workload import (bypass_layer_from_inputs,
+                                                         relu_layer_from_inputs, relu_logit_bias)
     cfg = WORKLOADS[name]
     c_bal, c_z = 1.0, 1e-3
-    _say(f"[case] full-size backward {name}: generating inputs")
+    _say(f"[case] full-size backward {name} {variant}: generating inputs")
     inp = generate(cfg)
     dy_h = generate_dy(cfg)
-    layer = build_layer(inp)
+    nz = nc = nk = 0
+    if variant == "relu":
+        k_run = min(cfg.E, RELU_K_MUL * cfg.k)
+        layer = relu_layer_from_inputs(inp, k_run, relu_logit_offset(cfg, cfg.k))
+    elif variant == "bypass":
+        k_run = cfg.k
+        nz, nc, nk = BYPASS_COUNTS
+        rows, const = generate_bypass(cfg, nz, nc, nk)
+        layer = bypass_layer_from_inputs(inp, rows, const, nz, nc)
+    else:
+        k_run = cfg.k
+        layer = build_layer(inp)
     x = to_device(inp["x"])
     dy = to_device(dy_h)
-    _say(f"[case] full-size backward {name}: running")
+    _say(f"[case] full-size backward {name} {variant}: running")
     res = layer.forward(x, train=True)
     layer.backward(dy, c_bal, c_z)
     torch.cuda.synchronize()
-    _say(f"[case] full-size backward {name}: checking")
-    T, E, k, d, h = cfg.T, cfg.E, cfg.k, cfg.d, cfg.h
+    _say(f"[case] full-size backward {name} {variant}: checking")
+    T, E, k, d, h = cfg.T, cfg.E, k_run, cfg.d, cfg.h
     xf, wr = as_f32(inp["x"]), as_f32(inp["w_router"])
+    if variant == "bypass":
+        wr = np.concatenate([wr, as_f32(rows)], 0)
+        cf = as_f32(const).astype(np.float64)
+    glg = oracle.relu_gate_logit_grad if variant == "relu" else oracle.gate_logit_grad
     dyf = as_f32(dy_h)
     gl = host(res["logits"])
     idx = host(res["topk_idx"]).astype(np.int64)
@@ -282,13 +310,21 @@ def test_backward_full_size_sampled(name):
     # gate and input gradients of the sampled tokens (routed part + router part)
     gdg = host(res["dgate"])
     gdx = host(res["dx"])
-    dl_rows = oracle.gate_logit_grad(gl[toks], idx[toks], gdg[toks])
+    dl_rows = glg(gl[toks], idx[toks], gdg[toks])
     dl_rows = dl_rows + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)[toks]
     dl_rows = dl_rows + c_z * oracle.z_loss_logit_grad(gl)[toks]
     dg_ref = np.zeros((toks.size, k))
     dx_ref = dl_rows @ wr.astype(np.float64)
     for n, t in enumerate(toks):
         for j in range(k):
+            if variant == "bypass" and idx[t, j] >= E:
+                kind, c = oracle.bypass_kind(int(idx[t, j]), E, nz, nc, nk)
+                if kind == "copy":
+                    dg_ref[n, j] = float(dyf[t] @ xf[t])
+                    dx_ref[n] += gate[t, j] * dyf[t]
+                elif kind == "const":
+                    dg_ref[n, j] = float(dyf[t] @ cf[c])
+                continue
             if pair_row[t, j] < 0:
                 continue
             wg, wu, wd = weights(int(idx[t, j]))
@@ -302,13 +338,20 @@ def test_backward_full_size_sampled(name):
     errs = {"dgate": normwise(gdg[toks], dg_ref), "dx": normwise(gdx[toks], dx_ref)}
 
     # logits and router weights on the GPU's gate gradients (fp32 kernels)
-    dl_same = oracle.gate_logit_grad(gl, idx, gdg)
+    dl_same = glg(gl, idx, gdg)
     dl_same = dl_same + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)
     dl_same = dl_same + c_z * oracle.z_loss_logit_grad(gl)
     gdl = host(res["dlogits"])
     errs["dlogits_same_in"] = normwise(gdl, dl_same)
     _, dwr_same, _ = oracle.router_linear_backward(xf, wr, gdl)
     errs["dw_router_same_in"] = normwise(host(res["dw_router"]), dwr_same)
+    if nk:  # the constant rows' gradient, in full
+        dc_ref = np.zeros((nk, d))
+        for c in range(nk):
+            t_, j_ = np.nonzero(idx == E + nz + nc + c)
+            dc_ref[c] = (gate[t_, j_][:, None] * dyf[t_]).sum(axis=0)
+        errs["dconst"] = normwise(host(res["dconst"])[:nk], dc_ref)
+        assert errs["dconst"] <= 1e-5, errs
 
     # sampled weight-gradient entries of a few experts (all of each expert's rows)
     row_pair = host(res["row_pair"])
@@ -344,7 +387,8 @@ def test_backward_full_size_sampled(name):
             scale = float(full.abs().max())
             worst[key] = max(worst[key], float(np.max(np.abs(got - ref))) / scale)
     errs.update(worst)
-    _say(f"[ok] full-size backward {name}: " + ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+    _say(f"[ok] full-size backward {name} {variant}: " +
+         ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
     assert errs["dlogits_same_in"] <= 1e-5 and errs["dw_router_same_in"] <= 1e-5, errs
     for key in ("dgate", "dx", "dw_gate", "dw_up", "dw_down"):
         assert errs[key] <= 2e-2, errs
