@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0: chosen per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time only --workload (by default the Mixtral-shaped headline run "
+                         "also times the fine-grained, capacity and decode workloads and "
+                         "reports them under \"workloads\")")
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared experts in line on the layer's stream instead of "
                          "overlapping them on a second stream")
@@ -148,6 +152,28 @@ def measured_ceilings(torch, gemm_shape):
     return res
 
 
+def cpu_threads():
+    """Host threads of the oracle's timing: ``cores`` is the number of BLAS
+    threads its matrix products ran on (the threads it actually used);
+    ``host_cpus`` the CPUs this process may run on, len(os.sched_getaffinity(0));
+    ``blas`` the BLAS library (threadpoolctl's report)."""
+    try:
+        host = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host = os.cpu_count() or 1
+    threads, vendor = 1, "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            threads = max(int(p.get("num_threads", 1)) for p in blas)
+            vendor = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}"
+                                       for p in blas}))
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cores": threads, "host_cpus": host, "blas": vendor, "blas_threads": threads}
+
+
 def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
     """The oracle as it stands, on the first n_tok tokens taken as a batch of
     their own (same shapes, weights, biases and capacity factor), repeated
@@ -157,11 +183,7 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
 
     import oracle
     from moe_inputs import as_f32
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    cpu = cpu_threads()
     x = as_f32(inp["x"])[:n_tok]
     wr = as_f32(inp["w_router"])
     shared = ()
@@ -187,7 +209,7 @@ def cpu_baseline(inp, cfg, n_tok, min_seconds=10.0, max_passes=5, variant=None):
                                   as_f32(ex["const"]), shared=shared, cap=cap, alpha=cfg.alpha)
         dt += time.perf_counter() - t0
         passes += 1
-    return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
+    return {"value": n_tok * passes / dt, "unit": "tokens/s", **cpu,
             "kind": "oracle",
             "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name}"
                       f"{'' if variant is None else ' (' + variant[0] + ' variant)'} as one "
@@ -204,11 +226,7 @@ def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max
 
     import oracle
     from moe_inputs import as_f32
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    cpu = cpu_threads()
     x = as_f32(inp["x"])[:n_tok]
     dyf = as_f32(dy)[:n_tok]
     wr = as_f32(inp["w_router"])
@@ -236,7 +254,7 @@ def cpu_baseline_backward(inp, dy, cfg, n_tok, c_bal, c_z, min_seconds=10.0, max
                                  c_z=c_z)
         dt += time.perf_counter() - t0
         passes += 1
-    return {"value": n_tok * passes / dt, "unit": "tokens/s", "cores": int(threads),
+    return {"value": n_tok * passes / dt, "unit": "tokens/s", **cpu,
             "kind": "oracle",
             "sample": f"first {n_tok} of {cfg.T} tokens of {cfg.name}"
                       f"{' (relu variant)' if relu else (' (bypass variant)' if bypass else '')}"
@@ -385,28 +403,28 @@ def main_backward(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
-    if args.backward:
-        return main_backward(args)
+EXTRA_WORKLOADS = ("finegrained_shared_bf16", "capacity_balance_bf16", "decode_bf16")
 
+
+def measure_forward(args, cfg, ceil=None, extra=False):
+    """Forward steps of workload ``cfg``: ``args.warmup`` untimed steps, then
+    ``args.steps`` timed ones, then the per-phase pass.  Returns (out, inp):
+    the bench fields of this workload and its host inputs.  ``ceil`` reuses
+    measured ceilings (else they are measured here); ``extra`` leaves out the
+    variant, balance and copy-calibration options."""
     import numpy as np
     import torch
 
-    from moe_inputs import WORKLOADS, generate
+    from moe_inputs import generate
     from sparse_mixture_experts_moe_amd.workload import layer_from_inputs, to_device
 
-    cfg = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     inp = generate(cfg)
-    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    print(f"# {cfg.name}: inputs generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
     layer = layer_from_inputs(inp, args.gather)
     variant = None
-    if args.variant == "relu":
+    if args.variant == "relu" and not extra:
         from moe_inputs import relu_logit_offset
         from sparse_mixture_experts_moe_amd.workload import relu_layer_from_inputs, relu_logit_bias
         off = relu_logit_offset(cfg, cfg.k)
@@ -414,7 +432,7 @@ def main():
         layer = relu_layer_from_inputs(inp, k_max, off, args.gather)
         variant = ("relu", {"k_max": k_max, "logit_offset": off,
                             "logit_bias": relu_logit_bias(inp, off)})
-    elif args.variant == "bypass":
+    elif args.variant == "bypass" and not extra:
         from moe_inputs import generate_bypass
         from sparse_mixture_experts_moe_amd.workload import bypass_layer_from_inputs
         rows, const = generate_bypass(cfg, *BYPASS_COUNTS)
@@ -426,7 +444,7 @@ def main():
     balance = None
     if args.balance and variant:
         raise SystemExit("--balance does not combine with --variant")
-    if args.balance:
+    if args.balance and not extra:
         balance = dict(bias_step=1e-3, ema_decay=0.9, cf_base=cfg.cf if cfg.cf > 0 else 1.0,
                        gamma=float(cfg.E))
         layer = type(layer)(layer.w_router, layer.w_gate, layer.w_up, layer.w_down, cfg.k,
@@ -447,7 +465,7 @@ def main():
             if mark:
                 mark("balance_update")
         return res_
-    if args.copy_calibration_mib > 0:
+    if args.copy_calibration_mib > 0 and not extra:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -510,8 +528,8 @@ def main():
     torch.cuda.synchronize()
     layer.overlap_shared = overlap
     phases = {}
-    for step in marks:
-        for (_, a), (name, b) in zip(step[:-1], step[1:]):
+    for st in marks:
+        for (_, a), (name, b) in zip(st[:-1], st[1:]):
             phases.setdefault(name, []).append(a.elapsed_time(b))
     phase_ms = {k: float(np.mean(v)) for k, v in phases.items()}
 
@@ -545,8 +563,9 @@ def main():
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs
     # recorded in profiles/ (scaled by a plain copy of known size), or null
     roof["traffic"] = None if variant else recorded_traffic(cfg.name)
-    ceil = measured_ceilings(torch, None if cfg.name.startswith("decode") or cfg.dtype != "bf16"
-                             else (R_kept, d, 2 * h))
+    if ceil is None:
+        ceil = measured_ceilings(torch, None if cfg.name.startswith("decode") or
+                                 cfg.dtype != "bf16" else (R_kept, d, 2 * h))
     if roof["bound"] == "hbm":
         roof["measured_peak"] = ceil["hbm_read_gbs"]
     elif cfg.dtype == "bf16":
@@ -618,11 +637,49 @@ def main():
                        else {}),
                     **({"bypass_pairs": bypass_pairs} if args.variant == "bypass" else {})},
     }
+    return out, inp, variant
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if args.backward:
+        return main_backward(args)
+
+    import torch
+
+    from moe_inputs import WORKLOADS
+
+    cfg = WORKLOADS[args.workload]
+    out, inp, variant = measure_forward(args, cfg)
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or {"tiny_f32": 64, "mixtral_bf16": 4096,
                                     "finegrained_shared_bf16": 8192,
                                     "capacity_balance_bf16": 8192, "decode_bf16": 64}[cfg.name]
         out["cpu_baseline"] = cpu_baseline(inp, cfg, n_tok, variant=variant)
+    del inp
+    # The other large workloads, each timed the same way (same K and W, inputs
+    # resident in HBM before its timed region), one after the other in this
+    # process; the headline value above stays that of --workload.
+    extra = [] if (args.no_extra_workloads or args.variant or args.balance or
+                   args.workload != "mixtral_bf16") else list(EXTRA_WORKLOADS)
+    if extra:
+        out["workloads"] = {}
+        keep = ("value", "unit", "ms_per_step", "step_ms", "dtype", "config", "roofline",
+                "expert_gemm_mfma_util", "layer_tflops", "layer_hbm_gbs", "phase_ms",
+                "phase_hbm_gbs", "routing")
+        for name in extra:
+            o, i_, _ = measure_forward(args, WORKLOADS[name], ceil=out["measured_ceilings"],
+                                       extra=True)
+            del i_
+            torch.cuda.empty_cache()
+            out["workloads"][name] = {key: o[key] for key in keep}
+            print(f"# {name}: {o['value']:.4g} tokens/s, {o['ms_per_step']:.3f} ms per step, "
+                  f"roofline frac {o['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

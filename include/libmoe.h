@@ -14,14 +14,16 @@
  *     Capability via Mixture-of-Experts Architecture", section
  *     "Auxiliary-Loss-Free Load Balancing");
  *   - an optional per-expert capacity drops pairs over the budget ("Every
- *     parameter, every token", section "A budget"; Zen MoDE, section
+ *     parameter, every token", section "A budget"; "Zen MoDE: Mixture of Distilled Experts
+ *     Architecture", section
  *     "Adaptive Capacity Factors");
  *   - each token runs its k SwiGLU experts (Zen-Max, section "Fine-Grained
  *     Expert Architecture", expert equation) plus any always-on shared experts
  *     (same section; "Every parameter, every token", section "A shared
  *     expert"), and the output is the gate-weighted sum ("The gating network");
  *   - the Switch balance statistics f, P and alpha*N*sum(f*P) are emitted
- *     alongside (Zen MoDE, section "Auxiliary Load Balancing Loss";
+ *     alongside ("Zen MoDE: Mixture of Distilled Experts Architecture", section "Auxiliary
+ *     Load Balancing Loss";
  *     "Every parameter, every token", section "A balance penalty").
  *
  * One layer call is five library calls on one stream:
@@ -29,8 +31,8 @@
  *   more for the shared experts) -> moe_combine, plus moe_balance_stats.
  * The backward pass, the balancing updates (moe_balance_update,
  * moe_permute_budgets) and the routing variants (MOE_ROUTE_RELU: ReLU
- * routing; moe_combine_bypass: zero, copy and constant experts, Zen MoDE,
- * section "Router") are described where they are declared below.
+ * routing; moe_combine_bypass: zero, copy and constant experts, "Zen MoDE:
+ * Mixture of Diverse Experts", section "Router") are described where they are declared below.
  *   - "Outputs are overwritten, never accumulated into" holds for every call
  *     except where a declaration says "accumulated" (moe_router_backward's
  *     dx on request, moe_bypass_backward's dx_acc).
@@ -95,7 +97,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * writes it (section "Auxiliary-Loss-Free Load Balancing", s_ij =
  * softmax(x_i W_g)_j + b_j), instead of the default logit plus bias. */
 #define MOE_ROUTE_BIAS_ON_PROBS 2u
-/* moe_route flag: ReLU routing ("Zen MoDE", section "Router": ReLU gating
+/* moe_route flag: ReLU routing ("Zen MoDE: Mixture of Diverse Experts", section
+ * "Router": ReLU gating
  * gives each token an adaptive number of experts instead of a fixed top-k).
  * Reading: the gate of expert e is max(logits[t,e], 0) with no
  * renormalisation; a token's slots hold, of its k largest logits, those above
@@ -113,14 +116,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 int moe_abi_version(void);
 
 /* Static description of a status code (host string, never NULL). */
-const char* moe_status_string(int status);
+const char* moe_status_string(moe_status_t status);
 
 /* Detail of the last failed call on this host thread (host string, never
  * NULL; empty after a successful call). */
 const char* moe_last_error(void);
 
 /* Per-expert token budget C = ceil(cf * T * k / E).
- * "Zen MoDE", section "Adaptive Capacity Factors": capacity = factor * tokens /
+ * "Zen MoDE: Mixture of Distilled Experts Architecture", section "Adaptive Capacity
+ * Factors": capacity = factor * tokens /
  * experts; "Every parameter, every token", section "A budget": a factor above
  * one leaves slack.  Reading: tokens are counted as routed pairs T*k, and the
  * quotient is rounded up.  cf is read as the shortest decimal that
@@ -140,7 +144,8 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E);
  *   topk_gate[t,j] = exp(l_j - m) / sum_{i in topk} exp(l_i - m), l the
  *                 logits WITHOUT select_bias, m their maximum over the set.
  * Sources: "Every parameter, every token", section "The gating network";
- * Zen MoDE, section "Router Architecture"; Zen-Max, section
+ * "Zen MoDE: Mixture of Distilled Experts Architecture", section "Router Architecture";
+ * Zen-Max, section
  * "Auxiliary-Loss-Free Load Balancing" (bias moves the choice only).
  *
  * x [T,d], w_router [E,d] in dtype dt; products accumulate in fp32.
@@ -161,8 +166,8 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E);
  * reduction over d is split across waves for small batches; 0 when it is not
  * and with MOE_ROUTE_LOGITS_IN).
  */
-size_t moe_route_workspace(int64_t T, int d, int E, int k, int dt);
-moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
+size_t moe_route_workspace(int64_t T, int d, int E, int k, moe_dtype_t dt);
+moe_status_t moe_route(const void* x, const void* w_router, moe_dtype_t dt, int64_t T, int d, int E,
                        int k, const float* logit_bias, const float* select_bias,
                        unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
                        void* ws, size_t ws_bytes, void* stream);
@@ -194,20 +199,21 @@ moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, i
  */
 size_t moe_permute_workspace(int64_t T, int k, int E);
 moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
-                         const void* x, int dt, int d, int32_t* expert_count,
+                         const void* x, moe_dtype_t dt, int d, int32_t* expert_count,
                          int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
                          void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_permute_budgets: moe_permute with one budget per expert,
  *   kept(p) = rank(p) < expert_capacity[topk_idx[p]]
  * (expert_capacity [E] int32 on the device, each >= 0; everything else as
- * moe_permute).  Source: Zen MoDE, section "Adaptive Capacity Factors"
+ * moe_permute).  Source: "Zen MoDE: Mixture of Distilled Experts Architecture", section
+ * "Adaptive Capacity Factors"
  * (capacity per expert); the budgets typically come from moe_balance_update. */
 moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int E,
-                                 const int32_t* expert_capacity, const void* x, int dt, int d,
-                                 int32_t* expert_count, int32_t* expert_offset, int32_t* pair_row,
-                                 int32_t* row_pair, void* x_perm, void* ws, size_t ws_bytes,
-                                 void* stream);
+                                 const int32_t* expert_capacity, const void* x, moe_dtype_t dt,
+                                 int d, int32_t* expert_count, int32_t* expert_offset,
+                                 int32_t* pair_row, int32_t* row_pair, void* x_perm, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* moe_balance_update: the per-step load-balancing updates, from the pre-drop
  * counts of the last step (expert_count of moe_permute, T tokens, k slots):
@@ -221,7 +227,8 @@ moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int 
  *       C_e = cf_base + gamma (load_ema[e] - 1/E) on the updated load_ema,
  *       in float64, if expert_capacity is not NULL.
  * Sources: Zen-Max, section "Auxiliary-Loss-Free Load Balancing" (bias moved
- * after each step against the load deviation); Zen MoDE, section "Adaptive
+ * after each step against the load deviation); "Zen MoDE: Mixture of Distilled Experts
+ * Architecture", section "Adaptive
  * Capacity Factors" (C_e(t) = C_base + gamma (fbar_e - 1/N_E) from rolling
  * load statistics).  The pages give neither the step size, the rolling
  * window nor gamma: they are the arguments (ema_decay in [0, 1]; 0 uses this
@@ -260,12 +267,12 @@ moe_status_t moe_balance_update(const int32_t* expert_count, int64_t T, int k, i
  * MOE_EUNSUPPORTED.
  * Workspace: moe_expert_swiglu_workspace(max_rows, d, h, G, dt) bytes.
  */
-size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt);
-moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
+size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, moe_dtype_t dt);
+moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,
                                const int32_t* group_offset, int64_t max_rows,
                                const int32_t* a_rows, int a_rows_div,
                                const void* w_gate, const void* w_up, const void* w_down,
-                               void* y, int y_dt, void* ws, size_t ws_bytes, void* stream);
+                               void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream);
 
 /* The two halves of moe_expert_swiglu, for callers that keep the hidden
  * activation or time the two expert GEMMs apart (same sources, limits and
@@ -286,14 +293,14 @@ moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
  * initialisation and are dead after the call. */
 size_t moe_expert_group_workspace(int G);
 size_t moe_expert_down_workspace(int G);
-moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_gate_up(const void* a, moe_dtype_t dt, int d, int h, int G,
                                 const int32_t* group_offset, int64_t max_rows,
                                 const int32_t* a_rows, int a_rows_div, const void* w_gate,
                                 const void* w_up, void* hid, void* ws, size_t ws_bytes,
                                 void* stream);
-moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
+moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int G,
                              const int32_t* group_offset, int64_t max_rows, const void* w_down,
-                             void* y, int y_dt, void* ws, size_t ws_bytes, void* stream);
+                             void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* moe_combine: gate-weighted sum of the kept expert rows plus the shared
@@ -312,12 +319,13 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
  * NULL for gates of 1 (the backward pass sums a token's input gradients
  * this way); shared_y [T,d] in y_dt or NULL; out [T,d] in out_dt.
  */
-moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
+moe_status_t moe_combine(const void* y_perm, moe_dtype_t y_dt, const int32_t* pair_row,
                          const float* topk_gate, int64_t T, int k, int d,
-                         const void* shared_y, void* out, int out_dt, void* stream);
+                         const void* shared_y, void* out, moe_dtype_t out_dt, void* stream);
 
 /* moe_combine_bypass: moe_combine for a router whose experts past the first
- * E_ffn are zero-computation experts ("Zen MoDE", section "Router": zero,
+ * E_ffn are zero-computation experts ("Zen MoDE: Mixture of Diverse Experts",
+ * section "Router": zero,
  * copy and constant experts let a token skip the FFN compute).  Router ids
  * E_ffn .. E_ffn+n_zero-1 are zero experts, the next n_copy copy experts, the
  * next n_const constant experts.  Slot j of token t adds, in slot order,
@@ -335,11 +343,11 @@ moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
  * NULL when n_copy == 0, const_rows when n_const == 0); other arguments as
  * moe_combine.  Ids at or past E_ffn+n_zero+n_copy+n_const contribute
  * nothing. */
-moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pair_row,
+moe_status_t moe_combine_bypass(const void* y_perm, moe_dtype_t y_dt, const int32_t* pair_row,
                                 const int32_t* topk_idx, const float* topk_gate, int64_t T,
                                 int k, int d, int E_ffn, int n_zero, int n_copy, int n_const,
                                 const void* x, const void* const_rows, const void* shared_y,
-                                void* out, int out_dt, void* stream);
+                                void* out, moe_dtype_t out_dt, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* moe_balance_stats: Switch balance statistics and the router z-loss.
@@ -348,7 +356,8 @@ moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pai
  *   P[e]  = (1/T) sum_t softmax(logits[t,:])[e]
  *   loss  = alpha * E * sum_e f[e] * P[e]
  *   zloss = (1/T) sum_t (log sum_e exp logits[t,e])^2
- * Sources: Zen MoDE, section "Auxiliary Load Balancing Loss" (f counts
+ * Sources: "Zen MoDE: Mixture of Distilled Experts Architecture", section "Auxiliary Load
+ * Balancing Loss" (f counts
  * membership in TopK, P the average routing probability, alpha = 0.01);
  * "Every parameter, every token", section "A balance penalty"; Zen-Max,
  * section "MoE-Specific Training Stability" (router z-loss).  Readings:
@@ -376,7 +385,8 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
  * weights of the experts that ran; an expert that was off for a token gets no
  * gradient from it), sections "A balance penalty" (router trained on the
  * task and the penalty together) and "A budget" (a dropped pair skips its
- * expert update); Zen MoDE, section "Auxiliary Load Balancing Loss"; Zen-Max,
+ * expert update); "Zen MoDE: Mixture of Distilled Experts Architecture", section
+ * "Auxiliary Load Balancing Loss"; Zen-Max,
  * sections "Fine-Grained Expert Architecture" and "MoE-Specific Training
  * Stability".  Readings: no gradient flows through the selection, the
  * capacity drop, the counts f or the selection bias; a dropped pair's gate
@@ -401,7 +411,7 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
  *   uv[r, 2c] = a_r . w_gate[g][c],  uv[r, 2c + 1] = a_r . w_up[g][c]
  * uv [max_rows, 2h] in dtype dt.  The bf16 path runs the tiled kernel at
  * every row count.  Workspace: moe_expert_group_workspace(G). */
-moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_gate_up_train(const void* a, moe_dtype_t dt, int d, int h, int G,
                                       const int32_t* group_offset, int64_t max_rows,
                                       const int32_t* a_rows, int a_rows_div, const void* w_gate,
                                       const void* w_up, void* hid, void* uv, void* ws,
@@ -433,9 +443,9 @@ moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G
  * gathered rows of a when a_rows is given, and du, dv interleaved in bf16: about
  * 2 max_rows (2h + d) bytes plus 64 MiB); contents need no initialisation
  * and are dead after the call. */
-size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, moe_dtype_t dt,
                                             int gather);
-moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_swiglu_backward(const void* a, moe_dtype_t dt, int d, int h, int G,
                                         const int32_t* group_offset, int64_t max_rows,
                                         const int32_t* a_rows, int a_rows_div, const void* dout,
                                         const void* uv, const void* hid, const void* w_gate,
@@ -452,9 +462,10 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
  * dy_dt; y_perm [*, d] in y_dt (the expert rows moe_expert_down wrote);
  * topk_gate [T, k] fp32 (needed with dout); dgate [T, k] fp32; dout [*, d]
  * or NULL (rows of dropped pairs do not exist; other rows untouched). */
-moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
-                                  const int32_t* pair_row, const float* topk_gate, int64_t T, int k,
-                                  int d, float* dgate, void* dout, void* stream);
+moe_status_t moe_combine_backward(const void* dy, moe_dtype_t dy_dt, const void* y_perm,
+                                  moe_dtype_t y_dt, const int32_t* pair_row,
+                                  const float* topk_gate, int64_t T, int k, int d, float* dgate,
+                                  void* dout, void* stream);
 
 /* moe_route_backward: dJ/dlogits [T, E] fp32,
  *   dl[t,e] = g_tj (dgate_tj - sum_i g_ti dgate_ti)    for e = topk_idx[t,j]
@@ -463,7 +474,8 @@ moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm,
  * with g = topk_gate (the forward's gates), p_t = softmax(logits[t,:]),
  * lse_t = log sum_e exp logits[t,e], f_e = expert_count[e] / (T k) (the
  * pre-drop counts of moe_permute).  Sources: "The gating network" (softmax
- * over the selected set), Zen MoDE "Auxiliary Load Balancing Loss", Zen-Max
+ * over the selected set), "Zen MoDE: Mixture of Distilled Experts Architecture" "Auxiliary
+ * Load Balancing Loss", Zen-Max
  * "MoE-Specific Training Stability".  expert_count may be NULL when
  * coef_balance == 0.
  * flags: 0, or MOE_ROUTE_RELU for the ReLU-routed forward (its gate is the
@@ -477,8 +489,10 @@ moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm,
  * constant row for a constant expert, nothing (dgate 0) for a zero expert,
  * a dropped pair or an id past the last; dout (optional) as
  * moe_combine_backward, for the FFN slots that ran.  x and const_rows in
- * y_dt.  Source: Zen MoDE, section "Router" (zero-computation experts). */
-moe_status_t moe_combine_backward_bypass(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+ * y_dt.  Source: "Zen MoDE: Mixture of Diverse Experts", section "Router"
+ * (zero-computation experts). */
+moe_status_t moe_combine_backward_bypass(const void* dy, moe_dtype_t dy_dt,
+                                         const void* y_perm, moe_dtype_t y_dt,
                                          const int32_t* pair_row, const int32_t* topk_idx,
                                          const float* topk_gate, int64_t T, int k, int d,
                                          int E_ffn, int n_zero, int n_copy, int n_const,
@@ -493,7 +507,7 @@ moe_status_t moe_combine_backward_bypass(const void* dy, int dy_dt, const void* 
  * fixed token ranges added in range order (deterministic).  Workspace:
  * moe_bypass_backward_workspace(T, d, n_const) bytes. */
 size_t moe_bypass_backward_workspace(int64_t T, int d, int n_const);
-moe_status_t moe_bypass_backward(const void* dy, int dy_dt, const int32_t* topk_idx,
+moe_status_t moe_bypass_backward(const void* dy, moe_dtype_t dy_dt, const int32_t* topk_idx,
                                  const float* topk_gate, int64_t T, int k, int d, int E_ffn,
                                  int n_zero, int n_copy, int n_const, float* dx_acc, float* dconst,
                                  void* ws, size_t ws_bytes, void* stream);
@@ -514,7 +528,7 @@ moe_status_t moe_route_backward(const float* logits, const int32_t* topk_idx,
  * linear gate).  Workspace: moe_router_backward_workspace(T, d, E) bytes
  * (only when dw_router is requested). */
 size_t moe_router_backward_workspace(int64_t T, int d, int E);
-moe_status_t moe_router_backward(const void* x, const void* w_router, int dt,
+moe_status_t moe_router_backward(const void* x, const void* w_router, moe_dtype_t dt,
                                  const float* dlogits, int64_t T, int d, int E, float* dw_router,
                                  float* dlogit_bias, float* dx, int accumulate_dx, void* ws,
                                  size_t ws_bytes, void* stream);

@@ -4,7 +4,7 @@ ReLU routing and zero-computation (zero, copy and constant) experts.
 TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
 imports this module.
 
-Source: "Zen MoDE: Mixture of Distilled Experts Architecture", section
+Source: "Zen MoDE: Mixture of Diverse Experts", section
 "Router" (the router adopts ReLU gating, which gives each token an adaptive
 number of experts instead of a fixed top-K, and zero-computation experts, of
 three kinds: zero, copy and constant, which let a token skip the FFN

@@ -6,7 +6,8 @@
 // (the selected set is held fixed; gradient reaches the router only through
 // the gates of the experts that ran, and experts that were off get none),
 // "A balance penalty" (the router is trained on the task and the penalty
-// together) and "A budget" (a dropped pair has no expert output); Zen MoDE,
+// together) and "A budget" (a dropped pair has no expert output); "Zen MoDE: Mixture of
+// Distilled Experts Architecture",
 // section "Auxiliary Load Balancing Loss"; Zen-Max, section "MoE-Specific
 // Training Stability" (z-loss).
 //

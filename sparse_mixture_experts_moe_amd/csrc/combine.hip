@@ -11,8 +11,8 @@
 // (a dropped pair contributes nothing) and "A shared expert"; "Zen-Max:
 // Maximum Capability via Mixture-of-Experts Architecture", section
 // "Fine-Grained Expert Architecture" (shared experts are added); "Zen MoDE:
-// Mixture of Distilled Experts Architecture", section "Router" (zero, copy
-// and constant experts that skip the FFN).
+// Mixture of Diverse Experts", section "Router" (zero, copy and constant
+// experts that skip the FFN).
 //
 // HBM-bound: one workgroup per token, each lane handles 8 consecutive
 // columns per step (16-byte bf16 loads and stores); the rows of up to

@@ -100,7 +100,7 @@ extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-const char* moe_status_string(int status) {
+const char* moe_status_string(moe_status_t status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument";
@@ -157,13 +157,13 @@ int64_t moe_capacity(double cf, int64_t T, int k, int E) {
 }
 
 // ---------------------------------------------------------------------------
-size_t moe_route_workspace(int64_t T, int d, int E, int k, int dt) {
+size_t moe_route_workspace(int64_t T, int d, int E, int k, moe_dtype_t dt) {
   if (T < 0 || d < 1 || E < 1 || k < 1 || !valid_dtype(dt)) return 0;
   if (E > moe::kMaxExperts || d % 32 != 0) return 0;
   return moe::route_workspace_bytes(T, d, E, dt == MOE_BF16);
 }
 
-moe_status_t moe_route(const void* x, const void* w_router, int dt, int64_t T, int d, int E,
+moe_status_t moe_route(const void* x, const void* w_router, moe_dtype_t dt, int64_t T, int d, int E,
                        int k, const float* logit_bias, const float* select_bias,
                        unsigned flags, float* logits, int32_t* topk_idx, float* topk_gate,
                        void* ws, size_t ws_bytes, void* stream) {
@@ -204,7 +204,7 @@ size_t moe_permute_workspace(int64_t T, int k, int E) {
 }
 
 moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
-                         const void* x, int dt, int d, int32_t* expert_count,
+                         const void* x, moe_dtype_t dt, int d, int32_t* expert_count,
                          int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
                          void* x_perm, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "moe_permute: T < 0");
@@ -235,10 +235,10 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
 }
 
 moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int E,
-                                 const int32_t* expert_capacity, const void* x, int dt, int d,
-                                 int32_t* expert_count, int32_t* expert_offset, int32_t* pair_row,
-                                 int32_t* row_pair, void* x_perm, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 const int32_t* expert_capacity, const void* x, moe_dtype_t dt,
+                                 int d, int32_t* expert_count, int32_t* expert_offset,
+                                 int32_t* pair_row, int32_t* row_pair, void* x_perm, void* ws,
+                                 size_t ws_bytes, void* stream) {
   if (!expert_capacity) return fail(MOE_EINVAL, "moe_permute_budgets: NULL expert_capacity");
   if (T < 0) return fail(MOE_EINVAL, "moe_permute_budgets: T < 0");
   if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_permute_budgets: need 1 <= k <= E");
@@ -319,13 +319,13 @@ size_t moe_expert_down_workspace(int G) {
   return G < 1 ? 0 : tile_table_bytes(G) + moe::split_k_workspace_bytes();
 }
 
-size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, int dt) {
+size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, moe_dtype_t dt) {
   if (max_rows < 0 || d < 1 || h < 1 || G < 1 || !valid_dtype(dt)) return 0;
   return align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt)) +
          moe_expert_down_workspace(G);
 }
 
-moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_gate_up(const void* a, moe_dtype_t dt, int d, int h, int G,
                                 const int32_t* group_offset, int64_t max_rows,
                                 const int32_t* a_rows, int a_rows_div, const void* w_gate,
                                 const void* w_up, void* hid, void* ws, size_t ws_bytes,
@@ -356,9 +356,9 @@ moe_status_t moe_expert_gate_up(const void* a, int dt, int d, int h, int G,
   return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up");
 }
 
-moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
+moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int G,
                              const int32_t* group_offset, int64_t max_rows, const void* w_down,
-                             void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+                             void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_experts("moe_expert_down", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -383,11 +383,11 @@ moe_status_t moe_expert_down(const void* hid, int dt, int d, int h, int G,
   return hip_status(moe::launch_down(s, as_stream(stream)), "moe_expert_down");
 }
 
-moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,
                                const int32_t* group_offset, int64_t max_rows,
                                const int32_t* a_rows, int a_rows_div,
                                const void* w_gate, const void* w_up, const void* w_down,
-                               void* y, int y_dt, void* ws, size_t ws_bytes, void* stream) {
+                               void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_experts("moe_expert_swiglu", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -409,9 +409,9 @@ moe_status_t moe_expert_swiglu(const void* a, int dt, int d, int h, int G,
 }
 
 // ---------------------------------------------------------------------------
-moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
+moe_status_t moe_combine(const void* y_perm, moe_dtype_t y_dt, const int32_t* pair_row,
                          const float* topk_gate, int64_t T, int k, int d,
-                         const void* shared_y, void* out, int out_dt, void* stream) {
+                         const void* shared_y, void* out, moe_dtype_t out_dt, void* stream) {
   if (T < 0 || k < 1 || d < 1) return fail(MOE_EINVAL, "moe_combine: need T >= 0, k >= 1, d >= 1");
   if (!valid_dtype(y_dt) || !valid_dtype(out_dt)) return fail(MOE_EINVAL, "moe_combine: dtype");
   if (T == 0) return ok();
@@ -421,11 +421,11 @@ moe_status_t moe_combine(const void* y_perm, int y_dt, const int32_t* pair_row,
                     "moe_combine");
 }
 
-moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pair_row,
+moe_status_t moe_combine_bypass(const void* y_perm, moe_dtype_t y_dt, const int32_t* pair_row,
                                 const int32_t* topk_idx, const float* topk_gate, int64_t T,
                                 int k, int d, int E_ffn, int n_zero, int n_copy, int n_const,
                                 const void* x, const void* const_rows, const void* shared_y,
-                                void* out, int out_dt, void* stream) {
+                                void* out, moe_dtype_t out_dt, void* stream) {
   if (T < 0 || k < 1 || d < 1)
     return fail(MOE_EINVAL, "moe_combine_bypass: need T >= 0, k >= 1, d >= 1");
   if (E_ffn < 0 || n_zero < 0 || n_copy < 0 || n_const < 0)
@@ -450,7 +450,7 @@ moe_status_t moe_combine_bypass(const void* y_perm, int y_dt, const int32_t* pai
 // ---------------------------------------------------------------------------
 // Backward pass
 // ---------------------------------------------------------------------------
-moe_status_t moe_expert_gate_up_train(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_gate_up_train(const void* a, moe_dtype_t dt, int d, int h, int G,
                                       const int32_t* group_offset, int64_t max_rows,
                                       const int32_t* a_rows, int a_rows_div, const void* w_gate,
                                       const void* w_up, void* hid, void* uv, void* ws,
@@ -508,13 +508,13 @@ BwdLayout bwd_layout(int64_t max_rows, int d, int h, int G, bool gather, bool bf
 
 }  // namespace
 
-size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, int dt,
+size_t moe_expert_swiglu_backward_workspace(int64_t max_rows, int d, int h, int G, moe_dtype_t dt,
                                             int gather) {
   if (max_rows < 0 || d < 1 || h < 1 || G < 1 || !valid_dtype(dt)) return 0;
   return bwd_layout(max_rows, d, h, G, gather != 0, dt == MOE_BF16).total;
 }
 
-moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int G,
+moe_status_t moe_expert_swiglu_backward(const void* a, moe_dtype_t dt, int d, int h, int G,
                                         const int32_t* group_offset, int64_t max_rows,
                                         const int32_t* a_rows, int a_rows_div, const void* dout,
                                         const void* uv, const void* hid, const void* w_gate,
@@ -565,9 +565,10 @@ moe_status_t moe_expert_swiglu_backward(const void* a, int dt, int d, int h, int
   return hip_status(moe::launch_expert_backward(b, as_stream(stream)), fn);
 }
 
-moe_status_t moe_combine_backward(const void* dy, int dy_dt, const void* y_perm, int y_dt,
-                                  const int32_t* pair_row, const float* topk_gate, int64_t T, int k,
-                                  int d, float* dgate, void* dout, void* stream) {
+moe_status_t moe_combine_backward(const void* dy, moe_dtype_t dy_dt, const void* y_perm,
+                                  moe_dtype_t y_dt, const int32_t* pair_row,
+                                  const float* topk_gate, int64_t T, int k, int d, float* dgate,
+                                  void* dout, void* stream) {
   if (T < 0 || k < 1 || d < 1)
     return fail(MOE_EINVAL, "moe_combine_backward: need T >= 0, k >= 1, d >= 1");
   if (!valid_dtype(dy_dt) || !valid_dtype(y_dt))
@@ -611,7 +612,8 @@ static moe_status_t check_bypass(const char* fn, int64_t T, int k, int d, int E_
   return MOE_OK;
 }
 
-moe_status_t moe_combine_backward_bypass(const void* dy, int dy_dt, const void* y_perm, int y_dt,
+moe_status_t moe_combine_backward_bypass(const void* dy, moe_dtype_t dy_dt,
+                                         const void* y_perm, moe_dtype_t y_dt,
                                          const int32_t* pair_row, const int32_t* topk_idx,
                                          const float* topk_gate, int64_t T, int k, int d,
                                          int E_ffn, int n_zero, int n_copy, int n_const,
@@ -638,7 +640,7 @@ size_t moe_bypass_backward_workspace(int64_t T, int d, int n_const) {
   return align256(moe::bypass_backward_workspace_bytes(T, d, n_const));
 }
 
-moe_status_t moe_bypass_backward(const void* dy, int dy_dt, const int32_t* topk_idx,
+moe_status_t moe_bypass_backward(const void* dy, moe_dtype_t dy_dt, const int32_t* topk_idx,
                                  const float* topk_gate, int64_t T, int k, int d, int E_ffn,
                                  int n_zero, int n_copy, int n_const, float* dx_acc, float* dconst,
                                  void* ws, size_t ws_bytes, void* stream) {
@@ -664,7 +666,7 @@ size_t moe_router_backward_workspace(int64_t T, int d, int E) {
   return align256(moe::router_backward_workspace_bytes(T, d, E));
 }
 
-moe_status_t moe_router_backward(const void* x, const void* w_router, int dt,
+moe_status_t moe_router_backward(const void* x, const void* w_router, moe_dtype_t dt,
                                  const float* dlogits, int64_t T, int d, int E, float* dw_router,
                                  float* dlogit_bias, float* dx, int accumulate_dx, void* ws,
                                  size_t ws_bytes, void* stream) {

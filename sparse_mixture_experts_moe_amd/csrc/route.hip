@@ -7,8 +7,9 @@
 //
 // Sources: "Every parameter, every token", section "The gating network";
 // "Zen MoDE: Mixture of Distilled Experts Architecture", section "Router
-// Architecture" (standard router equation) and section "Router" (ReLU gating,
-// an adaptive expert count per token); "Zen-Max: Maximum Capability via
+// Architecture" (standard router equation); "Zen MoDE: Mixture of Diverse
+// Experts", section "Router" (ReLU gating, an adaptive expert count per
+// token); "Zen-Max: Maximum Capability via
 // Mixture-of-Experts Architecture", section "Auxiliary-Loss-Free Load
 // Balancing" (selection-only bias).
 //

@@ -231,25 +231,17 @@ def test_expert_backward_groups(sizes, d, h, gather, dt):
             assert err <= (1e-4 if dt == "f32" else 2e-2), (g, name, err)
 
 
-def _silu(z):
-    return z / (1.0 + np.exp(-z))
-
-
-def _silu_grad(z):
-    s = 1.0 / (1.0 + np.exp(-z))
-    return s * (1.0 + z * (1.0 - s))
-
-
 @pytest.mark.parametrize("name,variant", [("mixtral_bf16", None), ("finegrained_shared_bf16", None),
+                                          ("capacity_balance_bf16", None),
                                           ("mixtral_bf16", "relu"), ("mixtral_bf16", "bypass")])
-def test_backward_full_size_sampled(name, variant):
+def test_backward_full_size(name, variant):
     """The training step at a workload's full size, in the bench's launch
     configuration (two streams; for a routing variant, the one of
-    ``bench.py --backward --variant``), checked on samples the oracle computes
-    one by one: gate and input gradients of sampled tokens, sampled entries of
-    every expert weight gradient, and the logit and router-weight gradients in
-    full on the GPU's own gate gradients (and the constant rows' gradient in
-    full)."""
+    ``bench.py --backward --variant``), against the oracle's whole backward
+    on the GPU's own logits: every token's gate and input gradients, every
+    logit and router-weight gradient, and every entry of every expert's (and
+    the shared experts') weight gradients, so that every tile of every
+    backward GEMM is compared."""
     from bench import BYPASS_COUNTS, RELU_K_MUL
     from moe_inputs import WORKLOADS, generate_bypass, relu_logit_offset
     from sparse_mixture_experts_moe_amd.workload import (bypass_layer_from_inputs,
@@ -262,6 +254,7 @@ def test_backward_full_size_sampled(name, variant):
     nz = nc = nk = 0
     if variant == "relu":
         k_run = min(cfg.E, RELU_K_MUL * cfg.k)
+        lb = relu_logit_bias(inp, relu_logit_offset(cfg, cfg.k))
         layer = relu_layer_from_inputs(inp, k_run, relu_logit_offset(cfg, cfg.k))
     elif variant == "bypass":
         k_run = cfg.k
@@ -277,114 +270,72 @@ def test_backward_full_size_sampled(name, variant):
     res = layer.forward(x, train=True)
     layer.backward(dy, c_bal, c_z)
     torch.cuda.synchronize()
-    _say(f"[case] full-size backward {name} {variant}: checking")
-    T, E, k, d, h = cfg.T, cfg.E, k_run, cfg.d, cfg.h
+    _say(f"[case] full-size backward {name} {variant}: oracle")
+    T, E, k = cfg.T, cfg.E, k_run
     xf, wr = as_f32(inp["x"]), as_f32(inp["w_router"])
-    if variant == "bypass":
-        wr = np.concatenate([wr, as_f32(rows)], 0)
-        cf = as_f32(const).astype(np.float64)
-    glg = oracle.relu_gate_logit_grad if variant == "relu" else oracle.gate_logit_grad
+    wg, wu, wd = as_f32(inp["w_gate"]), as_f32(inp["w_up"]), as_f32(inp["w_down"])
     dyf = as_f32(dy_h)
     gl = host(res["logits"])
-    idx = host(res["topk_idx"]).astype(np.int64)
-    gate = host(res["topk_gate"]).astype(np.float64)
-    pair_row = host(res["pair_row"]).reshape(T, k)
-    count = host(res["expert_count"])
-    off = host(res["expert_offset"])
-    rng = np.random.default_rng(7)
-    toks = np.sort(rng.choice(T, size=12, replace=False))
-    W = {}
-
-    def weights(e):
-        if e not in W:
-            W[e] = (inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
-        return W[e]
-
-    # gate and input gradients of the sampled tokens (routed part + router part)
+    cap = oracle.capacity(cfg.cf, T, cfg.k, E)
+    if variant == "relu":
+        ref = oracle.backward_relu(xf, wr, wg, wu, wd, k, dyf,
+                                   shared=shared_list(inp), logit_bias=lb, cap=cap,
+                                   alpha=cfg.alpha, c_bal=c_bal, c_z=c_z, logits=gl)
+        glg = oracle.relu_gate_logit_grad
+    elif variant == "bypass":
+        wr = np.concatenate([wr, as_f32(rows)], 0)
+        ref = oracle.backward_bypass(xf, wr, wg, wu, wd, k, nz, nc,
+                                     as_f32(const), dyf, shared=shared_list(inp), cap=cap,
+                                     alpha=cfg.alpha, c_bal=c_bal, c_z=c_z, logits=gl)
+        glg = oracle.gate_logit_grad
+    else:
+        ref = oracle.backward(xf, wr, wg, wu, wd, k, dyf,
+                              shared=shared_list(inp), logit_bias=inp["logit_bias"],
+                              select_bias=inp["select_bias"], cap=cap, alpha=cfg.alpha,
+                              c_bal=c_bal, c_z=c_z, logits=gl)
+        glg = oracle.gate_logit_grad
+    fw = ref["fwd"]
+    _say(f"[case] full-size backward {name} {variant}: checking")
+    # the selection and dispatch the gradients were taken for are the oracle's
+    assert np.array_equal(host(res["topk_idx"]), fw["topk_idx"])
+    assert np.array_equal(host(res["pair_row"]), fw["pair_row"])
+    errs = {}
+    # routing side on identical inputs (fp32 kernels)
     gdg = host(res["dgate"])
-    gdx = host(res["dx"])
-    dl_rows = glg(gl[toks], idx[toks], gdg[toks])
-    dl_rows = dl_rows + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)[toks]
-    dl_rows = dl_rows + c_z * oracle.z_loss_logit_grad(gl)[toks]
-    dg_ref = np.zeros((toks.size, k))
-    dx_ref = dl_rows @ wr.astype(np.float64)
-    for n, t in enumerate(toks):
-        for j in range(k):
-            if variant == "bypass" and idx[t, j] >= E:
-                kind, c = oracle.bypass_kind(int(idx[t, j]), E, nz, nc, nk)
-                if kind == "copy":
-                    dg_ref[n, j] = float(dyf[t] @ xf[t])
-                    dx_ref[n] += gate[t, j] * dyf[t]
-                elif kind == "const":
-                    dg_ref[n, j] = float(dyf[t] @ cf[c])
-                continue
-            if pair_row[t, j] < 0:
-                continue
-            wg, wu, wd = weights(int(idx[t, j]))
-            xt = xf[t].astype(np.float64)
-            dg_ref[n, j] = float(dyf[t] @ oracle.swiglu(xt[None], wg, wu, wd)[0])
-            dxs, _, _, _ = oracle.swiglu_backward(xt[None], wg, wu, wd, gate[t, j] * dyf[t][None])
-            dx_ref[n] += dxs[0]
-    for s in shared_list(inp):
-        dxs, _, _, _ = oracle.swiglu_backward(xf[toks], s[0], s[1], s[2], dyf[toks])
-        dx_ref += dxs
-    errs = {"dgate": normwise(gdg[toks], dg_ref), "dx": normwise(gdx[toks], dx_ref)}
-
-    # logits and router weights on the GPU's gate gradients (fp32 kernels)
-    dl_same = glg(gl, idx, gdg)
-    dl_same = dl_same + c_bal * oracle.balance_logit_grad(gl, count, k, cfg.alpha)
-    dl_same = dl_same + c_z * oracle.z_loss_logit_grad(gl)
     gdl = host(res["dlogits"])
+    dl_same = glg(gl, fw["topk_idx"], gdg)
+    dl_same = dl_same + c_bal * oracle.balance_logit_grad(gl, fw["count"], k, cfg.alpha)
+    dl_same = dl_same + c_z * oracle.z_loss_logit_grad(gl)
     errs["dlogits_same_in"] = normwise(gdl, dl_same)
     _, dwr_same, _ = oracle.router_linear_backward(xf, wr, gdl)
     errs["dw_router_same_in"] = normwise(host(res["dw_router"]), dwr_same)
-    if nk:  # the constant rows' gradient, in full
-        dc_ref = np.zeros((nk, d))
-        for c in range(nk):
-            t_, j_ = np.nonzero(idx == E + nz + nc + c)
-            dc_ref[c] = (gate[t_, j_][:, None] * dyf[t_]).sum(axis=0)
-        errs["dconst"] = normwise(host(res["dconst"])[:nk], dc_ref)
-        assert errs["dconst"] <= 1e-5, errs
-
-    # sampled weight-gradient entries of a few experts (all of each expert's rows)
-    row_pair = host(res["row_pair"])
-    dwg, dwu, dwd = res["dw_gate"], res["dw_up"], res["dw_down"]
-    worst = {"dw_gate": 0.0, "dw_up": 0.0, "dw_down": 0.0}
-    for e in (int(v) for v in rng.choice(E, size=min(3, E), replace=False)):
-        r0, r1 = int(off[e]), int(off[e + 1])
-        if r0 == r1:
-            assert float(dwg[e].abs().max()) == 0.0
-            continue
-        pairs = row_pair[r0:r1].astype(np.int64)
-        xs = xf[pairs // k].astype(np.float64)
-        dout = gate.reshape(-1)[pairs][:, None] * dyf[pairs // k]
-        wg, wu, wd = weights(e)
-        cols = rng.choice(h, size=6, replace=False)   # hidden units
-        feats = rng.choice(d, size=6, replace=False)  # model-width features
-        u = xs @ wg[cols].T.astype(np.float64)
-        v = xs @ wu[cols].T.astype(np.float64)
-        dh = dout @ wd[:, cols].astype(np.float64)
-        du = dh * v * _silu_grad(u)
-        dv = dh * _silu(u)
-        ref_g = du.T @ xs[:, feats]
-        ref_u = dv.T @ xs[:, feats]
-        ref_d = dout[:, feats].T @ (_silu(u) * v)
-        ci = torch.from_numpy(cols).cuda()
-        fi = torch.from_numpy(feats).cuda()
-        got_g = host(dwg[e].index_select(0, ci).index_select(1, fi))
-        got_u = host(dwu[e].index_select(0, ci).index_select(1, fi))
-        got_d = host(dwd[e].index_select(0, fi).index_select(1, ci))
-        # scale of each expert's gradient: its largest entry in the full GPU result
-        for key, got, ref, full in (("dw_gate", got_g, ref_g, dwg[e]), ("dw_up", got_u, ref_u, dwu[e]),
-                                    ("dw_down", got_d, ref_d, dwd[e])):
-            scale = float(full.abs().max())
-            worst[key] = max(worst[key], float(np.max(np.abs(got - ref))) / scale)
-    errs.update(worst)
+    assert errs["dlogits_same_in"] <= 1e-5 and errs["dw_router_same_in"] <= 1e-5, errs
+    # end to end against the float64 oracle, every entry
+    tol = 2e-2
+    for key in ("dgate", "dlogits", "dx", "dw_router"):
+        errs[key] = normwise(host(res[key]), ref[key])
+    if nk:
+        errs["dconst"] = normwise(host(res["dconst"])[:nk], ref["dconst"])
+    kept = fw["kept"]
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        worst = 0.0
+        for e in range(cfg.E):
+            got = host(res[key][e])
+            if kept[e] == 0:
+                assert np.all(got == 0.0), (key, e)
+                continue
+            worst = max(worst, normwise(got, ref[key][e]))
+        errs[key] = worst
+    if inp["shared_gate"] is not None:
+        got = _split_shared((host(res["shared_dw_gate"]), host(res["shared_dw_up"]),
+                             host(res["shared_dw_down"])), inp)
+        errs["shared"] = max(normwise(got[s][j], ref["dshared"][s][j])
+                             for s in range(len(got)) for j in range(3))
     _say(f"[ok] full-size backward {name} {variant}: " +
          ", ".join(f"{a}={b:.2e}" for a, b in errs.items()))
-    assert errs["dlogits_same_in"] <= 1e-5 and errs["dw_router_same_in"] <= 1e-5, errs
-    for key in ("dgate", "dx", "dw_gate", "dw_up", "dw_down"):
-        assert errs[key] <= 2e-2, errs
+    for key, v in errs.items():
+        if not key.endswith("_same_in"):
+            assert v <= tol, (key, errs)
 
 
 @pytest.mark.parametrize("T,E,k,d,dt,c_bal,c_z", [

@@ -264,18 +264,9 @@ def test_combine_isolated(with_shared):
 
 
 # ---------------------------------------------------------------------------
-# whole layer at the full workload sizes: every logit, every routing decision
-# and the permutation; outputs on sampled tokens
+# whole layer at the full workload sizes, in the bench's launch configuration:
+# every logit, every routing decision, the permutation and every output
 # ---------------------------------------------------------------------------
-def _sample_tokens(T, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    if T <= n:
-        return np.arange(T)
-    fixed = list(range(8)) + list(range(T - 8, T))
-    rest = rng.choice(np.arange(8, T - 8), size=n - 16, replace=False)
-    return np.sort(np.concatenate([fixed, rest]))
-
-
 @pytest.mark.parametrize("name", ["tiny_f32", "mixtral_bf16", "finegrained_shared_bf16",
                                   "capacity_balance_bf16", "decode_bf16"])
 def test_layer_full_size(name):
@@ -288,9 +279,13 @@ def test_layer_full_size(name):
     _say(f"[case] full-size {name}: running")
     res = layer(x)
     torch.cuda.synchronize()
-    _say(f"[case] full-size {name}: checking")
-    tokens = None if cfg.T <= 64 else _sample_tokens(cfg.T)
-    errs = check_layer(inp, res, tokens=tokens)
+    # every kept row of every group (so every tile, short tile, bundle and
+    # split-K part of both expert GEMMs) feeds a compared output row
+    pair_row = host(res["pair_row"])
+    R_kept = int(host(res["expert_offset"])[-1])
+    assert np.array_equal(np.sort(pair_row[pair_row >= 0]), np.arange(R_kept))
+    _say(f"[case] full-size {name}: checking all {cfg.T} tokens ({R_kept} expert rows)")
+    errs = check_layer(inp, res)
     _say(f"[ok] full-size {name}: {errs}")
 
 

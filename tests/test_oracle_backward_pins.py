@@ -14,7 +14,8 @@ that derivative without re-typing any of the oracle's formulas:
 
 Sources: "Every parameter, every token", sections "The gating network" (the
 selected set is held fixed, gradient flows through the gates of the experts
-that ran), "A balance penalty" and "A budget"; Zen MoDE, section "Auxiliary
+that ran), "A balance penalty" and "A budget"; "Zen MoDE: Mixture of Distilled Experts
+Architecture", section "Auxiliary
 Load Balancing Loss"; Zen-Max, sections "Fine-Grained Expert Architecture"
 and "MoE-Specific Training Stability".
 """

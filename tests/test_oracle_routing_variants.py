@@ -1,5 +1,5 @@
 """Pins of the routing-variant oracle (ReLU routing, zero-computation
-experts) from "Zen MoDE: Mixture of Distilled Experts Architecture", section
+experts) from "Zen MoDE: Mixture of Diverse Experts", section
 "Router": worked values, closed forms, special cases that reduce to the plain
 layer, and pure-Python brute force from the definitions (``tests/brute.py``
 style loops, written here without the oracle's code).  The last test plants
