@@ -913,8 +913,14 @@ __device__ __forceinline__ void gemm_tile(
 }
 
 // Next work item of a persistent workgroup on XCD x: a whole tile (or work
-// unit) of run x, else (n_parts > 0) a split-K part from the shared counter;
-// returns the item (>= 0), -2 - p for split part p, or -1 when none is left.
+// unit) of run x; once run x is empty, one of the other XCDs' runs, taken in
+// turn (x + 1, x + 2, ... mod 8) from the same counters, so that an XCD that
+// finishes early helps with the units another XCD has not started (the
+// estimated costs that cut the runs are only estimates); after all runs,
+// (n_parts > 0) a split-K part from the shared counter.  Returns the item
+// (>= 0), -2 - p for split part p, or -1 when none is left.  `victim`
+// (thread 0's, kept by the caller across calls) is the offset of the run
+// being taken from.
 // Thread 0 takes it from the counters and hands it to the four waves through
 // the first word of the third B stage: between two items no copy and no real
 // fragment read touches that word (it lies in row 0, which only wave 0's
@@ -922,17 +928,22 @@ __device__ __forceinline__ void gemm_tile(
 // previous item; the next item first writes the third stage after its
 // prologue barrier, which every wave reaches only after reading the word).
 __device__ __forceinline__ int next_work(const int32_t* __restrict__ runs, int32_t* counters, int x,
-                                         int n_parts, uint16_t* smem) {
+                                         int n_parts, uint16_t* smem, int& victim) {
   volatile int32_t* word =
       reinterpret_cast<volatile int32_t*>(smem + (kRingA * kTileM + 2 * 256) * kBK);
   if (threadIdx.x == 0) {
-    int code = runs[x] + atomicAdd(&counters[x], 1);
-    if (code >= runs[x + 1]) {
-      code = -1;
-      if (n_parts > 0) {
-        const int p = atomicAdd(&counters[kXcds], 1);
-        if (p < n_parts) code = -2 - p;
+    int code = -1;
+    for (; victim < kXcds; ++victim) {
+      const int v = (x + victim) & (kXcds - 1);
+      const int c = runs[v] + atomicAdd(&counters[v], 1);
+      if (c < runs[v + 1]) {
+        code = c;
+        break;
       }
+    }
+    if (code < 0 && n_parts > 0) {
+      const int p = atomicAdd(&counters[kXcds], 1);
+      if (p < n_parts) code = -2 - p;
     }
     *word = code;
   }
@@ -956,9 +967,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int32_t* runs = tt + tt_runs(G);
   int32_t* counters = tt + tt_counters(G);
   const int x = blockIdx.x % kXcds;
+  int victim = 0;
   if constexpr (kFused) {  // bundled order, no split
     for (;;) {
-      const int L = next_work(runs, counters, x, 0, smem);
+      const int L = next_work(runs, counters, x, 0, smem, victim);
       if (L < 0) return;
       const Unit u = unit_at(L, off, mstart, G, ntn);
       Tile t{u.g, u.m0, u.row_end, 0};
@@ -989,7 +1001,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const SkPlan plan = sk_plan(mstart[G] * ntn, ncu, nk_all, skw != nullptr);
     const int n_parts = plan.n_sk * plan.S;
     for (;;) {
-      const int code = next_work(runs, counters, x, n_parts, smem);
+      const int code = next_work(runs, counters, x, n_parts, smem, victim);
       if (code == -1) return;
       int L = code, ks0 = 0, nk = nk_all;
       float* part_out = nullptr;
