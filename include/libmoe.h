@@ -203,6 +203,23 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
                          int32_t* expert_offset, int32_t* pair_row, int32_t* row_pair,
                          void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute_noalloc: moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Arguments, results and
+ * errors are those of moe_permute; the workspace is instead a static device
+ * array of the library (5 MiB per device, held until the process ends), so
+ * T*k may be at most 1048576 pairs (MOE_EUNSUPPORTED beyond) and E at most
+ * MOE_MAX_EXPERTS.  The call allocates nothing.  Every call on a device
+ * shares that device's array: calls that overlap on one device (concurrent
+ * streams, several host threads) race and must be serialised by the caller.
+ * The first call on a device looks up the array's device address (with that
+ * device current); a failure there returns MOE_EHIP. */
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
+                                 int64_t capacity, const void* x, moe_dtype_t dt, int d,
+                                 int32_t* expert_count, int32_t* expert_offset,
+                                 int32_t* pair_row, int32_t* row_pair, void* x_perm,
+                                 void* stream);
+
 /* moe_permute_budgets: moe_permute with one budget per expert,
  *   kept(p) = rank(p) < expert_capacity[topk_idx[p]]
  * (expert_capacity [E] int32 on the device, each >= 0; everything else as

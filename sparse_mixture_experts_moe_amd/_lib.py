@@ -55,6 +55,7 @@ _SIGS = {
     "moe_permute": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute_budgets": (_i, [_p, _i64, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _sz,
                                  _p]),
+    "moe_permute_noalloc": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "moe_balance_update": (_i, [_p, _i64, _i, _i, _p, _f, _p, _f, _d, _d, _p, _p]),
     "moe_expert_swiglu_workspace": (_sz, [_i64, _i, _i, _i, _i]),
     "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
@@ -212,6 +213,35 @@ def moe_permute(topk_idx, E, capacity=-1, x=None, *, expert_count=None, expert_o
     _check(_L.moe_permute(_ptr(topk_idx), T, k, E, int(capacity), _ptr(x), dt, d,
                           _ptr(expert_count), _ptr(expert_offset), _ptr(pair_row),
                           _ptr(row_pair), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream)))
+    return expert_count, expert_offset, pair_row, row_pair, x_perm
+
+
+def moe_permute_noalloc(topk_idx, E, capacity=-1, x=None, *, expert_count=None,
+                        expert_offset=None, pair_row=None, row_pair=None, x_perm=None,
+                        stream=None):
+    """moe_permute with the library's static scratch instead of a workspace
+    (the call allocates no device memory; outputs not given are allocated
+    here, before it)."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    R = T * k
+    if expert_count is None:
+        expert_count = torch.empty(E, dtype=torch.int32, device=dev)
+    if expert_offset is None:
+        expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if pair_row is None:
+        pair_row = torch.empty(R, dtype=torch.int32, device=dev)
+    if row_pair is None:
+        row_pair = torch.empty(R, dtype=torch.int32, device=dev)
+    dt, d = MOE_F32, 0
+    if x is not None:
+        dt, d = _dt(x), x.shape[1]
+        if x_perm is None:
+            x_perm = torch.empty((R, d), dtype=x.dtype, device=dev)
+    _contig(topk_idx, x, expert_count, expert_offset, pair_row, row_pair, x_perm)
+    _check(_L.moe_permute_noalloc(_ptr(topk_idx), T, k, E, int(capacity), _ptr(x), dt, d,
+                                  _ptr(expert_count), _ptr(expert_offset), _ptr(pair_row),
+                                  _ptr(row_pair), _ptr(x_perm), _stream(stream)))
     return expert_count, expert_offset, pair_row, row_pair, x_perm
 
 

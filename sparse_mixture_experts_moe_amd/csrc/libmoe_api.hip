@@ -234,6 +234,89 @@ moe_status_t moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, int64
                     "moe_permute");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of moe_permute_noalloc: moe_permute's workspace (the local ranks,
+// int32 [T k], then the per-chunk histograms, int32 [chunks, E]) for at most
+// kNoAllocMaxPairs pairs and kMaxExperts experts, 5 MiB.  Each device that
+// runs the library holds its own copy until the process ends.  Every word a
+// call reads is written earlier in the same call, so nothing needs clearing.
+constexpr int64_t kNoAllocMaxPairs = int64_t{1} << 20;
+constexpr size_t kNoAllocRankBytes = sizeof(int32_t) * static_cast<size_t>(kNoAllocMaxPairs);
+constexpr size_t kNoAllocScratchBytes =
+    kNoAllocRankBytes +
+    sizeof(int32_t) * static_cast<size_t>((kNoAllocMaxPairs + 1023) / 1024) * moe::kMaxExperts;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of this device's `scratch` (in host code the array's name is
+// only a stand-in, not a device address), looked up once per device with that
+// device current.  nullptr with `err` set if the lookup fails.
+void* scratch_address(hipError_t& err) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
+                                 int64_t capacity, const void* x, moe_dtype_t dt, int d,
+                                 int32_t* expert_count, int32_t* expert_offset,
+                                 int32_t* pair_row, int32_t* row_pair, void* x_perm,
+                                 void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_permute_noalloc: T < 0");
+  if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_permute_noalloc: need 1 <= k <= E");
+  if (!expert_count || !expert_offset) return fail(MOE_EINVAL, "moe_permute_noalloc: NULL pointer");
+  if (T > 0 && (!topk_idx || !pair_row || !row_pair))
+    return fail(MOE_EINVAL, "moe_permute_noalloc: NULL pointer");
+  if (x && (!x_perm || d < 1 || !valid_dtype(dt)))
+    return fail(MOE_EINVAL, "moe_permute_noalloc: gather needs x_perm, d >= 1 and a valid dtype");
+  if (E > moe::kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "moe_permute_noalloc: E > %d", moe::kMaxExperts);
+  if (T > kNoAllocMaxPairs || T * k > kNoAllocMaxPairs)
+    return fail(MOE_EUNSUPPORTED,
+                "moe_permute_noalloc: T*k = %lld pairs exceeds the static scratch (%lld pairs)",
+                static_cast<long long>(T) * k, static_cast<long long>(kNoAllocMaxPairs));
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    e = moe::launch_fill_i32(expert_count, E, 0, as_stream(stream));
+    if (e == hipSuccess) e = moe::launch_fill_i32(expert_offset, E + 1, 0, as_stream(stream));
+    return hip_status(e, "moe_permute_noalloc");
+  }
+  if (static_cast<size_t>(moe::permute_chunks(T * k)) * E * sizeof(int32_t) >
+      kNoAllocScratchBytes - kNoAllocRankBytes)
+    return fail(MOE_EUNSUPPORTED, "moe_permute_noalloc: histograms exceed the static scratch");
+  void* ws = scratch_address(e);
+  if (!ws) return hip_status(e, "moe_permute_noalloc: hipGetSymbolAddress(scratch)");
+  int32_t* local_rank = static_cast<int32_t*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kNoAllocRankBytes);
+  return hip_status(moe::launch_permute(topk_idx, T, k, E, capacity, nullptr, x, elem_bytes(dt), d,
+                                        expert_count, expert_offset, pair_row, row_pair, x_perm,
+                                        local_rank, hist, as_stream(stream)),
+                    "moe_permute_noalloc");
+}
+
 moe_status_t moe_permute_budgets(const int32_t* topk_idx, int64_t T, int k, int E,
                                  const int32_t* expert_capacity, const void* x, moe_dtype_t dt,
                                  int d, int32_t* expert_count, int32_t* expert_offset,

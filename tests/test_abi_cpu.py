@@ -126,6 +126,25 @@ def test_permute_rejects():
     assert s == L.MOE_EINVAL
 
 
+def test_permute_noalloc_rejects():
+    """The no-allocation permute checks its arguments, and the static scratch's
+    limit of 2^20 pairs, on the host before it looks up the scratch or
+    launches anything."""
+    s = C.moe_permute_noalloc(FAKE, 131072 + 1, 8, 8, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE,
+                              None, None)
+    assert s == L.MOE_EUNSUPPORTED and "scratch" in _err()
+    s = C.moe_permute_noalloc(FAKE, 100, 2, 300, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None,
+                              None)
+    assert s == L.MOE_EUNSUPPORTED
+    s = C.moe_permute_noalloc(FAKE, 100, 3, 2, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert s == L.MOE_EINVAL
+    s = C.moe_permute_noalloc(None, 100, 2, 8, -1, None, 0, 0, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert s == L.MOE_EINVAL
+    s = C.moe_permute_noalloc(FAKE, 100, 2, 8, -1, FAKE, L.MOE_BF16, 64, FAKE, FAKE, FAKE, FAKE,
+                              None, None)
+    assert s == L.MOE_EINVAL and "x_perm" in _err()
+
+
 def test_expert_swiglu_rejects():
     ws = L.moe_expert_swiglu_workspace(1000, 128, 256, 8, L.MOE_BF16)
     assert ws >= 1000 * 256 * 2
