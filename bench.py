@@ -14,6 +14,7 @@ throughput on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -96,6 +97,16 @@ def recorded_traffic(workload):
     if not sha or not val or sha.group(1) != gate_up_sources():
         return None
     return float(val.group(1))
+
+
+def timing_events(torch, stream, n):
+    """n timing events, each recorded once on ``stream`` (which creates the
+    HIP event) and completed, ready to be recorded again in a timed region."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for ev in evs:
+        ev.record(stream)
+    torch.cuda.synchronize()
+    return evs
 
 
 def _median_ms(torch, fn, warmup=3, reps=7):
@@ -304,22 +315,25 @@ def main_backward(args):
     torch.cuda.synchronize()
 
     # timed region: events only around the expert backward call (the roofline)
+    events = timing_events(torch, stream, 2 * args.steps + 2)
     ex_marks = []
 
     def mark_experts(name):
         if name in ("route_bwd", "experts_bwd"):  # enqueued right before / after the call
-            ev = torch.cuda.Event(enable_timing=True)
+            ev = events.pop()
             ev.record(stream)
             ex_marks[-1].append(ev)
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    start, end = events.pop(), events.pop()
+    gc.collect()
+    gc.disable()
     start.record(stream)
     for _ in range(args.steps):
         ex_marks.append([])
         layer.forward(x, train=True)
         res = layer.backward(dy, c_bal, c_z, mark=mark_experts)
     end.record(stream)
+    gc.enable()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     ex_ms = float(np.mean([a.elapsed_time(b) for a, b in ex_marks]))
@@ -481,17 +495,22 @@ def measure_forward(args, cfg, ceil=None, extra=False):
     # the gate/up call (each event recorded on the stream delays the next
     # kernel by a few microseconds, so the per-phase events are kept out of
     # it).  Consecutive gate/up start events give the per-step durations.
+    # The events are created (recorded once) before the timed region and
+    # Python's garbage collector is paused inside it, so that neither event
+    # creation nor a collection stalls the host while it enqueues the steps.
+    events = timing_events(torch, stream, 2 * args.steps + 2)
     gu_marks = []
 
     def mark_gate_up(name):
         if name in ("permute", "gate_up"):  # enqueued right before / after the gate/up call
-            ev = torch.cuda.Event(enable_timing=True)
+            ev = events.pop()
             ev.record(stream)
             gu_marks[-1].append(ev)
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    start, end = events.pop(), events.pop()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     start.record(stream)
     t_host = time.perf_counter()
     for _ in range(args.steps):
@@ -499,6 +518,7 @@ def measure_forward(args, cfg, ceil=None, extra=False):
         res = step(mark_gate_up)
     end.record(stream)
     host_ms = (time.perf_counter() - t_host) * 1e3 / args.steps  # enqueue cost per step
+    gc.enable()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -261,10 +261,7 @@ moe_status_t moe_balance_update(const int32_t* expert_count, int64_t T, int k, i
 /* moe_expert_swiglu: G SwiGLU experts over contiguous row groups.
  *
  * For each group g and each row r in [group_offset[g], group_offset[g+1]):
- *   a_r     = a[r]                       if a_rows == NULL
- *           = a[a_rows[r] / a_rows_div]  otherwise (gathers token rows
- *             straight from x through moe_permute's row_pair, div = k)
- *   u       = a_r . w_gate[g]^T,  v = a_r . w_up[g]^T             ([h])
+ *   u       = a[r] . w_gate[g]^T,  v = a[r] . w_up[g]^T           ([h])
  *   hid     = SiLU(u) * v,  SiLU(z) = z / (1 + exp(-z))
  *   y[r]    = hid . w_down[g]^T                                   ([d])
  * Source: Zen-Max, section "Fine-Grained Expert Architecture", expert
@@ -273,27 +270,37 @@ moe_status_t moe_balance_update(const int32_t* expert_count, int64_t T, int k, i
  * concatenated along the hidden axis (sum_s SwiGLU_s = SwiGLU of the
  * concatenation, exactly).
  *
- * a [*, d] in dtype dt; weights in dtype dt; products accumulate in fp32;
- * the hidden activation is stored in dtype dt (bf16: rounded to nearest
+ * a [max_rows, d] in dtype dt; weights in dtype dt; products accumulate in
+ * fp32; the hidden activation is stored in dtype dt (bf16: rounded to nearest
  * even).  group_offset [G+1] int32 on the device, non-decreasing, with
  * group_offset[0] == 0 and group_offset[G] <= max_rows (host bound).
- * a_rows [max_rows] int32 or NULL; a_rows_div >= 1.
  * y [max_rows, d] in dtype y_dt (rows past group_offset[G] untouched).
  * Limits: bf16 needs d % 64 == 0, h % 64 == 0 and 2 d h < 2^32 (one
  * expert's weight matrix addressed with 32-bit offsets), else
  * MOE_EUNSUPPORTED.
  * Workspace: moe_expert_swiglu_workspace(max_rows, d, h, G, dt) bytes.
+ *
+ * moe_expert_swiglu_gather: the same with the rows read through an index,
+ *   a_r = a[r]                       if a_rows == NULL
+ *       = a[a_rows[r] / a_rows_div]  otherwise (token rows straight from x
+ *         through moe_permute's row_pair, a_rows_div = k),
+ * a_rows [max_rows] int32 or NULL, a_rows_div >= 1 (MOE_EINVAL otherwise).
  */
 size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, moe_dtype_t dt);
 moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,
-                               const int32_t* group_offset, int64_t max_rows,
-                               const int32_t* a_rows, int a_rows_div,
-                               const void* w_gate, const void* w_up, const void* w_down,
-                               void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream);
+                               const int32_t* group_offset, int64_t max_rows, const void* w_gate,
+                               const void* w_up, const void* w_down, void* y, moe_dtype_t y_dt,
+                               void* ws, size_t ws_bytes, void* stream);
+moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                      const int32_t* group_offset, int64_t max_rows,
+                                      const int32_t* a_rows, int a_rows_div,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
+                                      void* stream);
 
-/* The two halves of moe_expert_swiglu, for callers that keep the hidden
- * activation or time the two expert GEMMs apart (same sources, limits and
- * row-group semantics as moe_expert_swiglu).
+/* The two halves of moe_expert_swiglu_gather, for callers that keep the
+ * hidden activation or time the two expert GEMMs apart (same sources, limits
+ * and row-group semantics as moe_expert_swiglu_gather).
  *
  * moe_expert_gate_up: hid[r, :] = SiLU(a_r . w_gate[g]^T) * (a_r . w_up[g]^T)
  *   for r < group_offset[G]; hid [max_rows, h] in dtype dt (rows past
@@ -367,7 +374,7 @@ moe_status_t moe_combine_bypass(const void* y_perm, moe_dtype_t y_dt, const int3
                                 void* out, moe_dtype_t out_dt, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* moe_balance_stats: Switch balance statistics and the router z-loss.
+/* moe_balance_stats(_z): Switch balance statistics and the router z-loss.
  *
  *   f[e]  = expert_count[e] / (T * k)       (pre-drop counts; sum f = 1)
  *   P[e]  = (1/T) sum_t softmax(logits[t,:])[e]
@@ -383,20 +390,24 @@ moe_status_t moe_combine_bypass(const void* y_perm, moe_dtype_t y_dt, const int3
  * bias excluded); N = E.
  *
  * logits [T,E] fp32; expert_count [E] int32; outputs fp32: f [E], P [E],
- * loss [1], zloss [1] (zloss may be NULL).  Sums are fixed-order.
- * Workspace: moe_balance_stats_workspace(T, E) bytes.
+ * loss [1]; moe_balance_stats_z also writes zloss [1] (zloss may be NULL
+ * there).  Sums are fixed-order.
+ * Workspace: moe_balance_stats_workspace(T, E) bytes (both calls).
  */
 size_t moe_balance_stats_workspace(int64_t T, int E);
 moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
                                int E, int k, float alpha, float* f, float* P, float* loss,
-                               float* zloss, void* ws, size_t ws_bytes, void* stream);
+                               void* ws, size_t ws_bytes, void* stream);
+moe_status_t moe_balance_stats_z(const float* logits, const int32_t* expert_count, int64_t T,
+                                 int E, int k, float alpha, float* f, float* P, float* loss,
+                                 float* zloss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Backward pass.
  *
  * The objective differentiated is J = <dy, y> + coef_balance * loss +
  * coef_z * zloss, with y the layer output, dy its upstream gradient and
- * loss, zloss the outputs of moe_balance_stats.  Sources: "Every parameter,
+ * loss, zloss the outputs of moe_balance_stats_z.  Sources: "Every parameter,
  * every token", section "The gating network" (the selected set is held fixed
  * on the way forward; gradient reaches the router only through the gate
  * weights of the experts that ran; an expert that was off for a token gets no
@@ -435,7 +446,7 @@ moe_status_t moe_expert_gate_up_train(const void* a, moe_dtype_t dt, int d, int 
                                       size_t ws_bytes, void* stream);
 
 /* moe_expert_swiglu_backward: gradients of G SwiGLU experts over row groups
- * (same group semantics, gather and limits as moe_expert_swiglu).  For row r
+ * (same group semantics, gather and limits as moe_expert_swiglu_gather).  For row r
  * of group g with a_r = a[a_rows[r] / a_rows_div] (or a[r]) and dout_r the
  * upstream gradient of the row's expert output (gate already applied):
  *   u, v    = uv[r, 0::2], uv[r, 1::2]    (from moe_expert_gate_up_train)

@@ -58,7 +58,9 @@ _SIGS = {
     "moe_permute_noalloc": (_i, [_p, _i64, _i, _i, _i64, _p, _i, _i, _p, _p, _p, _p, _p, _p]),
     "moe_balance_update": (_i, [_p, _i64, _i, _i, _p, _f, _p, _f, _d, _d, _p, _p]),
     "moe_expert_swiglu_workspace": (_sz, [_i64, _i, _i, _i, _i]),
-    "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
+    "moe_expert_swiglu": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _p, _p, _p, _i, _p, _sz, _p]),
+    "moe_expert_swiglu_gather": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i,
+                                      _p,
                                _sz, _p]),
     "moe_expert_group_workspace": (_sz, [_i]),
     "moe_expert_down_workspace": (_sz, [_i]),
@@ -68,7 +70,8 @@ _SIGS = {
     "moe_combine_bypass": (_i, [_p, _i, _p, _p, _p, _i64, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
                                 _i, _p]),
     "moe_balance_stats_workspace": (_sz, [_i64, _i]),
-    "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_balance_stats": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _sz, _p]),
+    "moe_balance_stats_z": (_i, [_p, _p, _i64, _i, _i, _f, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_gate_up_train": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _p,
                                       _sz, _p]),
     "moe_expert_swiglu_backward_workspace": (_sz, [_i64, _i, _i, _i, _i, _i]),
@@ -298,7 +301,9 @@ def moe_expert_swiglu_workspace(max_rows, d, h, G, dt) -> int:
 
 def moe_expert_swiglu(a, group_offset, max_rows, w_gate, w_up, w_down, *, a_rows=None,
                       a_rows_div=1, y=None, y_dtype=None, ws=None, stream=None):
-    """G SwiGLU experts over contiguous row groups: y[r] = SwiGLU_g(a_r)."""
+    """G SwiGLU experts over contiguous row groups: y[r] = SwiGLU_g(a_r), with
+    a_r = a[a_rows[r] // a_rows_div] when ``a_rows`` is given
+    (moe_expert_swiglu_gather), else a[r] (moe_expert_swiglu)."""
     G, h, d = w_gate.shape
     dt = _dt(a)
     dev = a.device
@@ -308,10 +313,15 @@ def moe_expert_swiglu(a, group_offset, max_rows, w_gate, w_up, w_down, *, a_rows
     if ws is None:
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _contig(a, group_offset, a_rows, w_gate, w_up, w_down, y, ws)
-    _check(_L.moe_expert_swiglu(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
-                                _ptr(a_rows), a_rows_div, _ptr(w_gate), _ptr(w_up),
-                                _ptr(w_down), _ptr(y), _dt(y), _ptr(ws), ws.numel(),
-                                _stream(stream)))
+    if a_rows is None:
+        _check(_L.moe_expert_swiglu(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
+                                    _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _dt(y),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(_L.moe_expert_swiglu_gather(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
+                                           _ptr(a_rows), a_rows_div, _ptr(w_gate), _ptr(w_up),
+                                           _ptr(w_down), _ptr(y), _dt(y), _ptr(ws), ws.numel(),
+                                           _stream(stream)))
     return y
 
 
@@ -401,20 +411,27 @@ def moe_balance_stats_workspace(T, E) -> int:
 
 def moe_balance_stats(logits, expert_count, k, alpha=0.01, *, f=None, P=None, loss=None,
                       zloss=None, ws=None, stream=None):
-    """Switch balance statistics f, P, alpha*E*sum(f*P) and the router z-loss."""
+    """Switch balance statistics f, P, alpha*E*sum(f*P) and the router z-loss
+    (moe_balance_stats_z; with ``zloss=False``, moe_balance_stats and no z-loss)."""
     T, E = logits.shape
     dev = logits.device
     f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
     P = torch.empty(E, dtype=torch.float32, device=dev) if P is None else P
     loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
-    zloss = torch.empty(1, dtype=torch.float32, device=dev) if zloss is None else zloss
     nws = moe_balance_stats_workspace(T, E)
     if ws is None:
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    if zloss is False:
+        _contig(logits, expert_count, f, P, loss, ws)
+        _check(_L.moe_balance_stats(_ptr(logits), _ptr(expert_count), T, E, k, float(alpha),
+                                    _ptr(f), _ptr(P), _ptr(loss), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+        return f, P, loss, None
+    zloss = torch.empty(1, dtype=torch.float32, device=dev) if zloss is None else zloss
     _contig(logits, expert_count, f, P, loss, zloss, ws)
-    _check(_L.moe_balance_stats(_ptr(logits), _ptr(expert_count), T, E, k, float(alpha),
-                                _ptr(f), _ptr(P), _ptr(loss), _ptr(zloss), _ptr(ws), ws.numel(),
-                                _stream(stream)))
+    _check(_L.moe_balance_stats_z(_ptr(logits), _ptr(expert_count), T, E, k, float(alpha),
+                                  _ptr(f), _ptr(P), _ptr(loss), _ptr(zloss), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
     return f, P, loss, zloss
 
 

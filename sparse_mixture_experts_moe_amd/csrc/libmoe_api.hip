@@ -466,11 +466,12 @@ moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int 
   return hip_status(moe::launch_down(s, as_stream(stream)), "moe_expert_down");
 }
 
-moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,
-                               const int32_t* group_offset, int64_t max_rows,
-                               const int32_t* a_rows, int a_rows_div,
-                               const void* w_gate, const void* w_up, const void* w_down,
-                               void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                      const int32_t* group_offset, int64_t max_rows,
+                                      const int32_t* a_rows, int a_rows_div,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
+                                      void* stream) {
   moe_status_t st = check_experts("moe_expert_swiglu", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -489,6 +490,14 @@ moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int 
   if (st != MOE_OK) return st;
   return moe_expert_down(hid, dt, d, h, G, group_offset, max_rows, w_down, y, y_dt, table,
                          ws_bytes - hid_bytes, stream);
+}
+
+moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,
+                               const int32_t* group_offset, int64_t max_rows, const void* w_gate,
+                               const void* w_up, const void* w_down, void* y, moe_dtype_t y_dt,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return moe_expert_swiglu_gather(a, dt, d, h, G, group_offset, max_rows, nullptr, 1, w_gate,
+                                  w_up, w_down, y, y_dt, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -783,9 +792,9 @@ size_t moe_balance_stats_workspace(int64_t T, int E) {
   return align256(sizeof(float) * nb * E) + align256(sizeof(float) * nb);
 }
 
-moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
-                               int E, int k, float alpha, float* f, float* P, float* loss,
-                               float* zloss, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_balance_stats_z(const float* logits, const int32_t* expert_count, int64_t T,
+                                 int E, int k, float alpha, float* f, float* P, float* loss,
+                                 float* zloss, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "moe_balance_stats: T < 0");
   if (E < 1 || k < 1 || k > E) return fail(MOE_EINVAL, "moe_balance_stats: need 1 <= k <= E");
   if (!expert_count || !f || !P || !loss || (T > 0 && !logits))
@@ -810,6 +819,13 @@ moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count,
   return hip_status(moe::launch_balance_stats(logits, expert_count, T, E, k, alpha, f, P, loss,
                                               zloss, part, zpart, as_stream(stream)),
                     "moe_balance_stats");
+}
+
+moe_status_t moe_balance_stats(const float* logits, const int32_t* expert_count, int64_t T,
+                               int E, int k, float alpha, float* f, float* P, float* loss,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return moe_balance_stats_z(logits, expert_count, T, E, k, alpha, f, P, loss, nullptr, ws,
+                             ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert L.moe_status_string(L.MOE_OK) == "ok"
     assert L.moe_status_string(L.MOE_EWORKSPACE) == "workspace too small"
     assert L.moe_status_string(99) == "unknown status"
@@ -153,9 +153,9 @@ def test_expert_swiglu_rejects():
 
     def call(**kw):
         a = dict(args, **kw)
-        return C.moe_expert_swiglu(a["a"], a["dt"], a["d"], a["h"], a["G"], a["off"], a["mr"],
-                                   a["rows"], a["div"], a["wg"], a["wu"], a["wd"], a["y"],
-                                   a["ydt"], a["ws"], a["nws"], None)
+        return C.moe_expert_swiglu_gather(a["a"], a["dt"], a["d"], a["h"], a["G"], a["off"],
+                                          a["mr"], a["rows"], a["div"], a["wg"], a["wu"], a["wd"],
+                                          a["y"], a["ydt"], a["ws"], a["nws"], None)
 
     assert call(nws=ws - 1) == L.MOE_EWORKSPACE
     assert call(d=100) == L.MOE_EUNSUPPORTED
@@ -170,6 +170,11 @@ def test_expert_swiglu_rejects():
     assert call(ydt=5) == L.MOE_EINVAL
     # no rows: nothing to do
     assert call(mr=0, nws=L.moe_expert_swiglu_workspace(0, 128, 256, 8, L.MOE_BF16)) == L.MOE_OK
+    # the call without the row index (the survey's signature) checks the same way
+    assert C.moe_expert_swiglu(FAKE, L.MOE_BF16, 128, 256, 8, FAKE, 1000, FAKE, FAKE, FAKE, FAKE,
+                               L.MOE_BF16, FAKE, ws - 1, None) == L.MOE_EWORKSPACE
+    assert C.moe_expert_swiglu(FAKE, L.MOE_BF16, 100, 256, 8, FAKE, 1000, FAKE, FAKE, FAKE, FAKE,
+                               L.MOE_BF16, FAKE, ws, None) == L.MOE_EUNSUPPORTED
 
 
 def test_combine_and_stats_reject():
@@ -180,11 +185,16 @@ def test_combine_and_stats_reject():
     assert C.moe_combine(FAKE, L.MOE_BF16, FAKE, FAKE, 0, 2, 64, None, FAKE, L.MOE_BF16,
                          None) == L.MOE_OK
     ws = L.moe_balance_stats_workspace(1000, 64)
-    assert C.moe_balance_stats(FAKE, FAKE, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws - 1,
+    assert C.moe_balance_stats_z(FAKE, FAKE, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE,
+                                 ws - 1, None) == L.MOE_EWORKSPACE
+    assert C.moe_balance_stats_z(FAKE, FAKE, 1000, 300, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
+                                 None) == L.MOE_EUNSUPPORTED
+    assert C.moe_balance_stats_z(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
+                                 None) == L.MOE_EINVAL
+    # without the z-loss output (the survey's signature)
+    assert C.moe_balance_stats(FAKE, FAKE, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, FAKE, ws - 1,
                                None) == L.MOE_EWORKSPACE
-    assert C.moe_balance_stats(FAKE, FAKE, 1000, 300, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
-                               None) == L.MOE_EUNSUPPORTED
-    assert C.moe_balance_stats(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
+    assert C.moe_balance_stats(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, FAKE, ws,
                                None) == L.MOE_EINVAL
 
 

@@ -231,6 +231,35 @@ def test_expert_swiglu_groups(sizes, d, h, dt):
 # ---------------------------------------------------------------------------
 # moe_combine in isolation: oracle expert outputs in, oracle layer output out
 # ---------------------------------------------------------------------------
+def test_plain_and_extended_calls_agree():
+    """moe_expert_swiglu (no row index) against moe_expert_swiglu_gather with
+    the identity index, and moe_balance_stats against moe_balance_stats_z:
+    the same kernels, so the same bits."""
+    from sparse_mixture_experts_moe_amd import _lib
+    _say("[case] plain and extended entry points")
+    rng = np.random.default_rng(11)
+    G, d, h = 5, 128, 192
+    off = np.array([0, 0, 70, 300, 301, 560], dtype=np.int32)
+    R = int(off[-1])
+    a = torch.from_numpy(rng.standard_normal((R, d)).astype(np.float32)).cuda().to(torch.bfloat16)
+    wg, wu = (torch.from_numpy((rng.standard_normal((G, h, d)) / np.sqrt(d)).astype(np.float32))
+              .cuda().to(torch.bfloat16) for _ in range(2))
+    wd = torch.from_numpy((rng.standard_normal((G, d, h)) / np.sqrt(h)).astype(np.float32)).cuda() \
+        .to(torch.bfloat16)
+    goff = torch.from_numpy(off).cuda()
+    y0 = _lib.moe_expert_swiglu(a, goff, R, wg, wu, wd)
+    rows = torch.arange(R, dtype=torch.int32, device="cuda")
+    y1 = _lib.moe_expert_swiglu(a, goff, R, wg, wu, wd, a_rows=rows, a_rows_div=1)
+    logits = torch.from_numpy(rng.standard_normal((777, 40)).astype(np.float32)).cuda()
+    counts = torch.from_numpy(rng.integers(0, 60, 40).astype(np.int32)).cuda()
+    f0, P0, l0, z0 = _lib.moe_balance_stats(logits, counts, 3, 0.01, zloss=False)
+    f1, P1, l1, z1 = _lib.moe_balance_stats(logits, counts, 3, 0.01)
+    torch.cuda.synchronize()
+    assert z0 is None and z1 is not None
+    assert torch.equal(y0, y1)
+    assert torch.equal(f0, f1) and torch.equal(P0, P1) and torch.equal(l0, l1)
+
+
 @pytest.mark.parametrize("with_shared", [False, True])
 def test_combine_isolated(with_shared):
     from sparse_mixture_experts_moe_amd import _lib
