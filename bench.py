@@ -148,7 +148,8 @@ def measured_ceilings(torch, gemm_shape):
     del buf, rout
     res = {"mfma_bf16_tflops": mfma, "hbm_read_gbs": hbm,
            "how": f"MFMA: {ncu} workgroups x 4 waves x {iters} x 16 v_mfma_f32_32x32x16_bf16 on "
-                  "random-normal register operands; read: 4 GiB streamed once in 16-byte loads; "
+                  "random-normal register operands; read: 4 GiB streamed once in 16-byte non-temporal loads, "
+                  "16 in flight per lane; "
                   "median of 7 launches after 3"}
     if gemm_shape is not None:
         M, K, N = gemm_shape

@@ -51,12 +51,14 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_ceiling_kernel(const bf16x
   out[lane_id] = s;
 }
 
-// Grid-stride read of n 16-byte words, eight loads in flight per lane; every
-// lane folds what it read with XOR and stores one word.
+// Grid-stride read of n 16-byte words, sixteen non-temporal loads in flight
+// per lane (each word is read once; measured: 6.4-6.5 TB/s with 8192
+// workgroups, against 5.9 with eight ordinary loads in flight); every lane
+// folds what it read with XOR and stores one word.
 __global__ __launch_bounds__(kProbeThreads) void read_ceiling_kernel(const u32x4* __restrict__ p,
                                                                      size_t n,
                                                                      uint32_t* __restrict__ out) {
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = 16;
   const size_t tid = static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
   const size_t stride = static_cast<size_t>(gridDim.x) * kProbeThreads;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_ceiling_kernel(const u32x4
   for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
   }
