@@ -4,9 +4,12 @@ balance statistics).  Buffers are allocated on the first call for a token
 count and reused afterwards, so repeated calls allocate nothing.
 
 The shared experts depend on x alone, so by default they run on a second
-stream (default priority) from the start of the call, overlapping the routing
-and the routed experts; the balance statistics follow them there once the
-routing is done, and the combine waits for both.
+stream (default priority) beside the routed path: from the start of the call
+when the library streams their weights for a few rows (at most 64 tokens),
+where they overlap the latency-bound routing; otherwise once the routing is
+done, since their tiled GEMM launches hold every compute unit until they end
+and the routing kernels would wait behind them.  The balance statistics
+follow them there once the routing is done, and the combine waits for both.
 
 The layer output excludes the residual ("Every parameter, every token",
 section "The gating network": the weighted sum is added back to the residual
@@ -25,6 +28,12 @@ import torch
 from . import _lib
 
 
+# Up to this many rows per group the library runs an expert GEMM as a weight
+# stream (few rows, every weight read once) rather than as MFMA tiles; the
+# shared experts are one group of T rows.
+SHARED_STREAM_ROWS = 64
+
+
 class MoELayer:
     def __init__(self, w_router, w_gate, w_up, w_down, k, *, shared=None, logit_bias=None,
                  select_bias=None, capacity=-1, alpha=0.01, gather="fused",
@@ -36,7 +45,7 @@ class MoELayer:
         axis.  ``capacity`` < 0 means unlimited.  ``gather`` is "fused" (the
         first expert GEMM reads token rows through the permutation) or "copy"
         (moe_permute writes an expert-ordered copy of x first).  ``overlap_shared``
-        runs the shared experts on a second stream.  ``bias_on_probs`` adds
+        runs the shared experts on a second stream (see the module notes).  ``bias_on_probs`` adds
         the selection bias to the routing probability instead of the logit.
 
         ``balance`` turns on the per-step load-balancing updates that
@@ -221,14 +230,17 @@ class MoELayer:
         k, E = self.k, self.E
         mark = mark or (lambda name: None)
         main = stream if stream is not None else torch.cuda.current_stream(x.device)
-        shared_y = shared_done = None
-        if self.shared is not None and self.overlap_shared:
-            # the side stream starts once everything enqueued so far on the
-            # main stream (x, and the previous call's combine, which reads
-            # shared_y) is done
+        shared_y = shared_done = side = None
+        overlap = self.shared is not None and self.overlap_shared
+        early = overlap and T <= SHARED_STREAM_ROWS
+        if overlap:
             side = self._side.get(x.device)
             if side is None:
                 side = self._side[x.device] = torch.cuda.Stream(x.device)
+        if early:
+            # the side stream starts once everything enqueued so far on the
+            # main stream (x, and the previous call's combine, which reads
+            # shared_y) is done
             x_ready = torch.cuda.Event()
             x_ready.record(main)
             side.wait_event(x_ready)
@@ -266,12 +278,16 @@ class MoELayer:
         self._last_T = T
         self._last_counts = b["expert_count"]
         mark("permute")
-        if shared_y is not None:
+        if overlap:
             # the balance statistics need only the logits and the counts: on
-            # the side stream, after the shared experts, beside the routed GEMMs
+            # the side stream, after the shared experts, beside the routed
+            # GEMMs (the shared experts themselves start here unless they
+            # started with the call)
             routed = torch.cuda.Event()
             routed.record(main)
             side.wait_event(routed)
+            if not early:
+                shared_y = self._shared_forward(x, b, train, side)
             self._stats(b, k, side)
             shared_done = torch.cuda.Event()
             shared_done.record(side)

@@ -318,11 +318,13 @@ def test_layer_full_size(name):
     _say(f"[ok] full-size {name}: {errs}")
 
 
-def test_shared_overlap_matches_serial():
+@pytest.mark.parametrize("case", ["finegrained_small", "decode_small"])
+def test_shared_overlap_matches_serial(case):
     """The shared experts (and then the balance statistics) on a second stream
-    give the same bits as in line."""
-    inp = generate(SMALL["finegrained_small"])
-    _say("[case] shared experts overlapped vs in line")
+    give the same bits as in line: started after the routing (512 tokens,
+    tiled GEMMs) and with the call (64 tokens, weight stream)."""
+    inp = generate(SMALL[case])
+    _say(f"[case] shared experts overlapped vs in line, {case}")
     layer = build_layer(inp)
     x = to_device(inp["x"])
     outs = []
