@@ -543,6 +543,21 @@ struct EpiArgs {
   float* c_odd;   // kEpiRowPairs
 };
 
+// bf16 outputs leave the tile in 16-byte stores of eight columns.  For the
+// MFMA layout, lane l holds columns 8q + 4 (l / 32) + 0..3 of a 32-column
+// block (four bf16, `lo` for q, `hi` for q + 1, packed in pairs); exchanging
+// lane i's columns of q + 1 with lane i + 32's columns of q
+// (v_permlane32_swap: lanes 32..63 of the first operand trade places with
+// lanes 0..31 of the second) leaves lane i with columns 8q + 0..7 and lane
+// i + 32 with 8q + 8..15.  A compute unit issues stores at about one lane per
+// cycle whatever their width, so 16 bytes per lane halve the store phase of
+// a bf16 tile against 8.
+__device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
+  const auto a = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(lo[1], hi[1], false, false);
+  return u32x4{a[0], b[0], a[1], b[1]};
+}
+
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
 // waves form a WM x WN grid, each wave a (BM/WM) x (BN/WN) block of MFMA
 // tiles.  The LDS rings are laid out for kTileM rows of A whatever BM is.
@@ -853,26 +868,32 @@ __device__ __forceinline__ void gemm_tile(
     if constexpr (kFused) {
 #pragma unroll
       for (int j = 0; j < NT / 2; ++j) {
-        const int cb = tile.n0 + wn * (BN / (2 * WN)) + j * 32 + cq;
+        const int cb = tile.n0 + wn * (BN / (2 * WN)) + j * 32;  // the n-block's first column
+        u32x2 pk[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = cb + 8 * q;
-          if (col >= N) continue;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             v[e] = silu_f32(acc[i][j][4 * q + e]) * acc[i][j + NT / 2][4 * q + e];
-          u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(crow + col) = pk;
+          pk[q] = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           if constexpr (kEpi == kEpiSaveUV) {
             // (u, v) pairs of the four columns: one 16-byte store
+            const int col = cb + cq + 8 * q;
             const f32x16& ga = acc[i][j];
             const f32x16& ua = acc[i][j + NT / 2];
-            *reinterpret_cast<u32x4*>(ep.uv + static_cast<int64_t>(row) * (2 * N) + 2 * col) =
-                u32x4{pack_bf16x2(ga[4 * q], ua[4 * q]), pack_bf16x2(ga[4 * q + 1], ua[4 * q + 1]),
-                      pack_bf16x2(ga[4 * q + 2], ua[4 * q + 2]),
-                      pack_bf16x2(ga[4 * q + 3], ua[4 * q + 3])};
+            if (col < N)
+              *reinterpret_cast<u32x4*>(ep.uv + static_cast<int64_t>(row) * (2 * N) + 2 * col) =
+                  u32x4{pack_bf16x2(ga[4 * q], ua[4 * q]), pack_bf16x2(ga[4 * q + 1], ua[4 * q + 1]),
+                        pack_bf16x2(ga[4 * q + 2], ua[4 * q + 2]),
+                        pack_bf16x2(ga[4 * q + 3], ua[4 * q + 3])};
           }
+        }
+#pragma unroll
+        for (int qp = 0; qp < 4; qp += 2) {
+          const u32x4 o = pair_cols(pk[qp], pk[qp + 1]);
+          const int col = cb + 8 * qp + 2 * cq;
+          if (col < N) *reinterpret_cast<u32x4*>(crow + col) = o;
         }
       }
     } else if (part_out) {  // fp32 partial sums, [256][256] relative to (m0, n0)
@@ -892,16 +913,24 @@ __device__ __forceinline__ void gemm_tile(
     } else {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int cb = tile.n0 + wn * (BN / WN) + j * 32 + cq;
+        const int cb = tile.n0 + wn * (BN / WN) + j * 32;  // the n-block's first column
+        if constexpr (sizeof(OutT) == 2) {
+          u32x2 pk[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = cb + 8 * q;
-          if (col >= N) continue;
-          if constexpr (sizeof(OutT) == 2) {
-            u32x2 pk = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-            *reinterpret_cast<u32x2*>(crow + col) = pk;
-          } else {
+          for (int q = 0; q < 4; ++q)
+            pk[q] = u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                          pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+#pragma unroll
+          for (int qp = 0; qp < 4; qp += 2) {
+            const u32x4 o = pair_cols(pk[qp], pk[qp + 1]);
+            const int col = cb + 8 * qp + 2 * cq;
+            if (col < N) *reinterpret_cast<u32x4*>(crow + col) = o;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = cb + cq + 8 * q;
+            if (col >= N) continue;
             f32x4 o = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                        acc[i][j][4 * q + 3]};
             *reinterpret_cast<f32x4*>(crow + col) = o;
