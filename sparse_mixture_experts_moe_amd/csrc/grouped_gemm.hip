@@ -823,7 +823,8 @@ __device__ __forceinline__ void gemm_tile(
 #undef MOE_STEP
   // epilogue: acc[i][j] element 4q + e of lane l is C[row, col] with row =
   // m-block i row (l & 31) and col = n-block j column 8q + 4 (l >> 5) + e, so
-  // every lane stores runs of four columns (N % 64 == 0 keeps a run whole)
+  // every lane holds runs of four columns (bf16 outputs pair two runs into
+  // eight, pair_cols; N % 64 == 0 keeps a run whole)
   const int row0 = tile.m0 + wm * (BM / WM) + (lane & 31);
   const int cq = 4 * (lane >> 5);
   if constexpr (kEpi == kEpiSiluBwd) {
