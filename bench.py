@@ -310,12 +310,8 @@ def main_backward(args):
     x = to_device(inp["x"])
     dy = to_device(dy_h)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        layer.forward(x, train=True)
-        layer.backward(dy, c_bal, c_z)
-    torch.cuda.synchronize()
-
-    # timed region: events only around the expert backward call (the roofline)
+    # timed region: events only around the expert backward call (the roofline);
+    # events, collection and warmup ordered as in the forward measurement
     events = timing_events(torch, stream, 2 * args.steps + 2)
     ex_marks = []
 
@@ -328,6 +324,10 @@ def main_backward(args):
     start, end = events.pop(), events.pop()
     gc.collect()
     gc.disable()
+    for _ in range(args.warmup):
+        layer.forward(x, train=True)
+        layer.backward(dy, c_bal, c_z)
+    torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
         ex_marks.append([])
@@ -488,17 +488,16 @@ def measure_forward(args, cfg, ceil=None, extra=False):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     # Timed region: K steps with only the two events the roofline needs, around
     # the gate/up call (each event recorded on the stream delays the next
     # kernel by a few microseconds, so the per-phase events are kept out of
     # it).  Consecutive gate/up start events give the per-step durations.
-    # The events are created (recorded once) before the timed region and
-    # Python's garbage collector is paused inside it, so that neither event
-    # creation nor a collection stalls the host while it enqueues the steps.
+    # The events are created (recorded once) and Python's garbage collector
+    # runs before the warmup steps, and the collector stays paused until the
+    # timed steps end: the timed steps then follow the warmup with nothing
+    # but the synchronization between them (a GPU left idle for some 20 ms
+    # lowers its clock, and the first steps after such a gap run up to 35%
+    # slower), and no collection stalls the host while it enqueues them.
     events = timing_events(torch, stream, 2 * args.steps + 2)
     gu_marks = []
 
@@ -509,9 +508,11 @@ def measure_forward(args, cfg, ceil=None, extra=False):
             gu_marks[-1].append(ev)
 
     start, end = events.pop(), events.pop()
-    torch.cuda.synchronize()
     gc.collect()
     gc.disable()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
     start.record(stream)
     t_host = time.perf_counter()
     for _ in range(args.steps):
