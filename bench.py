@@ -111,20 +111,20 @@ def timing_events(torch, stream, n):
 
 def _median_ms(torch, fn, warmup=3, reps=7):
     """Median duration of fn() over reps launches (HIP events on the current
-    stream, one pair per launch), after warmup launches."""
+    stream, one pair per launch), after warmup launches.  All launches are
+    enqueued back to back and synchronized once at the end, so that the
+    device never idles between them (an idle device lowers its clock)."""
     import statistics
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
     for _ in range(warmup):
         fn()
-    times = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+    for a, b in evs:
         a.record()
         fn()
         b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b))
-    return statistics.median(times)
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in evs])
 
 
 def measured_ceilings(torch, gemm_shape):
@@ -678,15 +678,11 @@ def main():
     cfg = WORKLOADS[args.workload]
     out, inp, variant = measure_forward(args, cfg)
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        n_tok = args.cpu_tokens or {"tiny_f32": 64, "mixtral_bf16": 4096,
-                                    "finegrained_shared_bf16": 8192,
-                                    "capacity_balance_bf16": 8192, "decode_bf16": 64}[cfg.name]
-        out["cpu_baseline"] = cpu_baseline(inp, cfg, n_tok, variant=variant)
-    del inp
     # The other large workloads, each timed the same way (same K and W, inputs
     # resident in HBM before its timed region), one after the other in this
-    # process; the headline value above stays that of --workload.
+    # process; the headline value above stays that of --workload.  The CPU
+    # baseline runs after them, so that no workload's warmup follows the
+    # seconds the device would idle during it.
     extra = [] if (args.no_extra_workloads or args.variant or args.balance or
                    args.workload != "mixtral_bf16") else list(EXTRA_WORKLOADS)
     if extra:
@@ -702,6 +698,12 @@ def main():
             out["workloads"][name] = {key: o[key] for key in keep}
             print(f"# {name}: {o['value']:.4g} tokens/s, {o['ms_per_step']:.3f} ms per step, "
                   f"roofline frac {o['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or {"tiny_f32": 64, "mixtral_bf16": 4096,
+                                    "finegrained_shared_bf16": 8192,
+                                    "capacity_balance_bf16": 8192, "decode_bf16": 64}[cfg.name]
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, n_tok, variant=variant)
+    del inp
     print(json.dumps(out), flush=True)
 
 
