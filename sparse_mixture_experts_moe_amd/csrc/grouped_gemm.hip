@@ -1255,19 +1255,23 @@ __global__ __launch_bounds__(64) void skinny_kernel(
       if (row >= r1) continue;
       OutT* crow = C + static_cast<int64_t>(row) * N;
 #pragma unroll
-      for (int b = 0; b < (kFused ? NBW / 2 : NBW); ++b)
+      for (int b = 0; b < (kFused ? NBW / 2 : NBW); ++b) {
+        // four consecutive columns per lane, one store (N % 4 == 0 keeps the
+        // run whole; the stores issue about one lane per cycle, whatever
+        // their width)
+        const int n = n0 + 16 * b + (lane >> 4) * 4;
+        if (n >= N) continue;
+        float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = n0 + 16 * b + (lane >> 4) * 4 + j;
-          if (n >= N) continue;
-          float v = acc[b][tb][j];
-          if constexpr (kFused) v = silu_f32(v) * acc[b + NBW / 2][tb][j];
-          if constexpr (sizeof(OutT) == 2) {
-            crow[n] = f32_to_bf16_bits(v);
-          } else {
-            crow[n] = v;
-          }
+          v[j] = acc[b][tb][j];
+          if constexpr (kFused) v[j] = silu_f32(v[j]) * acc[b + NBW / 2][tb][j];
         }
+        if constexpr (sizeof(OutT) == 2)
+          *reinterpret_cast<u32x2*>(crow + n) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        else
+          *reinterpret_cast<f32x4*>(crow + n) = f32x4{v[0], v[1], v[2], v[3]};
+      }
     }
   }
 }  // slabs of this wave
