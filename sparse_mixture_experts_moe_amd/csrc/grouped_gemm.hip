@@ -669,9 +669,31 @@ __device__ __forceinline__ void gemm_tile(
   // the range read the zero row
   const int a_col = a_kcol < oa.a_cols ? a_kcol : oa.a_cols - 8;
   const int b_col = b_kcol < N ? b_kcol : N - 8;
-  auto rows_t_ptr = [&](const uint16_t* base, int ld, int col, int kr, int ks) {
-    const int row = oa.r0 + (ks0 + ks) * kBK + kr;
-    return row < oa.rend ? base + static_cast<int64_t>(row) * ld + col : oa.zero + col;
+  // Copy j's pointer at slice 0 and how far (in K rows) it may advance before
+  // its row passes rend, computed once per tile: a slice then costs one
+  // uniform 64-bit step and a compare per copy instead of a 64-bit multiply.
+  const uint16_t* at0[kAM == kOpRowsT ? AP : 1];
+  int alim[kAM == kOpRowsT ? AP : 1];
+  if constexpr (kAM == kOpRowsT) {
+#pragma unroll
+    for (int j = 0; j < AP; ++j) {
+      const int row = oa.r0 + ks0 * kBK + a_kr0 + 4 * j * AXR;
+      at0[j] = A + static_cast<int64_t>(row) * oa.lda + a_col;
+      alim[j] = oa.rend - row;
+    }
+  }
+  const uint16_t* bt0[kBM == kOpRowsT ? BP : 1];
+  int blim[kBM == kOpRowsT ? BP : 1];
+  if constexpr (kBM == kOpRowsT) {
+#pragma unroll
+    for (int j = 0; j < BP; ++j) {
+      const int row = oa.r0 + ks0 * kBK + b_kr0 + 4 * j * BXR;
+      bt0[j] = B0 + static_cast<int64_t>(row) * oa.ldb + b_col;
+      blim[j] = oa.rend - row;
+    }
+  }
+  auto rows_t_ptr = [&](const uint16_t* p0, int lim, int ld, int col, int ks) {
+    return ks * kBK < lim ? p0 + static_cast<int64_t>(ks * kBK) * ld : oa.zero + col;
   };
   auto slab_t_base = [&](int ks) { return bslab0 + static_cast<int64_t>(ks0 + ks) * kBK * N; };
   // copy K slice `ks` (clamped into range: surplus copies reload the last slice
@@ -683,7 +705,7 @@ __device__ __forceinline__ void gemm_tile(
     if constexpr (kAM == kOpRows)                                                    \
       dma_lds16(ap[(j)] + ksc_ * kBK, dst_);                                         \
     else                                                                             \
-      dma_lds16(rows_t_ptr(A, oa.lda, a_col, a_kr0 + 4 * (j) * AXR, ksc_), dst_);    \
+      dma_lds16(rows_t_ptr(at0[(j)], alim[(j)], oa.lda, a_col, ksc_), dst_);         \
   } while (0)
 #define MOE_COPY_B(j, stage, ks)                                                     \
   do {                                                                               \
@@ -698,7 +720,7 @@ __device__ __forceinline__ void gemm_tile(
       dma_lds16(bi_lane + (static_cast<int64_t>(ks0 + ksc_) * (kBK / 2) + 2 * (j) * BXR) * N, \
                 dst_);                                                               \
     else                                                                             \
-      dma_lds16(rows_t_ptr(B0, oa.ldb, b_col, b_kr0 + 4 * (j) * BXR, ksc_), dst_);   \
+      dma_lds16(rows_t_ptr(bt0[(j)], blim[(j)], oa.ldb, b_col, ksc_), dst_);         \
   } while (0)
 
   f32x16 acc[MT][NT];
