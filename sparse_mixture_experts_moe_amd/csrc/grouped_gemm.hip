@@ -558,6 +558,74 @@ __device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
   return u32x4{a[0], b[0], a[1], b[1]};
 }
 
+// fp32 weight-gradient tiles leave through LDS.  In the MFMA layout one store
+// of a wave covers 32 rows x 32 bytes, and a compute unit retires such stores
+// at about one lane per cycle: a 256 x 256 fp32 tile takes about 7 us even
+// when few compute units store at once.  Stores that each cover one whole
+// 1 KB row retire about 3.5 times as fast.  After the K loop the rings are
+// free, so the tile is written into a row-major LDS image (rounds of at most
+// 128 rows of 1 KB; 16-byte chunk c of image row r at chunk c ^ (r & 15), so
+// that the 16 rows of one write pass fall on distinct bank groups and the
+// chunks of a row, read by consecutive lanes, on all 64 banks) and copied out
+// one whole row per wave store.
+constexpr int kImgRows = 128;
+
+__device__ __forceinline__ int img_off(int r, int b) {  // image rows of 1 KB
+  return r * 1024 + ((((b >> 4) ^ (r & 15)) << 4) | (b & 15));
+}
+
+// acc[i][j] element 4q + e of lane l is C[row, col] with row = m-block i row
+// (l & 31) and col = n-block j column 8q + 4 (l >> 5) + e.  kEpiRowPairs:
+// even rows 2m go to row m of C, odd rows to row m of ep.c_odd.  Rows past
+// row_end and columns past N are not written.  The caller has passed a
+// barrier after the K loop (every wave has read its last slice and every copy
+// has landed).
+template <int BM, int WM, int WN, int BN, int kEpi, int MT, int NT>
+__device__ __forceinline__ void rows_out_f32(const f32x16 (&acc)[MT][NT], uint16_t* smem, int tid,
+                                             int lane, int wm, int wn, const Tile2& tile, int N,
+                                             float* C, const EpiArgs& ep) {
+  static_assert(BN * 4 == 1024, "image rows of 1 KB");
+  constexpr int RR = BM < kImgRows ? BM : kImgRows;  // image rows per round
+  constexpr int R = BM / RR;                          // rounds
+  constexpr int IPR = MT / R;                         // m-blocks of a wave per round
+  constexpr int RW = RR / WM;                         // image rows of a wave per round
+  static_assert(R * RR == BM && IPR * R == MT && RW == IPR * 32, "rounds of whole m-blocks");
+  static_assert(RR * 1024 <= (kRingA * kTileM + kRingB * 256) * kBK * 2, "image fits the rings");
+  char* img = reinterpret_cast<char*>(smem);
+  const int cq = 4 * (lane >> 5);
+#pragma unroll
+  for (int rho = 0; rho < R; ++rho) {
+    if (rho > 0) __syncthreads();  // the previous round's image has been read
+#pragma unroll
+    for (int ii = 0; ii < IPR; ++ii) {
+      const int i = rho * IPR + ii;
+      const int lr = wm * RW + ii * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lc = wn * (BN / WN) + j * 32 + cq + 8 * q;
+          *reinterpret_cast<f32x4*>(img + img_off(lr, 4 * lc)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+        }
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int it = 0; it < RR * 64 / kThreads; ++it) {
+      const int g = it * kThreads + tid;
+      const int lr = g >> 6, b = (g & 63) * 16;
+      const int row = tile.m0 + (lr / RW) * (BM / WM) + rho * RW + lr % RW;
+      const int col = tile.n0 + b / 4;
+      if (row >= tile.row_end || col >= N) continue;
+      float* dst = kEpi == kEpiRowPairs
+                       ? (row & 1 ? ep.c_odd : C) + static_cast<int64_t>(row >> 1) * N + col
+                       : C + static_cast<int64_t>(row) * N + col;
+      *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(img + img_off(lr, b));
+    }
+  }
+}
+
 // One output tile of BM rows (BM = 256, 128 or 64) and BN columns; the four
 // waves form a WM x WN grid, each wave a (BM/WM) x (BN/WN) block of MFMA
 // tiles.  The LDS rings are laid out for kTileM rows of A whatever BM is.
@@ -843,6 +911,13 @@ __device__ __forceinline__ void gemm_tile(
 #undef MOE_READ1
 #undef MOE_MFMA1
 #undef MOE_STEP
+  if constexpr (kAM == kOpRowsT) {  // weight gradients: fp32 tiles through the LDS image
+    static_assert(sizeof(OutT) == 4 && !kFused, "fp32 weight-gradient tiles");
+    __syncthreads();
+    rows_out_f32<BM, WM, WN, BN, kEpi>(acc, smem, tid, lane, wm, wn, tile, N,
+                                       reinterpret_cast<float*>(C), ep);
+    return;
+  }
   // epilogue: acc[i][j] element 4q + e of lane l is C[row, col] with row =
   // m-block i row (l & 31) and col = n-block j column 8q + 4 (l >> 5) + e, so
   // every lane holds runs of four columns (bf16 outputs pair two runs into
