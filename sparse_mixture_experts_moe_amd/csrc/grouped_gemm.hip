@@ -549,9 +549,9 @@ struct EpiArgs {
 // lane i's columns of q + 1 with lane i + 32's columns of q
 // (v_permlane32_swap: lanes 32..63 of the first operand trade places with
 // lanes 0..31 of the second) leaves lane i with columns 8q + 0..7 and lane
-// i + 32 with 8q + 8..15.  A compute unit issues stores at about one lane per
-// cycle whatever their width, so 16 bytes per lane halve the store phase of
-// a bf16 tile against 8.
+// i + 32 with 8q + 8..15.  In this layout a compute unit retires stores at
+// about one lane per cycle, 8 or 16 bytes alike, so 16 bytes per lane halve
+// the store phase of a bf16 tile against 8.
 __device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
   const auto a = __builtin_amdgcn_permlane32_swap(lo[0], hi[0], false, false);
   const auto b = __builtin_amdgcn_permlane32_swap(lo[1], hi[1], false, false);
