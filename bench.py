@@ -310,6 +310,14 @@ def main_backward(args):
     x = to_device(inp["x"])
     dy = to_device(dy_h)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib > 0:  # a copy of known size for counter runs, before the warmup
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     # timed region: events only around the expert backward call (the roofline);
     # events, collection and warmup ordered as in the forward measurement
     events = timing_events(torch, stream, 2 * args.steps + 2)
