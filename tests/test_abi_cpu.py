@@ -170,7 +170,7 @@ def test_expert_swiglu_rejects():
     assert call(ydt=5) == L.MOE_EINVAL
     # no rows: nothing to do
     assert call(mr=0, nws=L.moe_expert_swiglu_workspace(0, 128, 256, 8, L.MOE_BF16)) == L.MOE_OK
-    # the call without the row index (the survey's signature) checks the same way
+    # the plain call without the row index checks the same way
     assert C.moe_expert_swiglu(FAKE, L.MOE_BF16, 128, 256, 8, FAKE, 1000, FAKE, FAKE, FAKE, FAKE,
                                L.MOE_BF16, FAKE, ws - 1, None) == L.MOE_EWORKSPACE
     assert C.moe_expert_swiglu(FAKE, L.MOE_BF16, 100, 256, 8, FAKE, 1000, FAKE, FAKE, FAKE, FAKE,
@@ -191,7 +191,7 @@ def test_combine_and_stats_reject():
                                  None) == L.MOE_EUNSUPPORTED
     assert C.moe_balance_stats_z(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, None, FAKE, ws,
                                  None) == L.MOE_EINVAL
-    # without the z-loss output (the survey's signature)
+    # the plain call without the z-loss output
     assert C.moe_balance_stats(FAKE, FAKE, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, FAKE, ws - 1,
                                None) == L.MOE_EWORKSPACE
     assert C.moe_balance_stats(FAKE, None, 1000, 64, 2, 0.01, FAKE, FAKE, FAKE, FAKE, ws,
