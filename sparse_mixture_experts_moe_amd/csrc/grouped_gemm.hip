@@ -946,8 +946,9 @@ __device__ __forceinline__ void gemm_tile(
             const float u = __uint_as_float(uv[e] << 16);
             const float v = __uint_as_float(uv[e] & 0xFFFF0000u);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-u));  // 0 once exp overflows
-            const float dh = acc[i][j][4 * q + e];
-            o[e] = pack_bf16x2(dh * v * (sg * (1.0f + u * (1.0f - sg))), dh * (u * sg));
+            // dv = dh u sg, du = dh v sg (1 + u (1 - sg)), sharing dh sg
+            const float a = acc[i][j][4 * q + e] * sg;
+            o[e] = pack_bf16x2((a * v) * __builtin_fmaf(u, 1.0f - sg, 1.0f), a * u);
           }
           *reinterpret_cast<u32x4*>(drow + 2 * col) = u32x4{o[0], o[1], o[2], o[3]};
         }
