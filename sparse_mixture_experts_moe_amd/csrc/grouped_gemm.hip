@@ -562,7 +562,10 @@ __device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
 // of a wave covers 32 rows x 32 bytes, and a compute unit retires such stores
 // at about one lane per cycle: a 256 x 256 fp32 tile takes about 7 us even
 // when few compute units store at once.  Stores that each cover one whole
-// 1 KB row retire about 3.5 times as fast.  After the K loop the rings are
+// 1 KB row retire about 3.5 times as fast.  (When every compute unit stores
+// at once, as in lock-step weight-gradient tiles, the chip's write rate of
+// about 5.5 TB/s bounds both forms; the whole rows gain where the units
+// drift apart.)  After the K loop the rings are
 // free, so the tile is written into a row-major LDS image (rounds of at most
 // 128 rows of 1 KB; 16-byte chunk c of image row r at chunk c ^ (r & 15), so
 // that the 16 rows of one write pass fall on distinct bank groups and the
