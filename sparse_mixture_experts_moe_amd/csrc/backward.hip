@@ -373,49 +373,60 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
 }
 
 // dw[e, i] = sum_t dl[t, e] x[t, i]: workgroup (column tile of 256, expert
-// tile of 32, token chunk c) writes the chunk's partial sums to
-// part[c][e][i]; router_dw_reduce_kernel adds the chunks in order.
-constexpr int kDwExp = 32;
+// tile of kExp, token chunk c) writes the chunk's partial sums to
+// part[c][e][i]; router_dw_reduce_kernel adds the chunks in order.  The
+// expert tile is the smallest of 8, 16 or 32 that holds E (E > 32 takes
+// several tiles); each thread loads the x values of 8 tokens before their
+// FMAs, which still run token by token in order.
+constexpr int kDwExpMax = 32;
 constexpr int kDwSub = 64;  // tokens staged in LDS at a time
+constexpr int kDwLd = 8;    // x loads in flight per thread
 
-template <typename XT>
+template <typename XT, int kExp>
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
                                                         const XT* __restrict__ x, int64_t T, int d,
                                                         int E, int64_t chunk,
                                                         float* __restrict__ part) {
-  __shared__ __align__(16) float sdl[kDwSub][kDwExp];
+  __shared__ __align__(16) float sdl[kDwSub][kExp];
   const int col = blockIdx.x * 256 + threadIdx.x;
-  const int e0 = blockIdx.y * kDwExp;
+  const int e0 = blockIdx.y * kExp;
   const int64_t c0 = static_cast<int64_t>(blockIdx.z) * chunk;
   const int64_t c1 = c0 + chunk < T ? c0 + chunk : T;
-  float acc[kDwExp];
+  float acc[kExp];
 #pragma unroll
-  for (int u = 0; u < kDwExp; ++u) acc[u] = 0.0f;
+  for (int u = 0; u < kExp; ++u) acc[u] = 0.0f;
   for (int64_t s0 = c0; s0 < c1; s0 += kDwSub) {
     __syncthreads();
-    for (int i = threadIdx.x; i < kDwSub * kDwExp; i += 256) {
-      const int tt = i / kDwExp, u = i % kDwExp;
+    for (int i = threadIdx.x; i < kDwSub * kExp; i += 256) {
+      const int tt = i / kExp, u = i % kExp;
       const int64_t t = s0 + tt;
       sdl[tt][u] = (t < c1 && e0 + u < E) ? dl[t * E + e0 + u] : 0.0f;
     }
     __syncthreads();
     if (col < d) {
       const int n = static_cast<int>(c1 - s0 < kDwSub ? c1 - s0 : kDwSub);
-      for (int tt = 0; tt < n; ++tt) {
-        const float xv = load1(x + (s0 + tt) * d + col);
-        const f32x4* p = reinterpret_cast<const f32x4*>(&sdl[tt][0]);
+      for (int tb = 0; tb < n; tb += kDwLd) {
+        float xv[kDwLd];
 #pragma unroll
-        for (int q = 0; q < kDwExp / 4; ++q) {
-          const f32x4 a = p[q];
+        for (int z = 0; z < kDwLd; ++z)  // tokens past the staged ones load nothing
+          xv[z] = tb + z < n ? load1(x + (s0 + tb + z) * d + col) : 0.0f;
 #pragma unroll
-          for (int z = 0; z < 4; ++z) acc[4 * q + z] = fmaf(a[z], xv, acc[4 * q + z]);
+        for (int z = 0; z < kDwLd; ++z) {
+          if (tb + z >= n) break;
+          const f32x4* p = reinterpret_cast<const f32x4*>(&sdl[tb + z][0]);
+#pragma unroll
+          for (int q = 0; q < kExp / 4; ++q) {
+            const f32x4 a = p[q];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[4 * q + w] = fmaf(a[w], xv[z], acc[4 * q + w]);
+          }
         }
       }
     }
   }
   if (col >= d) return;
 #pragma unroll
-  for (int u = 0; u < kDwExp; ++u)
+  for (int u = 0; u < kExp; ++u)
     if (e0 + u < E) part[(static_cast<int64_t>(blockIdx.z) * E + e0 + u) * d + col] = acc[u];
 }
 
@@ -425,7 +436,8 @@ __global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __re
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.0f;
-  for (int c = 0; c < nchunk; ++c) s += part[c * n + i];
+#pragma unroll 8
+  for (int c = 0; c < nchunk; ++c) s += part[c * n + i];  // in chunk order
   dw[i] = s;
 }
 
@@ -447,8 +459,11 @@ __global__ __launch_bounds__(256) void router_db_kernel(const float* __restrict_
 }
 
 // token chunks of the dw partials: enough workgroups to cover the device
+int dw_exp_tile(int E) { return E <= 8 ? 8 : (E <= 16 ? 16 : kDwExpMax); }
+
 int dw_chunks(int64_t T, int d, int E) {
-  const int64_t tiles = static_cast<int64_t>((d + 255) / 256) * ((E + kDwExp - 1) / kDwExp);
+  const int et = dw_exp_tile(E);
+  const int64_t tiles = static_cast<int64_t>((d + 255) / 256) * ((E + et - 1) / et);
   int64_t c = (1024 + tiles - 1) / tiles;
   const int64_t cmax = (T + kDwSub - 1) / kDwSub;
   if (c > cmax) c = cmax;
@@ -469,8 +484,14 @@ hipError_t router_backward_typed(const void* x, const void* w, const float* dl, 
   if (dw) {
     const int nchunk = dw_chunks(T, d, E);
     const int64_t chunk = (T + nchunk - 1) / nchunk;
-    const dim3 grid((d + 255) / 256, (E + kDwExp - 1) / kDwExp, static_cast<unsigned>(nchunk));
-    router_dw_kernel<T_><<<grid, 256, 0, stream>>>(dl, xp, T, d, E, chunk, part);
+    const int et = dw_exp_tile(E);
+    const dim3 grid((d + 255) / 256, (E + et - 1) / et, static_cast<unsigned>(nchunk));
+    if (et == 8)
+      router_dw_kernel<T_, 8><<<grid, 256, 0, stream>>>(dl, xp, T, d, E, chunk, part);
+    else if (et == 16)
+      router_dw_kernel<T_, 16><<<grid, 256, 0, stream>>>(dl, xp, T, d, E, chunk, part);
+    else
+      router_dw_kernel<T_, kDwExpMax><<<grid, 256, 0, stream>>>(dl, xp, T, d, E, chunk, part);
     const int64_t n = static_cast<int64_t>(E) * d;
     router_dw_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
         part, nchunk, n, dw);
