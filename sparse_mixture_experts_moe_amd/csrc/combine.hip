@@ -15,9 +15,10 @@
 // experts that skip the FFN).
 //
 // HBM-bound: one workgroup per token, each lane handles 8 consecutive
-// columns per step (16-byte bf16 loads and stores); the rows of up to
-// kSlotBatch slots (and the shared row) are loaded together before they are
-// added in slot order, so a lane waits for memory once per batch.
+// columns per step (16-byte bf16 loads and stores); the rows of a batch of
+// slots (k rounded up to 1, 2, 4 or kSlotBatch; and the shared row) are
+// loaded together, unconditionally, before they are added in slot order, so
+// a lane waits for memory once per batch.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,7 +116,7 @@ __device__ __forceinline__ const YT* slot_row(const YT* y, const int32_t* pr, in
   return row >= 0 ? y + static_cast<int64_t>(row) * d : nullptr;
 }
 
-template <typename YT, typename OT, int BLOCK, bool kBypass = false>
+template <typename YT, typename OT, int BLOCK, int KB, bool kBypass = false>
 __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y,
                                                         const int32_t* __restrict__ pair_row,
                                                         const float* __restrict__ gate, int k,
@@ -129,21 +130,51 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y
     const int cw = gridDim.y == 1 ? d : BLOCK * 8;  // columns of this workgroup
     const int c0 = static_cast<int>(blockIdx.y) * cw;
     const int cend = min(d, c0 + cw);
+    // the first batch's source rows (the same for every lane and column); a
+    // slot without one (dropped, a zero expert, or past k) reads the batch's
+    // first row instead and contributes nothing, so that the batch's loads
+    // and the shared row's go out together before the first is used
+    const YT* src0[KB];
+    const YT* first0 = nullptr;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      src0[u] = u < k ? slot_row<YT, kBypass>(y, pr, u, t, k, d, bp) : nullptr;
+      if (!first0) first0 = src0[u];
+    }
     for (int c = c0 + threadIdx.x * 8; c < cend; c += BLOCK * 8) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      typename Vec8<YT>::Raw raw[KB];
       typename Vec8<YT>::Raw sh{};
+      if (first0) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) raw[u] = Vec8<YT>::load_raw((src0[u] ? src0[u] : first0) + c);
+      }
       if (shared) sh = Vec8<YT>::load_raw(shared + t * d + c);
-      for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
-        const YT* src[kSlotBatch];
-        typename Vec8<YT>::Raw raw[kSlotBatch];
+      if (first0) {
 #pragma unroll
-        for (int u = 0; u < kSlotBatch; ++u) {
-          src[u] = j0 + u < k ? slot_row<YT, kBypass>(y, pr, j0 + u, t, k, d, bp) : nullptr;
-          if (src[u]) raw[u] = Vec8<YT>::load_raw(src[u] + c);
+        for (int u = 0; u < KB; ++u) {
+          if (!src0[u]) continue;
+          const float gj = g ? g[u] : 1.0f;
+          float v[8];
+          Vec8<YT>::unpack(raw[u], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
         }
+      }
+      for (int j0 = KB; j0 < k; j0 += KB) {  // more than KB slots (k > kSlotBatch)
+        const YT* src[KB];
+        const YT* first = nullptr;
 #pragma unroll
-        for (int u = 0; u < kSlotBatch; ++u) {
-          if (!src[u]) continue;  // dropped, a zero expert, or past k: contributes nothing
+        for (int u = 0; u < KB; ++u) {
+          src[u] = j0 + u < k ? slot_row<YT, kBypass>(y, pr, j0 + u, t, k, d, bp) : nullptr;
+          if (!first) first = src[u];
+        }
+        if (!first) continue;
+#pragma unroll
+        for (int u = 0; u < KB; ++u) raw[u] = Vec8<YT>::load_raw((src[u] ? src[u] : first) + c);
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          if (!src[u]) continue;
           const float gj = g ? g[j0 + u] : 1.0f;
           float v[8];
           Vec8<YT>::unpack(raw[u], v);
@@ -177,6 +208,22 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(const YT* __restrict__ y
 // Enough workgroups for the device: whole rows per 256-thread workgroup when
 // there are many tokens; for a few tokens (decode), 64-thread workgroups on
 // 512-column chunks of a row.
+// Slots are batched by KB (k rounded up to 1, 2, 4 or kSlotBatch).
+template <typename YT, typename OT, int KB, bool kBypass>
+void launch_kb(const void* y, const int32_t* pr, const float* g, int64_t T, int k, int d,
+               const void* shared, void* out, const Bypass<YT>& bp, hipStream_t stream) {
+  if (T >= 1024 || (d & 7) != 0) {
+    combine_kernel<YT, OT, 256, KB, kBypass><<<dim3(static_cast<unsigned>(T), 1), 256, 0, stream>>>(
+        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
+        static_cast<OT*>(out), bp);
+  } else {
+    const unsigned chunks = static_cast<unsigned>((d + 511) / 512);
+    combine_kernel<YT, OT, 64, KB, kBypass><<<dim3(static_cast<unsigned>(T), chunks), 64, 0, stream>>>(
+        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
+        static_cast<OT*>(out), bp);
+  }
+}
+
 template <typename YT, typename OT, bool kBypass>
 hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_t T, int k, int d,
                         const void* shared, void* out, const BypassArgs* bpa, hipStream_t stream) {
@@ -184,16 +231,11 @@ hipError_t launch_typed(const void* y, const int32_t* pr, const float* g, int64_
   if (bpa)
     bp = Bypass<YT>{bpa->topk_idx, bpa->e_ffn, bpa->n_zero, bpa->n_copy, bpa->n_const,
                     static_cast<const YT*>(bpa->x), static_cast<const YT*>(bpa->const_rows)};
-  if (T >= 1024 || (d & 7) != 0) {
-    combine_kernel<YT, OT, 256, kBypass><<<dim3(static_cast<unsigned>(T), 1), 256, 0, stream>>>(
-        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
-        static_cast<OT*>(out), bp);
-  } else {
-    const unsigned chunks = static_cast<unsigned>((d + 511) / 512);
-    combine_kernel<YT, OT, 64, kBypass><<<dim3(static_cast<unsigned>(T), chunks), 64, 0, stream>>>(
-        static_cast<const YT*>(y), pr, g, k, d, static_cast<const YT*>(shared),
-        static_cast<OT*>(out), bp);
-  }
+  const int kb = k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : kSlotBatch));
+  if (kb == 1) launch_kb<YT, OT, 1, kBypass>(y, pr, g, T, k, d, shared, out, bp, stream);
+  else if (kb == 2) launch_kb<YT, OT, 2, kBypass>(y, pr, g, T, k, d, shared, out, bp, stream);
+  else if (kb == 4) launch_kb<YT, OT, 4, kBypass>(y, pr, g, T, k, d, shared, out, bp, stream);
+  else launch_kb<YT, OT, kSlotBatch, kBypass>(y, pr, g, T, k, d, shared, out, bp, stream);
   return hipGetLastError();
 }
 
