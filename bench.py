@@ -152,16 +152,22 @@ def measured_ceilings(torch, gemm_shape):
                   "16 in flight per lane; "
                   "median of 7 launches after 3"}
     if gemm_shape is not None:
-        M, K, N = gemm_shape
-        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
-        b = (torch.randn(K, N, device="cuda") * K ** -0.5).to(torch.bfloat16)
-        c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-        ms = _median_ms(torch, lambda: torch.matmul(a, b, out=c))
-        res["library_gemm"] = {"shape_mkn": [M, K, N], "tflops": 2.0 * M * K * N / (ms * 1e-3) / 1e12,
-                               "ms": ms}
-        del a, b, c
+        res["library_gemm"] = library_gemm(torch, gemm_shape)
     torch.cuda.synchronize()
     return res
+
+
+def library_gemm(torch, shape):
+    """The vendor library's dense bf16 GEMM (hipBLASLt through torch.matmul)
+    of shape [M, K, N]: median of 7 launches after 3."""
+    M, K, N = shape
+    a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    b = (torch.randn(K, N, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ms = _median_ms(torch, lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.synchronize()
+    return {"shape_mkn": [M, K, N], "tflops": 2.0 * M * K * N / (ms * 1e-3) / 1e12, "ms": ms}
 
 
 def cpu_threads():
@@ -593,9 +599,18 @@ def measure_forward(args, cfg, ceil=None, extra=False):
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs
     # recorded in profiles/ (scaled by a plain copy of known size), or null
     roof["traffic"] = None if variant else recorded_traffic(cfg.name)
+    # the vendor library's dense GEMM of the same FLOPs (one group of R_kept
+    # rows, no gather, no SiLU), timed right after the steps as the layer was,
+    # before the ceiling probes
+    lib = None
+    if roof["bound"] == "mfma" and cfg.dtype == "bf16" and R_kept > 0:
+        lib = library_gemm(torch, (R_kept, d, 2 * h))
+        roof["library_dense_gemm"] = lib
+        roof["vs_library_dense"] = achieved / lib["tflops"]
     if ceil is None:
-        ceil = measured_ceilings(torch, None if cfg.name.startswith("decode") or
-                                 cfg.dtype != "bf16" else (R_kept, d, 2 * h))
+        ceil = measured_ceilings(torch, None)
+        if lib is not None:
+            ceil["library_gemm"] = lib
     if roof["bound"] == "hbm":
         roof["measured_peak"] = ceil["hbm_read_gbs"]
     elif cfg.dtype == "bf16":
