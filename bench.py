@@ -619,6 +619,16 @@ def measure_forward(args, cfg, ceil=None, extra=False):
         roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
     roof["kernel"] = "moe_expert_gate_up (fused gate/up grouped GEMM + SiLU*mul)"
     roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": gu_ms}
+    if "gate_up" in phase_ms:
+        # the same call in the per-phase pass, where every call runs alone in
+        # line (in the timed steps a layer with shared experts runs them on a
+        # second stream, partly beside this call, whose duration then includes
+        # the compute units they hold); its opening event's few microseconds
+        # included
+        in_ms = phase_ms["gate_up"]
+        in_ach = (gu_bytes / (in_ms * 1e-3) / 1e9 if roof["bound"] == "hbm"
+                  else gu_flops / (in_ms * 1e-3) / 1e12)
+        roof["in_line"] = {"avg_ms": in_ms, "achieved": in_ach, "frac": in_ach / roof["peak"]}
 
     # algorithmic HBM bytes of the memory-bound phases (per call) and the rate
     # the phase achieved, against the 8 TB/s peak

@@ -298,6 +298,25 @@ moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int 
                                       void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
                                       void* stream);
 
+/* moe_expert_swiglu_cus: moe_expert_swiglu_gather whose tiled bf16 GEMMs run
+ * as persistent launches of at most max_cus workgroups (one per compute unit;
+ * rounded down to a multiple of 8, at least 8; max_cus <= 0 or at least the
+ * device's compute units: all of them), so that work enqueued on another
+ * stream at the same time keeps the other compute units.  A layer starts its
+ * shared experts this way on a second stream with the call, beside the
+ * routing, which then still finds free compute units.  Only the launch width
+ * changes: the tile order, its split among the XCDs and the split along K
+ * follow the device's compute-unit count, so y is bit-identical to
+ * moe_expert_swiglu_gather's.  The fp32 path and the few-row weight stream
+ * (groups averaging at most 64 rows) ignore max_cus.  Same source, arguments,
+ * limits and workspace as moe_expert_swiglu_gather. */
+moe_status_t moe_expert_swiglu_cus(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                   const int32_t* group_offset, int64_t max_rows,
+                                   const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                   const void* w_up, const void* w_down, void* y,
+                                   moe_dtype_t y_dt, void* ws, size_t ws_bytes, int max_cus,
+                                   void* stream);
+
 /* The two halves of moe_expert_swiglu_gather, for callers that keep the
  * hidden activation or time the two expert GEMMs apart (same sources, limits
  * and row-group semantics as moe_expert_swiglu_gather).

@@ -62,6 +62,8 @@ _SIGS = {
     "moe_expert_swiglu_gather": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i,
                                       _p,
                                _sz, _p]),
+    "moe_expert_swiglu_cus": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _i, _p,
+                                   _sz, _i, _p]),
     "moe_expert_group_workspace": (_sz, [_i]),
     "moe_expert_down_workspace": (_sz, [_i]),
     "moe_expert_gate_up": (_i, [_p, _i, _i, _i, _i, _p, _i64, _p, _i, _p, _p, _p, _p, _sz, _p]),
@@ -300,10 +302,12 @@ def moe_expert_swiglu_workspace(max_rows, d, h, G, dt) -> int:
 
 
 def moe_expert_swiglu(a, group_offset, max_rows, w_gate, w_up, w_down, *, a_rows=None,
-                      a_rows_div=1, y=None, y_dtype=None, ws=None, stream=None):
+                      a_rows_div=1, y=None, y_dtype=None, ws=None, stream=None, max_cus=0):
     """G SwiGLU experts over contiguous row groups: y[r] = SwiGLU_g(a_r), with
     a_r = a[a_rows[r] // a_rows_div] when ``a_rows`` is given
-    (moe_expert_swiglu_gather), else a[r] (moe_expert_swiglu)."""
+    (moe_expert_swiglu_gather), else a[r] (moe_expert_swiglu).  ``max_cus`` > 0
+    limits the tiled GEMMs' persistent launches to that many workgroups
+    (moe_expert_swiglu_cus; same results)."""
     G, h, d = w_gate.shape
     dt = _dt(a)
     dev = a.device
@@ -313,7 +317,12 @@ def moe_expert_swiglu(a, group_offset, max_rows, w_gate, w_up, w_down, *, a_rows
     if ws is None:
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _contig(a, group_offset, a_rows, w_gate, w_up, w_down, y, ws)
-    if a_rows is None:
+    if max_cus > 0:
+        _check(_L.moe_expert_swiglu_cus(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
+                                        _ptr(a_rows), a_rows_div if a_rows is not None else 1,
+                                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _dt(y),
+                                        _ptr(ws), ws.numel(), int(max_cus), _stream(stream)))
+    elif a_rows is None:
         _check(_L.moe_expert_swiglu(_ptr(a), dt, d, h, G, _ptr(group_offset), max_rows,
                                     _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _dt(y),
                                     _ptr(ws), ws.numel(), _stream(stream)))

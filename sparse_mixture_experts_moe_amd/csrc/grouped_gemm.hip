@@ -1497,6 +1497,16 @@ unsigned persistent_grid(int ncu) {
   return static_cast<unsigned>(ncu >= kXcds ? ncu / kXcds * kXcds : kXcds);
 }
 
+// The grid of a persistent launch limited to max_cus workgroups (<= 0: no
+// limit), so that a launch on another stream keeps the other compute units.
+// Only the grid shrinks: the tile table, the XCD runs and the split-K plan
+// still follow the device's compute-unit count, so every output tile is
+// computed exactly as by the unlimited launch (the persistent workgroups take
+// the same units in another interleaving).
+unsigned limited_grid(int ncu, int max_cus) {
+  return persistent_grid(max_cus > 0 && max_cus < ncu ? max_cus : ncu);
+}
+
 hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   const int ntn = (s.h + 127) / 128;
   const int ncu = compute_units();
@@ -1507,7 +1517,7 @@ hipError_t gate_up_bf16(const SwigluArgs& s, hipStream_t stream) {
   auto kern = s.uv ? gemm_bf16_kernel<true, uint16_t, kEpiSaveUV>
                    : gemm_bf16_kernel<true, uint16_t, kEpiNone>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-  kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
+  kern<<<limited_grid(ncu, s.max_cus), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.a), s.a_rows, s.a_div, static_cast<const uint16_t*>(s.w_gate),
       static_cast<const uint16_t*>(s.w_up), static_cast<int64_t>(s.h) * s.d, s.d, s.h,
       s.group_offset, s.mstart, s.G, ntn, static_cast<uint16_t*>(s.hid), nullptr, ncu, ep,
@@ -1523,7 +1533,7 @@ hipError_t down_bf16(const SwigluArgs& s, hipStream_t stream) {
                                             s.mstart, ncu, s.h / kBK, s.sk_ws != nullptr);
   auto kern = gemm_bf16_kernel<false, OutT, kEpiNone>;
   ensure_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kGemmLds));
-  kern<<<persistent_grid(ncu), kThreads, kGemmLds, stream>>>(
+  kern<<<limited_grid(ncu, s.max_cus), kThreads, kGemmLds, stream>>>(
       static_cast<const uint16_t*>(s.hid), nullptr, 1, static_cast<const uint16_t*>(s.w_down),
       nullptr, static_cast<int64_t>(s.d) * s.h, s.h, s.d, s.group_offset, s.mstart, s.G, ntn,
       static_cast<OutT*>(s.y), s.sk_ws, ncu, EpiArgs{}, OpArgs{});

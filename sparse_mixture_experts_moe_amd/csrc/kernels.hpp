@@ -50,6 +50,7 @@ struct SwigluArgs {
   void* uv;         // gate/up only: [max_rows, 2h] pre-activations kept (interleaved), or NULL
   int32_t* mstart;  // workspace: tile table (tile_table_bytes(G))
   float* sk_ws;     // workspace: split-K partial tiles (down projection), or NULL
+  int max_cus;      // bf16 tiled GEMMs: persistent workgroups at most (<= 0: one per compute unit)
 };
 // bytes of the split-K partial-tile workspace of the down projection
 size_t split_k_workspace_bytes();

@@ -408,11 +408,12 @@ size_t moe_expert_swiglu_workspace(int64_t max_rows, int d, int h, int G, moe_dt
          moe_expert_down_workspace(G);
 }
 
-moe_status_t moe_expert_gate_up(const void* a, moe_dtype_t dt, int d, int h, int G,
-                                const int32_t* group_offset, int64_t max_rows,
-                                const int32_t* a_rows, int a_rows_div, const void* w_gate,
-                                const void* w_up, void* hid, void* ws, size_t ws_bytes,
-                                void* stream) {
+namespace {
+
+moe_status_t gate_up_call(const void* a, moe_dtype_t dt, int d, int h, int G,
+                          const int32_t* group_offset, int64_t max_rows, const int32_t* a_rows,
+                          int a_rows_div, const void* w_gate, const void* w_up, void* hid,
+                          void* ws, size_t ws_bytes, int max_cus, void* stream) {
   moe_status_t st = check_experts("moe_expert_gate_up", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -436,12 +437,13 @@ moe_status_t moe_expert_gate_up(const void* a, moe_dtype_t dt, int d, int h, int
   s.hid = hid;
   s.mstart = static_cast<int32_t*>(ws);
   s.sk_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + tile_table_bytes(G));
+  s.max_cus = max_cus;
   return hip_status(moe::launch_gate_up(s, as_stream(stream)), "moe_expert_gate_up");
 }
 
-moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int G,
-                             const int32_t* group_offset, int64_t max_rows, const void* w_down,
-                             void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t down_call(const void* hid, moe_dtype_t dt, int d, int h, int G,
+                       const int32_t* group_offset, int64_t max_rows, const void* w_down, void* y,
+                       moe_dtype_t y_dt, void* ws, size_t ws_bytes, int max_cus, void* stream) {
   moe_status_t st = check_experts("moe_expert_down", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -463,15 +465,15 @@ moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int 
   s.hid = const_cast<void*>(hid);
   s.mstart = static_cast<int32_t*>(ws);
   s.sk_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + tile_table_bytes(G));
+  s.max_cus = max_cus;
   return hip_status(moe::launch_down(s, as_stream(stream)), "moe_expert_down");
 }
 
-moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int h, int G,
-                                      const int32_t* group_offset, int64_t max_rows,
-                                      const int32_t* a_rows, int a_rows_div,
-                                      const void* w_gate, const void* w_up, const void* w_down,
-                                      void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
-                                      void* stream) {
+moe_status_t swiglu_call(const void* a, moe_dtype_t dt, int d, int h, int G,
+                         const int32_t* group_offset, int64_t max_rows, const int32_t* a_rows,
+                         int a_rows_div, const void* w_gate, const void* w_up,
+                         const void* w_down, void* y, moe_dtype_t y_dt, void* ws,
+                         size_t ws_bytes, int max_cus, void* stream) {
   moe_status_t st = check_experts("moe_expert_swiglu", dt, d, h, G, max_rows, group_offset);
   if (st != MOE_OK) return st;
   if (max_rows == 0) return ok();  // no rows: buffers of zero size may be NULL
@@ -485,11 +487,49 @@ moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int 
   const size_t hid_bytes = align256(static_cast<size_t>(max_rows) * h * elem_bytes(dt));
   void* hid = ws;
   void* table = static_cast<char*>(ws) + hid_bytes;
-  st = moe_expert_gate_up(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate,
-                          w_up, hid, table, ws_bytes - hid_bytes, stream);
+  st = gate_up_call(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate, w_up,
+                    hid, table, ws_bytes - hid_bytes, max_cus, stream);
   if (st != MOE_OK) return st;
-  return moe_expert_down(hid, dt, d, h, G, group_offset, max_rows, w_down, y, y_dt, table,
-                         ws_bytes - hid_bytes, stream);
+  return down_call(hid, dt, d, h, G, group_offset, max_rows, w_down, y, y_dt, table,
+                   ws_bytes - hid_bytes, max_cus, stream);
+}
+
+}  // namespace
+
+moe_status_t moe_expert_gate_up(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                const int32_t* group_offset, int64_t max_rows,
+                                const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                const void* w_up, void* hid, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return gate_up_call(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate, w_up,
+                      hid, ws, ws_bytes, 0, stream);
+}
+
+moe_status_t moe_expert_down(const void* hid, moe_dtype_t dt, int d, int h, int G,
+                             const int32_t* group_offset, int64_t max_rows, const void* w_down,
+                             void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes, void* stream) {
+  return down_call(hid, dt, d, h, G, group_offset, max_rows, w_down, y, y_dt, ws, ws_bytes, 0,
+                   stream);
+}
+
+moe_status_t moe_expert_swiglu_gather(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                      const int32_t* group_offset, int64_t max_rows,
+                                      const int32_t* a_rows, int a_rows_div,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      void* y, moe_dtype_t y_dt, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return swiglu_call(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate, w_up,
+                     w_down, y, y_dt, ws, ws_bytes, 0, stream);
+}
+
+moe_status_t moe_expert_swiglu_cus(const void* a, moe_dtype_t dt, int d, int h, int G,
+                                   const int32_t* group_offset, int64_t max_rows,
+                                   const int32_t* a_rows, int a_rows_div, const void* w_gate,
+                                   const void* w_up, const void* w_down, void* y,
+                                   moe_dtype_t y_dt, void* ws, size_t ws_bytes, int max_cus,
+                                   void* stream) {
+  return swiglu_call(a, dt, d, h, G, group_offset, max_rows, a_rows, a_rows_div, w_gate, w_up,
+                     w_down, y, y_dt, ws, ws_bytes, max_cus, stream);
 }
 
 moe_status_t moe_expert_swiglu(const void* a, moe_dtype_t dt, int d, int h, int G,

@@ -4,12 +4,16 @@ balance statistics).  Buffers are allocated on the first call for a token
 count and reused afterwards, so repeated calls allocate nothing.
 
 The shared experts depend on x alone, so by default they run on a second
-stream (default priority) beside the routed path: from the start of the call
-when the library streams their weights for a few rows (at most 64 tokens),
-where they overlap the latency-bound routing; otherwise once the routing is
-done, since their tiled GEMM launches hold every compute unit until they end
-and the routing kernels would wait behind them.  The balance statistics
-follow them there once the routing is done, and the combine waits for both.
+stream (default priority) beside the routed path, from the start of the call,
+where they overlap the latency-bound routing.  When the library streams their
+weights (at most 64 tokens) its launches leave room for the routing kernels;
+their tiled GEMMs (more tokens) run as persistent launches on half of the
+compute units, so that the routing kernels, and then the routed experts'
+first workgroups, still find the other half free (a full-width launch would
+hold every compute unit until it ends).  In a training forward the shared
+experts start once the routing is done, at full width.  The balance
+statistics follow them on that stream once the routing is done, and the
+combine waits for both.
 
 The layer output excludes the residual ("Every parameter, every token",
 section "The gating network": the weighted sum is added back to the residual
@@ -32,6 +36,10 @@ from . import _lib
 # stream (few rows, every weight read once) rather than as MFMA tiles; the
 # shared experts are one group of T rows.
 SHARED_STREAM_ROWS = 64
+# Share of the compute units that the shared experts' tiled GEMMs take when
+# they start with the call (on the fine-grained layer, 8192 tokens and four
+# shared experts, half of them gave the fastest step of 96 to 256 workgroups).
+SHARED_CU_SHARE = 0.5
 
 
 class MoELayer:
@@ -205,12 +213,12 @@ class MoELayer:
         _lib.moe_balance_stats(b["logits"], b["expert_count"], k, self.alpha, f=b["f"], P=b["P"],
                                loss=b["loss"], zloss=b["zloss"], ws=b["stats_ws"], stream=stream)
 
-    def _shared_forward(self, x, b, train, stream):
+    def _shared_forward(self, x, b, train, stream, max_cus=0):
         sg, su, sd = self.shared
         T = x.shape[0]
         if not train:
             return _lib.moe_expert_swiglu(x, b["shared_off"], T, sg, su, sd, y=b["shared_y"],
-                                          ws=b["shared_ws"], stream=stream)
+                                          ws=b["shared_ws"], stream=stream, max_cus=max_cus)
         table = b["shared_ws"][-_lib.moe_expert_group_workspace(1):]
         _lib.moe_expert_gate_up_train(x, b["shared_off"], T, sg, su, hid=b["shared_hid"],
                                       uv=b["shared_uv"], ws=table, stream=stream)
@@ -232,7 +240,7 @@ class MoELayer:
         main = stream if stream is not None else torch.cuda.current_stream(x.device)
         shared_y = shared_done = side = None
         overlap = self.shared is not None and self.overlap_shared
-        early = overlap and T <= SHARED_STREAM_ROWS
+        early = overlap and (T <= SHARED_STREAM_ROWS or not train)
         if overlap:
             side = self._side.get(x.device)
             if side is None:
@@ -244,7 +252,11 @@ class MoELayer:
             x_ready = torch.cuda.Event()
             x_ready.record(main)
             side.wait_event(x_ready)
-            shared_y = self._shared_forward(x, b, train, side)
+            max_cus = 0
+            if T > SHARED_STREAM_ROWS:
+                ncu = torch.cuda.get_device_properties(x.device).multi_processor_count
+                max_cus = max(8, int(ncu * SHARED_CU_SHARE))
+            shared_y = self._shared_forward(x, b, train, side, max_cus=max_cus)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
                        bias_on_probs=self.bias_on_probs, relu=self.relu, ws=b["route_ws"],

@@ -228,6 +228,42 @@ def test_expert_swiglu_groups(sizes, d, h, dt):
             assert normwise(yn[r0:r1], ref) <= tol, (g, gather)
 
 
+@pytest.mark.parametrize("sizes,d,h", [
+    # bundled short tiles (88 and 77 remainder rows), a full-height remainder
+    # (232 rows) and a down projection whose 18 tiles are all split along K
+    ([600, 1000, 333], 512, 2048),
+    # one shared-expert-like group: 64 down tiles split in four along K
+    ([2048], 2048, 4096)])
+def test_swiglu_cus_matches_full_width(sizes, d, h):
+    """moe_expert_swiglu_cus, which narrows the persistent launches, against
+    moe_expert_swiglu_gather at full width: only the launch width differs, so
+    the same bits (and within tolerance of the oracle)."""
+    from sparse_mixture_experts_moe_amd import _lib
+    _say(f"[case] swiglu_cus groups={sizes} d={d} h={h}")
+    rng = np.random.default_rng(sum(sizes) + d)
+    G, R = len(sizes), int(sum(sizes))
+
+    def mk(shape, sc):
+        return torch.from_numpy((rng.standard_normal(shape) * sc).astype(np.float32)).cuda() \
+            .to(torch.bfloat16)
+    a = mk((R, d), 1.0)
+    wg, wu, wd = mk((G, h, d), d ** -0.5), mk((G, h, d), d ** -0.5), mk((G, d, h), h ** -0.5)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    goff = torch.from_numpy(off).cuda()
+    rows = torch.from_numpy(rng.permutation(R).astype(np.int32)).cuda()
+    want = _lib.moe_expert_swiglu(a, goff, R, wg, wu, wd, a_rows=rows, a_rows_div=1)
+    for max_cus in (8, 20, 128, -5, 1 << 20):
+        got = _lib.moe_expert_swiglu(a, goff, R, wg, wu, wd, a_rows=rows, a_rows_div=1,
+                                     max_cus=max_cus)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), max_cus
+    an, wgn, wun, wdn, yn, rn = (host(t) for t in (a, wg, wu, wd, want, rows))
+    for g in range(G):
+        r0, r1 = off[g], off[g + 1]
+        ref = oracle.swiglu(an[rn[r0:r1]], wgn[g], wun[g], wdn[g])
+        assert normwise(yn[r0:r1], ref) <= 2e-2, g
+
+
 # ---------------------------------------------------------------------------
 # moe_combine in isolation: oracle expert outputs in, oracle layer output out
 # ---------------------------------------------------------------------------
