@@ -175,6 +175,18 @@ def test_expert_swiglu_rejects():
                                L.MOE_BF16, FAKE, ws - 1, None) == L.MOE_EWORKSPACE
     assert C.moe_expert_swiglu(FAKE, L.MOE_BF16, 100, 256, 8, FAKE, 1000, FAKE, FAKE, FAKE, FAKE,
                                L.MOE_BF16, FAKE, ws, None) == L.MOE_EUNSUPPORTED
+    # the workgroup-limited call checks the same way, whatever the limit
+    for cus in (-1, 0, 8, 100, 1 << 20):
+        assert C.moe_expert_swiglu_cus(FAKE, L.MOE_BF16, 128, 256, 8, FAKE, 1000, None, 1, FAKE,
+                                       FAKE, FAKE, FAKE, L.MOE_BF16, FAKE, ws - 1, cus,
+                                       None) == L.MOE_EWORKSPACE
+        assert C.moe_expert_swiglu_cus(FAKE, L.MOE_BF16, 128, 256, 8, FAKE, 1000, FAKE, 0, FAKE,
+                                       FAKE, FAKE, FAKE, L.MOE_BF16, FAKE, ws, cus,
+                                       None) == L.MOE_EINVAL
+        assert C.moe_expert_swiglu_cus(FAKE, L.MOE_BF16, 128, 256, 8, FAKE, 0, None, 1, FAKE,
+                                       FAKE, FAKE, FAKE, L.MOE_BF16, FAKE,
+                                       L.moe_expert_swiglu_workspace(0, 128, 256, 8, L.MOE_BF16),
+                                       cus, None) == L.MOE_OK
 
 
 def test_combine_and_stats_reject():
