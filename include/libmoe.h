@@ -26,9 +26,11 @@
  *     Load Balancing Loss";
  *     "Every parameter, every token", section "A balance penalty").
  *
- * One layer call is five library calls on one stream:
+ * One layer call is five library calls:
  *   moe_route -> moe_permute -> moe_expert_swiglu (routed experts; and once
- *   more for the shared experts) -> moe_combine, plus moe_balance_stats.
+ *   more for the shared experts, which may run on a second stream from the
+ *   start of the call, on part of the chip: moe_expert_swiglu_cus) ->
+ *   moe_combine, plus moe_balance_stats.
  * The backward pass, the balancing updates (moe_balance_update,
  * moe_permute_budgets) and the routing variants (MOE_ROUTE_RELU: ReLU
  * routing; moe_combine_bypass: zero, copy and constant experts, "Zen MoDE:
@@ -40,7 +42,8 @@
  * General contract
  *   - Every pointer is a DEVICE pointer unless marked (host).  Buffers are
  *     owned by the caller; the library never allocates or frees memory and
- *     keeps no device state besides its code objects.
+ *     keeps no device state besides its code objects and the static scratch
+ *     array of moe_permute_noalloc.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *     default stream) and never synchronises.  Device-resident sizes (expert
  *     counts and offsets) stay on the device.
