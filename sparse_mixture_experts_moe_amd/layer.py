@@ -37,8 +37,10 @@ from . import _lib
 # shared experts are one group of T rows.
 SHARED_STREAM_ROWS = 64
 # Share of the compute units that the shared experts' tiled GEMMs take when
-# they start with the call (on the fine-grained layer, 8192 tokens and four
-# shared experts, half of them gave the fastest step of 96 to 256 workgroups).
+# they start with the call: half (on the fine-grained layer, 8192 tokens and
+# four shared experts against eight routed ones per token, half gave the
+# fastest step of 96 to 256 workgroups), or their share of the expert FLOPs
+# where that is larger, so that they do not end after the routed experts.
 SHARED_CU_SHARE = 0.5
 
 
@@ -255,7 +257,9 @@ class MoELayer:
             max_cus = 0
             if T > SHARED_STREAM_ROWS:
                 ncu = torch.cuda.get_device_properties(x.device).multi_processor_count
-                max_cus = max(8, int(ncu * SHARED_CU_SHARE))
+                hs = self.shared[0].shape[1]
+                share = max(SHARED_CU_SHARE, hs / (hs + self.k * self.h))
+                max_cus = max(8, int(ncu * share))
             shared_y = self._shared_forward(x, b, train, side, max_cus=max_cus)
         _lib.moe_route(x, self.w_router, k, self.logit_bias, self.select_bias,
                        logits=b["logits"], topk_idx=b["topk_idx"], topk_gate=b["topk_gate"],
