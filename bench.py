@@ -629,6 +629,11 @@ def measure_forward(args, cfg, ceil=None, extra=False):
         in_ach = (gu_bytes / (in_ms * 1e-3) / 1e9 if roof["bound"] == "hbm"
                   else gu_flops / (in_ms * 1e-3) / 1e12)
         roof["in_line"] = {"avg_ms": in_ms, "achieved": in_ach, "frac": in_ach / roof["peak"]}
+    if cfg.n_shared and layer.overlap_shared:
+        roof["timed_beside"] = ("the shared experts' launches on a second stream (from the start "
+                                "of the call; tiled ones on part of the compute units), so the "
+                                "timed duration includes the compute units they hold; in_line "
+                                "is the call alone")
 
     # algorithmic HBM bytes of the memory-bound phases (per call) and the rate
     # the phase achieved, against the 8 TB/s peak
